@@ -1,0 +1,405 @@
+"""Seeded synthetic inputs for block-sparse attention (shared by tests, bench and smoke).
+
+This module only draws inputs: sequence lengths, page tables, block
+selections and N(0,1) values. It contains none of the attention arithmetic
+and imports neither the oracle nor the GPU library.
+
+Five named workloads (sizes and pick rules in ``CONFIGS`` below):
+  tiny            1 seq, Tq=4, Hq=16, Hkv=1, L=512, page 64 (8 permuted pages),
+                  2 of 4 blocks per (token, kv head), non-causal, bf16
+  decode_gqa      64 seqs x 1 token, Hq=64, Hkv=8, L ~ U{8192..32768}, page 64,
+                  last block + 15 uniform picks, causal, bf16
+  prefill_shared  1 seq, Tq=L=16384, Hq=64, Hkv=8, page 128, top-k 16; chunks
+                  of 64 queries share 12 of 16 picks, diagonal block always
+                  picked, causal, bf16
+  varlen_mqa      16 seqs, Tq_s lognormal (median 256, sigma 1) clipped to
+                  [1, 2048], L = U{4096..131072} + Tq_s, Hq=32, Hkv=1, page 128,
+                  top-k 32 (diagonal + 31 uniform), causal, fp16
+  decode_fp8      256 seqs x 1 token, L=65536, Hq=64, Hkv=8, page 64, top-k 16
+                  uniform picks, K/V e4m3fn (clamp to +-448 then cast), q bf16
+
+Values are float32 N(0,1) draws converted with torch: bf16 / fp16 by
+round-to-nearest-even ``.to()``, e4m3fn by ``.clamp(-448, 448).to(...)``,
+the cast rule stated in the sglang pull request "Speed up MiniMax-M3 sparse
+attention on Hopper", section "Verification".
+
+Only the (physical page, KV head) slices that some pick can touch receive
+drawn values; the rest of the pool is filled on the device (NaN poison for
+correctness runs, zeros for timing). Rows of a sequence's last page beyond
+its used length are poisoned too when ``poison`` is set.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+BLOCK = 128
+HEAD_DIM = 128
+
+_POISON_BITS = {torch.bfloat16: 0x7FC0, torch.float16: 0x7E00, torch.float8_e4m3fn: 0x7F}
+
+CONFIGS = {
+    "tiny": dict(seed=1001),
+    "decode_gqa": dict(seed=1002),
+    "prefill_shared": dict(seed=1003),
+    "varlen_mqa": dict(seed=1004),
+    "decode_fp8": dict(seed=1005),
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    Hq: int
+    Hkv: int
+    page_size: int
+    topk: int
+    causal: bool
+    q_dtype: torch.dtype
+    kv_dtype: torch.dtype
+    cu_seqlens_q: np.ndarray     # [B+1] int64
+    used_kv_lens: np.ndarray     # [B] int32
+    block_tables: np.ndarray     # [B, max_pages] int32 (-1 = unused)
+    selected: np.ndarray         # [Tq, Hkv, topk] int32
+    num_pages: int
+    q: torch.Tensor              # [Tq, Hq, 128] cpu
+    slice_page: np.ndarray       # [n] physical page of each drawn slice
+    slice_head: np.ndarray       # [n] kv head of each drawn slice
+    k_vals: torch.Tensor         # [n, page_size, 128] cpu, kv_dtype
+    v_vals: torch.Tensor
+    poison: bool = True
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return int(self.used_kv_lens.shape[0])
+
+    @property
+    def Tq(self):
+        return int(self.q.shape[0])
+
+    @property
+    def G(self):
+        return self.Hq // self.Hkv
+
+
+# ----------------------------------------------------------------------------
+# value conversion
+# ----------------------------------------------------------------------------
+def to_dtype(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == torch.float8_e4m3fn:
+        return t.clamp(-448, 448).to(torch.float8_e4m3fn)
+    return t.to(dtype)
+
+
+def filled(shape, dtype: torch.dtype, poison: bool, device="cpu") -> torch.Tensor:
+    """A tensor of the given dtype filled with NaN poison or zeros."""
+    if dtype == torch.float8_e4m3fn:
+        raw = torch.full(shape, _POISON_BITS[dtype] if poison else 0, dtype=torch.uint8, device=device)
+        return raw.view(torch.float8_e4m3fn)
+    raw = torch.full(shape, _POISON_BITS[dtype] if poison else 0, dtype=torch.int16, device=device)
+    return raw.view(dtype)
+
+
+# ----------------------------------------------------------------------------
+# structure helpers
+# ----------------------------------------------------------------------------
+def _page_tables(rng, used, page_size, max_pages=None, extra_pages=0):
+    """Random permutation of every page the sequences need, handed out in order."""
+    npages = [(int(L) + page_size - 1) // page_size for L in used]
+    total = int(sum(npages)) + int(extra_pages)
+    perm = rng.permutation(total).astype(np.int32)
+    MP = max(npages) if max_pages is None else max_pages
+    MP = max(MP, 1)
+    bt = np.full((len(used), MP), -1, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(npages):
+        bt[s, :n] = perm[off:off + n]
+        off += n
+    return bt, total
+
+
+def _draw_slices(seed, wl_pages, wl_heads, page_size, kv_dtype, poison_rows=None):
+    n = len(wl_pages)
+    kr = np.random.default_rng([seed, 2])
+    vr = np.random.default_rng([seed, 3])
+    kv = []
+    for r in (kr, vr):
+        out = torch.empty((n, page_size, HEAD_DIM), dtype=kv_dtype)
+        step = max(1, (1 << 24) // (page_size * HEAD_DIM))
+        for i in range(0, n, step):
+            x = r.standard_normal((min(step, n - i), page_size, HEAD_DIM), dtype=np.float32)
+            out[i:i + x.shape[0]] = to_dtype(x, kv_dtype)
+        if poison_rows is not None:
+            bits = out.view(torch.uint8) if kv_dtype == torch.float8_e4m3fn else out.view(torch.int16)
+            for i, first_bad in poison_rows:
+                bits[i, first_bad:] = _POISON_BITS[kv_dtype]
+        kv.append(out)
+    return kv[0], kv[1]
+
+
+def needed_slices(block_tables, used, selected, cu, page_size, Hkv, all_pages=False, num_pages=0):
+    """(page, head) slices that some pick with 0 <= b < ceil(L/128) can read."""
+    if all_pages:
+        pages = np.repeat(np.arange(num_pages), Hkv)
+        heads = np.tile(np.arange(Hkv), num_pages)
+        return pages.astype(np.int64), heads.astype(np.int64)
+    keys = set()
+    Tq = selected.shape[0]
+    cu = np.asarray(cu)
+    for s in range(len(used)):
+        L = int(used[s])
+        nblk = (L + BLOCK - 1) // BLOCK
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        if q1 <= q0:
+            continue
+        picks = selected[q0:q1]  # [Tq_s, Hkv, K]
+        for g in range(Hkv):
+            for b in np.unique(picks[:, g, :]):
+                b = int(b)
+                if b < 0 or b >= nblk:
+                    continue
+                lp0 = (BLOCK * b) // page_size
+                lp1 = (min(BLOCK * b + BLOCK, L) + page_size - 1) // page_size
+                for lp in range(lp0, lp1):
+                    keys.add((int(block_tables[s, lp]), g))
+    arr = np.array(sorted(keys), dtype=np.int64).reshape(-1, 2)
+    return arr[:, 0], arr[:, 1]
+
+
+def _poison_rows(slice_page, block_tables, used, page_size):
+    """Slices holding rows at or beyond a sequence's used length."""
+    owner = {}
+    for s in range(block_tables.shape[0]):
+        L = int(used[s])
+        n = (L + page_size - 1) // page_size
+        if n and L % page_size:
+            owner[int(block_tables[s, n - 1])] = L % page_size
+    return [(i, owner[int(p)]) for i, p in enumerate(slice_page) if int(p) in owner]
+
+
+def assemble(name, seed, Hq, Hkv, page_size, topk, causal, q_dtype, kv_dtype, cu, used, bt,
+             selected, num_pages, poison=True, all_pages=False, meta=None):
+    cu = np.asarray(cu, dtype=np.int64)
+    used = np.asarray(used, dtype=np.int32)
+    selected = np.ascontiguousarray(selected, dtype=np.int32)
+    Tq = int(selected.shape[0])
+    qr = np.random.default_rng([seed, 1])
+    q = to_dtype(qr.standard_normal((Tq, Hq, HEAD_DIM), dtype=np.float32), q_dtype)
+    pages, heads = needed_slices(bt, used, selected, cu, page_size, Hkv, all_pages, num_pages)
+    prow = _poison_rows(pages, bt, used, page_size) if poison else None
+    kv, vv = _draw_slices(seed, pages, heads, page_size, kv_dtype, prow)
+    return Workload(name=name, seed=seed, Hq=Hq, Hkv=Hkv, page_size=page_size, topk=topk,
+                    causal=causal, q_dtype=q_dtype, kv_dtype=kv_dtype, cu_seqlens_q=cu,
+                    used_kv_lens=used, block_tables=bt, selected=selected, num_pages=num_pages,
+                    q=q, slice_page=pages, slice_head=heads, k_vals=kv, v_vals=vv,
+                    poison=poison, meta=dict(meta or {}))
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+def make_tiny(seed=1001, poison=True):
+    rng = np.random.default_rng(seed)
+    L, P = 512, 64
+    bt = rng.permutation(8).astype(np.int32)[None, :]
+    sel = np.stack([rng.permutation(4)[:2] for _ in range(4 * 1)]).reshape(4, 1, 2)
+    return assemble("tiny", seed, 16, 1, P, 2, False, torch.bfloat16, torch.bfloat16,
+                    [0, 4], [L], bt, sel, 8, poison, all_pages=True)
+
+
+def make_decode_gqa(seed=1002, poison=True, batch=64):
+    rng = np.random.default_rng(seed)
+    P, Hkv, K = 64, 8, 16
+    used = rng.integers(8192, 32768, size=batch, endpoint=True).astype(np.int32)
+    bt, NP = _page_tables(rng, used, P, max_pages=32768 // P)
+    sel = np.empty((batch, Hkv, K), dtype=np.int32)
+    for s in range(batch):
+        nblk = (int(used[s]) + BLOCK - 1) // BLOCK
+        for g in range(Hkv):
+            picks = np.concatenate([[nblk - 1], rng.choice(nblk - 1, size=K - 1, replace=False)])
+            sel[s, g] = rng.permutation(picks)
+    return assemble("decode_gqa", seed, 64, Hkv, P, K, True, torch.bfloat16, torch.bfloat16,
+                    np.arange(batch + 1), used, bt, sel, NP, poison)
+
+
+def make_prefill_shared(seed=1003, poison=True, seqlen=16384):
+    rng = np.random.default_rng(seed)
+    P, Hkv, K, C = 128, 8, 16, 64
+    T = L = seqlen
+    bt, NP = _page_tables(rng, [L], P)
+    sel = np.full((T, Hkv, K), -1, dtype=np.int32)
+    for c in range(T // C):
+        d = (C * c) // BLOCK
+        for g in range(Hkv):
+            shared = [d] + list(rng.choice(d, size=min(11, d), replace=False)) if d > 0 else [d]
+            rest = np.setdiff1d(np.arange(d + 1), shared)
+            for i in range(C):
+                t = C * c + i
+                n_extra = min(4, d + 1 - len(shared))
+                extra = list(rng.choice(rest, size=n_extra, replace=False)) if n_extra > 0 else []
+                picks = rng.permutation(np.array(shared + extra, dtype=np.int64))
+                sel[t, g, :picks.size] = picks
+    return assemble("prefill_shared", seed, 64, Hkv, P, K, True, torch.bfloat16, torch.bfloat16,
+                    [0, T], [L], bt, sel, NP, poison, all_pages=True)
+
+
+def make_varlen_mqa(seed=1004, poison=True, batch=16):
+    rng = np.random.default_rng(seed)
+    P, K = 128, 32
+    tq = np.clip(np.rint(np.exp(rng.normal(np.log(256.0), 1.0, size=batch))), 1, 2048).astype(np.int64)
+    prefix = rng.integers(4096, 131072, size=batch, endpoint=True)
+    used = (prefix + tq).astype(np.int32)
+    bt, NP = _page_tables(rng, used, P)
+    cu = np.concatenate([[0], np.cumsum(tq)]).astype(np.int64)
+    sel = np.empty((int(cu[-1]), 1, K), dtype=np.int32)
+    for s in range(batch):
+        for i in range(int(tq[s])):
+            pos = int(used[s]) - int(tq[s]) + i
+            d = pos // BLOCK
+            picks = np.concatenate([[d], rng.choice(d, size=K - 1, replace=False)])
+            sel[cu[s] + i, 0] = rng.permutation(picks)
+    return assemble("varlen_mqa", seed, 32, 1, P, K, True, torch.float16, torch.float16,
+                    cu, used, bt, sel, NP, poison, all_pages=True)
+
+
+def make_decode_fp8(seed=1005, poison=True, batch=256):
+    rng = np.random.default_rng(seed)
+    P, Hkv, K, L = 64, 8, 16, 65536
+    used = np.full(batch, L, dtype=np.int32)
+    bt, NP = _page_tables(rng, used, P)
+    nblk = L // BLOCK
+    sel = np.empty((batch, Hkv, K), dtype=np.int32)
+    for s in range(batch):
+        for g in range(Hkv):
+            sel[s, g] = rng.permutation(rng.choice(nblk, size=K, replace=False))
+    return assemble("decode_fp8", seed, 64, Hkv, P, K, True, torch.bfloat16, torch.float8_e4m3fn,
+                    np.arange(batch + 1), used, bt, sel, NP, poison)
+
+
+MAKERS = {
+    "tiny": make_tiny,
+    "decode_gqa": make_decode_gqa,
+    "prefill_shared": make_prefill_shared,
+    "varlen_mqa": make_varlen_mqa,
+    "decode_fp8": make_decode_fp8,
+}
+
+
+def make(name: str, seed: int | None = None, poison: bool = True, **kw) -> Workload:
+    if seed is None:
+        seed = CONFIGS[name]["seed"]
+    return MAKERS[name](seed=seed, poison=poison, **kw)
+
+
+# ----------------------------------------------------------------------------
+# small custom workloads for edge cases
+# ----------------------------------------------------------------------------
+def make_custom(seed, tq_per_seq, kv_lens, Hq, Hkv, page_size, topk, causal=False,
+                q_dtype=torch.bfloat16, kv_dtype=None, pick="random", pad_every=0,
+                extra_pages=3, poison=True, max_pages=None, shared_chunk=0, shared_picks=0):
+    """Small workloads with a chosen pick rule.
+
+    pick: "random"  -- up to topk distinct uniform picks among the blocks a
+                       token can see (all blocks when non-causal), -1 pads
+          "all"     -- every visible block (topk must be large enough)
+          "diag"    -- the token's own block plus random others
+          "oob"     -- like random, plus ids >= nblk and negative ids
+    pad_every: every n-th slot is forced to -1.
+    shared_chunk/shared_picks: tokens in chunks of shared_chunk share that
+                       many picks (drawn per chunk and kv head).
+    """
+    rng = np.random.default_rng(seed)
+    kv_dtype = kv_dtype or q_dtype
+    tq = np.asarray(tq_per_seq, dtype=np.int64)
+    used = np.asarray(kv_lens, dtype=np.int32)
+    bt, NP = _page_tables(rng, used, page_size, max_pages=max_pages, extra_pages=extra_pages)
+    cu = np.concatenate([[0], np.cumsum(tq)]).astype(np.int64)
+    Tq = int(cu[-1])
+    sel = np.full((Tq, Hkv, topk), -1, dtype=np.int32)
+    for s in range(len(tq)):
+        L = int(used[s])
+        nblk = (L + BLOCK - 1) // BLOCK
+        shared = {}
+        for i in range(int(tq[s])):
+            t = int(cu[s]) + i
+            pos = L - int(tq[s]) + i
+            vis = nblk if not causal else max(0, min(nblk, pos // BLOCK + 1)) if pos >= 0 else 0
+            for g in range(Hkv):
+                if pick == "all":
+                    picks = list(range(vis))[:topk]
+                else:
+                    base = []
+                    if shared_chunk and vis > 0:
+                        key = (i // shared_chunk, g)
+                        if key not in shared:
+                            shared[key] = list(rng.choice(vis, size=min(shared_picks, vis), replace=False))
+                        base = [b for b in shared[key] if b < vis]
+                    if pick == "diag" and vis > 0 and (vis - 1) not in base:
+                        base = [vis - 1] + base
+                    rest = np.setdiff1d(np.arange(vis), base)
+                    n = min(topk - len(base), rest.size)
+                    picks = base + (list(rng.choice(rest, size=n, replace=False)) if n > 0 else [])
+                    if pick == "oob":
+                        picks = picks[:max(0, topk - 2)] + [nblk + int(rng.integers(0, 5)), -int(rng.integers(1, 4))]
+                    picks = list(rng.permutation(np.array(picks, dtype=np.int64)))
+                row = np.full(topk, -1, dtype=np.int32)
+                row[:len(picks)] = picks[:topk]
+                if pad_every:
+                    row[::pad_every] = -1
+                sel[t, g] = row
+    return assemble("custom", seed, Hq, Hkv, page_size, topk, causal, q_dtype, kv_dtype,
+                    cu, used, bt, sel, NP, poison, all_pages=True)
+
+
+# ----------------------------------------------------------------------------
+# materialisation
+# ----------------------------------------------------------------------------
+def kv_pool(wl: Workload, device="cpu", poison=None):
+    """Full [num_pages, Hkv, P, 128] K and V pools on ``device``."""
+    poison = wl.poison if poison is None else poison
+    shape = (wl.num_pages, wl.Hkv, wl.page_size, HEAD_DIM)
+    k = filled(shape, wl.kv_dtype, poison, device)
+    v = filled(shape, wl.kv_dtype, poison, device)
+    if len(wl.slice_page):
+        pg = torch.from_numpy(wl.slice_page).to(device)
+        hd = torch.from_numpy(wl.slice_head).to(device)
+        _bits(k)[pg, hd] = _bits(wl.k_vals.to(device))
+        _bits(v)[pg, hd] = _bits(wl.v_vals.to(device))
+    return k, v
+
+
+def _bits(x: torch.Tensor) -> torch.Tensor:
+    return x.view(torch.uint8) if x.element_size() == 1 else x.view(torch.int16)
+
+
+def compact_cache(wl: Workload, heads=None):
+    """CPU cache holding only the drawn slices of ``heads``, with a remapped table.
+
+    Returns ``(k, v, block_tables)`` with ``k``/``v`` of shape
+    [n_pages, len(heads), P, 128]; table entries of pages that hold no drawn
+    slice become -1. Renumbering physical pages together with the table
+    leaves every result unchanged.
+    """
+    heads = list(range(wl.Hkv)) if heads is None else list(heads)
+    hsel = np.isin(wl.slice_head, heads)
+    pages = np.unique(wl.slice_page[hsel])
+    remap = np.full(wl.num_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(pages.size)
+    shape = (pages.size, len(heads), wl.page_size, HEAD_DIM)
+    k = filled(shape, wl.kv_dtype, True)
+    v = filled(shape, wl.kv_dtype, True)
+    hpos = np.full(wl.Hkv, -1, dtype=np.int64)
+    hpos[heads] = np.arange(len(heads))
+    idx = np.nonzero(hsel)[0]
+    pg = torch.from_numpy(remap[wl.slice_page[idx]])
+    hd = torch.from_numpy(hpos[wl.slice_head[idx]])
+    _bits(k)[pg, hd] = _bits(wl.k_vals[torch.from_numpy(idx)])
+    _bits(v)[pg, hd] = _bits(wl.v_vals[torch.from_numpy(idx)])
+    bt = wl.block_tables.astype(np.int64)
+    bt_c = np.where(bt >= 0, remap[np.clip(bt, 0, None)], -1).astype(np.int32)
+    return k, v, bt_c
