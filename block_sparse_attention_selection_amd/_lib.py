@@ -1,0 +1,207 @@
+"""ctypes binding of libmsa_kvouter.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libmsa_kvouter.so")
+
+MSA_BF16, MSA_FP16, MSA_FP8_E4M3FN, MSA_FP32, MSA_INT32, MSA_INT64, MSA_UINT8 = range(7)
+_DTYPES = {
+    torch.bfloat16: MSA_BF16,
+    torch.float16: MSA_FP16,
+    torch.float8_e4m3fn: MSA_FP8_E4M3FN,
+    torch.float32: MSA_FP32,
+    torch.int32: MSA_INT32,
+    torch.int64: MSA_INT64,
+    torch.uint8: MSA_UINT8,
+}
+ERRORS = {
+    -1: "invalid argument",
+    -2: "unsupported",
+    -3: "out of memory",
+    -4: "HIP error",
+    -5: "precondition violated",
+}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class MsaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+    ]
+
+
+class MsaIndexOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "slot_flag", "tok_chain", "tok_nres", "chain_blk", "row_off", "unit_off",
+        "ent", "slot_pos", "narrow_items", "wide_items", "counters")]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing; build it with "
+                "`python -m block_sparse_attention_selection_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        T = ctypes.POINTER(MsaTensor)
+        i32, vp = ctypes.c_int32, ctypes.c_void_p
+        lib.msa_kvouter_attention.restype = i32
+        lib.msa_kvouter_attention.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
+        lib.msa_build_index.restype = i32
+        lib.msa_build_index.argtypes = [T, T, T, i32, i32, i32, i32, i32, ctypes.POINTER(MsaIndexOut), vp]
+        lib.msa_widen_fp8.restype = i32
+        lib.msa_widen_fp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
+        lib.msa_validate_inputs.restype = i32
+        lib.msa_validate_inputs.argtypes = [T, T, T, T, T, T, T, i32, i32, vp]
+        lib.msa_last_error.restype = ctypes.c_char_p
+        lib.msa_last_error.argtypes = []
+        lib.msa_version.restype = ctypes.c_char_p
+        lib.msa_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def version() -> str:
+    return load().msa_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MsaError(rc, load().msa_last_error().decode())
+
+
+def describe(t: torch.Tensor | None):
+    """msa_tensor descriptor of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    d = MsaTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i, n in enumerate(t.shape):
+        d.shape[i] = n
+    return d
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _device_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kvouter_attention takes device (HIP) tensors only")
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
+                      page_size: int, causal: bool = False, return_lse: bool = False,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Block-sparse attention forward; see include/msa_kvouter.h for the contract.
+
+    Returns ``out`` ``[Tq, Hq, 128]`` (q's dtype), or ``(out, lse)`` with
+    ``lse`` fp32 ``[Hq, Tq]`` when ``return_lse`` is set.
+    """
+    lib = load()
+    _device_check(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, out, lse)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    ds = [describe(x) for x in (q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)]
+    do, dl = describe(out), describe(lse if return_lse or lse is not None else None)
+    with torch.cuda.device(q.device):
+        rc = lib.msa_kvouter_attention(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                       _ref(do), _ref(dl), _stream(q.device))
+    _check(rc)
+    return (out, lse) if return_lse else out
+
+
+def validate_inputs(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
+                    page_size: int, causal: bool = False):
+    """Synchronous check of the data-dependent preconditions; raises MsaError."""
+    lib = load()
+    _device_check(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)
+    ds = [describe(x) for x in (q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)]
+    with torch.cuda.device(q.device):
+        rc = lib.msa_validate_inputs(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                     _stream(q.device))
+    _check(rc)
+
+
+def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, causal: bool,
+                tile_tokens: int, unit_tokens: int):
+    """Run the index builder alone; returns its device arrays as a dict."""
+    lib = load()
+    _device_check(selected, cu_seqlens_q, used_kv_lens)
+    Tq, Hkv, K = selected.shape
+    dev = selected.device
+    NR = nb_max * Hkv
+    i32 = dict(dtype=torch.int32, device=dev)
+    res = dict(
+        slot_flag=torch.zeros(Tq * Hkv * K, dtype=torch.uint8, device=dev),
+        tok_chain=torch.zeros(Tq * Hkv, **i32),
+        tok_nres=torch.zeros(Tq * Hkv, **i32),
+        chain_blk=torch.full((Tq * Hkv * K,), -1, **i32),
+        row_off=torch.zeros(NR + 1, **i32),
+        unit_off=torch.zeros(NR + 1, **i32),
+        ent=torch.full((max(1, Tq * Hkv * K),), -1, **i32),
+        slot_pos=torch.zeros(Tq * Hkv * K, **i32),
+        narrow_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
+        wide_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
+        counters=torch.zeros(8, **i32),
+    )
+    o = MsaIndexOut(**{k: v.data_ptr() for k, v in res.items()})
+    ds = [describe(x) for x in (selected, cu_seqlens_q, used_kv_lens)]
+    with torch.cuda.device(dev):
+        rc = lib.msa_build_index(*[_ref(d) for d in ds], int(Hq), int(nb_max), int(bool(causal)),
+                                 int(tile_tokens), int(unit_tokens), ctypes.byref(o), _stream(dev))
+    _check(rc)
+    return res
+
+
+def widen_fp8(x: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """Widen e4m3fn values with the kernels' conversion (numel % 16 == 0)."""
+    lib = load()
+    _device_check(x)
+    x = x.contiguous()
+    out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = lib.msa_widen_fp8(x.data_ptr(), x.numel(), _DTYPES[out_dtype], out.data_ptr(), _stream(x.device))
+    _check(rc)
+    return out

@@ -1,0 +1,431 @@
+// msa_api.hip -- the C ABI: descriptor validation, workspace, launches.
+//
+// Entry points and their contracts are declared in include/msa_kvouter.h.
+// Validation reads shapes only (no device memory), runs before anything is
+// enqueued, and never falls back to another path.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/msa_kvouter.h"
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return MSA_OK;
+}
+
+const char* dname(int32_t d) {
+  switch (d) {
+    case MSA_BF16: return "bf16";
+    case MSA_FP16: return "fp16";
+    case MSA_FP8_E4M3FN: return "fp8_e4m3fn";
+    case MSA_FP32: return "fp32";
+    case MSA_INT32: return "int32";
+    case MSA_INT64: return "int64";
+    case MSA_UINT8: return "uint8";
+    default: return "unknown";
+  }
+}
+
+int64_t numel(const msa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+int32_t check_tensor(const msa_tensor* t, const char* name, int ndim, int32_t dtype, size_t align) {
+  if (!t) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: null descriptor", name);
+  if (t->ndim != ndim) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: expected rank %d, got %d", name, ndim, t->ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: negative extent", name);
+  if (dtype >= 0 && t->dtype != dtype)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "%s: expected %s, got %s", name, dname(dtype), dname(t->dtype));
+  if (numel(t) > 0) {
+    if (!t->data) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: null data pointer", name);
+    if (((uintptr_t)t->data) % align) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: data not %zu-byte aligned", name, align);
+  }
+  return MSA_OK;
+}
+
+struct Dims {
+  int Tq, Hq, Hkv, G, K, B, MP, P, NP, nb_max, NR, W, T, Tu;
+  int q_elem, kv_elem;
+};
+
+int elem_of(int32_t d) {
+  return d == MSA_BF16 ? msa::kElemBF16 : d == MSA_FP16 ? msa::kElemF16 : msa::kElemFP8;
+}
+
+int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, const msa_tensor* sel,
+                 const msa_tensor* bt, const msa_tensor* cu, const msa_tensor* used, int32_t page_size,
+                 int32_t causal, const msa_tensor* out, const msa_tensor* lse, Dims* d) {
+  int32_t rc;
+  if ((rc = check_tensor(q, "q", 3, -1, 16))) return rc;
+  if (q->dtype == MSA_FP8_E4M3FN) return fail(MSA_ERR_UNSUPPORTED, "q: fp8 queries are not supported");
+  if (q->dtype != MSA_BF16 && q->dtype != MSA_FP16)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q: dtype must be bf16 or fp16, got %s", dname(q->dtype));
+  if (q->shape[2] != 128) return fail(MSA_ERR_UNSUPPORTED, "q: head dim %lld, only 128 is supported", (long long)q->shape[2]);
+  if ((rc = check_tensor(k, "k_cache", 4, -1, 16))) return rc;
+  if ((rc = check_tensor(v, "v_cache", 4, -1, 16))) return rc;
+  if (k->dtype != q->dtype && k->dtype != MSA_FP8_E4M3FN)
+    return fail(k->dtype == MSA_BF16 || k->dtype == MSA_FP16 ? MSA_ERR_UNSUPPORTED : MSA_ERR_INVALID_ARGUMENT,
+                "k_cache: dtype %s must equal q's (%s) or be fp8_e4m3fn", dname(k->dtype), dname(q->dtype));
+  if (v->dtype != k->dtype) return fail(MSA_ERR_INVALID_ARGUMENT, "v_cache: dtype differs from k_cache");
+  for (int i = 0; i < 4; ++i)
+    if (v->shape[i] != k->shape[i]) return fail(MSA_ERR_INVALID_ARGUMENT, "v_cache: shape differs from k_cache");
+  if (k->shape[3] != 128) return fail(MSA_ERR_UNSUPPORTED, "k_cache: head dim %lld, only 128 is supported", (long long)k->shape[3]);
+  if (page_size != 64 && page_size != 128) return fail(MSA_ERR_UNSUPPORTED, "page_size %d: only 64 and 128 are supported", page_size);
+  if (k->shape[2] != page_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: page dimension %lld != page_size %d", (long long)k->shape[2], page_size);
+  if ((rc = check_tensor(sel, "selected", 3, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(bt, "block_tables", 2, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(cu, "cu_seqlens_q", 1, MSA_INT64, 8))) return rc;
+  if ((rc = check_tensor(used, "used_kv_lens", 1, MSA_INT32, 4))) return rc;
+  if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const int64_t Tq = q->shape[0], Hq = q->shape[1], Hkv = k->shape[1], NP = k->shape[0];
+  const int64_t B = bt->shape[0], MP = bt->shape[1];
+  if (Hkv <= 0 || Hq <= 0) return fail(MSA_ERR_INVALID_ARGUMENT, "head counts must be positive");
+  if (Hq % Hkv) return fail(MSA_ERR_INVALID_ARGUMENT, "Hq (%lld) is not a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (Hq / Hkv > 128) return fail(MSA_ERR_UNSUPPORTED, "Hq/Hkv = %lld exceeds 128", (long long)(Hq / Hkv));
+  if (sel->shape[0] != Tq || sel->shape[1] != Hkv)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "selected: shape must be [Tq=%lld, Hkv=%lld, topk]", (long long)Tq, (long long)Hkv);
+  const int64_t K = sel->shape[2];
+  if (K < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "selected: topk must be >= 1");
+  if (K > 64) return fail(MSA_ERR_UNSUPPORTED, "selected: topk %lld exceeds 64", (long long)K);
+  if (cu->shape[0] != B + 1) return fail(MSA_ERR_INVALID_ARGUMENT, "cu_seqlens_q: expected %lld entries", (long long)(B + 1));
+  if (used->shape[0] != B) return fail(MSA_ERR_INVALID_ARGUMENT, "used_kv_lens: expected %lld entries", (long long)B);
+  if (B > 0 && MP < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "block_tables: max_pages must be >= 1");
+  if (out) {
+    if ((rc = check_tensor(out, "out", 3, q->dtype, 16))) return rc;
+    if (out->shape[0] != Tq || out->shape[1] != Hq || out->shape[2] != 128)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "out: shape must equal q's");
+  }
+  if (lse) {
+    if ((rc = check_tensor(lse, "lse", 2, MSA_FP32, 4))) return rc;
+    if (lse->shape[0] != Hq || lse->shape[1] != Tq) return fail(MSA_ERR_INVALID_ARGUMENT, "lse: shape must be [Hq, Tq]");
+  }
+  // int32 indexing limits of the kernels
+  const int64_t nb_max = (MP * page_size + 127) / 128;
+  if (Tq * Hkv * K >= (1ll << 31) || Tq >= (1ll << 30) || B >= (1 << 30) || NP >= (1ll << 31) ||
+      nb_max * Hkv >= (1ll << 30) || MP * page_size >= (1ll << 31) || Tq * Hq >= (1ll << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit indices");
+  d->Tq = (int)Tq;
+  d->Hq = (int)Hq;
+  d->Hkv = (int)Hkv;
+  d->G = (int)(Hq / Hkv);
+  d->K = (int)K;
+  d->B = (int)B;
+  d->MP = (int)MP;
+  d->P = page_size;
+  d->NP = (int)NP;
+  d->nb_max = (int)std::max<int64_t>(nb_max, 1);
+  d->NR = d->nb_max * d->Hkv;
+  d->W = (int)((Tq + 31) / 32);
+  d->T = std::max(1, 128 / d->G);
+  d->Tu = d->T;
+  d->q_elem = elem_of(q->dtype);
+  d->kv_elem = elem_of(k->dtype);
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace: one growable device buffer per device
+// ---------------------------------------------------------------------------
+struct Carve {
+  size_t off = 0;
+  template <typename T>
+  T* take(char* base, size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// Lays the planning and partial arrays out in `base` (or only sizes them when
+// base is null). The counters and the bitmaps come first and are contiguous,
+// so one fill clears both. Returns the bytes used.
+size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials, size_t* clear_words) {
+  Carve c;
+  const size_t nslots = (size_t)d.Tq * d.Hkv * d.K;
+  const size_t TG = (size_t)d.Tq * d.Hkv;
+  const size_t words = (size_t)d.NR * d.W;
+  p->counters = c.take<int32_t>(base, 64);
+  p->bitmap = c.take<uint32_t>(base, words);
+  *clear_words = (c.off) / 4;  // counters .. end of bitmap
+  p->wordpre = c.take<uint32_t>(base, words);
+  p->slot_flag = c.take<uint8_t>(base, nslots);
+  p->tok_chain = c.take<int32_t>(base, TG);
+  p->tok_nres = c.take<int32_t>(base, TG);
+  p->chain_blk = c.take<int32_t>(base, nslots);
+  p->narrow_items = c.take<int32_t>(base, TG);
+  p->wide_items = c.take<int32_t>(base, TG);
+  p->row_cnt = c.take<int32_t>(base, d.NR);
+  p->row_off = c.take<int32_t>(base, (size_t)d.NR + 1);
+  p->unit_off = c.take<int32_t>(base, (size_t)d.NR + 1);
+  p->ent = c.take<int32_t>(base, nslots);
+  p->slot_pos = c.take<int32_t>(base, nslots);
+  if (with_partials) {
+    p->cpart = c.take<float>(base, (size_t)d.Tq * d.Hq * 128);
+    p->clse = c.take<float>(base, (size_t)d.Tq * d.Hq);
+    p->opart = c.take<float>(base, nslots * d.G * 128);
+    p->lpart = c.take<float>(base, nslots * d.G);
+  } else {
+    p->cpart = p->clse = p->opart = p->lpart = nullptr;
+  }
+  return c.off + 256;
+}
+
+struct DeviceWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  int num_cu = 0;
+};
+
+std::mutex g_ws_mutex;
+std::vector<DeviceWs> g_ws;
+
+int32_t get_workspace(size_t need, void** ptr, int* num_cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DeviceWs& w = g_ws[dev];
+  if (w.num_cu == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fail(MSA_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
+    w.num_cu = n;
+  }
+  if (w.bytes < need) {
+    if (w.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return fail(MSA_ERR_HIP, "hipDeviceSynchronize failed while growing the workspace");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    size_t alloc = std::max(need, (size_t)1 << 20);
+    if (hipMalloc(&w.ptr, alloc) != hipSuccess) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return fail(MSA_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", alloc);
+    }
+    w.bytes = alloc;
+  }
+  *ptr = w.ptr;
+  *num_cu = w.num_cu;
+  return MSA_OK;
+}
+
+void fill_inputs(msa::Params* p, const Dims& d, const msa_tensor* sel, const msa_tensor* bt,
+                 const msa_tensor* cu, const msa_tensor* used, int32_t causal) {
+  p->selected = (const int32_t*)sel->data;
+  p->block_tables = bt ? (const int32_t*)bt->data : nullptr;
+  p->cu = (const int64_t*)cu->data;
+  p->used = (const int32_t*)used->data;
+  p->Tq = d.Tq;
+  p->Hq = d.Hq;
+  p->Hkv = d.Hkv;
+  p->G = d.G;
+  p->K = d.K;
+  p->B = d.B;
+  p->MP = d.MP;
+  p->P = d.P;
+  p->NP = d.NP;
+  p->nb_max = d.nb_max;
+  p->NR = d.NR;
+  p->W = d.W;
+  p->T = d.T;
+  p->Tu = d.Tu;
+  p->causal = causal;
+  p->scale_log2 = (float)(1.0 / std::sqrt(128.0) * 1.4426950408889634);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_err.c_str(); }
+
+const char* msa_version(void) { return "msa_kvouter 0.1.0 (gfx950)"; }
+
+int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                              const msa_tensor* selected, const msa_tensor* block_tables,
+                              const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                              int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                              void* stream) {
+  Dims d;
+  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                        causal, out, lse, &d);
+  if (rc) return rc;
+  if (d.Tq == 0) return ok();
+  msa::Params p{};
+  size_t clear_words = 0;
+  const size_t need = layout(d, nullptr, &p, true, &clear_words);
+  void* ws = nullptr;
+  int num_cu = 0;
+  if ((rc = get_workspace(need, &ws, &num_cu))) return rc;
+  layout(d, (char*)ws, &p, true, &clear_words);
+  fill_inputs(&p, d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
+  p.q = q->data;
+  p.k = k_cache->data;
+  p.v = v_cache->data;
+  p.out = out->data;
+  p.lse = lse ? (float*)lse->data : nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = msa::launch_fill((uint32_t*)p.counters, (int64_t)clear_words, 0u, st);
+  if (e == hipSuccess) e = msa::launch_plan(p, st);
+  if (e == hipSuccess) e = msa::launch_forward(p, d.q_elem, d.kv_elem, num_cu, st);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
+                        const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max, int32_t causal,
+                        int32_t tile_tokens, int32_t unit_tokens, const msa_index_out* o, void* stream) {
+  int32_t rc;
+  if ((rc = check_tensor(selected, "selected", 3, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(cu_seqlens_q, "cu_seqlens_q", 1, MSA_INT64, 8))) return rc;
+  if ((rc = check_tensor(used_kv_lens, "used_kv_lens", 1, MSA_INT32, 4))) return rc;
+  if (!o) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  const int64_t Tq = selected->shape[0], Hkv = selected->shape[1], K = selected->shape[2];
+  const int64_t B = used_kv_lens->shape[0];
+  if (cu_seqlens_q->shape[0] != B + 1) return fail(MSA_ERR_INVALID_ARGUMENT, "cu_seqlens_q: expected B+1 entries");
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv) return fail(MSA_ERR_INVALID_ARGUMENT, "Hq must be a positive multiple of Hkv");
+  if (K < 1 || K > 64) return fail(MSA_ERR_UNSUPPORTED, "topk must be in [1, 64]");
+  if (tile_tokens < 0 || tile_tokens > 128) return fail(MSA_ERR_INVALID_ARGUMENT, "tile_tokens must be in [0, 128]");
+  if (unit_tokens < 1 || unit_tokens > 128) return fail(MSA_ERR_INVALID_ARGUMENT, "unit_tokens must be in [1, 128]");
+  if (nb_max < 1 || (int64_t)nb_max * Hkv >= (1ll << 30)) return fail(MSA_ERR_INVALID_ARGUMENT, "nb_max out of range");
+  if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (Tq * Hkv * K >= (1ll << 31)) return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit indices");
+  if (!o->slot_flag || !o->tok_chain || !o->tok_nres || !o->chain_blk || !o->row_off || !o->unit_off ||
+      !o->ent || !o->slot_pos || !o->narrow_items || !o->wide_items || !o->counters)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "msa_index_out: null buffer");
+  if (Tq == 0) return ok();
+  Dims d{};
+  d.Tq = (int)Tq;
+  d.Hq = Hq;
+  d.Hkv = (int)Hkv;
+  d.G = (int)(Hq / Hkv);
+  d.K = (int)K;
+  d.B = (int)B;
+  d.nb_max = nb_max;
+  d.NR = nb_max * (int)Hkv;
+  d.W = (int)((Tq + 31) / 32);
+  d.T = tile_tokens;
+  d.Tu = unit_tokens;
+  msa::Params p{};
+  size_t clear_words = 0;
+  const size_t need = layout(d, nullptr, &p, false, &clear_words);
+  void* ws = nullptr;
+  int num_cu = 0;
+  if ((rc = get_workspace(need, &ws, &num_cu))) return rc;
+  layout(d, (char*)ws, &p, false, &clear_words);
+  fill_inputs(&p, d, selected, nullptr, cu_seqlens_q, used_kv_lens, causal);
+  p.T = tile_tokens;
+  p.Tu = unit_tokens;
+  p.counters = o->counters;  // caller-visible counters; the bitmap stays internal
+  p.slot_flag = o->slot_flag;
+  p.tok_chain = o->tok_chain;
+  p.tok_nres = o->tok_nres;
+  p.chain_blk = o->chain_blk;
+  p.row_off = o->row_off;
+  p.unit_off = o->unit_off;
+  p.ent = o->ent;
+  p.slot_pos = o->slot_pos;
+  p.narrow_items = o->narrow_items;
+  p.wide_items = o->wide_items;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = msa::launch_fill((uint32_t*)o->counters, 8, 0u, st);
+  if (e == hipSuccess) e = msa::launch_fill(p.bitmap, (int64_t)d.NR * d.W, 0u, st);
+  if (e == hipSuccess) e = msa::launch_plan(p, st);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t msa_widen_fp8(const void* in, int64_t n, int32_t out_dtype, void* out, void* stream) {
+  if (!in || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "null buffer");
+  if (n < 0 || n % 16) return fail(MSA_ERR_INVALID_ARGUMENT, "n must be a non-negative multiple of 16");
+  if (((uintptr_t)in) % 16 || ((uintptr_t)out) % 16) return fail(MSA_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  if (out_dtype != MSA_BF16 && out_dtype != MSA_FP16) return fail(MSA_ERR_INVALID_ARGUMENT, "out dtype must be bf16 or fp16");
+  hipError_t e = msa::launch_widen_fp8(in, n, elem_of(out_dtype), out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                            const msa_tensor* selected, const msa_tensor* block_tables,
+                            const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens, int32_t page_size,
+                            int32_t causal, void* stream) {
+  Dims d;
+  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                        causal, nullptr, nullptr, &d);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return fail(MSA_ERR_HIP, "hipStreamSynchronize failed");
+  std::vector<int64_t> cu(d.B + 1);
+  std::vector<int32_t> used(d.B), bt((size_t)d.B * d.MP), sel((size_t)d.Tq * d.Hkv * d.K);
+  auto cp = [](void* dst, const void* src, size_t bytes) {
+    return bytes == 0 || hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost) == hipSuccess;
+  };
+  if (!cp(cu.data(), cu_seqlens_q->data, cu.size() * 8) || !cp(used.data(), used_kv_lens->data, used.size() * 4) ||
+      !cp(bt.data(), block_tables->data, bt.size() * 4) || !cp(sel.data(), selected->data, sel.size() * 4))
+    return fail(MSA_ERR_HIP, "device-to-host copy failed");
+  if (cu[0] != 0) return fail(MSA_ERR_PRECONDITION, "cu_seqlens_q[0] = %lld, expected 0", (long long)cu[0]);
+  for (int s = 0; s < d.B; ++s) {
+    if (cu[s + 1] < cu[s]) return fail(MSA_ERR_PRECONDITION, "cu_seqlens_q decreases at %d", s);
+    if (used[s] < 0 || (int64_t)used[s] > (int64_t)d.MP * d.P)
+      return fail(MSA_ERR_PRECONDITION, "used_kv_lens[%d] = %d outside [0, max_pages*page_size]", s, used[s]);
+    if (causal && used[s] < cu[s + 1] - cu[s])
+      return fail(MSA_ERR_PRECONDITION, "sequence %d: used_kv_lens < query count under causal masking", s);
+  }
+  if (cu[d.B] != d.Tq) return fail(MSA_ERR_PRECONDITION, "cu_seqlens_q[B] = %lld, expected Tq = %d", (long long)cu[d.B], d.Tq);
+  for (int s = 0; s < d.B; ++s) {
+    const int L = used[s];
+    const int nblk = (L + 127) / 128;
+    for (int64_t t = cu[s]; t < cu[s + 1]; ++t)
+      for (int g = 0; g < d.Hkv; ++g) {
+        const int32_t* row = &sel[((size_t)t * d.Hkv + g) * d.K];
+        for (int k = 0; k < d.K; ++k) {
+          const int b = row[k];
+          if (b < 0 || b >= nblk) continue;
+          for (int k2 = 0; k2 < k; ++k2)
+            if (row[k2] == b)
+              return fail(MSA_ERR_PRECONDITION, "selected[%lld, %d]: block %d appears twice", (long long)t, g, b);
+          const int lp0 = (128 * b) / d.P, lp1 = (std::min(128 * b + 128, L) + d.P - 1) / d.P;
+          for (int lp = lp0; lp < lp1; ++lp) {
+            const int page = bt[(size_t)s * d.MP + lp];
+            if (page < 0 || page >= d.NP)
+              return fail(MSA_ERR_PRECONDITION, "block_tables[%d, %d] = %d outside [0, %d)", s, lp, page, d.NP);
+          }
+        }
+      }
+  }
+  return ok();
+}
+
+}  // extern "C"

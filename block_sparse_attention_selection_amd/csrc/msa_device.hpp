@@ -1,0 +1,160 @@
+// msa_device.hpp -- device-side types and helpers for the gfx950 kernels.
+//
+// Register-fragment conventions used by every attention kernel (one wave,
+// 16 query rows, MFMA v_mfma_f32_16x16x32_{bf16,f16}):
+//   lane l = 16*q + c   (q = l / 16 in 0..3, c = l % 16)
+//   A operand: lane holds 8 consecutive k-values of row m = c
+//   B operand: lane holds 8 consecutive k-values of column n = c
+//   D (4 fp32): lane holds rows m = 4*q + r (r = 0..3) of column n = c
+// Both operands pair their k-values by (lane group q, element e), so any
+// assignment of the contraction index to (q, e) is valid as long as A and B
+// use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kD = 128;    // head dimension
+constexpr int kBlk = 128;  // tokens per selection block
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+struct fp8_e4m3_t {  // storage tag for e4m3fn caches
+  uint8_t bits;
+};
+
+// ---------------------------------------------------------------------------
+// MFMA on raw 128-bit fragments, by 16-bit element type
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16_t> {
+  static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<f16_t> {
+  static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fp32 -> 16-bit (round to nearest even) and packing
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ uint32_t to_bits16(float x);
+
+template <>
+__device__ __forceinline__ uint32_t to_bits16<bf16_t>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <>
+__device__ __forceinline__ uint32_t to_bits16<f16_t>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return to_bits16<T>(lo) | (to_bits16<T>(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float from_bits16(uint32_t b);
+
+template <>
+__device__ __forceinline__ float from_bits16<bf16_t>(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+template <>
+__device__ __forceinline__ float from_bits16<f16_t>(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// ---------------------------------------------------------------------------
+// e4m3fn -> 16-bit widening (exact: every e4m3fn value is a bf16 and an fp16
+// value). Uses the gfx950 scaled conversion with scale 1.0.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ uint32_t widen2_lo(uint32_t w);  // bytes 0,1 of w
+template <typename T>
+__device__ __forceinline__ uint32_t widen2_hi(uint32_t w);  // bytes 2,3 of w
+
+template <>
+__device__ __forceinline__ uint32_t widen2_lo<bf16_t>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen2_hi<bf16_t>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t widen2_lo<f16_t>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen2_hi<f16_t>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// 8 e4m3fn values (two dwords) -> 8 16-bit values (four dwords)
+template <typename T>
+__device__ __forceinline__ u32x4 widen8(u32x2 v) {
+  u32x4 r;
+  r[0] = widen2_lo<T>(v[0]);
+  r[1] = widen2_hi<T>(v[0]);
+  r[2] = widen2_lo<T>(v[1]);
+  r[3] = widen2_hi<T>(v[1]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions over the four lane groups holding one row
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// Owner sequence of token t: the largest s with cu[s] <= t, provided
+// t < cu[s+1]; -1 when t lies in no sequence. Stays inside cu[0..B].
+__device__ __forceinline__ int seq_of(const int64_t* __restrict__ cu, int B, int64_t t) {
+  if (B <= 0 || t < cu[0]) return -1;
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return (t < cu[lo + 1]) ? lo : -1;
+}
+
+}  // namespace msa

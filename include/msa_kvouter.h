@@ -1,0 +1,196 @@
+/*
+ * msa_kvouter.h -- C ABI of the MI355X (gfx950) MiniMax-M3 block-sparse
+ * attention forward pass.
+ *
+ * The operation (fw-ai/minimax-kernels README, intro and "Quick start"):
+ * every query token and query head attends only to the keys of the 128-token
+ * blocks that the token selected for the head's KV head. Keys and values are
+ * read through a logical-to-physical page table from a paged cache; the pass
+ * returns O [Tq, Hq, 128] and, on request, the fp32 log-sum-exp [Hq, Tq].
+ * The KV-outer organisation of that README's intro (load a selected block
+ * once, serve every query that picked it) is how the work is scheduled; the
+ * result is the plain definition:
+ *
+ *   for token t of sequence s (cu_seqlens_q[s] <= t < cu_seqlens_q[s+1]),
+ *   L = used_kv_lens[s], Tq_s = cu_seqlens_q[s+1] - cu_seqlens_q[s],
+ *   pos = L - Tq_s + (t - cu_seqlens_q[s])      (bottom-right causal alignment)
+ *   J = union over k of the positions j with 128*b <= j < min(128*b+128, L),
+ *       b = selected[t, g, k], 0 <= b < ceil(L/128), and j <= pos if causal
+ *   for head h with g = h / (Hq/Hkv):
+ *       x_j = <q[t,h,:], K_j> / sqrt(128)
+ *       lse[h,t] = ln sum_j exp(x_j),   out[t,h,:] = sum_j exp(x_j - lse) V_j
+ *   K_j = k_cache[block_tables[s, j / page_size], g, j % page_size, :]
+ *   An empty J gives out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point
+ *   - Buffers are dense, row-major, contiguous DEVICE memory owned by the
+ *     caller; the library keeps no pointer after it returns. Buffers must stay
+ *     valid until the stream reaches the enqueued work (usual HIP rules).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without waiting for it, except where stated.
+ *   - Return 0 (MSA_OK) or a negative MSA_ERR_* code; msa_last_error() then
+ *     holds a message (thread-local). Nothing throws or aborts across the
+ *     ABI, and an invalid call enqueues nothing. There is no fallback path:
+ *     an unsupported request is an error, never silently served another way
+ *     (the README's "Backends" section states the same rule for its backends).
+ */
+#ifndef MSA_KVOUTER_H
+#define MSA_KVOUTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum msa_dtype {
+  MSA_BF16 = 0,
+  MSA_FP16 = 1,
+  MSA_FP8_E4M3FN = 2, /* OCP e4m3fn: bias 7, max 448, NaN = 0x7F/0xFF, no inf */
+  MSA_FP32 = 3,
+  MSA_INT32 = 4,
+  MSA_INT64 = 5,
+  MSA_UINT8 = 6,
+} msa_dtype;
+
+enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, wrong rank/shape/dtype, misalignment */
+  MSA_ERR_UNSUPPORTED = -2,      /* head_dim != 128, fp8 q, page_size not 64/128, ... */
+  MSA_ERR_OUT_OF_MEMORY = -3,    /* workspace allocation failed */
+  MSA_ERR_HIP = -4,              /* a HIP runtime call failed (no device, launch error) */
+  MSA_ERR_PRECONDITION = -5,     /* msa_validate_inputs found a data violation */
+};
+
+/* Descriptor of a dense row-major device buffer. Unused shape entries are
+ * ignored. `data` must be 16-byte aligned for q, caches, out. */
+typedef struct msa_tensor {
+  void* data;
+  int32_t dtype; /* msa_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+} msa_tensor;
+
+/*
+ * msa_kvouter_attention -- the block-sparse attention forward pass.
+ *
+ *   q            [Tq, Hq, 128]                 bf16 or fp16
+ *   k_cache      [num_pages, Hkv, page_size, 128]  q's dtype, or fp8 e4m3fn
+ *   v_cache      same shape and dtype as k_cache
+ *   selected     [Tq, Hkv, topk] int32, logical 128-token block ids; ids
+ *                outside [0, ceil(L/128)) are ignored (use -1 as padding)
+ *   block_tables [B, max_pages] int32, physical page of each logical page
+ *   cu_seqlens_q [B + 1] int64, query offsets of the B sequences
+ *   used_kv_lens [B] int32, keys of each sequence
+ *   page_size    64 or 128
+ *   causal       0 or 1 (bottom-right aligned)
+ *   out          [Tq, Hq, 128] in q's dtype (written for every token)
+ *   lse          [Hq, Tq] fp32, natural log, softmax scale included; NULL
+ *                when not wanted
+ *   stream       hipStream_t
+ *
+ * Sizes: Hq % Hkv == 0, Hq/Hkv <= 128, 1 <= topk <= 64. The softmax scale is
+ * 1/sqrt(128). fp8 caches hold unscaled e4m3fn values (the cast rule of the
+ * sglang pull request "Speed up MiniMax-M3 sparse attention on Hopper",
+ * section "Verification"); they are widened exactly before use.
+ *
+ * Data-dependent preconditions that are not checked here (checking them
+ * needs a device-to-host copy; msa_validate_inputs reports them): ids in one
+ * (t, g) list are distinct, cu_seqlens_q is non-decreasing with
+ * cu_seqlens_q[0] == 0 and cu_seqlens_q[B] == Tq, used_kv_lens[s] <=
+ * max_pages*page_size, and every page id reached by a selected key lies in
+ * [0, num_pages). A violation gives unspecified output values but the
+ * kernels stay within the buffers given: a page id outside the pool is
+ * treated as holding no keys. Tokens outside every sequence get out = 0 and
+ * lse = -inf. Tq == 0 returns MSA_OK and enqueues nothing.
+ *
+ * Scratch memory: the library keeps one growable workspace per device
+ * (allocated with hipMalloc on first use or when a larger problem arrives;
+ * growing synchronises the device). Concurrent calls on different streams of
+ * the same device share that workspace and must not overlap in time.
+ */
+int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
+                              const msa_tensor* v_cache, const msa_tensor* selected,
+                              const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                              const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                              msa_tensor* out, msa_tensor* lse, void* stream);
+
+/*
+ * msa_build_index -- the selection inversion and work split, exposed so that
+ * their integer outputs can be compared bit for bit with a CPU reference.
+ * (The pages name an index builder and a load-balancing scheduler among the
+ * kernels of this pass: fw-ai/minimax-kernels README, "Tests".)
+ *
+ * Rules. Slot (t, g, k) holds b = selected[t, g, k]; it is valid when t lies
+ * in a sequence s, 0 <= b < min(ceil(L/128), nb_max), and 128*b <= pos(t)
+ * if causal. Each sequence's tokens are cut into tiles of `tile_tokens`
+ * consecutive tokens (the first is the tile's leader). A tile's chain, per
+ * KV head g, is the list of blocks that every token of the tile selected
+ * validly, ordered as in the leader's list; tile_tokens == 0 disables chains.
+ * Valid slots whose block is in the chain are "covered" (flag 1), other
+ * valid slots are "residual" (flag 2), invalid slots have flag 0. Residual
+ * slots are inverted into rows r = b*Hkv + g: row_off is the exclusive scan
+ * of the row counts, ent lists each row's slot ids in ascending order, and
+ * slot_pos[slot] is the slot's index in ent (-1 if not residual). unit_off is
+ * the exclusive scan of ceil(row count / unit_tokens). A chain is listed in
+ * narrow_items when tile_tokens_in_tile * (Hq/Hkv) <= 16, else in
+ * wide_items, as t_leader*Hkv + g; those two lists are in unspecified order.
+ *
+ * All output buffers are caller-owned device memory of the sizes given;
+ * chain_blk holds valid entries only at leader tokens (first tok_chain
+ * entries). counters[0..3] = residual slots, narrow items, wide items, units.
+ * Inputs as in msa_kvouter_attention; nb_max = ceil(max_pages*page_size/128).
+ */
+typedef struct msa_index_out {
+  uint8_t* slot_flag;    /* [Tq*Hkv*topk] */
+  int32_t* tok_chain;    /* [Tq*Hkv] chain length of the token's tile */
+  int32_t* tok_nres;     /* [Tq*Hkv] residual slots of (t, g) */
+  int32_t* chain_blk;    /* [Tq*Hkv*topk] */
+  int32_t* row_off;      /* [nb_max*Hkv + 1] */
+  int32_t* unit_off;     /* [nb_max*Hkv + 1] */
+  int32_t* ent;          /* [Tq*Hkv*topk] capacity */
+  int32_t* slot_pos;     /* [Tq*Hkv*topk] */
+  int32_t* narrow_items; /* [Tq*Hkv] capacity */
+  int32_t* wide_items;   /* [Tq*Hkv] capacity */
+  int32_t* counters;     /* [8] */
+} msa_index_out;
+
+int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
+                        const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max,
+                        int32_t causal, int32_t tile_tokens, int32_t unit_tokens,
+                        const msa_index_out* out, void* stream);
+
+/*
+ * msa_widen_fp8 -- widen n e4m3fn values (device bytes `in`) to bf16 or fp16
+ * (`out_dtype`, device buffer `out` of n elements) with the same conversion
+ * the attention kernels apply to fp8 caches. Exposed for exhaustive tests of
+ * that conversion. in and out must be 16-byte aligned; n % 16 == 0.
+ */
+int32_t msa_widen_fp8(const void* in, int64_t n, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * msa_validate_inputs -- synchronous check of the data-dependent
+ * preconditions of msa_kvouter_attention (copies the small index arrays to
+ * the host and waits for `stream`). Returns MSA_OK or MSA_ERR_PRECONDITION
+ * with the first violation in msa_last_error(); descriptor errors are
+ * reported as by msa_kvouter_attention.
+ */
+int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache,
+                            const msa_tensor* v_cache, const msa_tensor* selected,
+                            const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                            const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                            void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* Library version string. */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_KVOUTER_H */

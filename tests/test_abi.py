@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports what its header declares, and rejects
+bad descriptors on the host before touching any device memory (CPU only).
+
+Descriptor data pointers here are fake aligned addresses: every case must be
+refused by host validation, so nothing is ever dereferenced or launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_attention_selection_amd as msa
+from block_sparse_attention_selection_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_kvouter.h")
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(msa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["msa_kvouter_attention", "msa_build_index", "msa_widen_fp8", "msa_validate_inputs",
+              "msa_last_error", "msa_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(msa.lib_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_string():
+    assert "gfx950" in msa.version()
+
+
+def desc(shape, dtype, data=FAKE):
+    d = _lib.MsaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    for i, n in enumerate(shape):
+        d.shape[i] = n
+    return d
+
+
+def good(Tq=4, Hq=16, Hkv=2, NP=8, P=64, K=4, B=2, MP=4):
+    return dict(
+        q=desc([Tq, Hq, 128], msa.MSA_BF16),
+        k=desc([NP, Hkv, P, 128], msa.MSA_BF16),
+        v=desc([NP, Hkv, P, 128], msa.MSA_BF16),
+        sel=desc([Tq, Hkv, K], msa.MSA_INT32),
+        bt=desc([B, MP], msa.MSA_INT32),
+        cu=desc([B + 1], msa.MSA_INT64),
+        used=desc([B], msa.MSA_INT32),
+        out=desc([Tq, Hq, 128], msa.MSA_BF16),
+        lse=desc([Hq, Tq], msa.MSA_FP32),
+        P=P,
+        causal=1,
+    )
+
+
+def call(a):
+    lib = msa.load()
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    rc = lib.msa_kvouter_attention(r(a["q"]), r(a["k"]), r(a["v"]), r(a["sel"]), r(a["bt"]), r(a["cu"]),
+                                   r(a["used"]), a["P"], a["causal"], r(a["out"]), r(a["lse"]), None)
+    return rc, lib.msa_last_error().decode()
+
+
+INV, UNS = -1, -2
+BAD = [
+    ("q rank", lambda a: a.update(q=desc([4, 16], msa.MSA_BF16)), INV),
+    ("fp8 q", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_FP8_E4M3FN)), UNS),
+    ("fp32 q", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_FP32)), INV),
+    ("head dim 64", lambda a: a.update(q=desc([4, 16, 64], msa.MSA_BF16)), UNS),
+    ("page size 32", lambda a: a.update(P=32, k=desc([8, 2, 32, 128], msa.MSA_BF16),
+                                        v=desc([8, 2, 32, 128], msa.MSA_BF16)), UNS),
+    ("page dim mismatch", lambda a: a.update(P=128), INV),
+    ("kv dtype fp16 vs bf16 q", lambda a: a.update(k=desc([8, 2, 64, 128], msa.MSA_FP16),
+                                                   v=desc([8, 2, 64, 128], msa.MSA_FP16)), UNS),
+    ("v dtype differs", lambda a: a.update(v=desc([8, 2, 64, 128], msa.MSA_FP8_E4M3FN)), INV),
+    ("v shape differs", lambda a: a.update(v=desc([9, 2, 64, 128], msa.MSA_BF16)), INV),
+    ("Hq % Hkv", lambda a: a.update(k=desc([8, 3, 64, 128], msa.MSA_BF16), v=desc([8, 3, 64, 128], msa.MSA_BF16),
+                                    sel=desc([4, 3, 4], msa.MSA_INT32)), INV),
+    ("selected dtype", lambda a: a.update(sel=desc([4, 2, 4], msa.MSA_INT64)), INV),
+    ("selected shape", lambda a: a.update(sel=desc([5, 2, 4], msa.MSA_INT32)), INV),
+    ("topk 65", lambda a: a.update(sel=desc([4, 2, 65], msa.MSA_INT32)), UNS),
+    ("cu dtype", lambda a: a.update(cu=desc([3], msa.MSA_INT32)), INV),
+    ("cu length", lambda a: a.update(cu=desc([4], msa.MSA_INT64)), INV),
+    ("used length", lambda a: a.update(used=desc([3], msa.MSA_INT32)), INV),
+    ("out dtype", lambda a: a.update(out=desc([4, 16, 128], msa.MSA_FP16)), INV),
+    ("out shape", lambda a: a.update(out=desc([4, 8, 128], msa.MSA_BF16)), INV),
+    ("lse shape", lambda a: a.update(lse=desc([4, 16], msa.MSA_FP32)), INV),
+    ("lse dtype", lambda a: a.update(lse=desc([16, 4], msa.MSA_BF16)), INV),
+    ("null q data", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_BF16, data=0)), INV),
+    ("misaligned k", lambda a: a.update(k=desc([8, 2, 64, 128], msa.MSA_BF16, data=FAKE + 8)), INV),
+    ("causal 2", lambda a: a.update(causal=2), INV),
+    ("null q descriptor", lambda a: a.update(q=None), INV),
+    ("null out descriptor", lambda a: a.update(out=None), INV),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", BAD, ids=[b[0] for b in BAD])
+def test_invalid_descriptors_are_refused_on_the_host(name, mutate, code):
+    a = good()
+    mutate(a)
+    rc, msg = call(a)
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_empty_batch_enqueues_nothing():
+    a = good(Tq=0)
+    rc, msg = call(a)
+    assert rc == 0, msg
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_no_device_is_an_error_not_a_crash():
+    rc, msg = call(good())
+    assert rc == -4 and msg
+
+
+def test_widen_argument_checks():
+    lib = msa.load()
+    assert lib.msa_widen_fp8(None, 16, msa.MSA_BF16, FAKE, None) == INV
+    assert lib.msa_widen_fp8(FAKE, 15, msa.MSA_BF16, FAKE, None) == INV
+    assert lib.msa_widen_fp8(FAKE, 16, msa.MSA_FP32, FAKE, None) == INV
+    assert lib.msa_widen_fp8(FAKE + 4, 16, msa.MSA_BF16, FAKE, None) == INV
+
+
+def test_build_index_argument_checks():
+    lib = msa.load()
+    o = _lib.MsaIndexOut(*([FAKE] * 11))
+    sel = desc([4, 2, 4], msa.MSA_INT32)
+    cu = desc([3], msa.MSA_INT64)
+    used = desc([2], msa.MSA_INT32)
+    r = ctypes.byref
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 15, 4, 0, 8, 8, r(o), None) == INV   # Hq % Hkv
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 129, 8, r(o), None) == INV  # tile too big
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 0, r(o), None) == INV    # unit 0
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 0, 0, 8, 8, r(o), None) == INV    # nb_max 0
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, None, None) == INV

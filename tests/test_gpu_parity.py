@@ -1,0 +1,223 @@
+"""GPU parity: the HIP library against the fp64 oracle (MI355X only).
+
+Tolerances: |dO| <= 1e-2 + 1e-2*|O_ref| per element, |dLSE| <= 1e-3, rows
+without keys must give O = 0 and LSE = -inf on both sides. Index arrays are
+compared bit for bit with the integer CPU reference. Unselected pages and
+rows beyond each sequence's used length hold NaN poison throughout.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+from _helpers import all_pairs, compare, device_inputs, oracle_pairs, run_gpu, sample_pairs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_selection_amd as msa
+
+    msa.load()
+    yield
+
+
+def _full(wl):
+    out, lse = run_gpu(wl)
+    pairs = all_pairs(wl)
+    ref_o, ref_l = oracle_pairs(wl, pairs)
+    return compare(wl, out, lse, pairs, ref_o, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# fp8 widening: every e4m3fn code against the oracle's exact decoding
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_widen_fp8_every_code(out_dtype):
+    import block_sparse_attention_selection_amd as msa
+    import oracle
+
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(4)
+    x = codes.view(torch.float8_e4m3fn).cuda()
+    got = msa.widen_fp8(x, out_dtype).cpu().double().numpy()
+    want = oracle.decode(codes.view(torch.float8_e4m3fn))
+    finite = ~np.isnan(want)
+    assert np.array_equal(got[finite], want[finite])
+    assert np.isnan(got[~finite]).all()
+
+
+# ---------------------------------------------------------------------------
+# index builder: bit-exact against the CPU reference
+# ---------------------------------------------------------------------------
+def _index_case(wl, T, Tu):
+    import block_sparse_attention_selection_amd as msa
+    from oracle import index_ref
+
+    nb_max = (wl.block_tables.shape[1] * wl.page_size + 127) // 128
+    ref = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G)
+    got = msa.build_index(torch.from_numpy(wl.selected).cuda(), torch.from_numpy(wl.cu_seqlens_q).cuda(),
+                          torch.from_numpy(wl.used_kv_lens).cuda(), Hq=wl.Hq, nb_max=nb_max,
+                          causal=wl.causal, tile_tokens=T, unit_tokens=Tu)
+    got = {k: v.cpu().numpy() for k, v in got.items()}
+    Tq, Hkv, K = wl.selected.shape
+    assert np.array_equal(got["slot_flag"], ref.slot_flag.reshape(-1))
+    assert np.array_equal(got["tok_chain"], ref.tok_chain.reshape(-1))
+    assert np.array_equal(got["tok_nres"], ref.tok_nres.reshape(-1))
+    assert np.array_equal(got["row_off"], ref.row_off)
+    assert np.array_equal(got["unit_off"], ref.unit_off)
+    n = ref.ent.size
+    assert got["counters"][0] == n
+    assert np.array_equal(got["ent"][:n], ref.ent)
+    assert np.array_equal(got["slot_pos"], ref.slot_pos.reshape(-1))
+    assert got["counters"][3] == ref.unit_off[-1]
+    cb = got["chain_blk"].reshape(Tq, Hkv, K)
+    for (t0, g), ch in ref.chain_blk.items():
+        assert list(cb[t0, g, :len(ch)]) == ch, (t0, g)
+    nn, nw = got["counters"][1], got["counters"][2]
+    assert set(got["narrow_items"][:nn].tolist()) == ref.narrow_items
+    assert set(got["wide_items"][:nw].tolist()) == ref.wide_items
+
+
+@pytest.mark.parametrize("T,Tu", [(0, 3), (1, 2), (2, 2), (3, 4), (16, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_index_builder_bitexact_custom(T, Tu, causal):
+    wl = W.make_custom(300 + T, [3, 5, 1, 0, 40, 7], [300, 700, 129, 50, 5200, 900], 16, 2, 64, topk=6,
+                       causal=causal, pick="oob", shared_chunk=8, shared_picks=3, pad_every=5)
+    _index_case(wl, T, Tu)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_gqa", "varlen_mqa"])
+def test_index_builder_bitexact_named(name):
+    wl = W.make(name)
+    T = max(1, 128 // wl.G)
+    _index_case(wl, T, T)
+
+
+def test_index_builder_bitexact_prefill_shared():
+    wl = W.make("prefill_shared")
+    _index_case(wl, 16, 16)
+
+
+# ---------------------------------------------------------------------------
+# attention parity
+# ---------------------------------------------------------------------------
+def test_parity_tiny():
+    _full(W.make("tiny"))
+
+
+def test_parity_quickstart_shape():
+    # the README quick-start call: 1 query, 16 heads, 4 pages of 64, both blocks
+    wl = W.make_custom(7, [1], [256], 16, 1, 64, topk=2, causal=False, pick="all", extra_pages=0)
+    _full(wl)
+
+
+EDGE = [
+    # (tq_per_seq, kv_lens, Hq, Hkv, P, topk, causal, pick, dtypes)
+    ([1, 1, 1], [1, 129, 640], 8, 1, 64, 4, True, "random", None),            # L=1, partial blocks
+    ([3, 0, 5, 2], [300, 77, 900, 2], 8, 2, 64, 4, True, "diag", None),          # empty sequence
+    ([6], [3], 4, 1, 64, 2, True, "all", None),                                  # Tq_s > L: keyless rows
+    ([4, 4], [1000, 257], 16, 1, 128, 5, False, "oob", None),                    # pads and out-of-range ids
+    ([33, 17], [2000, 700], 32, 1, 128, 8, True, "diag", None),                  # MQA G=32
+    ([20, 9], [1500, 600], 4, 4, 64, 6, True, "random", None),                   # MHA G=1
+    ([40], [4000], 8, 2, 128, 8, True, "random", None),                          # shared chunks below
+    ([5, 3], [700, 350], 8, 2, 64, 4, True, "random", (torch.float16, torch.float16)),
+    ([5, 3], [700, 350], 8, 2, 64, 4, True, "random", (torch.bfloat16, torch.float8_e4m3fn)),
+    ([5, 3], [700, 350], 8, 2, 128, 4, False, "random", (torch.float16, torch.float8_e4m3fn)),
+    ([2, 1], [64, 190], 64, 8, 64, 3, True, "all", None),                        # G=8, small
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_parity_edge_cases(case):
+    tq, lens, Hq, Hkv, P, K, causal, pick, dt = EDGE[case]
+    qd, kvd = dt if dt else (torch.bfloat16, None)
+    wl = W.make_custom(500 + case, tq, lens, Hq, Hkv, P, topk=K, causal=causal, pick=pick,
+                       q_dtype=qd, kv_dtype=kvd, shared_chunk=16 if case == 6 else 0,
+                       shared_picks=5 if case == 6 else 0, pad_every=7 if pick == "oob" else 0)
+    _full(wl)
+
+
+def test_parity_shared_chunks_with_residuals():
+    # tiles with long chains plus residual picks (the prefill pattern at small size)
+    wl = W.make_custom(611, [64, 48], [4096, 3000], 16, 2, 128, topk=10, causal=True, pick="diag",
+                       shared_chunk=16, shared_picks=6)
+    _full(wl)
+
+
+def test_parity_decode_gqa():
+    _full(W.make("decode_gqa"))
+
+
+def test_parity_decode_fp8_sampled():
+    wl = W.make("decode_fp8")
+    out, lse = run_gpu(wl)
+    pairs = sample_pairs(wl, 96)
+    ref_o, ref_l = oracle_pairs(wl, pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+
+
+def test_parity_prefill_shared_sampled():
+    wl = W.make("prefill_shared")
+    out, lse = run_gpu(wl)
+    pairs = sample_pairs(wl, 128)
+    ref_o, ref_l = oracle_pairs(wl, pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+    assert not torch.isnan(out.float()).any()
+
+
+def test_parity_varlen_mqa_sampled():
+    wl = W.make("varlen_mqa")
+    out, lse = run_gpu(wl)
+    pairs = sample_pairs(wl, 128)
+    ref_o, ref_l = oracle_pairs(wl, pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+    assert not torch.isnan(out.float()).any()
+
+
+# ---------------------------------------------------------------------------
+# properties
+# ---------------------------------------------------------------------------
+def test_deterministic_bits():
+    wl = W.make_custom(701, [24, 8, 1], [3000, 900, 5000], 16, 2, 64, topk=8, causal=True,
+                       pick="diag", shared_chunk=8, shared_picks=4)
+    inputs = device_inputs(wl)
+    o1, l1 = run_gpu(wl, inputs)
+    o2, l2 = run_gpu(wl, inputs)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_tq_zero_is_a_no_op():
+    import block_sparse_attention_selection_amd as msa
+
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((2, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    out = msa.kvouter_attention(q, k, k, torch.empty((0, 1, 4), dtype=torch.int32, device="cuda"),
+                                torch.zeros((1, 2), dtype=torch.int32, device="cuda"),
+                                cu_seqlens_q=torch.zeros(2, dtype=torch.int64, device="cuda"),
+                                used_kv_lens=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                                page_size=64)
+    assert out.shape == (0, 8, 128)
+
+
+def test_validate_inputs_reports_violations():
+    import block_sparse_attention_selection_amd as msa
+
+    wl = W.make_custom(801, [3, 2], [500, 300], 8, 2, 64, topk=3, causal=True, pick="random")
+    d = device_inputs(wl)
+    kw = dict(cu_seqlens_q=d["cu_seqlens_q"], used_kv_lens=d["used_kv_lens"], page_size=64, causal=True)
+    msa.validate_inputs(d["q"], d["k_cache"], d["v_cache"], d["selected"], d["block_tables"], **kw)
+    bad = d["selected"].clone()
+    bad[0, 0, 1] = bad[0, 0, 0] = 0
+    with pytest.raises(msa.MsaError, match="twice"):
+        msa.validate_inputs(d["q"], d["k_cache"], d["v_cache"], bad, d["block_tables"], **kw)
+    bt = d["block_tables"].clone()
+    bt[0, 0] = wl.num_pages + 3
+    sel = d["selected"].clone()
+    sel[0, 0, :] = torch.tensor([0, -1, -1], dtype=torch.int32)
+    with pytest.raises(msa.MsaError, match="block_tables"):
+        msa.validate_inputs(d["q"], d["k_cache"], d["v_cache"], sel, bt, **kw)
