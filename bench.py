@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_gqa]
+
+One step is one complete ``msa_kvouter_attention`` call (index build, work
+split, attention, combine) over one synthetic batch already resident in HBM.
+Two independently drawn batches alternate between steps so that the 256 MB
+last-level cache cannot serve a step from the previous one.
+
+Prints ONE JSON line on stdout:
+  value      unique-KV bytes per step / seconds per step, in GB/s (the pass's
+             headline figure for decode); effective TFLOP/s and the step time
+             in microseconds are reported beside it
+  roofline   dominant kernel: algorithmic bytes (or flops) per launch divided
+             by its average launch time, measured with HIP events recorded on
+             the call's stream around that kernel during the timed steps
+  cpu_baseline  the fp64 oracle (test infrastructure) timed on this host's
+             cores over a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "unique-KV HBM GB/s + effective TFLOP/s, sparse attn fwd; decode step µs"
+
+DESCRIPTIONS = {
+    "tiny": "1 seq x 4 queries, Hq=16, Hkv=1, d=128, L=512, page 64, top-2 of 4 blocks, non-causal, bf16",
+    "decode_gqa": "64 seqs x 1 query, Hq=64, Hkv=8, d=128, L~U[8192,32768], page 64 shuffled, "
+                  "top-16 blocks of 128 (last block forced), causal, bf16",
+    "prefill_shared": "1 seq, Tq=L=16384, Hq=64, Hkv=8, d=128, page 128, top-16; chunks of 64 queries "
+                      "share 12 picks, diagonal forced, causal, bf16",
+    "varlen_mqa": "16 seqs, Tq lognormal(median 256, sigma 1) in [1,2048], L=U[4096,131072]+Tq, "
+                  "Hq=32, Hkv=1, d=128, page 128, top-32, causal, fp16",
+    "decode_fp8": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
+                  "K/V fp8 e4m3fn, q bf16, causal",
+}
+DOMINANT = {"tiny": "work", "decode_gqa": "front", "decode_fp8": "front",
+            "prefill_shared": "work", "varlen_mqa": "work"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def accounting(wl):
+    """Algorithmic work of one batch: unique KV bytes, effective flops, Q/O bytes."""
+    sel = wl.selected.astype(np.int64)
+    Tq, Hkv, K = sel.shape
+    cu = wl.cu_seqlens_q.astype(np.int64)
+    used = wl.used_kv_lens.astype(np.int64)
+    seq = np.full(Tq, -1, dtype=np.int64)
+    for s in range(wl.B):
+        seq[cu[s]:cu[s + 1]] = s
+    has = seq >= 0
+    s_ = np.where(has, seq, 0)
+    L = np.where(has, used[s_], 0)
+    pos = L - (cu[s_ + 1] - cu[s_]) + (np.arange(Tq) - cu[s_])
+    nblk = (L + 127) // 128
+    valid = has[:, None, None] & (sel >= 0) & (sel < nblk[:, None, None])
+    hi = np.minimum(128 * sel + 128, L[:, None, None])
+    if wl.causal:
+        valid &= 128 * sel <= pos[:, None, None]
+        hi = np.minimum(hi, pos[:, None, None] + 1)
+    nkeys = np.where(valid, hi - 128 * sel, 0)
+    flops = 4.0 * 128 * wl.G * float(nkeys.sum())
+    nbmax = int(nblk.max()) + 1 if Tq else 1
+    g = np.broadcast_to(np.arange(Hkv)[None, :, None], sel.shape)
+    key = (np.broadcast_to(s_[:, None, None], sel.shape) * Hkv + g) * nbmax + sel
+    uk = np.unique(key[valid])
+    ub = uk % nbmax
+    us = uk // nbmax // Hkv
+    kv_elem = wl.k_vals.element_size()
+    block_tokens = np.minimum(128 * ub + 128, used[us]) - 128 * ub
+    unique_kv = float(block_tokens.sum()) * 128 * 2 * kv_elem
+    q_elem = wl.q.element_size()
+    qo = float(Tq * wl.Hq) * (128 * q_elem * 2 + 4)
+    return dict(unique_kv_bytes=unique_kv, effective_flops=flops, qo_bytes=qo)
+
+
+def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
+    """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
+
+    The sample is repeated until at least ``min_seconds`` of oracle time has
+    accumulated; the rate is unique-KV bytes of the sample per second.
+    """
+    import oracle
+    import workloads as W
+
+    tot = wl.Tq * wl.Hkv
+    n = tot if budget_pairs is None else min(tot, budget_pairs)
+    rng = np.random.default_rng(0)
+    pairs = np.sort(rng.choice(tot, size=n, replace=False)) if n < tot else np.arange(tot)
+    G = wl.G
+    groups = []
+    for g in np.unique(pairs % wl.Hkv):
+        toks = pairs[pairs % wl.Hkv == g] // wl.Hkv
+        k, v, bt = W.compact_cache(wl, heads=[int(g)])
+        q = wl.q[:, g * G:(g + 1) * G, :].contiguous()
+        sel = np.ascontiguousarray(wl.selected[:, g:g + 1, :])
+        groups.append((q, k, v, sel, bt, toks))
+    secs, reps = 0.0, 0
+    while secs < min_seconds or reps == 0:
+        for q, k, v, sel, bt, toks in groups:
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, sel, bt, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, pairs=toks)
+            secs += time.perf_counter() - t0
+        reps += 1
+    frac = n / tot
+    return dict(
+        value=round(acct["unique_kv_bytes"] * frac * reps / secs / 1e9, 4),
+        unit="GB/s",
+        cores=oracle.max_threads(),
+        kind="oracle",
+        sample=f"{n} of {tot} (token, kv-head) pairs of one batch ({100 * frac:.0f}%), repeated {reps}x "
+               f"({secs:.1f} s of fp64 oracle time); unique-KV bytes scaled by the sampled fraction",
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_gqa", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=None, help="oracle sample size in (token, kv-head) pairs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_selection_amd as msa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed0 = W.CONFIGS[args.workload]["seed"]
+
+    batches = []
+    for i in range(2):
+        t0 = time.time()
+        wl = W.make(args.workload, seed=seed0 + 1000 * i, poison=False)
+        k, v = W.kv_pool(wl, device=dev)
+        d = dict(q=wl.q.to(dev), k=k, v=v, sel=torch.from_numpy(wl.selected).to(dev),
+                 bt=torch.from_numpy(wl.block_tables).to(dev),
+                 cu=torch.from_numpy(wl.cu_seqlens_q).to(dev), used=torch.from_numpy(wl.used_kv_lens).to(dev))
+        d["out"] = torch.empty_like(d["q"])
+        d["lse"] = torch.empty((wl.Hq, wl.Tq), dtype=torch.float32, device=dev)
+        acct = accounting(wl)
+        batches.append((wl, d, acct))
+        log(f"batch {i}: {args.workload} generated in {time.time() - t0:.1f}s, "
+            f"unique KV {acct['unique_kv_bytes'] / 1e6:.1f} MB, {acct['effective_flops'] / 1e9:.2f} GFLOP")
+
+    def step(i):
+        wl, d, _ = batches[i % 2]
+        msa.kvouter_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], cu_seqlens_q=d["cu"],
+                              used_kv_lens=d["used"], page_size=wl.page_size, causal=wl.causal,
+                              return_lse=True, out=d["out"], lse=d["lse"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    dom = DOMINANT[args.workload]
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+
+    # timed region: whole calls, no instrumentation inside
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    stop.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    # same steps again with HIP events recorded on the call's stream around
+    # the dominant kernel (the events add a little time between kernels, so
+    # the step time above is taken without them)
+    msa.profile_enable([dom])
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    k_ms, k_n = msa.profile_collect(dom)
+    msa.profile_enable([])
+
+    ukv = np.mean([b[2]["unique_kv_bytes"] for b in batches])
+    flops = np.mean([b[2]["effective_flops"] for b in batches])
+    qo = np.mean([b[2]["qo_bytes"] for b in batches])
+    value = ukv / (ms_step * 1e-3) / 1e9
+    k_avg_ms = k_ms / max(k_n, 1)
+    wl0 = batches[0][0]
+    decode = args.workload.startswith("decode")
+    if decode or args.workload == "tiny":
+        alg = ukv + qo
+        achieved = alg / (k_avg_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        achieved = flops / (k_avg_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+    roof["kernel"] = dom
+    roof["kernel_avg_us"] = round(k_avg_ms * 1e3, 2)
+    roof["launches"] = k_n
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(wl0, batches[0][2], args.cpu_pairs)
+        except Exception as e:  # the baseline is informative; never fail the bench on it
+            log("cpu baseline failed:", repr(e))
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bfloat16": "bf16", "float16": "fp16"}[str(wl0.q_dtype).split(".")[-1]]
+                 + ("+fp8kv" if wl0.kv_dtype != wl0.q_dtype else ""),
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+            "batch_sequences": wl0.B,
+            "query_tokens": wl0.Tq,
+            "unique_kv_bytes_per_step": int(ukv),
+            "effective_flops_per_step": int(flops),
+            "decode_step_us": round(ms_step * 1e3, 2),
+            "effective_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
+            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "parallelism": "single GPU",
+            "input_sets": 2,
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

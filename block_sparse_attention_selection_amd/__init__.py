@@ -25,6 +25,8 @@ from ._lib import (
     kvouter_attention,
     lib_path,
     load,
+    profile_collect,
+    profile_enable,
     validate_inputs,
     version,
     widen_fp8,
@@ -37,6 +39,8 @@ __all__ = [
     "validate_inputs",
     "version",
     "load",
+    "profile_enable",
+    "profile_collect",
     "lib_path",
     "MsaError",
     "MSA_BF16",

@@ -47,7 +47,7 @@ class MsaTensor(ctypes.Structure):
 class MsaIndexOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "slot_flag", "tok_chain", "tok_nres", "chain_blk", "row_off", "unit_off",
-        "ent", "slot_pos", "narrow_items", "wide_items", "counters")]
+        "ent", "slot_pos", "combine_items", "wide_items", "counters")]
 
 
 _lock = threading.Lock()
@@ -74,11 +74,15 @@ def load():
         lib.msa_kvouter_attention.restype = i32
         lib.msa_kvouter_attention.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
         lib.msa_build_index.restype = i32
-        lib.msa_build_index.argtypes = [T, T, T, i32, i32, i32, i32, i32, ctypes.POINTER(MsaIndexOut), vp]
+        lib.msa_build_index.argtypes = [T, T, T, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MsaIndexOut), vp]
         lib.msa_widen_fp8.restype = i32
         lib.msa_widen_fp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
         lib.msa_validate_inputs.restype = i32
         lib.msa_validate_inputs.argtypes = [T, T, T, T, T, T, T, i32, i32, vp]
+        lib.msa_profile_enable.restype = i32
+        lib.msa_profile_enable.argtypes = [ctypes.c_uint32]
+        lib.msa_profile_collect.restype = i32
+        lib.msa_profile_collect.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         lib.msa_last_error.restype = ctypes.c_char_p
         lib.msa_last_error.argtypes = []
         lib.msa_version.restype = ctypes.c_char_p
@@ -165,7 +169,7 @@ def validate_inputs(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q
 
 
 def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, causal: bool,
-                tile_tokens: int, unit_tokens: int):
+                tile_tokens: int, unit_tokens: int, list_all_chains: bool = False):
     """Run the index builder alone; returns its device arrays as a dict."""
     lib = load()
     _device_check(selected, cu_seqlens_q, used_kv_lens)
@@ -182,7 +186,7 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
         unit_off=torch.zeros(NR + 1, **i32),
         ent=torch.full((max(1, Tq * Hkv * K),), -1, **i32),
         slot_pos=torch.zeros(Tq * Hkv * K, **i32),
-        narrow_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
+        combine_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
         wide_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
         counters=torch.zeros(8, **i32),
     )
@@ -190,9 +194,29 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
     ds = [describe(x) for x in (selected, cu_seqlens_q, used_kv_lens)]
     with torch.cuda.device(dev):
         rc = lib.msa_build_index(*[_ref(d) for d in ds], int(Hq), int(nb_max), int(bool(causal)),
-                                 int(tile_tokens), int(unit_tokens), ctypes.byref(o), _stream(dev))
+                                 int(tile_tokens), int(unit_tokens), int(bool(list_all_chains)),
+                                 ctypes.byref(o), _stream(dev))
     _check(rc)
     return res
+
+
+KERNELS = {"index": 0, "front": 1, "work": 2, "merge": 3}
+
+
+def profile_enable(kernels=()):
+    """Record HIP events around launches of the named kernels (empty: off)."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS[k]
+    _check(load().msa_profile_enable(mask))
+
+
+def profile_collect(kernel: str):
+    """(total ms, launches) of the recorded launches of one kernel."""
+    tot = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(load().msa_profile_collect(KERNELS[kernel], ctypes.byref(tot), ctypes.byref(n)))
+    return tot.value, n.value
 
 
 def widen_fp8(x: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:

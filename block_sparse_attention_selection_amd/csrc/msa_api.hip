@@ -166,22 +166,20 @@ struct Carve {
 };
 
 // Lays the planning and partial arrays out in `base` (or only sizes them when
-// base is null). The counters and the bitmaps come first and are contiguous,
-// so one fill clears both. Returns the bytes used.
-size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials, size_t* clear_words) {
+// base is null). Returns the bytes used. The counters, the zero page and the
+// bitmap live in the separate zero-state buffer.
+size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   Carve c;
   const size_t nslots = (size_t)d.Tq * d.Hkv * d.K;
   const size_t TG = (size_t)d.Tq * d.Hkv;
   const size_t words = (size_t)d.NR * d.W;
-  p->counters = c.take<int32_t>(base, 64);
-  p->bitmap = c.take<uint32_t>(base, words);
-  *clear_words = (c.off) / 4;  // counters .. end of bitmap
   p->wordpre = c.take<uint32_t>(base, words);
+  p->wordbits = c.take<uint32_t>(base, words);
   p->slot_flag = c.take<uint8_t>(base, nslots);
   p->tok_chain = c.take<int32_t>(base, TG);
   p->tok_nres = c.take<int32_t>(base, TG);
   p->chain_blk = c.take<int32_t>(base, nslots);
-  p->narrow_items = c.take<int32_t>(base, TG);
+  p->combine_items = c.take<int32_t>(base, TG);
   p->wide_items = c.take<int32_t>(base, TG);
   p->row_cnt = c.take<int32_t>(base, d.NR);
   p->row_off = c.take<int32_t>(base, (size_t)d.NR + 1);
@@ -200,15 +198,30 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials, siz
 }
 
 struct DeviceWs {
-  void* ptr = nullptr;
+  void* ptr = nullptr;   // scratch: planning arrays and partial results
   size_t bytes = 0;
+  void* zs = nullptr;    // zero-state: counter sets, zero page, bitmap
+  size_t zs_bytes = 0;
   int num_cu = 0;
+  int parity = 0;        // counter set of the next call
+  bool dirty = false;    // zero-state must be cleared before use
 };
 
 std::mutex g_ws_mutex;
 std::vector<DeviceWs> g_ws;
 
-int32_t get_workspace(size_t need, void** ptr, int* num_cu) {
+struct WsLease {
+  void* scratch;
+  char* zs;
+  int num_cu;
+  int parity;
+  bool clear;
+  DeviceWs* ws;
+};
+
+// Scratch of `need` bytes and a zero-state buffer holding `bitmap_words`.
+// Growing either synchronises the device; a new zero-state buffer is zeroed.
+int32_t get_workspace(size_t need, size_t bitmap_words, WsLease* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
   std::lock_guard<std::mutex> lk(g_ws_mutex);
@@ -220,23 +233,48 @@ int32_t get_workspace(size_t need, void** ptr, int* num_cu) {
       return fail(MSA_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
     w.num_cu = n;
   }
-  if (w.bytes < need) {
-    if (w.ptr) {
+  const size_t zs_need = msa::kZsHeaderBytes + bitmap_words * 4;
+  if (w.bytes < need || w.zs_bytes < zs_need) {
+    if (w.ptr || w.zs) {
       if (hipDeviceSynchronize() != hipSuccess) return fail(MSA_ERR_HIP, "hipDeviceSynchronize failed while growing the workspace");
-      (void)hipFree(w.ptr);
+    }
+    if (w.bytes < need) {
+      if (w.ptr) (void)hipFree(w.ptr);
       w.ptr = nullptr;
       w.bytes = 0;
+      const size_t alloc = std::max(need, (size_t)1 << 20);
+      if (hipMalloc(&w.ptr, alloc) != hipSuccess) {
+        (void)hipGetLastError();
+        w.ptr = nullptr;
+        return fail(MSA_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", alloc);
+      }
+      w.bytes = alloc;
     }
-    size_t alloc = std::max(need, (size_t)1 << 20);
-    if (hipMalloc(&w.ptr, alloc) != hipSuccess) {
-      (void)hipGetLastError();
-      w.ptr = nullptr;
-      return fail(MSA_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", alloc);
+    if (w.zs_bytes < zs_need) {
+      if (w.zs) (void)hipFree(w.zs);
+      w.zs = nullptr;
+      w.zs_bytes = 0;
+      const size_t alloc = std::max(zs_need, (size_t)1 << 20);
+      if (hipMalloc(&w.zs, alloc) != hipSuccess) {
+        (void)hipGetLastError();
+        w.zs = nullptr;
+        return fail(MSA_ERR_OUT_OF_MEMORY, "zero-state allocation of %zu bytes failed", alloc);
+      }
+      if (hipMemset(w.zs, 0, alloc) != hipSuccess) {
+        w.dirty = true;
+      } else {
+        w.dirty = false;
+      }
+      w.zs_bytes = alloc;
+      w.parity = 0;
     }
-    w.bytes = alloc;
   }
-  *ptr = w.ptr;
-  *num_cu = w.num_cu;
+  out->scratch = w.ptr;
+  out->zs = (char*)w.zs;
+  out->num_cu = w.num_cu;
+  out->parity = w.parity;
+  out->clear = w.dirty;
+  out->ws = &w;
   return MSA_OK;
 }
 
@@ -266,7 +304,90 @@ void fill_inputs(msa::Params* p, const Dims& d, const msa_tensor* sel, const msa
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// kernel timing hooks
+// ---------------------------------------------------------------------------
+namespace msa {
+volatile uint32_t g_profile_mask = 0;
+}
+
+namespace {
+struct ProfRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mutex;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+hipEvent_t g_open[4] = {nullptr, nullptr, nullptr, nullptr};
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void msa::profile_mark(int kernel, bool begin, hipStream_t st) {
+  if (!(g_profile_mask & (1u << kernel))) return;
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  hipEvent_t e = pooled_event();
+  if (!e) return;
+  (void)hipEventRecord(e, st);
+  if (begin) {
+    g_open[kernel] = e;
+  } else if (g_open[kernel]) {
+    g_prof.push_back({kernel, g_open[kernel], e});
+    g_open[kernel] = nullptr;
+  } else {
+    g_event_pool.push_back(e);
+  }
+}
+
 extern "C" {
+
+int32_t msa_profile_enable(uint32_t kernel_mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  for (auto& r : g_prof) {
+    (void)hipEventSynchronize(r.b);
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  msa::g_profile_mask = kernel_mask & 0xFu;
+  return ok();
+}
+
+int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches || kernel < 0 || kernel > 3) return fail(MSA_ERR_INVALID_ARGUMENT, "bad profile query");
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  double tot = 0.0;
+  int64_t n = 0;
+  std::vector<ProfRec> keep;
+  for (auto& r : g_prof) {
+    if (r.kernel != kernel) {
+      keep.push_back(r);
+      continue;
+    }
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(MSA_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(MSA_ERR_HIP, "hipEventElapsedTime failed");
+    tot += ms;
+    ++n;
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.swap(keep);
+  *total_ms = tot;
+  *launches = n;
+  return ok();
+}
+
 
 const char* msa_last_error(void) { return g_err.c_str(); }
 
@@ -284,29 +405,50 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   if (rc) return rc;
   if (d.Tq == 0) return ok();
   msa::Params p{};
-  size_t clear_words = 0;
-  const size_t need = layout(d, nullptr, &p, true, &clear_words);
-  void* ws = nullptr;
-  int num_cu = 0;
-  if ((rc = get_workspace(need, &ws, &num_cu))) return rc;
-  layout(d, (char*)ws, &p, true, &clear_words);
+  const size_t need = layout(d, nullptr, &p, true);
+  WsLease ws;
+  if ((rc = get_workspace(need, (size_t)d.NR * d.W, &ws))) return rc;
+  layout(d, (char*)ws.scratch, &p, true);
   fill_inputs(&p, d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
+  // decode-shaped batches (few queries per sequence, at most 16 query rows
+  // per token) stream their chains from the front kernel, one workgroup per
+  // token; otherwise the front kernel runs one workgroup per tile and every
+  // chain goes to the back kernel
+  p.stream_narrow = (d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B) ? 1 : 0;
+  int32_t* sets = (int32_t*)ws.zs;
+  p.counters = sets + ws.parity * msa::kCntSlots;
+  p.counters_next = sets + (1 - ws.parity) * msa::kCntSlots;
+  p.zero_page = ws.zs + 2 * msa::kCntSlots * sizeof(int32_t);
+  p.bitmap = (uint32_t*)(ws.zs + msa::kZsHeaderBytes);
   p.q = q->data;
   p.k = k_cache->data;
   p.v = v_cache->data;
   p.out = out->data;
   p.lse = lse ? (float*)lse->data : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = msa::launch_fill((uint32_t*)p.counters, (int64_t)clear_words, 0u, st);
-  if (e == hipSuccess) e = msa::launch_plan(p, st);
-  if (e == hipSuccess) e = msa::launch_forward(p, d.q_elem, d.kv_elem, num_cu, st);
+  hipError_t e = hipSuccess;
+  if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
+  if (e == hipSuccess) e = msa::launch_front(p, d.q_elem, d.kv_elem, st);
+  if (e == hipSuccess) e = msa::launch_index(p, false, st);
+  if (e == hipSuccess) e = msa::launch_work(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+  if (e == hipSuccess) e = msa::launch_merge(p, d.q_elem, ws.num_cu, st);
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    if (e != hipSuccess) {
+      ws.ws->dirty = true;  // some kernels may not have run: clear everything next time
+    } else {
+      ws.ws->dirty = false;
+      ws.ws->parity = 1 - ws.parity;
+    }
+  }
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
 int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
                         const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max, int32_t causal,
-                        int32_t tile_tokens, int32_t unit_tokens, const msa_index_out* o, void* stream) {
+                        int32_t tile_tokens, int32_t unit_tokens, int32_t list_all_chains,
+                        const msa_index_out* o, void* stream) {
   int32_t rc;
   if ((rc = check_tensor(selected, "selected", 3, MSA_INT32, 4))) return rc;
   if ((rc = check_tensor(cu_seqlens_q, "cu_seqlens_q", 1, MSA_INT64, 8))) return rc;
@@ -321,9 +463,10 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   if (unit_tokens < 1 || unit_tokens > 128) return fail(MSA_ERR_INVALID_ARGUMENT, "unit_tokens must be in [1, 128]");
   if (nb_max < 1 || (int64_t)nb_max * Hkv >= (1ll << 30)) return fail(MSA_ERR_INVALID_ARGUMENT, "nb_max out of range");
   if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (list_all_chains != 0 && list_all_chains != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "list_all_chains must be 0 or 1");
   if (Tq * Hkv * K >= (1ll << 31)) return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit indices");
   if (!o->slot_flag || !o->tok_chain || !o->tok_nres || !o->chain_blk || !o->row_off || !o->unit_off ||
-      !o->ent || !o->slot_pos || !o->narrow_items || !o->wide_items || !o->counters)
+      !o->ent || !o->slot_pos || !o->combine_items || !o->wide_items || !o->counters)
     return fail(MSA_ERR_INVALID_ARGUMENT, "msa_index_out: null buffer");
   if (Tq == 0) return ok();
   Dims d{};
@@ -339,16 +482,18 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   d.T = tile_tokens;
   d.Tu = unit_tokens;
   msa::Params p{};
-  size_t clear_words = 0;
-  const size_t need = layout(d, nullptr, &p, false, &clear_words);
-  void* ws = nullptr;
-  int num_cu = 0;
-  if ((rc = get_workspace(need, &ws, &num_cu))) return rc;
-  layout(d, (char*)ws, &p, false, &clear_words);
+  const size_t need = layout(d, nullptr, &p, false);
+  WsLease ws;
+  if ((rc = get_workspace(need, (size_t)d.NR * d.W, &ws))) return rc;
+  layout(d, (char*)ws.scratch, &p, false);
   fill_inputs(&p, d, selected, nullptr, cu_seqlens_q, used_kv_lens, causal);
   p.T = tile_tokens;
   p.Tu = unit_tokens;
+  p.stream_narrow = list_all_chains ? 0 : 1;
   p.counters = o->counters;  // caller-visible counters; the bitmap stays internal
+  p.counters_next = nullptr;
+  p.zero_page = ws.zs + 2 * msa::kCntSlots * sizeof(int32_t);
+  p.bitmap = (uint32_t*)(ws.zs + msa::kZsHeaderBytes);
   p.slot_flag = o->slot_flag;
   p.tok_chain = o->tok_chain;
   p.tok_nres = o->tok_nres;
@@ -357,12 +502,20 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   p.unit_off = o->unit_off;
   p.ent = o->ent;
   p.slot_pos = o->slot_pos;
-  p.narrow_items = o->narrow_items;
+  p.combine_items = o->combine_items;
   p.wide_items = o->wide_items;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = msa::launch_fill((uint32_t*)o->counters, 8, 0u, st);
-  if (e == hipSuccess) e = msa::launch_fill(p.bitmap, (int64_t)d.NR * d.W, 0u, st);
-  if (e == hipSuccess) e = msa::launch_plan(p, st);
+  hipError_t e = hipSuccess;
+  if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
+  if (e == hipSuccess) e = msa::launch_fill((uint32_t*)o->counters, 8, 0u, st);
+  if (e == hipSuccess) e = msa::launch_fill((uint32_t*)o->slot_pos, (int64_t)Tq * Hkv * K, 0xFFFFFFFFu, st);
+  if (e == hipSuccess) e = msa::launch_front(p, -1, -1, st);
+  if (e == hipSuccess) e = msa::launch_index(p, true, st);
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    if (e != hipSuccess) ws.ws->dirty = true;
+    else if (ws.clear) ws.ws->dirty = false;
+  }
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

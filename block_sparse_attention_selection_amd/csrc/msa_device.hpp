@@ -157,4 +157,73 @@ __device__ __forceinline__ int seq_of(const int64_t* __restrict__ cu, int B, int
   return (t < cu[lo + 1]) ? lo : -1;
 }
 
+// Wave-cooperative version of seq_of: every lane of the wave gets the same
+// answer after at most two rounds of parallel loads (B <= 4095), falling
+// back to a scalar binary search for larger batches. For a non-decreasing
+// cu it returns the largest s with cu[s] <= t, then checks t < cu[s+1].
+__device__ __forceinline__ int wave_seq_of(const int64_t* __restrict__ cu, int B, int64_t t) {
+  if (B <= 0) return -1;
+  const int n = B + 1;
+  if (n > 64 * 64) return seq_of(cu, B, t);
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  if (n > 64) {
+    const int nb = (n + 63) / 64;
+    const bool le = lane < nb && cu[64 * lane] <= t;
+    const int c1 = __popcll(__ballot(le));
+    if (c1 == 0) return -1;
+    base = 64 * (c1 - 1);
+  }
+  const int idx = base + lane;
+  const bool le = idx < n && cu[idx] <= t;
+  const int c2 = __popcll(__ballot(le));
+  if (c2 == 0) return -1;
+  int s = base + c2 - 1;
+  if (s > B - 1) s = B - 1;
+  return (cu[s] <= t && t < cu[s + 1]) ? s : -1;
+}
+
+// Tile j of the batch, tiles being runs of T consecutive tokens numbered
+// sequence by sequence: returns its sequence and sets its first token, or
+// returns -1 beyond the last tile. Token ranges are clamped to [0, Tq).
+__device__ __forceinline__ int wave_tile_of(const int64_t* __restrict__ cu, int B, int Tq, int T, int j,
+                                            int64_t* t0) {
+  const int lane = threadIdx.x & 63;
+  const int per = (B + 63) / 64;
+  const int s0 = min(lane * per, B), s1 = min(s0 + per, B);
+  int cnt = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int64_t n = min(cu[s + 1], (int64_t)Tq) - max(cu[s], (int64_t)0);
+    if (n > 0) cnt += (int)((n + T - 1) / T);
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const int excl = incl - cnt;
+  const uint64_t m = __ballot(j >= excl && j < incl);
+  if (m == 0) return -1;
+  const int owner = __ffsll((unsigned long long)m) - 1;
+  int s_out = -1, t_out = 0;
+  if (lane == owner) {
+    int jj = j - excl;
+    for (int s = s0; s < s1; ++s) {
+      const int64_t a = max(cu[s], (int64_t)0);
+      const int64_t n = min(cu[s + 1], (int64_t)Tq) - a;
+      const int nt = n > 0 ? (int)((n + T - 1) / T) : 0;
+      if (jj < nt) {
+        s_out = s;
+        t_out = (int)(a + (int64_t)jj * T);
+        break;
+      }
+      jj -= nt;
+    }
+  }
+  s_out = __shfl(s_out, owner, 64);
+  *t0 = __shfl(t_out, owner, 64);
+  return s_out;
+}
+
 }  // namespace msa

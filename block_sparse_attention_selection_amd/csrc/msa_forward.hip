@@ -24,6 +24,7 @@
 #include <limits.h>
 
 #include "msa_device.hpp"
+#include "msa_index_dev.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -66,6 +67,11 @@ __device__ __forceinline__ void tile_load_q(RowTile<CT>& rt, const Params& p, in
   for (int s = 0; s < 4; ++s) rt.qb[s] = *(const u32x4*)(base + kmap(s, q));
 }
 
+// A row's reference maximum is only raised when a chunk's scores exceed it
+// by more than this many powers of two, so the accumulators are rescaled
+// rarely; the probabilities stay below 2^kRescale.
+constexpr float kRescale = 8.0f;
+
 // One 32-key chunk: scores, masked online softmax, P*V.
 //   ka[j][s]  K fragment: key 16j + c, dims of k-step s
 //   va[e]     V fragment: key key_of(q, e), dims 8c .. 8c+7
@@ -93,24 +99,26 @@ __device__ __forceinline__ void tile_chunk(RowTile<CT>& rt, const u32x4 (&ka)[2]
     cmax = fmaxf(cmax, x[e]);
   }
   cmax = max_over_groups(cmax);
-  const float m_new = fmaxf(rt.m, cmax);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f(rt.m - m_use);
+  if (__any(cmax > rt.m + kRescale)) {
+    const float m_new = fmaxf(rt.m, cmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(rt.m - m_new);
+    rt.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) rt.o[t] *= alpha;
+    rt.m = m_new;
+  }
+  const float m_use = (rt.m == -INFINITY) ? 0.f : rt.m;
   float p[8];
-  float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(x[e] - m_use);
-    psum += p[e];
+    p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+    rt.l += p[e];
   }
-  rt.l = rt.l * alpha + psum;
-  rt.m = m_new;
   u32x4 pb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) pb[i] = pack2<CT>(p[2 * i], p[2 * i + 1]);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    rt.o[t] *= alpha;
     u32x4 a;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -119,6 +127,15 @@ __device__ __forceinline__ void tile_chunk(RowTile<CT>& rt, const u32x4 (&ka)[2]
     }
     rt.o[t] = Mma<CT>::run(a, pb, rt.o[t]);
   }
+}
+
+// Zero the V fragments of keys at or beyond lim (their probabilities are
+// exactly zero, but the cache rows may hold anything, NaN included).
+__device__ __forceinline__ void zero_absent_v(u32x4 (&va)[8], int key0, int lim, int q) {
+  if (key0 + 32 <= lim) return;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (key0 + key_of(q, e) >= lim) va[e] = u32x4{0u, 0u, 0u, 0u};
 }
 
 template <typename KVT>
@@ -130,27 +147,10 @@ struct KvElem<fp8_e4m3_t> {
   typedef uint8_t type;
 };
 
-// Locate one 32-key chunk of block b of sequence s, KV head g.
-// Returns the number of present keys (0: nothing to do) and sets the bases.
-template <typename KVT>
-__device__ __forceinline__ int chunk_base(const Params& p, int s, int g, int b, int part, int L,
-                                          const typename KvElem<KVT>::type*& kb,
-                                          const typename KvElem<KVT>::type*& vb) {
-  typedef typename KvElem<KVT>::type E;
-  const int key0 = kBlk * b + 32 * part;
-  if (key0 >= L) return 0;  // L is already clamped to the page table's reach
-  const int page = p.block_tables[(size_t)s * p.MP + key0 / p.P];
-  if (page < 0 || page >= p.NP) return 0;
-  const size_t off = (((size_t)page * p.Hkv + g) * p.P + (key0 % p.P)) * kD;
-  kb = (const E*)p.k + off;
-  vb = (const E*)p.v + off;
-  return min(32, L - key0);
-}
-
 // ---------------------------------------------------------------------------
-// global -> register fragments of one chunk (narrow kernel). Raw cache bytes
-// are held until the chunk is multiplied, so the loads of the next chunk
-// stay in flight while the current one is being computed.
+// register fragments of one 32-key chunk, loaded straight from HBM. The loads
+// are unconditional (absent chunks read the zero page), so the compiler can
+// keep the next chunk's loads in flight while the current one is multiplied.
 // ---------------------------------------------------------------------------
 template <typename CT, typename KVT>
 struct Frag;
@@ -159,50 +159,33 @@ template <typename CT>
 struct Frag<CT, CT> {  // 16-bit cache: fragments are used as loaded
   u32x4 ka[2][4];
   u32x4 va[8];
-  int key0;
-  int nv;  // keys present in the chunk (0: skip)
   __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, int q, int c) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = 16 * j + c;
-      const bool ok = key < nv;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        ka[j][s] = ok ? *(const u32x4*)(kb + key * kD + kmap(s, q)) : u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int s = 0; s < 4; ++s) ka[j][s] = *(const u32x4*)(kb + (16 * j + c) * kD + kmap(s, q));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = key_of(q, e);
-      va[e] = (key < nv) ? *(const u32x4*)(vb + key * kD + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int e = 0; e < 8; ++e) va[e] = *(const u32x4*)(vb + key_of(q, e) * kD + 8 * c);
   }
-  __device__ __forceinline__ void compute(RowTile<CT>& rt, int L, int s, int q, float sl2) const {
-    tile_chunk(rt, ka, va, key0, L, s, q, sl2);
+  __device__ __forceinline__ void compute(RowTile<CT>& rt, int key0, int lim, int seq, int q, float sl2) {
+    zero_absent_v(va, key0, lim, q);
+    tile_chunk(rt, ka, va, key0, lim, seq, q, sl2);
   }
 };
 
 template <typename CT>
-struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: 16 raw bytes per K pair, 8 per V row
+struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is used
   u32x4 kr[2][2];
   u32x2 vr[8];
-  int key0;
-  int nv;
   __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, int q, int c) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = 16 * j + c;
-      const bool ok = key < nv;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        kr[j][pp] = ok ? *(const u32x4*)(kb + key * kD + 64 * pp + 16 * q) : u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int pp = 0; pp < 2; ++pp) kr[j][pp] = *(const u32x4*)(kb + (16 * j + c) * kD + 64 * pp + 16 * q);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = key_of(q, e);
-      vr[e] = (key < nv) ? *(const u32x2*)(vb + key * kD + 8 * c) : u32x2{0u, 0u};
-    }
+    for (int e = 0; e < 8; ++e) vr[e] = *(const u32x2*)(vb + key_of(q, e) * kD + 8 * c);
   }
-  __device__ __forceinline__ void compute(RowTile<CT>& rt, int L, int s, int q, float sl2) const {
+  __device__ __forceinline__ void compute(RowTile<CT>& rt, int key0, int lim, int seq, int q, float sl2) {
     u32x4 ka[2][4], va[8];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -213,129 +196,285 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: 16 raw bytes per K pair, 8 per V
       }
 #pragma unroll
     for (int e = 0; e < 8; ++e) va[e] = widen8<CT>(vr[e]);
-    tile_chunk(rt, ka, va, key0, L, s, q, sl2);
+    zero_absent_v(va, key0, lim, q);
+    tile_chunk(rt, ka, va, key0, lim, seq, q, sl2);
   }
 };
 
-// Fragments of chunk ci (block ci/4, keys 32*(ci%4) ..) of a chain.
+// Streams the chain of a tile of at most 16 query rows (see k_front).
 template <typename CT, typename KVT>
-__device__ __forceinline__ void fetch_chunk(Frag<CT, KVT>& f, const Params& p, const int32_t* blocks,
-                                            int nchunks, int ci, int s, int g, int L, int q, int c) {
+__device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int s, int L, int Tq_s,
+                                             int64_t q0, int rows, int n_ch, int ppb,
+                                             const int* s_chain, const int* s_chain_k,
+                                             const int* s_page, const int* s_nres) {
   typedef typename KvElem<KVT>::type E;
-  f.nv = 0;
-  if (ci >= nchunks) return;
-  const int b = blocks[ci >> 2], part = ci & 3;
-  const E* kb = nullptr;
-  const E* vb = nullptr;
-  f.nv = chunk_base<KVT>(p, s, g, b, part, L, kb, vb);
-  f.key0 = kBlk * b + 32 * part;
-  if (f.nv > 0) f.load(kb, vb, q, c);
-}
-
-// ---------------------------------------------------------------------------
-// narrow kernel: chain items with at most 16 rows (decode and tiny tiles).
-// The item's chunks are split over the four waves, each streaming its K/V
-// fragments straight from HBM into registers; the waves' softmax states are
-// merged through LDS at the end.
-// ---------------------------------------------------------------------------
-template <typename CT, typename KVT>
-__global__ __launch_bounds__(256) void k_fwd_narrow(Params p) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int Hkv = p.Hkv;
+  __shared__ int64_t s_koff[256];  // element offset of each chunk; -1: absent
   __shared__ float s_o[4][16][kD + 4];
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int n_items = p.counters[kCntNarrow];
-  const int Teff = p.T > 0 ? p.T : 1;
+  const int Leff = min(L, p.MP * p.P);  // keys the page table can reach
+  const int nchunks = n_ch * 4;
+  for (int ci = tid; ci < nchunks; ci += 256) {
+    const int c = ci >> 2, part = ci & 3;
+    const int key0 = kBlk * s_chain[c] + 32 * part;
+    const int page = s_page[s_chain_k[c] * ppb + (32 * part) / p.P];
+    s_koff[ci] = (key0 < Leff && page >= 0 && page < p.NP)
+                     ? (((int64_t)page * Hkv + g) * p.P + (key0 % p.P)) * kD
+                     : (int64_t)-1;
+  }
+  const int q = lane >> 4, c = lane & 15;
+  RowTile<CT> rt;
+  tile_reset(rt);
+  int tok = -1, h = 0;
+  rt.seq = -1;
+  rt.pos = -1;
+  if (c < rows) {
+    tok = t + c / p.G;
+    h = g * p.G + (c % p.G);
+    rt.seq = s;
+    rt.pos = p.causal ? (int)(L - Tq_s + (tok - q0)) : INT_MAX;
+  }
+  tile_load_q(rt, p, tok, h, q);
+  __syncthreads();
 
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int code = p.narrow_items[it];
-    const int t0 = code / p.Hkv, g = code - (code / p.Hkv) * p.Hkv;
-    const int s = seq_of(p.cu, p.B, t0);
-    const int64_t q0 = p.cu[s], q1 = min(p.cu[s + 1], (int64_t)p.Tq);
-    const int Tq_s = (int)(p.cu[s + 1] - q0);
-    const int L = min(p.used[s], p.MP * p.P);  // keys the page table can reach
-    const int nt = (int)min((int64_t)Teff, q1 - t0);
-    const int rows = nt * p.G;
-    const int nch = p.tok_chain[(size_t)t0 * p.Hkv + g];
-    const int32_t* blocks = p.chain_blk + ((size_t)t0 * p.Hkv + g) * p.K;
-
-    RowTile<CT> rt;
-    tile_reset(rt);
-    int tok = -1, h = 0;
-    if (c < rows) {
-      tok = t0 + c / p.G;
-      h = g * p.G + (c % p.G);
-      rt.pos = p.causal ? (int)(p.used[s] - Tq_s + (tok - q0)) : INT_MAX;
-      rt.seq = s;
-    } else {
-      rt.pos = -1;
-      rt.seq = -1;
-    }
-    tile_load_q(rt, p, tok, h, q);
-
-    // software pipeline: fragments of the next chunk are in flight while
-    // the current one is multiplied
-    const int nchunks = nch * 4;
+  const E* kbase = (const E*)p.k;
+  const E* vbase = (const E*)p.v;
+  const E* zero = (const E*)p.zero_page;
+  auto kaddr = [&](int ci) -> const E* {
+    const int64_t off = ci < nchunks ? s_koff[ci] : (int64_t)-1;
+    return off >= 0 ? kbase + off : zero;
+  };
+  auto vaddr = [&](int ci) -> const E* {
+    const int64_t off = ci < nchunks ? s_koff[ci] : (int64_t)-1;
+    return off >= 0 ? vbase + off : zero;
+  };
+  auto key0_of = [&](int ci) { return s_koff[ci] >= 0 ? kBlk * s_chain[ci >> 2] + 32 * (ci & 3) : Leff; };
+  const int nmine = (nchunks - wave + 3) / 4;
+  if (nmine > 0) {
     Frag<CT, KVT> fa, fb;
     int ci = wave;
-    fetch_chunk<CT, KVT>(fa, p, blocks, nchunks, ci, s, g, L, q, c);
-    while (ci < nchunks) {
-      fetch_chunk<CT, KVT>(fb, p, blocks, nchunks, ci + 4, s, g, L, q, c);
-      if (fa.nv > 0) fa.compute(rt, L, s, q, p.scale_log2);
+    fa.load(kaddr(ci), vaddr(ci), q, c);
+    for (;;) {
+      fb.load(kaddr(ci + 4), vaddr(ci + 4), q, c);
+      fa.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
       ci += 4;
       if (ci >= nchunks) break;
-      fetch_chunk<CT, KVT>(fa, p, blocks, nchunks, ci + 4, s, g, L, q, c);
-      if (fb.nv > 0) fb.compute(rt, L, s, q, p.scale_log2);
+      fa.load(kaddr(ci + 4), vaddr(ci + 4), q, c);
+      fb.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
       ci += 4;
+      if (ci >= nchunks) break;
     }
+  }
 
-    // merge the four waves
-    const float l_row = sum_over_groups(rt.l);
-    if (q == 0) {
-      s_m[wave][c] = rt.m;
-      s_l[wave][c] = l_row;
+  // merge the four waves
+  const float l_row = sum_over_groups(rt.l);
+  if (q == 0) {
+    s_m[wave][c] = rt.m;
+    s_l[wave][c] = l_row;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_o[wave][c][32 * q + 8 * r + tt] = rt.o[tt][r];
+  __syncthreads();
+  const int row = tid >> 4, d0 = (tid & 15) * 8;
+  if (row >= rows) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float wsum = 0.f, acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float f = exp2f(s_m[w][row] - Mu);
+    wsum += f * s_l[w][row];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] += f * s_o[w][row][d0 + d];
+  }
+  const int rtok = t + row / p.G;
+  const int rh = g * p.G + (row % p.G);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float lse2 = wsum > 0.f ? Mu + log2f(wsum) : -INFINITY;
+  if (s_nres[row / p.G] == 0) {
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
+    if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
+  } else {
+    float* dst = p.cpart + ((size_t)rtok * p.Hq + rh) * kD + d0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) dst[d] = acc[d] * inv;
+    if (d0 == 0) p.clse[(size_t)rtok * p.Hq + rh] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// front kernel: one workgroup per (token t, KV head g); only tile leaders do
+// work. It classifies the tile's slots (chain, covered/residual flags,
+// residual bitmap bits, work lists) and, when the tile has at most 16 query
+// rows (decode: one token x G heads), streams the chain's blocks right away:
+// the chain's chunks are split over the four waves, each keeping two chunks
+// of K/V in flight in registers, and the waves' softmax states are merged
+// through LDS. The chunk addresses are resolved once, up front, so no page
+// lookup sits between consecutive loads.
+// ---------------------------------------------------------------------------
+template <typename CT, typename KVT, bool ATTN>
+__global__ __launch_bounds__(256, 2) void k_front(Params p) {
+  extern __shared__ int s_sel[];  // [nt][K] picks, -1 where the slot is invalid
+  __shared__ int s_chain[64];     // chain blocks
+  __shared__ int s_chain_k[64];   // leader slot of each chain block
+  __shared__ int s_nres[128];     // residual slots per tile token
+  __shared__ int s_page[128];     // pages of the leader's picks (ppb per pick)
+  __shared__ int s_nch;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = p.K, Hkv = p.Hkv;
+  const int Teff = p.T > 0 ? p.T : 1;
+  int t, s;
+  int b_raw = -1;
+  if (p.stream_narrow) {
+    // one workgroup per token; the leader's picks do not depend on the
+    // sequence, so their loads are issued before the search
+    t = blockIdx.x;
+    if (tid < K) b_raw = p.selected[((size_t)t * Hkv + g) * K + tid];
+    s = wave_seq_of(p.cu, p.B, t);
+    if (s < 0) {  // outside every sequence: no keys; the combine writes zeros
+      const size_t tg = (size_t)t * Hkv + g;
+      if (tid < K) p.slot_flag[tg * K + tid] = 0;
+      if (tid == 0) {
+        p.tok_chain[tg] = 0;
+        p.tok_nres[tg] = 0;
+        p.combine_items[atomicAdd(&p.counters[kCntCombine], 1)] = (int)tg;
+      }
+      return;
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[wave][c][32 * q + 8 * r + t] = rt.o[t][r];
-    __syncthreads();
-    {
-      const int row = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-      if (row < rows) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float wsum = 0.f, acc[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float f = exp2f(s_m[w][row] - Mu);
-          wsum += f * s_l[w][row];
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[d] += f * s_o[w][row][d0 + d];
-        }
-        const int rtok = t0 + row / p.G;
-        const int rh = g * p.G + (row % p.G);
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-        const float lse2 = wsum > 0.f ? Mu + log2f(wsum) : -INFINITY;
-        if (p.tok_nres[(size_t)rtok * p.Hkv + g] == 0) {
-          u32x4 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-          *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
-          if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
-        } else {
-          float* dst = p.cpart + ((size_t)rtok * p.Hq + rh) * kD + d0;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) dst[d] = acc[d] * inv;
-          if (d0 == 0) p.clse[(size_t)rtok * p.Hq + rh] = lse2;
-        }
+    if ((t - p.cu[s]) % Teff != 0) return;  // the tile's leader handles this token
+  } else {
+    // one workgroup per tile
+    int64_t t0;
+    s = wave_tile_of(p.cu, p.B, p.Tq, Teff, blockIdx.x, &t0);
+    if (s < 0) return;
+    t = (int)t0;
+    if (tid < K) b_raw = p.selected[((size_t)t * Hkv + g) * K + tid];
+  }
+  const size_t tg = (size_t)t * Hkv + g;
+  const int64_t q0 = p.cu[s], qe = p.cu[s + 1];
+  const int64_t q1 = min(qe, (int64_t)p.Tq);
+  const int i0 = (int)(t - q0);
+  const int nt = (int)min((int64_t)Teff, q1 - t);
+  const int rows = nt * p.G;
+  const bool stream = ATTN && p.stream_narrow && rows <= 16;
+  const int ppb = kBlk / p.P;  // pages per block
+
+  // pages of the leader's picks, looked up while the sequence length loads
+  int my_page = -1;
+  if (stream && tid < K * ppb) {
+    const int k = tid / ppb, j = tid - (tid / ppb) * ppb;
+    const int b = p.selected[tg * K + k];
+    const int lp = b * ppb + j;
+    if (b >= 0 && b < p.nb_max && lp < p.MP) my_page = p.block_tables[(size_t)s * p.MP + lp];
+  }
+  const int L = p.used[s];
+  const int Tq_s = (int)(qe - q0);
+  const int nblk = L > 0 ? min((L + kBlk - 1) / kBlk, p.nb_max) : 0;
+
+  for (int idx = tid; idx < nt * K; idx += 256) {
+    const int tau = idx / K, k = idx - tau * K;
+    const int b = (idx < K) ? b_raw : p.selected[((size_t)(t + tau) * Hkv + g) * K + k];
+    const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
+    const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
+    s_sel[idx] = valid ? b : -1;
+  }
+  for (int tau = tid; tau < nt; tau += 256) s_nres[tau] = 0;
+  if (stream && tid < K * ppb) s_page[tid] = my_page;
+  __syncthreads();
+
+  // the chain: the leader's valid picks present in every token of the tile
+  if (wave == 0) {
+    bool in_chain = false;
+    int bl = -1;
+    if (p.T > 0 && lane < K) {
+      bl = s_sel[lane];
+      in_chain = bl >= 0;
+      for (int k2 = 0; k2 < lane && in_chain; ++k2) in_chain = s_sel[k2] != bl;
+      for (int tau = 1; tau < nt && in_chain; ++tau) {
+        bool found = false;
+        for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
+        in_chain = found;
       }
     }
-    __syncthreads();
+    const uint64_t mask = __ballot(in_chain);
+    if (in_chain) {
+      const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+      s_chain[rank] = bl;
+      s_chain_k[rank] = lane;
+      p.chain_blk[tg * K + rank] = bl;
+    }
+    if (lane == 0) s_nch = __popcll(mask);
+  }
+  __syncthreads();
+  const int n_ch = s_nch;
+
+  // flags, residual bits, residual counts
+  for (int idx = tid; idx < nt * K; idx += 256) {
+    const int tau = idx / K;
+    const int b = s_sel[idx];
+    uint8_t flag = 0;
+    if (b >= 0) {
+      bool cov = false;
+      for (int c = 0; c < n_ch; ++c) cov |= (s_chain[c] == b);
+      flag = cov ? 1 : 2;
+      if (!cov) {
+        const int tt = t + tau;
+        atomicOr(&p.bitmap[((size_t)b * Hkv + g) * p.W + (tt >> 5)], 1u << (tt & 31));
+        atomicAdd(&s_nres[tau], 1);
+      }
+    }
+    p.slot_flag[((size_t)(t + tau) * Hkv + g) * K + (idx - tau * K)] = flag;
+  }
+  __syncthreads();
+
+  // per-token results and work lists (one atomic per list per tile)
+  if (wave == 0) {
+    int res = 0, need = 0;
+    for (int tau = lane; tau < nt; tau += 64) {
+      const size_t tg2 = (size_t)(t + tau) * Hkv + g;
+      const int nr = s_nres[tau];
+      p.tok_chain[tg2] = n_ch;
+      p.tok_nres[tg2] = nr;
+      res += nr;
+      need += (nr > 0 || n_ch == 0) ? 1 : 0;
+    }
+    int excl = need;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(excl, off, 64);
+      if (lane >= off) excl += y;
+    }
+    const int tot_need = __shfl(excl, 63, 64);
+    excl -= need;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) res += __shfl_xor(res, off, 64);
+    int base = 0;
+    if (lane == 0) {
+      if (res > 0) atomicAdd(&p.counters[kCntResidual], res);
+      if (tot_need > 0) base = atomicAdd(&p.counters[kCntCombine], tot_need);
+      if (n_ch > 0 && (rows > 16 || !p.stream_narrow)) p.wide_items[atomicAdd(&p.counters[kCntWide], 1)] = (int)tg;
+    }
+    base = __shfl(base, 0, 64);
+    for (int tau = lane; tau < nt; tau += 64) {
+      const int nr = s_nres[tau];
+      if (nr > 0 || n_ch == 0) p.combine_items[base + excl++] = (int)((size_t)(t + tau) * Hkv + g);
+    }
+  }
+  if constexpr (ATTN) {
+    if (stream && n_ch > 0)
+      stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page, s_nres);
   }
 }
 
@@ -413,220 +552,346 @@ __device__ __forceinline__ void lds_fragments(u32x4 (&ka)[2][4], u32x4 (&va)[8],
   for (int e = 0; e < 8; ++e) va[e] = sv[swz(32 * part + key_of(q, e), c)];
 }
 
-template <typename CT, typename KVT>
-__global__ __launch_bounds__(256) void k_fwd_wide(Params p) {
-  __shared__ u32x4 s_k[kBlk * 16];
-  __shared__ u32x4 s_v[kBlk * 16];
-  __shared__ int s_tok[128];
-  __shared__ int s_seq[128];
-  __shared__ int s_item;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int n_chain = p.counters[kCntWide];
-  const int total = n_chain + p.counters[kCntUnits];
-  const int Teff = p.T > 0 ? p.T : 1;
-
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(&p.counters[kCntWideNext], 1);
-    __syncthreads();
-    const int it = s_item;
-    if (it >= total) break;
-
-    // ---- item description
-    int g, ntok, nblocks, b_unit = 0, e0 = 0;
-    const int32_t* blocks = nullptr;
-    const bool is_chain = it < n_chain;
-    if (is_chain) {
-      const int code = p.wide_items[it];
-      const int t0 = code / p.Hkv;
-      g = code - t0 * p.Hkv;
-      const int s = seq_of(p.cu, p.B, t0);
-      ntok = (int)min((int64_t)Teff, min(p.cu[s + 1], (int64_t)p.Tq) - t0);
-      nblocks = p.tok_chain[(size_t)t0 * p.Hkv + g];
-      blocks = p.chain_blk + ((size_t)t0 * p.Hkv + g) * p.K;
-      if (threadIdx.x < ntok) {
-        s_tok[threadIdx.x] = t0 + threadIdx.x;
-        s_seq[threadIdx.x] = s;
-      }
-    } else {
-      const int u = it - n_chain;
-      int lo = 0, hi = p.NR;  // largest r with unit_off[r] <= u
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.unit_off[mid] <= u)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const int r = lo;
-      b_unit = r / p.Hkv;
-      g = r - b_unit * p.Hkv;
-      e0 = p.row_off[r] + (u - p.unit_off[r]) * p.Tu;
-      ntok = min(p.Tu, p.row_off[r + 1] - e0);
-      nblocks = 1;
-      if (threadIdx.x < ntok) {
-        const int slot = p.ent[e0 + threadIdx.x];
-        const int tk = slot / (p.Hkv * p.K);
-        s_tok[threadIdx.x] = tk;
-        s_seq[threadIdx.x] = seq_of(p.cu, p.B, tk);
-      }
+// Tokens with ranks [rank0, rank0 + n) among the set bits of row r (one
+// wave): the word holding rank0 is found by two rounds of sampled loads of
+// the row's exclusive popcount prefix, then consecutive words are scanned
+// 64 at a time, each lane expanding its own word.
+__device__ __forceinline__ void unit_tokens(const Params& p, int r, int rank0, int n, int* s_tok) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* pre = p.wordpre + (size_t)r * p.W;
+  const uint32_t* bits = p.wordbits + (size_t)r * p.W;
+  int lo = 0, hi = p.W;  // the word is the largest w with pre[w] <= rank0
+  while (hi - lo > 64) {
+    const int stride = (hi - lo + 63) / 64;
+    const int w = lo + lane * stride;
+    const bool le = w < hi && (int)pre[w] <= rank0;
+    const int c = __popcll(__ballot(le));
+    lo = lo + (c - 1) * stride;
+    hi = min(lo + stride, hi);
+  }
+  {
+    const int w = lo + lane;
+    const bool le = w < hi && (int)pre[w] <= rank0;
+    lo = lo + __popcll(__ballot(le)) - 1;
+  }
+  for (int wb = lo; wb < p.W; wb += 64) {
+    const int w = wb + lane;
+    uint32_t x = 0u;
+    int rk = 0;
+    if (w < p.W) {
+      x = bits[w];
+      rk = (int)pre[w];
     }
-    __syncthreads();
-    const int rows = ntok * p.G;
-
-    // ---- the wave's row tiles (w and w + 4)
-    RowTile<CT> rt[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      tile_reset(rt[i]);
-      const int rho = 16 * (wave + 4 * i) + c;
-      int tok = -1, h = 0;
-      rt[i].seq = -1;
-      rt[i].pos = -1;
-      if (rho < rows) {
-        const int tau = rho / p.G;
-        tok = s_tok[tau];
-        h = g * p.G + (rho - tau * p.G);
-        const int s = s_seq[tau];
-        rt[i].seq = s;
-        const int64_t q0 = p.cu[s];
-        rt[i].pos = p.causal ? (int)(p.used[s] - (p.cu[s + 1] - q0) + (tok - q0)) : INT_MAX;
-      }
-      tile_load_q(rt[i], p, tok, h, q);
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1u;
+      if (rk >= rank0 && rk < rank0 + n) s_tok[rk - rank0] = w * 32 + bit;
+      ++rk;
     }
-    const bool has0 = 16 * wave < rows, has1 = 16 * (wave + 4) < rows;
-
-    // ---- blocks (a unit may span several sequences: one run per sequence)
-    int run_start = 0;
-    for (int bi = 0; bi < nblocks;) {
-      int s_run, b;
-      if (is_chain) {
-        s_run = s_seq[0];
-        b = blocks[bi];
-      } else {
-        s_run = s_seq[run_start];
-        b = b_unit;
-      }
-      const int L = min(p.used[s_run], p.MP * p.P);  // keys the page table can reach
-      BlockStager<CT, KVT>::stage(s_k, s_v, p, s_run, g, b, L);
-      __syncthreads();
-      const int nparts = min(4, (L - kBlk * b + 31) / 32);
-      for (int part = 0; part < nparts; ++part) {
-        u32x4 ka[2][4], va[8];
-        lds_fragments<CT>(ka, va, s_k, s_v, part, q, c);
-        const int key0 = kBlk * b + 32 * part;
-        if (has0) tile_chunk(rt[0], ka, va, key0, L, s_run, q, p.scale_log2);
-        if (has1) tile_chunk(rt[1], ka, va, key0, L, s_run, q, p.scale_log2);
-      }
-      __syncthreads();
-      if (is_chain) {
-        ++bi;
-      } else {
-        int nxt = run_start;
-        while (nxt < ntok && s_seq[nxt] == s_run) ++nxt;
-        run_start = nxt;
-        if (run_start >= ntok) bi = nblocks;
-      }
-    }
-
-    // ---- results of the wave's tiles
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float l_row = sum_over_groups(rt[i].l);
-      const int rho = 16 * (wave + 4 * i) + c;
-      if (rho >= rows) continue;
-      const int tau = rho / p.G;
-      const int hr = rho - tau * p.G;
-      const int tok = s_tok[tau];
-      const int h = g * p.G + hr;
-      const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-      const float mu = rt[i].m == -INFINITY ? 0.f : rt[i].m;
-      const float lse2 = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
-      if (is_chain && p.tok_nres[(size_t)tok * p.Hkv + g] == 0) {
-        uint16_t* dst = (uint16_t*)p.out + ((size_t)tok * p.Hq + h) * kD + 32 * q;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x4 pk;
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2)
-            pk[k2] = pack2<CT>(rt[i].o[2 * k2][r] * inv, rt[i].o[2 * k2 + 1][r] * inv);
-          *(u32x4*)(dst + 8 * r) = pk;
-        }
-        if (q == 0 && p.lse) p.lse[(size_t)h * p.Tq + tok] = lse2 * kLn2;
-      } else {
-        float* dst;
-        float* lsd;
-        if (is_chain) {
-          dst = p.cpart + ((size_t)tok * p.Hq + h) * kD;
-          lsd = p.clse + (size_t)tok * p.Hq + h;
-        } else {
-          const size_t pos = (size_t)(e0 + tau);
-          dst = p.opart + (pos * p.G + hr) * kD;
-          lsd = p.lpart + pos * p.G + hr;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f32x4 a, bq;
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2) {
-            a[k2] = rt[i].o[k2][r] * inv;
-            bq[k2] = rt[i].o[4 + k2][r] * inv;
-          }
-          *(f32x4*)(dst + 32 * q + 8 * r) = a;
-          *(f32x4*)(dst + 32 * q + 8 * r + 4) = bq;
-        }
-        if (q == 0) *lsd = lse2;
-      }
-    }
-    __syncthreads();
+    if (!__any(w < p.W && rk < rank0 + n)) break;  // every lane is past the unit's last rank
   }
 }
 
-// ---------------------------------------------------------------------------
-// combine: merge the chain partial and the residual partials of (t, g) by
-// their log-sum-exp; writes out[t, h, :] and lse[h, t]
-// ---------------------------------------------------------------------------
+// One wide item: a chain of a tile with more than 16 query rows (or any
+// chain in prefill mode), or a KV-outer unit (up to Tu tokens that picked one
+// block outside their tile's chain). Each block is staged once in LDS (K and
+// V, 16-bit, 16-byte chunks XOR-swizzled by row so both operand read patterns
+// are bank-conflict free) and every wave multiplies its one or two 16-row
+// tiles against it.
+template <typename CT, typename KVT>
+__device__ __forceinline__ void wide_item(const Params& p, bool is_chain, int index, u32x4* s_k, u32x4* s_v,
+                                          int* s_tok, int* s_seq, const int64_t* cu) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int Teff = p.T > 0 ? p.T : 1;
+  const int it = index;
+  // ---- item description
+  int g, ntok, nblocks, b_unit = 0, e0 = 0;
+  const int32_t* blocks = nullptr;
+  if (is_chain) {
+    const int code = p.wide_items[it];
+    const int t0 = code / p.Hkv;
+    g = code - t0 * p.Hkv;
+    const int s = seq_of(cu, p.B, t0);
+    ntok = (int)min((int64_t)Teff, min(p.cu[s + 1], (int64_t)p.Tq) - t0);
+    nblocks = p.tok_chain[(size_t)t0 * p.Hkv + g];
+    blocks = p.chain_blk + ((size_t)t0 * p.Hkv + g) * p.K;
+    if (threadIdx.x < ntok) {
+      s_tok[threadIdx.x] = t0 + threadIdx.x;
+      s_seq[threadIdx.x] = s;
+    }
+  } else {
+    const int u = it;
+    int lo = 0, hi = p.NR;  // largest r with unit_off[r] <= u
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.unit_off[mid] <= u)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int r = lo;
+    b_unit = r / p.Hkv;
+    g = r - b_unit * p.Hkv;
+    const int rank0 = (u - p.unit_off[r]) * p.Tu;
+    e0 = p.row_off[r] + rank0;
+    ntok = min(p.Tu, p.row_off[r + 1] - e0);
+    nblocks = 1;
+    if (wave == 0) unit_tokens(p, r, rank0, ntok, s_tok);
+    __syncthreads();
+    if (threadIdx.x < ntok) s_seq[threadIdx.x] = seq_of(cu, p.B, s_tok[threadIdx.x]);
+  }
+  __syncthreads();
+  const int rows = ntok * p.G;
+
+  // ---- the wave's row tiles (w and w + 4)
+  RowTile<CT> rt[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    tile_reset(rt[i]);
+    const int rho = 16 * (wave + 4 * i) + c;
+    int tok = -1, h = 0;
+    rt[i].seq = -1;
+    rt[i].pos = -1;
+    if (rho < rows) {
+      const int tau = rho / p.G;
+      tok = s_tok[tau];
+      h = g * p.G + (rho - tau * p.G);
+      const int s = s_seq[tau];
+      rt[i].seq = s;
+      const int64_t q0 = p.cu[s];
+      rt[i].pos = p.causal ? (int)(p.used[s] - (p.cu[s + 1] - q0) + (tok - q0)) : INT_MAX;
+    }
+    tile_load_q(rt[i], p, tok, h, q);
+  }
+  const bool has0 = 16 * wave < rows, has1 = 16 * (wave + 4) < rows;
+
+  // ---- blocks (a unit may span several sequences: one run per sequence)
+  int run_start = 0;
+  for (int bi = 0; bi < nblocks;) {
+    int s_run, b;
+    if (is_chain) {
+      s_run = s_seq[0];
+      b = blocks[bi];
+    } else {
+      s_run = s_seq[run_start];
+      b = b_unit;
+    }
+    const int L = min(p.used[s_run], p.MP * p.P);  // keys the page table can reach
+    BlockStager<CT, KVT>::stage(s_k, s_v, p, s_run, g, b, L);
+    __syncthreads();
+    const int nparts = min(4, (L - kBlk * b + 31) / 32);
+    for (int part = 0; part < nparts; ++part) {
+      u32x4 ka[2][4], va[8];
+      lds_fragments<CT>(ka, va, s_k, s_v, part, q, c);
+      const int key0 = kBlk * b + 32 * part;
+      if (has0) tile_chunk(rt[0], ka, va, key0, L, s_run, q, p.scale_log2);
+      if (has1) tile_chunk(rt[1], ka, va, key0, L, s_run, q, p.scale_log2);
+    }
+    __syncthreads();
+    if (is_chain) {
+      ++bi;
+    } else {
+      int nxt = run_start;
+      while (nxt < ntok && s_seq[nxt] == s_run) ++nxt;
+      run_start = nxt;
+      if (run_start >= ntok) bi = nblocks;
+    }
+  }
+
+  // ---- results of the wave's tiles
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float l_row = sum_over_groups(rt[i].l);
+    const int rho = 16 * (wave + 4 * i) + c;
+    if (rho >= rows) continue;
+    const int tau = rho / p.G;
+    const int hr = rho - tau * p.G;
+    const int tok = s_tok[tau];
+    const int h = g * p.G + hr;
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const float mu = rt[i].m == -INFINITY ? 0.f : rt[i].m;
+    const float lse2 = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
+    if (is_chain && p.tok_nres[(size_t)tok * p.Hkv + g] == 0) {
+      uint16_t* dst = (uint16_t*)p.out + ((size_t)tok * p.Hq + h) * kD + 32 * q;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 pk;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2)
+          pk[k2] = pack2<CT>(rt[i].o[2 * k2][r] * inv, rt[i].o[2 * k2 + 1][r] * inv);
+        *(u32x4*)(dst + 8 * r) = pk;
+      }
+      if (q == 0 && p.lse) p.lse[(size_t)h * p.Tq + tok] = lse2 * kLn2;
+    } else {
+      float* dst;
+      float* lsd;
+      if (is_chain) {
+        dst = p.cpart + ((size_t)tok * p.Hq + h) * kD;
+        lsd = p.clse + (size_t)tok * p.Hq + h;
+      } else {
+        const size_t pos = (size_t)(e0 + tau);
+        dst = p.opart + (pos * p.G + hr) * kD;
+        lsd = p.lpart + pos * p.G + hr;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 a, bq;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          a[k2] = rt[i].o[k2][r] * inv;
+          bq[k2] = rt[i].o[4 + k2][r] * inv;
+        }
+        *(f32x4*)(dst + 32 * q + 8 * r) = a;
+        *(f32x4*)(dst + 32 * q + 8 * r + 4) = bq;
+      }
+      if (q == 0) *lsd = lse2;
+    }
+  }}
+
+// Merge the partial results of one (token, KV head) pair by their
+// log-sum-exp (the chain's partial first, then the residual slots in slot
+// order) and write out[t, h, :] and lse[h, t]. One wave per pair: the
+// residual slots are found with one parallel load per lane, and the partial
+// results are read in batches of independent loads.
 template <typename CT>
-__global__ __launch_bounds__(128) void k_combine(Params p) {
-  const int t = blockIdx.x, g = blockIdx.y;
-  const size_t tg = (size_t)t * p.Hkv + g;
-  const int nch = p.tok_chain[tg];
-  const int nres = p.tok_nres[tg];
-  if (nch > 0 && nres == 0) return;  // the chain item wrote the final rows
+__device__ __forceinline__ void combine_pair(const Params& p, int code) {
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63;
+  const int t = code / p.Hkv, g = code - (code / p.Hkv) * p.Hkv;
+  const size_t tg = (size_t)code;
   const int K = p.K;
-  for (int idx = threadIdx.x; idx < p.G * 16; idx += 128) {
-    const int r = idx >> 4, d0 = (idx & 15) * 8;
+  int my_pos = -1;
+  if (lane < K && p.slot_flag[tg * K + lane] == 2) my_pos = residual_pos(p, t, g, p.selected[tg * K + lane]);
+  const uint64_t mres = __ballot(my_pos >= 0);
+  const int nparts = __popcll(mres);
+  // loads past the last part read the first part again (always a valid index)
+  const int pos0 = mres ? __shfl(my_pos, __ffsll((unsigned long long)mres) - 1, 64) : 0;
+  const bool has_chain = p.tok_chain[tg] > 0;
+  // every lane runs every iteration (the shuffles need all lanes active)
+  for (int base = 0; base < p.G * 16; base += 64) {
+    const int idx = base + lane;
+    const bool act = idx < p.G * 16;
+    const int r = act ? idx >> 4 : 0, d0 = (idx & 15) * 8;
     const int h = g * p.G + r;
-    float M = -INFINITY;
-    if (nch > 0) M = p.clse[(size_t)t * p.Hq + h];
-    for (int k = 0; k < K; ++k)
-      if (p.slot_flag[tg * K + k] == 2) M = fmaxf(M, p.lpart[(size_t)p.slot_pos[tg * K + k] * p.G + r]);
+    const float lc = has_chain ? p.clse[(size_t)t * p.Hq + h] : -INFINITY;
+    float M = lc;
+    uint64_t rest = mres;
+    for (int i0 = 0; i0 < nparts; i0 += kBatch) {
+      float l[kBatch];
+      uint64_t m = rest;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int k = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        const int pos = m ? __shfl(my_pos, k, 64) : pos0;
+        const float lv = p.lpart[(size_t)pos * p.G + r];
+        l[j] = (i0 + j < nparts) ? lv : -INFINITY;
+        m &= m - 1;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) M = fmaxf(M, l[j]);
+      rest = m;
+    }
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float wsum = 0.f, acc[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-    if (nch > 0) {
-      const float f = exp2f(p.clse[(size_t)t * p.Hq + h] - Mu);
-      const float* src = p.cpart + ((size_t)t * p.Hq + h) * kD + d0;
+    if (has_chain) {
+      const float f = exp2f(lc - Mu);
+      const f32x4* src = (const f32x4*)(p.cpart + ((size_t)t * p.Hq + h) * kD + d0);
+      const f32x4 a0 = src[0], a1 = src[1];
       wsum += f;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] += f * src[d];
+      for (int d = 0; d < 4; ++d) {
+        acc[d] += f * a0[d];
+        acc[4 + d] += f * a1[d];
+      }
     }
-    for (int k = 0; k < K; ++k) {
-      if (p.slot_flag[tg * K + k] != 2) continue;
-      const size_t pos = (size_t)p.slot_pos[tg * K + k];
-      const float f = exp2f(p.lpart[pos * p.G + r] - Mu);
-      const float* src = p.opart + (pos * p.G + r) * kD + d0;
-      wsum += f;
+    rest = mres;
+    for (int i0 = 0; i0 < nparts; i0 += kBatch) {
+      float l[kBatch];
+      f32x4 o0[kBatch], o1[kBatch];
+      uint64_t m = rest;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] += f * src[d];
+      for (int j = 0; j < kBatch; ++j) {
+        const int k = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        const size_t pos = (size_t)(m ? __shfl(my_pos, k, 64) : pos0);
+        const bool live = i0 + j < nparts;
+        const f32x4* src = (const f32x4*)(p.opart + (pos * p.G + r) * kD + d0);
+        const float lv = p.lpart[pos * p.G + r];
+        const f32x4 v0 = src[0], v1 = src[1];
+        l[j] = live ? lv : -INFINITY;
+        o0[j] = live ? v0 : f32x4{0.f, 0.f, 0.f, 0.f};
+        o1[j] = live ? v1 : f32x4{0.f, 0.f, 0.f, 0.f};
+        m &= m - 1;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float f = exp2f(l[j] - Mu);
+        wsum += f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[d] += f * o0[j][d];
+          acc[4 + d] += f * o1[j][d];
+        }
+      }
+      rest = m;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (!act) continue;
     u32x4 pk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
     *(u32x4*)((uint16_t*)p.out + ((size_t)t * p.Hq + h) * kD + d0) = pk;
     if (d0 == 0 && p.lse) p.lse[(size_t)h * p.Tq + t] = wsum > 0.f ? (Mu + log2f(wsum)) * kLn2 : -INFINITY;
   }
+}
+
+// ---------------------------------------------------------------------------
+// work kernel: a persistent grid pulls wide chains, then KV-outer units, from
+// a shared counter. Items are independent: nothing produced inside this
+// kernel is read inside it.
+// ---------------------------------------------------------------------------
+template <typename CT, typename KVT>
+__global__ __launch_bounds__(256) void k_work(Params p) {
+  __shared__ u32x4 s_k[kBlk * 16];
+  __shared__ u32x4 s_v[kBlk * 16];
+  __shared__ int s_tok[128];
+  __shared__ int s_seq[128];
+  __shared__ int64_t s_cu[1024];  // cu_seqlens_q, when it fits, for the sequence lookups
+  __shared__ int s_task;
+  const int nC = p.counters[kCntWide];
+  const int nU = p.counters[kCntUnits];
+  const int total = nC + nU;
+  if (total == 0) return;
+  const bool cu_in_lds = p.B + 1 <= 1024;
+  if (cu_in_lds)
+    for (int i = threadIdx.x; i <= p.B; i += 256) s_cu[i] = p.cu[i];
+  const int64_t* cu = cu_in_lds ? s_cu : p.cu;
+  for (bool first = true;; first = false) {
+    if (threadIdx.x == 0)
+      s_task = first ? (int)blockIdx.x : (int)gridDim.x + atomicAdd(&p.counters[kCntTask], 1);
+    __syncthreads();
+    const int id = s_task;
+    __syncthreads();
+    if (id >= total) break;
+    if (id < nC)
+      wide_item<CT, KVT>(p, true, id, s_k, s_v, s_tok, s_seq, cu);
+    else
+      wide_item<CT, KVT>(p, false, id - nC, s_k, s_v, s_tok, s_seq, cu);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge kernel: one wave per listed (token, KV head) pair; workgroup 0 also
+// clears the counter set of the next call.
+// ---------------------------------------------------------------------------
+template <typename CT>
+__global__ __launch_bounds__(256) void k_merge(Params p) {
+  if (blockIdx.x == 0 && p.counters_next)
+    for (int i = threadIdx.x; i < kCntSlots; i += 256) p.counters_next[i] = 0;
+  const int n = p.counters[kCntCombine];
+  const int wave = threadIdx.x >> 6;
+  for (int pair = blockIdx.x * 4 + wave; pair < n; pair += gridDim.x * 4) combine_pair<CT>(p, p.combine_items[pair]);
 }
 
 // ---------------------------------------------------------------------------
@@ -652,26 +917,59 @@ hipError_t launch_widen_fp8(const void* in, int64_t n, int out_elem, void* out, 
   return hipGetLastError();
 }
 
-template <typename CT, typename KVT>
-static hipError_t launch_forward_t(const Params& p, int num_cu, hipStream_t st) {
-  const int max_items = p.Tq * p.Hkv;
-  int narrow_grid = min(max_items, num_cu * 8);
-  if (narrow_grid < 1) narrow_grid = 1;
-  hipLaunchKernelGGL((k_fwd_narrow<CT, KVT>), dim3(narrow_grid), dim3(256), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_fwd_wide<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_combine<CT>), dim3(p.Tq, p.Hkv), dim3(128), 0, st, p);
+template <typename CT, typename KVT, bool ATTN>
+static hipError_t launch_front_t(const Params& p, hipStream_t st) {
+  const int Teff = p.T > 0 ? p.T : 1;
+  const size_t lds = (size_t)Teff * p.K * sizeof(int);
+  const unsigned gx = p.stream_narrow ? (unsigned)p.Tq : (unsigned)((p.Tq + Teff - 1) / Teff + p.B);
+  hipLaunchKernelGGL((k_front<CT, KVT, ATTN>), dim3(gx, p.Hkv), dim3(256), lds, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
+hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st) {
+  profile_mark(kKFront, true, st);
+  hipError_t e;
+  if (q_elem < 0)
+    e = launch_front_t<bf16_t, bf16_t, false>(p, st);
+  else if (q_elem == kElemBF16)
+    e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(p, st)
+                            : launch_front_t<bf16_t, bf16_t, true>(p, st);
+  else
+    e = kv_elem == kElemFP8 ? launch_front_t<f16_t, fp8_e4m3_t, true>(p, st)
+                            : launch_front_t<f16_t, f16_t, true>(p, st);
+  profile_mark(kKFront, false, st);
+  return e;
+}
+
+template <typename CT, typename KVT>
+static hipError_t launch_work_t(const Params& p, int num_cu, hipStream_t st) {
+  profile_mark(kKWork, true, st);
+  hipLaunchKernelGGL((k_work<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  profile_mark(kKWork, false, st);
+  return e;
+}
+
+hipError_t launch_work(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
   if (q_elem == kElemBF16)
-    return kv_elem == kElemFP8 ? launch_forward_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
-                               : launch_forward_t<bf16_t, bf16_t>(p, num_cu, st);
-  return kv_elem == kElemFP8 ? launch_forward_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
-                             : launch_forward_t<f16_t, f16_t>(p, num_cu, st);
+    return kv_elem == kElemFP8 ? launch_work_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
+                               : launch_work_t<bf16_t, bf16_t>(p, num_cu, st);
+  return kv_elem == kElemFP8 ? launch_work_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
+                             : launch_work_t<f16_t, f16_t>(p, num_cu, st);
+}
+
+hipError_t launch_merge(const Params& p, int q_elem, int num_cu, hipStream_t st) {
+  const int64_t pairs = (int64_t)p.Tq * p.Hkv;
+  int grid = (int)min((pairs + 3) / 4, (int64_t)num_cu * 8);
+  if (grid < 1) grid = 1;
+  profile_mark(kKMerge, true, st);
+  if (q_elem == kElemBF16)
+    hipLaunchKernelGGL((k_merge<bf16_t>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_merge<f16_t>), dim3(grid), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  profile_mark(kKMerge, false, st);
+  return e;
 }
 
 }  // namespace msa

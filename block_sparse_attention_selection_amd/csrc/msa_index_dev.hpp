@@ -1,0 +1,127 @@
+// msa_index_dev.hpp -- device functions of the residual inversion, shared by
+// the staged index kernels (msa_index.hip) and the persistent back kernel
+// (msa_forward.hip).
+#pragma once
+
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// exclusive scan across a workgroup of NT threads (NT a multiple of 64)
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, int* total, int* smem) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) smem[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int v = (lane < NW) ? smem[lane] : 0;
+    int vi = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(vi, off, 64);
+      if (lane >= off) vi += y;
+    }
+    if (lane < NW) smem[lane] = vi - v;
+    if (lane == NW - 1) smem[NW] = vi;
+  }
+  __syncthreads();
+  const int res = smem[wid] + incl - x;
+  *total = smem[NW];
+  __syncthreads();
+  return res;
+}
+
+// Row r (block b, KV head g): popcount prefix of its token bitmap; the words
+// are copied to wordbits and cleared. Returns the row's count to every
+// thread. smem: NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int rowcount_row(const Params& p, int r, int* smem) {
+  uint32_t* bm = p.bitmap + (size_t)r * p.W;
+  uint32_t* pre = p.wordpre + (size_t)r * p.W;
+  uint32_t* bits = p.wordbits + (size_t)r * p.W;
+  const int per = (p.W + NT - 1) / NT;
+  const int w0 = min((int)threadIdx.x * per, p.W);
+  const int w1 = min(w0 + per, p.W);
+  int sum = 0;
+  for (int w = w0; w < w1; ++w) sum += __popc(bm[w]);
+  int total;
+  int run = block_excl_scan<NT>(sum, &total, smem);
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = bm[w];
+    pre[w] = (uint32_t)run;
+    bits[w] = x;
+    bm[w] = 0u;  // leave the bitmap clear for the next call
+    run += __popc(x);
+  }
+  return total;
+}
+
+// Exclusive scans of the row counts (row_off) and of the units per row
+// (unit_off); the unit total goes to counters[kCntUnits]. The row counts are
+// read with agent-scope atomic loads: they were published by other
+// workgroups of the same kernel through atomic stores.
+template <int NT>
+__device__ __forceinline__ void rowscan_all(const Params& p, int* smem) {
+  const int NR = p.NR;
+  const int per = (NR + NT - 1) / NT;
+  const int r0 = min((int)threadIdx.x * per, NR);
+  const int r1 = min(r0 + per, NR);
+  int cnt = 0, units = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int c = __hip_atomic_load(&p.row_cnt[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cnt += c;
+    units += (c + p.Tu - 1) / p.Tu;
+  }
+  int tot_cnt, tot_units;
+  int run_c = block_excl_scan<NT>(cnt, &tot_cnt, smem);
+  int run_u = block_excl_scan<NT>(units, &tot_units, smem);
+  for (int r = r0; r < r1; ++r) {
+    const int c = __hip_atomic_load(&p.row_cnt[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    p.row_off[r] = run_c;
+    p.unit_off[r] = run_u;
+    run_c += c;
+    run_u += (c + p.Tu - 1) / p.Tu;
+  }
+  if (threadIdx.x == 0) {
+    p.row_off[NR] = tot_cnt;
+    p.unit_off[NR] = tot_units;
+    p.counters[kCntUnits] = tot_units;
+  }
+}
+
+// Index of residual slot (t, g) -> block b in the residual order: the row's
+// offset plus the token's rank among the row's set bits. The row data were
+// written by an earlier kernel.
+__device__ __forceinline__ int residual_pos(const Params& p, int t, int g, int b) {
+  const size_t r = (size_t)b * p.Hkv + g;
+  const size_t w = r * p.W + (t >> 5);
+  const uint32_t below = p.wordbits[w] & ((1u << (t & 31)) - 1u);
+  return p.row_off[r] + (int)p.wordpre[w] + __popc(below);
+}
+
+// Materialises the residual order for one slot (ent, slot_pos); used by the
+// staged index entry point, which returns these arrays for testing. Flags of
+// tokens this call did not classify (only with malformed cu_seqlens) are
+// ignored: their bit is not set.
+__device__ __forceinline__ void emit_slot(const Params& p, int64_t slot) {
+  if (p.slot_flag[slot] != 2) return;
+  const int t = (int)(slot / ((int64_t)p.Hkv * p.K));
+  const int g = (int)((slot / p.K) % p.Hkv);
+  const int b = p.selected[slot];
+  if (b < 0 || b >= p.nb_max) return;
+  const size_t w = ((size_t)b * p.Hkv + g) * p.W + (t >> 5);
+  if (!((p.wordbits[w] >> (t & 31)) & 1u)) return;
+  const int pos = residual_pos(p, t, g, b);
+  p.ent[pos] = (int)slot;
+  p.slot_pos[slot] = pos;
+}
+
+}  // namespace msa

@@ -102,10 +102,11 @@ typedef struct msa_tensor {
  * (t, g) list are distinct, cu_seqlens_q is non-decreasing with
  * cu_seqlens_q[0] == 0 and cu_seqlens_q[B] == Tq, used_kv_lens[s] <=
  * max_pages*page_size, and every page id reached by a selected key lies in
- * [0, num_pages). A violation gives unspecified output values but the
- * kernels stay within the buffers given: a page id outside the pool is
- * treated as holding no keys. Tokens outside every sequence get out = 0 and
- * lse = -inf. Tq == 0 returns MSA_OK and enqueues nothing.
+ * [0, num_pages). A violation gives unspecified output values (tokens outside
+ * every sequence may be left unwritten) but the kernels stay within the
+ * buffers given: a page id outside the pool is treated as holding no keys,
+ * and every wait inside the kernels is bounded. Tq == 0 returns MSA_OK and
+ * enqueues nothing.
  *
  * Scratch memory: the library keeps one growable workspace per device
  * (allocated with hipMalloc on first use or when a larger problem arrives;
@@ -135,13 +136,17 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  * slots are inverted into rows r = b*Hkv + g: row_off is the exclusive scan
  * of the row counts, ent lists each row's slot ids in ascending order, and
  * slot_pos[slot] is the slot's index in ent (-1 if not residual). unit_off is
- * the exclusive scan of ceil(row count / unit_tokens). A chain is listed in
- * narrow_items when tile_tokens_in_tile * (Hq/Hkv) <= 16, else in
- * wide_items, as t_leader*Hkv + g; those two lists are in unspecified order.
+ * the exclusive scan of ceil(row count / unit_tokens). Chains of tiles with
+ * more than 16 query rows (tokens in the tile * Hq/Hkv), or every chain when
+ * list_all_chains is 1, are listed in wide_items as t_leader*Hkv + g (the
+ * two settings are the two launch shapes of the classifier: one workgroup
+ * per token, or one per tile); pairs (t, g) whose output is produced by
+ * merging partial results (a residual slot, or no chain) are listed in
+ * combine_items as t*Hkv + g. Both lists are in unspecified order.
  *
  * All output buffers are caller-owned device memory of the sizes given;
  * chain_blk holds valid entries only at leader tokens (first tok_chain
- * entries). counters[0..3] = residual slots, narrow items, wide items, units.
+ * entries). counters[0..3] = residual slots, combine items, wide items, units.
  * Inputs as in msa_kvouter_attention; nb_max = ceil(max_pages*page_size/128).
  */
 typedef struct msa_index_out {
@@ -153,7 +158,7 @@ typedef struct msa_index_out {
   int32_t* unit_off;     /* [nb_max*Hkv + 1] */
   int32_t* ent;          /* [Tq*Hkv*topk] capacity */
   int32_t* slot_pos;     /* [Tq*Hkv*topk] */
-  int32_t* narrow_items; /* [Tq*Hkv] capacity */
+  int32_t* combine_items; /* [Tq*Hkv] capacity */
   int32_t* wide_items;   /* [Tq*Hkv] capacity */
   int32_t* counters;     /* [8] */
 } msa_index_out;
@@ -161,7 +166,7 @@ typedef struct msa_index_out {
 int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
                         const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max,
                         int32_t causal, int32_t tile_tokens, int32_t unit_tokens,
-                        const msa_index_out* out, void* stream);
+                        int32_t list_all_chains, const msa_index_out* out, void* stream);
 
 /*
  * msa_widen_fp8 -- widen n e4m3fn values (device bytes `in`) to bf16 or fp16
@@ -183,6 +188,24 @@ int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache,
                             const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
                             const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
                             void* stream);
+
+/*
+ * Kernel timing for benchmarks. msa_profile_enable(mask) makes every later
+ * msa_kvouter_attention call record a pair of HIP events on its stream
+ * around each launch of the kernels whose bit is set in `mask`
+ * (1 << MSA_KERNEL_*); mask 0 turns recording off. Enabling discards
+ * earlier records. msa_profile_collect waits for the recorded events of one
+ * kernel and returns their summed duration (ms) and the number of launches,
+ * then forgets them. Recording costs one event pair per timed launch.
+ */
+enum {
+  MSA_KERNEL_INDEX = 0, /* residual inversion: row counts and scan */
+  MSA_KERNEL_FRONT = 1, /* classification + streaming of tiles of <= 16 rows */
+  MSA_KERNEL_WORK = 2,  /* wide tiles and KV-outer units (LDS-staged) */
+  MSA_KERNEL_MERGE = 3, /* LSE merges of partial results */
+};
+int32_t msa_profile_enable(uint32_t kernel_mask);
+int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* msa_last_error(void);

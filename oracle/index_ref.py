@@ -28,7 +28,11 @@ into units of at most ``unit_tokens`` entries; ``unit_off`` is the
 exclusive scan of ceil(count/unit_tokens).
 
 Per (t, g): ``tok_chain`` is the chain length of t's tile and ``tok_nres``
-the number of residual slots of (t, g).
+the number of residual slots of (t, g). Chains of tiles with more than 16
+query rows (tile tokens x G) form the wide work list (every chain when
+``list_all_chains`` is set); pairs whose output is
+merged from partial results (a residual slot, or no chain) form the combine
+list.
 """
 from __future__ import annotations
 
@@ -50,8 +54,8 @@ class Plan:
     ent: np.ndarray            # [nres] int32
     slot_pos: np.ndarray       # [Tq, Hkv, K] int32
     unit_off: np.ndarray       # [nb_max*Hkv + 1] int32
-    narrow_items: set          # {t0*Hkv + g} chains with tile rows <= 16
     wide_items: set            # {t0*Hkv + g} chains with tile rows > 16
+    combine_items: set         # {t*Hkv + g} outputs merged from partials
 
 
 def token_sequence(cu: np.ndarray, Tq: int) -> np.ndarray:
@@ -84,7 +88,7 @@ def slot_validity(selected, cu, used, causal, nb_max):
 
 
 def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
-          nb_max: int, G: int) -> Plan:
+          nb_max: int, G: int, list_all_chains: bool = False) -> Plan:
     selected = np.asarray(selected, dtype=np.int32)
     Tq, Hkv, K = selected.shape
     cu = np.asarray(cu, dtype=np.int64)
@@ -103,7 +107,7 @@ def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
     slot_flag = np.where(valid, 2, 0).astype(np.uint8)
     tok_chain = np.zeros((Tq, Hkv), dtype=np.int32)
     chain_blk = {}
-    narrow, wide = set(), set()
+    wide = set()
     if tile_tokens > 0:
         for s in range(len(cu) - 1):
             q0, q1 = int(cu[s]), int(cu[s + 1])
@@ -125,8 +129,11 @@ def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
                     if chain:
                         cover = valid[t0:t1, g, :] & np.isin(b64[t0:t1, g, :], chain)
                         slot_flag[t0:t1, g, :][cover] = 1
-                        (narrow if (t1 - t0) * G <= 16 else wide).add(t0 * Hkv + g)
+                        if list_all_chains or (t1 - t0) * G > 16:
+                            wide.add(t0 * Hkv + g)
     tok_nres = (slot_flag == 2).sum(axis=2).astype(np.int32)
+    need = (tok_nres > 0) | (tok_chain == 0)
+    combine = set(int(x) for x in np.nonzero(need.reshape(-1))[0])
 
     NR = nb_max * Hkv
     slot_ids = np.arange(Tq * Hkv * K, dtype=np.int64).reshape(Tq, Hkv, K)
@@ -148,5 +155,5 @@ def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
         slot_flag=slot_flag, tok_chain=tok_chain, tok_nres=tok_nres, chain_blk=chain_blk,
         row_off=row_off.astype(np.int32), ent=ids.astype(np.int32),
         slot_pos=slot_pos.reshape(Tq, Hkv, K).astype(np.int32),
-        unit_off=unit_off.astype(np.int32), narrow_items=narrow, wide_items=wide,
+        unit_off=unit_off.astype(np.int32), wide_items=wide, combine_items=combine,
     )

@@ -144,8 +144,9 @@ def test_build_index_argument_checks():
     cu = desc([3], msa.MSA_INT64)
     used = desc([2], msa.MSA_INT32)
     r = ctypes.byref
-    assert lib.msa_build_index(r(sel), r(cu), r(used), 15, 4, 0, 8, 8, r(o), None) == INV   # Hq % Hkv
-    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 129, 8, r(o), None) == INV  # tile too big
-    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 0, r(o), None) == INV    # unit 0
-    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 0, 0, 8, 8, r(o), None) == INV    # nb_max 0
-    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, None, None) == INV
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 15, 4, 0, 8, 8, 0, r(o), None) == INV   # Hq % Hkv
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 129, 8, 0, r(o), None) == INV  # tile too big
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 0, 0, r(o), None) == INV    # unit 0
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 0, 0, 8, 8, 0, r(o), None) == INV    # nb_max 0
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, 2, r(o), None) == INV    # flag
+    assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, 0, None, None) == INV

@@ -53,15 +53,16 @@ def test_widen_fp8_every_code(out_dtype):
 # ---------------------------------------------------------------------------
 # index builder: bit-exact against the CPU reference
 # ---------------------------------------------------------------------------
-def _index_case(wl, T, Tu):
+def _index_case(wl, T, Tu, list_all=False):
     import block_sparse_attention_selection_amd as msa
     from oracle import index_ref
 
     nb_max = (wl.block_tables.shape[1] * wl.page_size + 127) // 128
-    ref = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G)
+    ref = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G,
+                          list_all_chains=list_all)
     got = msa.build_index(torch.from_numpy(wl.selected).cuda(), torch.from_numpy(wl.cu_seqlens_q).cuda(),
                           torch.from_numpy(wl.used_kv_lens).cuda(), Hq=wl.Hq, nb_max=nb_max,
-                          causal=wl.causal, tile_tokens=T, unit_tokens=Tu)
+                          causal=wl.causal, tile_tokens=T, unit_tokens=Tu, list_all_chains=list_all)
     got = {k: v.cpu().numpy() for k, v in got.items()}
     Tq, Hkv, K = wl.selected.shape
     assert np.array_equal(got["slot_flag"], ref.slot_flag.reshape(-1))
@@ -77,29 +78,30 @@ def _index_case(wl, T, Tu):
     cb = got["chain_blk"].reshape(Tq, Hkv, K)
     for (t0, g), ch in ref.chain_blk.items():
         assert list(cb[t0, g, :len(ch)]) == ch, (t0, g)
-    nn, nw = got["counters"][1], got["counters"][2]
-    assert set(got["narrow_items"][:nn].tolist()) == ref.narrow_items
-    assert set(got["wide_items"][:nw].tolist()) == ref.wide_items
+    nc, nw = got["counters"][1], got["counters"][2]
+    assert sorted(got["combine_items"][:nc].tolist()) == sorted(ref.combine_items)
+    assert sorted(got["wide_items"][:nw].tolist()) == sorted(ref.wide_items)
 
 
+@pytest.mark.parametrize("list_all", [False, True])
 @pytest.mark.parametrize("T,Tu", [(0, 3), (1, 2), (2, 2), (3, 4), (16, 16)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_index_builder_bitexact_custom(T, Tu, causal):
+def test_index_builder_bitexact_custom(T, Tu, causal, list_all):
     wl = W.make_custom(300 + T, [3, 5, 1, 0, 40, 7], [300, 700, 129, 50, 5200, 900], 16, 2, 64, topk=6,
                        causal=causal, pick="oob", shared_chunk=8, shared_picks=3, pad_every=5)
-    _index_case(wl, T, Tu)
+    _index_case(wl, T, Tu, list_all)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_gqa", "varlen_mqa"])
 def test_index_builder_bitexact_named(name):
     wl = W.make(name)
     T = max(1, 128 // wl.G)
-    _index_case(wl, T, T)
+    _index_case(wl, T, T, list_all=name == "varlen_mqa")
 
 
 def test_index_builder_bitexact_prefill_shared():
     wl = W.make("prefill_shared")
-    _index_case(wl, 16, 16)
+    _index_case(wl, 16, 16, list_all=True)
 
 
 # ---------------------------------------------------------------------------
