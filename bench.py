@@ -46,8 +46,8 @@ DESCRIPTIONS = {
     "decode_fp8": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
                   "K/V fp8 e4m3fn, q bf16, causal",
 }
-DOMINANT = {"tiny": "work", "decode_gqa": "front", "decode_fp8": "front",
-            "prefill_shared": "work", "varlen_mqa": "work"}
+DOMINANT = {"tiny": "tiles", "decode_gqa": "front", "decode_fp8": "front",
+            "prefill_shared": "tiles", "varlen_mqa": "tiles"}
 
 
 def log(*a):

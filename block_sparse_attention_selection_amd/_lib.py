@@ -47,7 +47,7 @@ class MsaTensor(ctypes.Structure):
 class MsaIndexOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "slot_flag", "tok_chain", "tok_nres", "chain_blk", "row_off", "unit_off",
-        "ent", "slot_pos", "combine_items", "wide_items", "counters")]
+        "ent", "slot_pos", "tile_items", "counters")]
 
 
 _lock = threading.Lock()
@@ -169,7 +169,7 @@ def validate_inputs(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q
 
 
 def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, causal: bool,
-                tile_tokens: int, unit_tokens: int, list_all_chains: bool = False):
+                tile_tokens: int, unit_tokens: int, list_all_tiles: bool = False):
     """Run the index builder alone; returns its device arrays as a dict."""
     lib = load()
     _device_check(selected, cu_seqlens_q, used_kv_lens)
@@ -186,21 +186,20 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
         unit_off=torch.zeros(NR + 1, **i32),
         ent=torch.full((max(1, Tq * Hkv * K),), -1, **i32),
         slot_pos=torch.zeros(Tq * Hkv * K, **i32),
-        combine_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
-        wide_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
+        tile_items=torch.full((max(1, Tq * Hkv),), -1, **i32),
         counters=torch.zeros(8, **i32),
     )
     o = MsaIndexOut(**{k: v.data_ptr() for k, v in res.items()})
     ds = [describe(x) for x in (selected, cu_seqlens_q, used_kv_lens)]
     with torch.cuda.device(dev):
         rc = lib.msa_build_index(*[_ref(d) for d in ds], int(Hq), int(nb_max), int(bool(causal)),
-                                 int(tile_tokens), int(unit_tokens), int(bool(list_all_chains)),
+                                 int(tile_tokens), int(unit_tokens), int(bool(list_all_tiles)),
                                  ctypes.byref(o), _stream(dev))
     _check(rc)
     return res
 
 
-KERNELS = {"index": 0, "front": 1, "work": 2, "merge": 3}
+KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3}
 
 
 def profile_enable(kernels=()):

@@ -179,20 +179,18 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->tok_chain = c.take<int32_t>(base, TG);
   p->tok_nres = c.take<int32_t>(base, TG);
   p->chain_blk = c.take<int32_t>(base, nslots);
-  p->combine_items = c.take<int32_t>(base, TG);
-  p->wide_items = c.take<int32_t>(base, TG);
+  p->tile_items = c.take<int32_t>(base, TG);
   p->row_cnt = c.take<int32_t>(base, d.NR);
   p->row_off = c.take<int32_t>(base, (size_t)d.NR + 1);
   p->unit_off = c.take<int32_t>(base, (size_t)d.NR + 1);
   p->ent = c.take<int32_t>(base, nslots);
   p->slot_pos = c.take<int32_t>(base, nslots);
   if (with_partials) {
-    p->cpart = c.take<float>(base, (size_t)d.Tq * d.Hq * 128);
-    p->clse = c.take<float>(base, (size_t)d.Tq * d.Hq);
-    p->opart = c.take<float>(base, nslots * d.G * 128);
+    p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
-    p->cpart = p->clse = p->opart = p->lpart = nullptr;
+    p->opart = nullptr;
+    p->lpart = nullptr;
   }
   return c.off + 256;
 }
@@ -411,10 +409,11 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   layout(d, (char*)ws.scratch, &p, true);
   fill_inputs(&p, d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
   // decode-shaped batches (few queries per sequence, at most 16 query rows
-  // per token) stream their chains from the front kernel, one workgroup per
-  // token; otherwise the front kernel runs one workgroup per tile and every
-  // chain goes to the back kernel
+  // per token) finish their residual-free tiles in the front kernel, one
+  // workgroup per token; otherwise the front kernel runs one workgroup per
+  // tile and lists every tile for the tile kernel
   p.stream_narrow = (d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B) ? 1 : 0;
+  p.list_tiles = p.stream_narrow;  // otherwise the tile kernel enumerates every tile itself
   int32_t* sets = (int32_t*)ws.zs;
   p.counters = sets + ws.parity * msa::kCntSlots;
   p.counters_next = sets + (1 - ws.parity) * msa::kCntSlots;
@@ -430,8 +429,8 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
   if (e == hipSuccess) e = msa::launch_front(p, d.q_elem, d.kv_elem, st);
   if (e == hipSuccess) e = msa::launch_index(p, false, st);
-  if (e == hipSuccess) e = msa::launch_work(p, d.q_elem, d.kv_elem, ws.num_cu, st);
-  if (e == hipSuccess) e = msa::launch_merge(p, d.q_elem, ws.num_cu, st);
+  if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+  if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, ws.num_cu, st);
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     if (e != hipSuccess) {
@@ -447,7 +446,7 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
 
 int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
                         const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max, int32_t causal,
-                        int32_t tile_tokens, int32_t unit_tokens, int32_t list_all_chains,
+                        int32_t tile_tokens, int32_t unit_tokens, int32_t list_all_tiles,
                         const msa_index_out* o, void* stream) {
   int32_t rc;
   if ((rc = check_tensor(selected, "selected", 3, MSA_INT32, 4))) return rc;
@@ -463,10 +462,10 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   if (unit_tokens < 1 || unit_tokens > 128) return fail(MSA_ERR_INVALID_ARGUMENT, "unit_tokens must be in [1, 128]");
   if (nb_max < 1 || (int64_t)nb_max * Hkv >= (1ll << 30)) return fail(MSA_ERR_INVALID_ARGUMENT, "nb_max out of range");
   if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
-  if (list_all_chains != 0 && list_all_chains != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "list_all_chains must be 0 or 1");
+  if (list_all_tiles != 0 && list_all_tiles != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "list_all_tiles must be 0 or 1");
   if (Tq * Hkv * K >= (1ll << 31)) return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit indices");
   if (!o->slot_flag || !o->tok_chain || !o->tok_nres || !o->chain_blk || !o->row_off || !o->unit_off ||
-      !o->ent || !o->slot_pos || !o->combine_items || !o->wide_items || !o->counters)
+      !o->ent || !o->slot_pos || !o->tile_items || !o->counters)
     return fail(MSA_ERR_INVALID_ARGUMENT, "msa_index_out: null buffer");
   if (Tq == 0) return ok();
   Dims d{};
@@ -489,7 +488,8 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   fill_inputs(&p, d, selected, nullptr, cu_seqlens_q, used_kv_lens, causal);
   p.T = tile_tokens;
   p.Tu = unit_tokens;
-  p.stream_narrow = list_all_chains ? 0 : 1;
+  p.stream_narrow = list_all_tiles ? 0 : 1;
+  p.list_tiles = 1;
   p.counters = o->counters;  // caller-visible counters; the bitmap stays internal
   p.counters_next = nullptr;
   p.zero_page = ws.zs + 2 * msa::kCntSlots * sizeof(int32_t);
@@ -502,8 +502,7 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   p.unit_off = o->unit_off;
   p.ent = o->ent;
   p.slot_pos = o->slot_pos;
-  p.combine_items = o->combine_items;
-  p.wide_items = o->wide_items;
+  p.tile_items = o->tile_items;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);

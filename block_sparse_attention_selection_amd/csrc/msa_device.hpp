@@ -72,9 +72,12 @@ __device__ __forceinline__ uint32_t to_bits16<f16_t>(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
+// two values, one v_cvt_pk_{bf16,f16}_f32
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return to_bits16<T>(lo) | (to_bits16<T>(hi) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), t2));
 }
 
 template <typename T>

@@ -1,17 +1,21 @@
-// msa_forward.hip -- KV-stationary block-sparse attention on gfx950 MFMA.
+// msa_forward.hip -- the front kernel: classification of every tile, and
+// the decode-shaped tiles finished in place, on gfx950 MFMA (16x16x32).
 //
 // fw-ai/minimax-kernels README, intro: a selected KV block is loaded once
-// and every query that selected it is processed against it. Work arrives as
-//   chain items  a tile of consecutive tokens of one sequence (x the G query
-//                heads of KV head g) and the blocks that every token of the
-//                tile selected: query rows stay in registers while the
-//                blocks stream past (decode is the one-token case);
-//   units        up to Tu tokens that picked one block outside their tile's
-//                chain (KV-outer proper): the block is staged once in LDS
-//                and all the units' rows are multiplied against it.
-// Each wave owns 16 query rows. Scores are computed transposed,
-// S^T = K * Q^T, so that a lane's D fragment holds one query row; the
-// probabilities are then already laid out as the B operand of
+// and every query that selected it is processed against it. Queries are cut
+// into tiles of consecutive tokens of one sequence (x the G query heads of
+// KV head g); a tile's CHAIN is the blocks every token of the tile selected.
+// The front kernel runs one workgroup per tile leader: it finds the chain,
+// flags each slot covered (its block is in the chain) or residual, sets the
+// residual bits of the per-(block, KV head) token bitmaps, and either
+//   finishes the tile itself (decode-shaped batches: at most 16 query rows
+//   and no residual slot -- one decode token x G heads is the common case),
+//   streaming the chain's blocks with the rows held in registers, or
+//   lists the tile for the tile kernel (msa_tiles.hip), which also merges
+//   the KV-outer partials of the residual slots.
+// Each wave of the streaming path owns 16 query rows. Scores are computed
+// transposed, S^T = K * Q^T, so that a lane's D fragment holds one query
+// row; the probabilities are then already laid out as the B operand of
 // O^T = V^T * P^T and the online-softmax rescale stays lane-local.
 // Rows whose keys are masked (beyond the used length, causally invisible,
 // or from another sequence) are removed by select, never by arithmetic, and
@@ -201,12 +205,14 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
   }
 };
 
-// Streams the chain of a tile of at most 16 query rows (see k_front).
+// Streams the chain of a residual-free tile of at most 16 query rows (see
+// k_front) and writes its final O and LSE. An empty chain writes zeros and
+// an LSE of -inf.
 template <typename CT, typename KVT>
 __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int s, int L, int Tq_s,
                                              int64_t q0, int rows, int n_ch, int ppb,
                                              const int* s_chain, const int* s_chain_k,
-                                             const int* s_page, const int* s_nres) {
+                                             const int* s_page) {
   typedef typename KvElem<KVT>::type E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Hkv = p.Hkv;
@@ -299,29 +305,24 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
   const int rh = g * p.G + (row % p.G);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const float lse2 = wsum > 0.f ? Mu + log2f(wsum) : -INFINITY;
-  if (s_nres[row / p.G] == 0) {
-    u32x4 pk;
+  u32x4 pk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-    *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
-    if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
-  } else {
-    float* dst = p.cpart + ((size_t)rtok * p.Hq + rh) * kD + d0;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) dst[d] = acc[d] * inv;
-    if (d0 == 0) p.clse[(size_t)rtok * p.Hq + rh] = lse2;
-  }
+  for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
+  if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
 }
 
 // ---------------------------------------------------------------------------
-// front kernel: one workgroup per (token t, KV head g); only tile leaders do
-// work. It classifies the tile's slots (chain, covered/residual flags,
-// residual bitmap bits, work lists) and, when the tile has at most 16 query
-// rows (decode: one token x G heads), streams the chain's blocks right away:
-// the chain's chunks are split over the four waves, each keeping two chunks
-// of K/V in flight in registers, and the waves' softmax states are merged
-// through LDS. The chunk addresses are resolved once, up front, so no page
-// lookup sits between consecutive loads.
+// front kernel: one workgroup per (token t, KV head g) in decode mode, per
+// tile otherwise; only tile leaders do work. It classifies the tile's slots
+// (chain, covered/residual flags, residual bitmap bits) and, in decode mode,
+// when the tile has at most 16 query rows and no residual slot, streams the
+// chain's blocks right away: the chain's chunks are split over the four
+// waves, each keeping two chunks of K/V in flight in registers, and the
+// waves' softmax states are merged through LDS. The chunk addresses are
+// resolved once, up front, so no page lookup sits between consecutive loads.
+// Every other tile is appended to the tile list. Tokens outside every
+// sequence (decode mode) get zero outputs and an LSE of -inf here.
 // ---------------------------------------------------------------------------
 template <typename CT, typename KVT, bool ATTN>
 __global__ __launch_bounds__(256, 2) void k_front(Params p) {
@@ -331,6 +332,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   __shared__ int s_nres[128];     // residual slots per tile token
   __shared__ int s_page[128];     // pages of the leader's picks (ppb per pick)
   __shared__ int s_nch;
+  __shared__ int s_tile_res;      // residual slots of the tile
   const int g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = p.K, Hkv = p.Hkv;
@@ -343,13 +345,19 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     t = blockIdx.x;
     if (tid < K) b_raw = p.selected[((size_t)t * Hkv + g) * K + tid];
     s = wave_seq_of(p.cu, p.B, t);
-    if (s < 0) {  // outside every sequence: no keys; the combine writes zeros
+    if (s < 0) {  // outside every sequence: no keys
       const size_t tg = (size_t)t * Hkv + g;
       if (tid < K) p.slot_flag[tg * K + tid] = 0;
       if (tid == 0) {
         p.tok_chain[tg] = 0;
         p.tok_nres[tg] = 0;
-        p.combine_items[atomicAdd(&p.counters[kCntCombine], 1)] = (int)tg;
+      }
+      if constexpr (ATTN) {
+        for (int i = tid; i < p.G * 16; i += 256) {
+          const int hh = g * p.G + (i >> 4);
+          *(u32x4*)((uint16_t*)p.out + ((size_t)t * p.Hq + hh) * kD + 8 * (i & 15)) = u32x4{0u, 0u, 0u, 0u};
+          if ((i & 15) == 0 && p.lse) p.lse[(size_t)hh * p.Tq + t] = -INFINITY;
+        }
       }
       return;
     }
@@ -368,6 +376,8 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   const int i0 = (int)(t - q0);
   const int nt = (int)min((int64_t)Teff, q1 - t);
   const int rows = nt * p.G;
+  // a decode-mode tile of at most 16 rows is streamed here unless it turns
+  // out to have residual slots
   const bool stream = ATTN && p.stream_narrow && rows <= 16;
   const int ppb = kBlk / p.P;  // pages per block
 
@@ -439,459 +449,30 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   }
   __syncthreads();
 
-  // per-token results and work lists (one atomic per list per tile)
+  // per-token results; the tile is finished here or listed
   if (wave == 0) {
-    int res = 0, need = 0;
+    int res = 0;
     for (int tau = lane; tau < nt; tau += 64) {
       const size_t tg2 = (size_t)(t + tau) * Hkv + g;
       const int nr = s_nres[tau];
       p.tok_chain[tg2] = n_ch;
       p.tok_nres[tg2] = nr;
       res += nr;
-      need += (nr > 0 || n_ch == 0) ? 1 : 0;
     }
-    int excl = need;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(excl, off, 64);
-      if (lane >= off) excl += y;
-    }
-    const int tot_need = __shfl(excl, 63, 64);
-    excl -= need;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) res += __shfl_xor(res, off, 64);
-    int base = 0;
     if (lane == 0) {
+      s_tile_res = res;
       if (res > 0) atomicAdd(&p.counters[kCntResidual], res);
-      if (tot_need > 0) base = atomicAdd(&p.counters[kCntCombine], tot_need);
-      if (n_ch > 0 && (rows > 16 || !p.stream_narrow)) p.wide_items[atomicAdd(&p.counters[kCntWide], 1)] = (int)tg;
-    }
-    base = __shfl(base, 0, 64);
-    for (int tau = lane; tau < nt; tau += 64) {
-      const int nr = s_nres[tau];
-      if (nr > 0 || n_ch == 0) p.combine_items[base + excl++] = (int)((size_t)(t + tau) * Hkv + g);
+      const bool here = p.stream_narrow && rows <= 16 && res == 0;
+      if (!here && p.list_tiles) p.tile_items[atomicAdd(&p.counters[kCntTiles], 1)] = (int)tg;
     }
   }
   if constexpr (ATTN) {
-    if (stream && n_ch > 0)
-      stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page, s_nres);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// wide kernel: chain items with more than 16 rows, then KV-outer units.
-// Each block is staged once in LDS (K and V, 16-bit, 16-byte chunks XOR-
-// swizzled by row so both operand read patterns are bank-conflict free) and
-// every wave multiplies its one or two 16-row tiles against it.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
-
-template <typename CT, typename KVT>
-struct BlockStager;
-
-template <typename CT>
-struct BlockStager<CT, CT> {
-  // 128 rows x 16 chunks per tensor; 8 chunks of K and 8 of V per thread
-  static __device__ __forceinline__ void stage(u32x4* sk, u32x4* sv, const Params& p, int s, int g,
-                                               int b, int L) {
-    for (int i = 0; i < 8; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int row = idx >> 4, ch = idx & 15;
-      const int tok = kBlk * b + row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (tok < L) {
-        const int page = p.block_tables[(size_t)s * p.MP + tok / p.P];
-        if (page >= 0 && page < p.NP) {
-          const size_t off = (((size_t)page * p.Hkv + g) * p.P + (tok % p.P)) * kD + 8 * ch;
-          kv = *(const u32x4*)((const uint16_t*)p.k + off);
-          vv = *(const u32x4*)((const uint16_t*)p.v + off);
-        }
-      }
-      sk[swz(row, ch)] = kv;
-      sv[swz(row, ch)] = vv;
-    }
-  }
-};
-
-template <typename CT>
-struct BlockStager<CT, fp8_e4m3_t> {
-  // 128 rows x 8 chunks of 16 fp8 per tensor; 4 chunks of K and 4 of V per thread
-  static __device__ __forceinline__ void stage(u32x4* sk, u32x4* sv, const Params& p, int s, int g,
-                                               int b, int L) {
-    for (int i = 0; i < 4; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int row = idx >> 3, ch = idx & 7;
-      const int tok = kBlk * b + row;
-      u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-      if (tok < L) {
-        const int page = p.block_tables[(size_t)s * p.MP + tok / p.P];
-        if (page >= 0 && page < p.NP) {
-          const size_t off = (((size_t)page * p.Hkv + g) * p.P + (tok % p.P)) * kD + 16 * ch;
-          kr = *(const u32x4*)((const uint8_t*)p.k + off);
-          vr = *(const u32x4*)((const uint8_t*)p.v + off);
-        }
-      }
-      sk[swz(row, 2 * ch)] = widen8<CT>(u32x2{kr[0], kr[1]});
-      sk[swz(row, 2 * ch + 1)] = widen8<CT>(u32x2{kr[2], kr[3]});
-      sv[swz(row, 2 * ch)] = widen8<CT>(u32x2{vr[0], vr[1]});
-      sv[swz(row, 2 * ch + 1)] = widen8<CT>(u32x2{vr[2], vr[3]});
-    }
-  }
-};
-
-template <typename CT>
-__device__ __forceinline__ void lds_fragments(u32x4 (&ka)[2][4], u32x4 (&va)[8], const u32x4* sk,
-                                              const u32x4* sv, int part, int q, int c) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 32 * part + 16 * j + c;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ka[j][s] = sk[swz(row, kmap(s, q) >> 3)];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) va[e] = sv[swz(32 * part + key_of(q, e), c)];
-}
-
-// Tokens with ranks [rank0, rank0 + n) among the set bits of row r (one
-// wave): the word holding rank0 is found by two rounds of sampled loads of
-// the row's exclusive popcount prefix, then consecutive words are scanned
-// 64 at a time, each lane expanding its own word.
-__device__ __forceinline__ void unit_tokens(const Params& p, int r, int rank0, int n, int* s_tok) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t* pre = p.wordpre + (size_t)r * p.W;
-  const uint32_t* bits = p.wordbits + (size_t)r * p.W;
-  int lo = 0, hi = p.W;  // the word is the largest w with pre[w] <= rank0
-  while (hi - lo > 64) {
-    const int stride = (hi - lo + 63) / 64;
-    const int w = lo + lane * stride;
-    const bool le = w < hi && (int)pre[w] <= rank0;
-    const int c = __popcll(__ballot(le));
-    lo = lo + (c - 1) * stride;
-    hi = min(lo + stride, hi);
-  }
-  {
-    const int w = lo + lane;
-    const bool le = w < hi && (int)pre[w] <= rank0;
-    lo = lo + __popcll(__ballot(le)) - 1;
-  }
-  for (int wb = lo; wb < p.W; wb += 64) {
-    const int w = wb + lane;
-    uint32_t x = 0u;
-    int rk = 0;
-    if (w < p.W) {
-      x = bits[w];
-      rk = (int)pre[w];
-    }
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      x &= x - 1u;
-      if (rk >= rank0 && rk < rank0 + n) s_tok[rk - rank0] = w * 32 + bit;
-      ++rk;
-    }
-    if (!__any(w < p.W && rk < rank0 + n)) break;  // every lane is past the unit's last rank
-  }
-}
-
-// One wide item: a chain of a tile with more than 16 query rows (or any
-// chain in prefill mode), or a KV-outer unit (up to Tu tokens that picked one
-// block outside their tile's chain). Each block is staged once in LDS (K and
-// V, 16-bit, 16-byte chunks XOR-swizzled by row so both operand read patterns
-// are bank-conflict free) and every wave multiplies its one or two 16-row
-// tiles against it.
-template <typename CT, typename KVT>
-__device__ __forceinline__ void wide_item(const Params& p, bool is_chain, int index, u32x4* s_k, u32x4* s_v,
-                                          int* s_tok, int* s_seq, const int64_t* cu) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int Teff = p.T > 0 ? p.T : 1;
-  const int it = index;
-  // ---- item description
-  int g, ntok, nblocks, b_unit = 0, e0 = 0;
-  const int32_t* blocks = nullptr;
-  if (is_chain) {
-    const int code = p.wide_items[it];
-    const int t0 = code / p.Hkv;
-    g = code - t0 * p.Hkv;
-    const int s = seq_of(cu, p.B, t0);
-    ntok = (int)min((int64_t)Teff, min(p.cu[s + 1], (int64_t)p.Tq) - t0);
-    nblocks = p.tok_chain[(size_t)t0 * p.Hkv + g];
-    blocks = p.chain_blk + ((size_t)t0 * p.Hkv + g) * p.K;
-    if (threadIdx.x < ntok) {
-      s_tok[threadIdx.x] = t0 + threadIdx.x;
-      s_seq[threadIdx.x] = s;
-    }
-  } else {
-    const int u = it;
-    int lo = 0, hi = p.NR;  // largest r with unit_off[r] <= u
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.unit_off[mid] <= u)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    const int r = lo;
-    b_unit = r / p.Hkv;
-    g = r - b_unit * p.Hkv;
-    const int rank0 = (u - p.unit_off[r]) * p.Tu;
-    e0 = p.row_off[r] + rank0;
-    ntok = min(p.Tu, p.row_off[r + 1] - e0);
-    nblocks = 1;
-    if (wave == 0) unit_tokens(p, r, rank0, ntok, s_tok);
     __syncthreads();
-    if (threadIdx.x < ntok) s_seq[threadIdx.x] = seq_of(cu, p.B, s_tok[threadIdx.x]);
+    if (stream && s_tile_res == 0)
+      stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
   }
-  __syncthreads();
-  const int rows = ntok * p.G;
-
-  // ---- the wave's row tiles (w and w + 4)
-  RowTile<CT> rt[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    tile_reset(rt[i]);
-    const int rho = 16 * (wave + 4 * i) + c;
-    int tok = -1, h = 0;
-    rt[i].seq = -1;
-    rt[i].pos = -1;
-    if (rho < rows) {
-      const int tau = rho / p.G;
-      tok = s_tok[tau];
-      h = g * p.G + (rho - tau * p.G);
-      const int s = s_seq[tau];
-      rt[i].seq = s;
-      const int64_t q0 = p.cu[s];
-      rt[i].pos = p.causal ? (int)(p.used[s] - (p.cu[s + 1] - q0) + (tok - q0)) : INT_MAX;
-    }
-    tile_load_q(rt[i], p, tok, h, q);
-  }
-  const bool has0 = 16 * wave < rows, has1 = 16 * (wave + 4) < rows;
-
-  // ---- blocks (a unit may span several sequences: one run per sequence)
-  int run_start = 0;
-  for (int bi = 0; bi < nblocks;) {
-    int s_run, b;
-    if (is_chain) {
-      s_run = s_seq[0];
-      b = blocks[bi];
-    } else {
-      s_run = s_seq[run_start];
-      b = b_unit;
-    }
-    const int L = min(p.used[s_run], p.MP * p.P);  // keys the page table can reach
-    BlockStager<CT, KVT>::stage(s_k, s_v, p, s_run, g, b, L);
-    __syncthreads();
-    const int nparts = min(4, (L - kBlk * b + 31) / 32);
-    for (int part = 0; part < nparts; ++part) {
-      u32x4 ka[2][4], va[8];
-      lds_fragments<CT>(ka, va, s_k, s_v, part, q, c);
-      const int key0 = kBlk * b + 32 * part;
-      if (has0) tile_chunk(rt[0], ka, va, key0, L, s_run, q, p.scale_log2);
-      if (has1) tile_chunk(rt[1], ka, va, key0, L, s_run, q, p.scale_log2);
-    }
-    __syncthreads();
-    if (is_chain) {
-      ++bi;
-    } else {
-      int nxt = run_start;
-      while (nxt < ntok && s_seq[nxt] == s_run) ++nxt;
-      run_start = nxt;
-      if (run_start >= ntok) bi = nblocks;
-    }
-  }
-
-  // ---- results of the wave's tiles
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float l_row = sum_over_groups(rt[i].l);
-    const int rho = 16 * (wave + 4 * i) + c;
-    if (rho >= rows) continue;
-    const int tau = rho / p.G;
-    const int hr = rho - tau * p.G;
-    const int tok = s_tok[tau];
-    const int h = g * p.G + hr;
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const float mu = rt[i].m == -INFINITY ? 0.f : rt[i].m;
-    const float lse2 = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
-    if (is_chain && p.tok_nres[(size_t)tok * p.Hkv + g] == 0) {
-      uint16_t* dst = (uint16_t*)p.out + ((size_t)tok * p.Hq + h) * kD + 32 * q;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x4 pk;
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2)
-          pk[k2] = pack2<CT>(rt[i].o[2 * k2][r] * inv, rt[i].o[2 * k2 + 1][r] * inv);
-        *(u32x4*)(dst + 8 * r) = pk;
-      }
-      if (q == 0 && p.lse) p.lse[(size_t)h * p.Tq + tok] = lse2 * kLn2;
-    } else {
-      float* dst;
-      float* lsd;
-      if (is_chain) {
-        dst = p.cpart + ((size_t)tok * p.Hq + h) * kD;
-        lsd = p.clse + (size_t)tok * p.Hq + h;
-      } else {
-        const size_t pos = (size_t)(e0 + tau);
-        dst = p.opart + (pos * p.G + hr) * kD;
-        lsd = p.lpart + pos * p.G + hr;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        f32x4 a, bq;
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-          a[k2] = rt[i].o[k2][r] * inv;
-          bq[k2] = rt[i].o[4 + k2][r] * inv;
-        }
-        *(f32x4*)(dst + 32 * q + 8 * r) = a;
-        *(f32x4*)(dst + 32 * q + 8 * r + 4) = bq;
-      }
-      if (q == 0) *lsd = lse2;
-    }
-  }}
-
-// Merge the partial results of one (token, KV head) pair by their
-// log-sum-exp (the chain's partial first, then the residual slots in slot
-// order) and write out[t, h, :] and lse[h, t]. One wave per pair: the
-// residual slots are found with one parallel load per lane, and the partial
-// results are read in batches of independent loads.
-template <typename CT>
-__device__ __forceinline__ void combine_pair(const Params& p, int code) {
-  constexpr int kBatch = 8;
-  const int lane = threadIdx.x & 63;
-  const int t = code / p.Hkv, g = code - (code / p.Hkv) * p.Hkv;
-  const size_t tg = (size_t)code;
-  const int K = p.K;
-  int my_pos = -1;
-  if (lane < K && p.slot_flag[tg * K + lane] == 2) my_pos = residual_pos(p, t, g, p.selected[tg * K + lane]);
-  const uint64_t mres = __ballot(my_pos >= 0);
-  const int nparts = __popcll(mres);
-  // loads past the last part read the first part again (always a valid index)
-  const int pos0 = mres ? __shfl(my_pos, __ffsll((unsigned long long)mres) - 1, 64) : 0;
-  const bool has_chain = p.tok_chain[tg] > 0;
-  // every lane runs every iteration (the shuffles need all lanes active)
-  for (int base = 0; base < p.G * 16; base += 64) {
-    const int idx = base + lane;
-    const bool act = idx < p.G * 16;
-    const int r = act ? idx >> 4 : 0, d0 = (idx & 15) * 8;
-    const int h = g * p.G + r;
-    const float lc = has_chain ? p.clse[(size_t)t * p.Hq + h] : -INFINITY;
-    float M = lc;
-    uint64_t rest = mres;
-    for (int i0 = 0; i0 < nparts; i0 += kBatch) {
-      float l[kBatch];
-      uint64_t m = rest;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int k = m ? __ffsll((unsigned long long)m) - 1 : 0;
-        const int pos = m ? __shfl(my_pos, k, 64) : pos0;
-        const float lv = p.lpart[(size_t)pos * p.G + r];
-        l[j] = (i0 + j < nparts) ? lv : -INFINITY;
-        m &= m - 1;
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) M = fmaxf(M, l[j]);
-      rest = m;
-    }
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float wsum = 0.f, acc[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-    if (has_chain) {
-      const float f = exp2f(lc - Mu);
-      const f32x4* src = (const f32x4*)(p.cpart + ((size_t)t * p.Hq + h) * kD + d0);
-      const f32x4 a0 = src[0], a1 = src[1];
-      wsum += f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[d] += f * a0[d];
-        acc[4 + d] += f * a1[d];
-      }
-    }
-    rest = mres;
-    for (int i0 = 0; i0 < nparts; i0 += kBatch) {
-      float l[kBatch];
-      f32x4 o0[kBatch], o1[kBatch];
-      uint64_t m = rest;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int k = m ? __ffsll((unsigned long long)m) - 1 : 0;
-        const size_t pos = (size_t)(m ? __shfl(my_pos, k, 64) : pos0);
-        const bool live = i0 + j < nparts;
-        const f32x4* src = (const f32x4*)(p.opart + (pos * p.G + r) * kD + d0);
-        const float lv = p.lpart[pos * p.G + r];
-        const f32x4 v0 = src[0], v1 = src[1];
-        l[j] = live ? lv : -INFINITY;
-        o0[j] = live ? v0 : f32x4{0.f, 0.f, 0.f, 0.f};
-        o1[j] = live ? v1 : f32x4{0.f, 0.f, 0.f, 0.f};
-        m &= m - 1;
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const float f = exp2f(l[j] - Mu);
-        wsum += f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          acc[d] += f * o0[j][d];
-          acc[4 + d] += f * o1[j][d];
-        }
-      }
-      rest = m;
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    if (!act) continue;
-    u32x4 pk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-    *(u32x4*)((uint16_t*)p.out + ((size_t)t * p.Hq + h) * kD + d0) = pk;
-    if (d0 == 0 && p.lse) p.lse[(size_t)h * p.Tq + t] = wsum > 0.f ? (Mu + log2f(wsum)) * kLn2 : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// work kernel: a persistent grid pulls wide chains, then KV-outer units, from
-// a shared counter. Items are independent: nothing produced inside this
-// kernel is read inside it.
-// ---------------------------------------------------------------------------
-template <typename CT, typename KVT>
-__global__ __launch_bounds__(256) void k_work(Params p) {
-  __shared__ u32x4 s_k[kBlk * 16];
-  __shared__ u32x4 s_v[kBlk * 16];
-  __shared__ int s_tok[128];
-  __shared__ int s_seq[128];
-  __shared__ int64_t s_cu[1024];  // cu_seqlens_q, when it fits, for the sequence lookups
-  __shared__ int s_task;
-  const int nC = p.counters[kCntWide];
-  const int nU = p.counters[kCntUnits];
-  const int total = nC + nU;
-  if (total == 0) return;
-  const bool cu_in_lds = p.B + 1 <= 1024;
-  if (cu_in_lds)
-    for (int i = threadIdx.x; i <= p.B; i += 256) s_cu[i] = p.cu[i];
-  const int64_t* cu = cu_in_lds ? s_cu : p.cu;
-  for (bool first = true;; first = false) {
-    if (threadIdx.x == 0)
-      s_task = first ? (int)blockIdx.x : (int)gridDim.x + atomicAdd(&p.counters[kCntTask], 1);
-    __syncthreads();
-    const int id = s_task;
-    __syncthreads();
-    if (id >= total) break;
-    if (id < nC)
-      wide_item<CT, KVT>(p, true, id, s_k, s_v, s_tok, s_seq, cu);
-    else
-      wide_item<CT, KVT>(p, false, id - nC, s_k, s_v, s_tok, s_seq, cu);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// merge kernel: one wave per listed (token, KV head) pair; workgroup 0 also
-// clears the counter set of the next call.
-// ---------------------------------------------------------------------------
-template <typename CT>
-__global__ __launch_bounds__(256) void k_merge(Params p) {
-  if (blockIdx.x == 0 && p.counters_next)
-    for (int i = threadIdx.x; i < kCntSlots; i += 256) p.counters_next[i] = 0;
-  const int n = p.counters[kCntCombine];
-  const int wave = threadIdx.x >> 6;
-  for (int pair = blockIdx.x * 4 + wave; pair < n; pair += gridDim.x * 4) combine_pair<CT>(p, p.combine_items[pair]);
 }
 
 // ---------------------------------------------------------------------------
@@ -929,7 +510,9 @@ static hipError_t launch_front_t(const Params& p, hipStream_t st) {
 hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st) {
   profile_mark(kKFront, true, st);
   hipError_t e;
-  if (q_elem < 0)
+  // outside decode mode the front kernel only classifies: the light
+  // instantiation (no attention registers or LDS) keeps many workgroups per CU
+  if (q_elem < 0 || !p.stream_narrow)
     e = launch_front_t<bf16_t, bf16_t, false>(p, st);
   else if (q_elem == kElemBF16)
     e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(p, st)
@@ -938,37 +521,6 @@ hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st
     e = kv_elem == kElemFP8 ? launch_front_t<f16_t, fp8_e4m3_t, true>(p, st)
                             : launch_front_t<f16_t, f16_t, true>(p, st);
   profile_mark(kKFront, false, st);
-  return e;
-}
-
-template <typename CT, typename KVT>
-static hipError_t launch_work_t(const Params& p, int num_cu, hipStream_t st) {
-  profile_mark(kKWork, true, st);
-  hipLaunchKernelGGL((k_work<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
-  hipError_t e = hipGetLastError();
-  profile_mark(kKWork, false, st);
-  return e;
-}
-
-hipError_t launch_work(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
-  if (q_elem == kElemBF16)
-    return kv_elem == kElemFP8 ? launch_work_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
-                               : launch_work_t<bf16_t, bf16_t>(p, num_cu, st);
-  return kv_elem == kElemFP8 ? launch_work_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
-                             : launch_work_t<f16_t, f16_t>(p, num_cu, st);
-}
-
-hipError_t launch_merge(const Params& p, int q_elem, int num_cu, hipStream_t st) {
-  const int64_t pairs = (int64_t)p.Tq * p.Hkv;
-  int grid = (int)min((pairs + 3) / 4, (int64_t)num_cu * 8);
-  if (grid < 1) grid = 1;
-  profile_mark(kKMerge, true, st);
-  if (q_elem == kElemBF16)
-    hipLaunchKernelGGL((k_merge<bf16_t>), dim3(grid), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_merge<f16_t>), dim3(grid), dim3(256), 0, st, p);
-  hipError_t e = hipGetLastError();
-  profile_mark(kKMerge, false, st);
   return e;
 }
 

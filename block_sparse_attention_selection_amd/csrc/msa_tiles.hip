@@ -1,0 +1,724 @@
+// msa_tiles.hip -- 128-row query tiles on v_mfma_f32_32x32x16 (gfx950).
+//
+// Two kernels of the prefill-shaped path (fw-ai/minimax-kernels README,
+// intro: a selected KV block is loaded once and every query that selected it
+// is processed against it):
+//   k_units  KV-outer units. A unit is up to Tu tokens that picked block b of
+//            KV head g outside their tile's chain; its rows are the tokens x
+//            the G query heads of g. A workgroup takes a run of consecutive
+//            units, keeps the block staged in LDS while the row stays the
+//            same, and writes one normalised bf16/fp16 partial O and one LSE
+//            per (residual slot, head).
+//   k_tiles  one tile per item: the chain (blocks picked by every token of
+//            the tile) streams through a ring of LDS chunk slots while the
+//            tile's rows stay in registers; the unit partials of the tile's
+//            residual slots are then merged by their LSE and the final O and
+//            LSE are written (the combine of the pages' design, fused into
+//            the tile's epilogue).
+//
+// Each of the four waves owns 32 query rows. Scores are computed transposed,
+// S^T = K Q^T, so that the D fragment of a lane holds 16 keys of one query
+// row; those probabilities are the B operand of O^T = V^T P^T as they stand.
+// The V^T operand is read from the row-major LDS tile with the transposing
+// ds_read_b64_tr_b16, so no register shuffles are needed.
+//
+// MFMA 32x32x16 fragment layout (lane l, h = l / 32, c = l % 32):
+//   A: lane holds A[m = c][k = 8h + e], e = 0..7
+//   B: lane holds B[k = 8h + e][n = c]
+//   D: lane holds D[m = 8(j/4) + 4h + (j%4)][n = c], j = 0..15
+// QK k-step s (0..7) covers head dims 16s .. 16s+15 (lane: 16s + 8h + e).
+// PV k-step s' (0..1) of a 32-key chunk covers keys 16s' .. 16s'+15, with
+// key(s', 8h + e) = 16s' + 8(e/4) + 4h + (e%4), which is where the score
+// accumulator already holds them. O^T d-tile t (0..3) covers d = 32t + m.
+//
+// LDS tiles of 32 keys x 128 dims (16-bit) are stored row-major with the
+// 16-byte pieces of row r XOR-swizzled by r & 15, which keeps the K-operand
+// reads (one row per lane) and the transposing V reads conflict-light.
+#include <limits.h>
+
+#include "msa_device.hpp"
+#include "msa_index_dev.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T>
+struct Mma32;
+
+template <>
+struct Mma32<bf16_t> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+
+template <>
+struct Mma32<f16_t> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+};
+
+constexpr int kChunkU4 = 512;       // one 32-key tile of K or V (16-bit): 8 KB
+constexpr int kSlotU4 = 1024;       // one ring slot: the K tile, then the V tile
+constexpr int kRing = 4;            // ring slots (bf16/fp16 caches)
+constexpr int kUnitsPerSeg = 4;     // consecutive units per k_units work item
+constexpr float kRescale32 = 8.0f;  // lazy rescale threshold (powers of two)
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses (compiler level) without the
+// vmcnt(0) a release fence would add: the ring's direct-to-LDS loads are
+// waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// swizzled 16-byte piece of a 32 x 128 16-bit tile
+__device__ __forceinline__ int piece(int row, int lc) { return row * 16 + (lc ^ (row & 15)); }
+
+// ---------------------------------------------------------------------------
+// the wave's 32 query rows
+// ---------------------------------------------------------------------------
+struct Rows32 {
+  u32x4 qb[8];   // Q^T B fragments: k-step s holds dims 16s + 8h .. +7 of row c
+  f32x16 o[4];   // O^T accumulators: d-tile t, element j -> d = 32t + 8(j/4) + 4h + (j%4)
+  float m;       // running reference max of the row (log2 units)
+  float l;       // this lane's share of the row sum
+  int pos;       // causal position (INT_MAX when not causal or padding)
+  int seq;       // owning sequence (-1: padding row)
+};
+
+__device__ __forceinline__ void rows_reset(Rows32& rt) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rt.o[t][j] = 0.f;
+  rt.m = -INFINITY;
+  rt.l = 0.f;
+}
+
+__device__ __forceinline__ void rows_load_q(Rows32& rt, const Params& p, int tok, int head, int h) {
+  if (tok < 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) rt.qb[s] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const uint16_t* base = (const uint16_t*)p.q + ((size_t)tok * p.Hq + head) * kD + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rt.qb[s] = *(const u32x4*)(base + 16 * s);
+}
+
+// One 32-key chunk staged in LDS (sK: K tile, sV: V tile): scores, online
+// softmax (lazy rescale), P V. Keys at or beyond lim, keys after a row's
+// causal position and rows of another sequence are removed by select when
+// `mask` is set; the caller clears it only for chunks fully visible to every
+// row. (One instantiation for both cases keeps the register allocation
+// within 256 VGPRs.)
+template <typename CT>
+__device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u32x4* sV, int key0, int lim,
+                                           int run_seq, bool mask, float sl2) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+  f32x16 sa;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sa[j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) sa = Mma32<CT>::run(sK[piece(c, 2 * s + h)], rt.qb[s], sa);
+
+  float x[16];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float v = sa[j] * sl2;
+    if (mask) {
+      const int key = key0 + 8 * (j >> 2) + 4 * h + (j & 3);
+      const bool ok = rt.seq == run_seq && key < lim && key <= rt.pos;
+      v = ok ? v : -INFINITY;
+    }
+    x[j] = v;
+    cmax = fmaxf(cmax, v);
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  if (__any(cmax > rt.m + kRescale32)) {
+    const float m_new = fmaxf(rt.m, cmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(rt.m - m_new);
+    rt.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rt.o[t] *= alpha;
+    rt.m = m_new;
+  }
+  const float mu = (rt.m == -INFINITY) ? 0.f : rt.m;
+  u32x4 pb[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p0 = __builtin_amdgcn_exp2f(x[2 * i] - mu);
+    const float p1 = __builtin_amdgcn_exp2f(x[2 * i + 1] - mu);
+    rt.l += p0 + p1;
+    pb[i >> 2][i & 3] = pack2<CT>(p0, p1);
+  }
+
+  // V^T fragments by transposing reads: lane (h, c) receives V[key][32t + c]
+  // for the four keys 16s' + 8r + 4h + i (i = 0..3); its source lanes read 8
+  // bytes each at row 16s' + 8r + 4h + ((l >> 2) & 3), dims 32t + 16((l >> 4) & 1)
+  // + 4(l & 3) .. +3.
+  const int rsub = 4 * h + ((lane >> 2) & 3);          // 0..7
+  const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // logical piece within the d-tile: 0..3
+  const int half = 8 * (lane & 1);
+  const char* vbytes = (const char*)sV;
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 a;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 16 * sp + 8 * r + rsub;
+        const int off = row * 256 + (((4 * t + psub) ^ (row & 15)) << 4) + half;
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbytes + off));
+        const u32x2 w = __builtin_bit_cast(u32x2, v);
+        a[2 * r] = w[0];
+        a[2 * r + 1] = w[1];
+      }
+      rt.o[t] = Mma32<CT>::run(a, pb[sp], rt.o[t]);
+    }
+  }
+}
+
+// Final row state: total sum over the lane pair, reference max, log2 LSE.
+__device__ __forceinline__ float rows_total(const Rows32& rt) { return rt.l + __shfl_xor(rt.l, 32, 64); }
+
+// 16-bit row stores/loads in the D layout: for d-tile t and group a the lane
+// holds d = 32t + 8a + 4h + (0..3), i.e. 8 contiguous bytes.
+template <typename CT>
+__device__ __forceinline__ void store_row16(uint16_t* row, const Rows32& rt, float scale) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      u32x2 w;
+      w[0] = pack2<CT>(rt.o[t][4 * a] * scale, rt.o[t][4 * a + 1] * scale);
+      w[1] = pack2<CT>(rt.o[t][4 * a + 2] * scale, rt.o[t][4 * a + 3] * scale);
+      *(u32x2*)(row + 32 * t + 8 * a + 4 * h) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chunk staging
+// ---------------------------------------------------------------------------
+// 16-bit caches: direct-to-LDS 16-byte loads. One chunk is 32 key rows of K
+// and of V (8 KB each); each thread issues two loads per tensor. Lane i of
+// wave w's j-th load fills LDS piece (2w + j) * 64 + i; the global piece it
+// reads is chosen so that LDS holds the swizzled layout. Absent chunks
+// (off < 0) and rows at or beyond `nrows` (keys past the used length, whose
+// cache rows may hold anything) read the zero page: a masked probability is
+// exactly zero, but 0 * NaN is not.
+__device__ __forceinline__ void issue_chunk16(const uint16_t* kb, const uint16_t* vb, int64_t off, int nrows,
+                                              const void* zero, u32x4* sK, u32x4* sV) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int pc = (2 * wave + j) * 64 + lane;
+    const int row = pc >> 4, phys = pc & 15;
+    const int64_t e = (int64_t)row * kD + 8 * (phys ^ (row & 15));
+    const bool ok = off >= 0 && row < nrows;
+    const void* gk = ok ? (const void*)(kb + off + e) : (const void*)((const char*)zero + 16 * lane);
+    const void* gv = ok ? (const void*)(vb + off + e) : (const void*)((const char*)zero + 16 * lane);
+    __builtin_amdgcn_global_load_lds(gk, (lds_void*)(sK + (2 * wave + j) * 64), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gv, (lds_void*)(sV + (2 * wave + j) * 64), 16, 0, 0);
+  }
+}
+
+// e4m3fn caches: each thread loads 16 raw bytes of K and of V (16 dims of
+// one key row) into registers, then widens them exactly into two swizzled
+// 16-bit pieces.
+struct Raw8 {
+  u32x4 k, v;
+};
+
+__device__ __forceinline__ Raw8 load_chunk8(const uint8_t* kb, const uint8_t* vb, int64_t off, int nrows,
+                                            const void* zero) {
+  const int row = threadIdx.x >> 3, lc = threadIdx.x & 7;
+  const int64_t e = (int64_t)row * kD + 16 * lc;
+  const bool ok = off >= 0 && row < nrows;
+  Raw8 r;
+  r.k = ok ? *(const u32x4*)(kb + off + e) : *(const u32x4*)((const char*)zero + 16 * (threadIdx.x & 63));
+  r.v = ok ? *(const u32x4*)(vb + off + e) : *(const u32x4*)((const char*)zero + 16 * (threadIdx.x & 63));
+  return r;
+}
+
+template <typename CT>
+__device__ __forceinline__ void store_chunk8(const Raw8& r, u32x4* sK, u32x4* sV) {
+  const int row = threadIdx.x >> 3, lc = threadIdx.x & 7;
+  sK[piece(row, 2 * lc)] = widen8<CT>(u32x2{r.k[0], r.k[1]});
+  sK[piece(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.k[2], r.k[3]});
+  sV[piece(row, 2 * lc)] = widen8<CT>(u32x2{r.v[0], r.v[1]});
+  sV[piece(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.v[2], r.v[3]});
+}
+
+// ---------------------------------------------------------------------------
+// Tokens with ranks [rank0, rank0 + n) among the set bits of row r (one
+// wave): the word holding rank0 is found by two rounds of sampled loads of
+// the row's exclusive popcount prefix, then consecutive words are scanned
+// 64 at a time, each lane expanding its own word.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unit_tokens(const Params& p, int r, int rank0, int n, int* s_tok) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* pre = p.wordpre + (size_t)r * p.W;
+  const uint32_t* bits = p.wordbits + (size_t)r * p.W;
+  int lo = 0, hi = p.W;  // the word is the largest w with pre[w] <= rank0
+  while (hi - lo > 64) {
+    const int stride = (hi - lo + 63) / 64;
+    const int w = lo + lane * stride;
+    const bool le = w < hi && (int)pre[w] <= rank0;
+    const int cnt = __popcll(__ballot(le));
+    lo = lo + (cnt - 1) * stride;
+    hi = min(lo + stride, hi);
+  }
+  {
+    const int w = lo + lane;
+    const bool le = w < hi && (int)pre[w] <= rank0;
+    lo = lo + __popcll(__ballot(le)) - 1;
+  }
+  for (int wb = lo; wb < p.W; wb += 64) {
+    const int w = wb + lane;
+    uint32_t x = 0u;
+    int rk = 0;
+    if (w < p.W) {
+      x = bits[w];
+      rk = (int)pre[w];
+    }
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1u;
+      if (rk >= rank0 && rk < rank0 + n) s_tok[rk - rank0] = w * 32 + bit;
+      ++rk;
+    }
+    if (!__any(w < p.W && rk < rank0 + n)) break;  // every lane is past the unit's last rank
+  }
+}
+
+// element offset of the 32-key chunk starting at key0 of sequence s, KV head
+// g, or -1 when the chunk lies beyond the keys the page table can reach or
+// its page is out of range (its keys are then treated as absent)
+__device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, int key0, int Leff) {
+  if (key0 >= Leff) return -1;
+  const int page = p.block_tables[(size_t)s * p.MP + key0 / p.P];
+  if (page < 0 || page >= p.NP) return -1;
+  return (((int64_t)page * p.Hkv + g) * p.P + (key0 % p.P)) * kD;
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware work queue. Workgroups of a launch are dispatched round-robin
+// over the 8 XCDs, each with its own L2, so workgroup i runs on XCD i % 8.
+// The item space [0, total) is cut into 8 contiguous ranges, one per XCD;
+// neighbouring items (tiles of one KV head and nearby tokens, units of one
+// block) share KV blocks, which then stay in that XCD's L2. A workgroup's
+// first item is fixed by its rank on the XCD, later ones come from the XCD's
+// own counter. Returns the item, or -1 when the range is exhausted.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+struct XcdQueue {
+  int lo, hi, rank, nwg;
+  int32_t* head;
+  __device__ __forceinline__ void init(int total, int32_t* heads) {
+    const int x = blockIdx.x % kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    lo = min(x * per, total);
+    hi = min(lo + per, total);
+    rank = blockIdx.x / kXcds;
+    nwg = (gridDim.x - x + kXcds - 1) / kXcds;  // workgroups on this XCD
+    head = heads + x;
+  }
+  __device__ __forceinline__ int next(bool first) {
+    const int i = lo + (first ? rank : nwg + atomicAdd(head, 1));
+    return i < hi ? i : -1;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// k_units: KV-outer units, KV-stationary. Work item = kUnitsPerSeg
+// consecutive units of the residual order (units of one row are adjacent,
+// so the staged block is reused until the row or the sequence changes).
+// ---------------------------------------------------------------------------
+template <typename CT, typename KVT>
+__global__ __launch_bounds__(256, 2) void k_units(Params p) {
+  constexpr bool kFp8 = sizeof(KVT) == 1;
+  __shared__ u32x4 s_blk[kRing * kSlotU4];  // the staged block: chunk q at q * kSlotU4 (K), + kChunkU4 (V)
+  __shared__ int s_tok[128];
+  __shared__ int s_seq[128];
+  __shared__ int s_item;
+  const int nU = p.counters[kCntUnits];
+  if (nU == 0) return;
+  const int nseg = (nU + kUnitsPerSeg - 1) / kUnitsPerSeg;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int G = p.G, Hkv = p.Hkv, K = p.K;
+  int st_s = -1, st_b = -1, st_g = -1;  // staged block (uniform)
+  XcdQueue wq;
+  wq.init(nseg, p.counters + kCntXcdU);
+  for (bool first = true;; first = false) {
+    if (tid == 0) s_item = wq.next(first);
+    __syncthreads();
+    const int id = s_item;
+    if (id < 0) break;
+    const int u0 = id * kUnitsPerSeg, u1 = min(u0 + kUnitsPerSeg, nU);
+    int r = 0;
+    {
+      int lo = 0, hi = p.NR;  // largest r with unit_off[r] <= u0
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.unit_off[mid] <= u0)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      r = lo;
+    }
+    for (int u = u0; u < u1; ++u) {
+      while (p.unit_off[r + 1] <= u) ++r;
+      const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
+      const int rank0 = (u - p.unit_off[r]) * p.Tu;
+      const int e0 = p.row_off[r] + rank0;
+      const int ntok = min(p.Tu, p.row_off[r + 1] - e0);
+      __syncthreads();  // the previous unit's readers of s_tok / s_seq are done
+      if (tid < 128) s_tok[tid] = -1;
+      __syncthreads();
+      if (wave == 0) unit_tokens(p, r, rank0, ntok, s_tok);
+      __syncthreads();
+      if (tid < ntok) s_seq[tid] = s_tok[tid] >= 0 ? seq_of(p.cu, p.B, s_tok[tid]) : -1;
+      // the residual order of each entry, by slot (read by the tile merges)
+      for (int idx = tid; idx < ntok * K; idx += 256) {
+        const int tau = idx / K, k = idx - tau * K;
+        if (s_tok[tau] < 0) continue;
+        const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
+        if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.slot_pos[slot] = e0 + tau;
+      }
+      __syncthreads();
+      const int rows = ntok * G;
+      const int rho = 32 * wave + c;
+      const bool valid = rho < rows;
+      const int tau = valid ? rho / G : 0;
+      const int hr = rho - tau * G;
+      Rows32 rt;
+      rows_reset(rt);
+      rt.seq = -1;
+      rt.pos = INT_MAX;
+      int tok = -1;
+      if (valid) {
+        tok = s_tok[tau];
+        const int s = s_seq[tau];
+        rt.seq = s;
+        if (s >= 0 && p.causal) {
+          const int64_t q0 = p.cu[s];
+          rt.pos = (int)(p.used[s] - (p.cu[s + 1] - q0) + (tok - q0));
+        }
+      }
+      rows_load_q(rt, p, valid && rt.seq >= 0 ? tok : -1, g * G + hr, h);
+      const bool wave_has = 32 * wave < rows;
+
+      for (int run0 = 0; run0 < ntok;) {
+        const int s_run = s_seq[run0];
+        int run1 = run0 + 1;
+        while (run1 < ntok && s_seq[run1] == s_run) ++run1;
+        if (s_run >= 0) {
+          const int L = p.used[s_run];
+          const int Leff = min(L, p.MP * p.P);
+          if (s_run != st_s || b != st_b || g != st_g) {
+            ring_barrier();  // every wave is done with the previous block
+            if constexpr (kFp8) {
+              Raw8 raw[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v,
+                                     chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
+                                     p.zero_page);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+              __syncthreads();
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                issue_chunk16((const uint16_t*)p.k, (const uint16_t*)p.v,
+                              chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
+                              p.zero_page, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+              wait_vmcnt<0>();
+              ring_barrier();
+            }
+            st_s = s_run;
+            st_b = b;
+            st_g = g;
+          }
+          // visibility bounds of the run's rows
+          const bool single = run0 == 0 && run1 == ntok;
+          int pmin = INT_MAX, pmax = INT_MAX;
+          if (p.causal) {
+            const int64_t q0 = p.cu[s_run];
+            const int base = (int)(L - (p.cu[s_run + 1] - q0) - q0);
+            pmin = base + s_tok[run0];
+            pmax = base + s_tok[run1 - 1];
+          }
+          if (wave_has) {
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) {
+              const int key0 = kBlk * b + 32 * q;
+              if (key0 >= Leff || key0 > pmax) break;
+              const bool full = single && key0 + 31 < Leff && key0 + 31 <= pmin;
+              rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, Leff, s_run, !full,
+                                 p.scale_log2);
+            }
+          }
+        }
+        run0 = run1;
+      }
+
+      // partial result of the unit's rows: normalised O and log2 LSE
+      const float l_row = rows_total(rt);
+      if (valid) {
+        const size_t pidx = (size_t)(e0 + tau) * G + hr;
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+        store_row16<CT>((uint16_t*)p.opart + pidx * kD, rt, inv);
+        if (h == 0) {
+          const float mu = rt.m == -INFINITY ? 0.f : rt.m;
+          p.lpart[pidx] = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_tiles: one tile (t0, g) per item. The chain's chunks stream through the
+// ring; then the residual partials of each row are merged and O / LSE are
+// written. Workgroup 0 also clears the counter set of the next call.
+// ---------------------------------------------------------------------------
+template <typename CT, typename KVT>
+__global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
+  constexpr bool kFp8 = sizeof(KVT) == 1;
+  __shared__ u32x4 s_ring[kRing * kSlotU4];
+  __shared__ int64_t s_koff[4 * 64];
+  __shared__ int s_key0[4 * 64];
+  __shared__ int s_item;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  if (blockIdx.x == 0 && p.counters_next)
+    for (int i = tid; i < kCntSlots; i += 256) p.counters_next[i] = 0;
+  const int G = p.G, Hkv = p.Hkv, K = p.K;
+  const int Teff = p.T > 0 ? p.T : 1;
+  // decode mode: the listed tiles; otherwise every tile, enumerated as
+  // (KV head, tile number) so that an XCD's range holds neighbouring tiles
+  // of one KV head
+  const bool listed = p.stream_narrow != 0;
+  const int ntiles = (p.Tq + Teff - 1) / Teff + p.B;  // bound on the tile count
+  const int total = listed ? p.counters[kCntTiles] : ntiles * Hkv;
+  if (total == 0) return;
+  XcdQueue wq;
+  wq.init(total, p.counters + kCntXcd);
+  for (bool first = true;; first = false) {
+    if (tid == 0) s_item = wq.next(first);
+    __syncthreads();
+    const int id = s_item;
+    if (id < 0) break;
+    int t0, g, s;
+    if (listed) {
+      const int code = p.tile_items[id];
+      t0 = code / Hkv;
+      g = code - t0 * Hkv;
+      s = wave_seq_of(p.cu, p.B, t0);
+    } else {
+      g = id / ntiles;
+      int64_t t0l;
+      s = wave_tile_of(p.cu, p.B, p.Tq, Teff, id - g * ntiles, &t0l);
+      t0 = (int)t0l;
+    }
+    if (s < 0) {  // beyond the last tile
+      __syncthreads();
+      continue;
+    }
+    const int code = t0 * Hkv + g;
+    const int64_t q0 = p.cu[s];
+    const int64_t q1 = min(p.cu[s + 1], (int64_t)p.Tq);
+    const int nt = (int)min((int64_t)Teff, q1 - t0);
+    const int rows = nt * G;
+    const int L = p.used[s];
+    const int Leff = min(L, p.MP * p.P);
+    const int base_pos = (int)(L - (p.cu[s + 1] - q0) - q0);  // pos = base_pos + token
+    const int pmin = p.causal ? base_pos + t0 : INT_MAX;
+    const int pmax = p.causal ? base_pos + t0 + nt - 1 : INT_MAX;
+    const int n_ch = p.tok_chain[code];
+    const int nck = 4 * n_ch;
+    // chunk table: element offset (-1: skip) and first key
+    for (int ci = tid; ci < nck; ci += 256) {
+      const int key0 = kBlk * p.chain_blk[(size_t)code * K + (ci >> 2)] + 32 * (ci & 3);
+      int64_t off = chunk_offset(p, s, g, key0, Leff);
+      if (key0 > pmax) off = -1;  // causally invisible to every row of the tile
+      s_koff[ci] = off;
+      s_key0[ci] = key0;
+    }
+    // the wave's rows
+    const int rho = 32 * wave + c;
+    const bool valid = rho < rows;
+    const int tau = valid ? rho / G : 0;
+    const int hr = rho - tau * G;
+    const int tok = t0 + tau;
+    const int head = g * G + hr;
+    Rows32 rt;
+    rows_reset(rt);
+    rt.seq = s;
+    rt.pos = (valid && p.causal) ? base_pos + tok : INT_MAX;
+    rows_load_q(rt, p, valid ? tok : -1, head, h);
+    const bool wave_has = 32 * wave < rows;
+    __syncthreads();  // chunk table visible
+
+    if (nck > 0) {
+      if constexpr (kFp8) {
+        // register-staged double buffer: chunk ci+1 loads while ci is multiplied
+        Raw8 raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, s_koff[0], Leff - s_key0[0], p.zero_page);
+        store_chunk8<CT>(raw, s_ring, s_ring + kChunkU4);
+        __syncthreads();
+        for (int ci = 0; ci < nck; ++ci) {
+          const int nxt = ci + 1 < nck ? ci + 1 : ci;
+          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, s_koff[nxt], Leff - s_key0[nxt], p.zero_page);
+          const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
+          const int64_t off = s_koff[ci];
+          if (wave_has && off >= 0) {
+            const int key0 = s_key0[ci];
+            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
+            rows_chunk<CT>(rt, sK, sK + kChunkU4, key0, Leff, s, !full, p.scale_log2);
+          }
+          if (ci + 1 < nck) store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+          __syncthreads();
+        }
+      } else {
+        const uint16_t* kb = (const uint16_t*)p.k;
+        const uint16_t* vb = (const uint16_t*)p.v;
+        asm volatile("" ::: "memory");  // the Q loads above are older than the ring loads
+#pragma unroll
+        for (int ci = 0; ci < kRing - 1; ++ci)
+          issue_chunk16(kb, vb, ci < nck ? s_koff[ci] : (int64_t)-1, ci < nck ? Leff - s_key0[ci] : 0, p.zero_page,
+                        s_ring + ci * kSlotU4, s_ring + ci * kSlotU4 + kChunkU4);
+        for (int ci = 0; ci < nck; ++ci) {
+          wait_vmcnt<8>();  // chunk ci has landed (two newer chunks may be in flight)
+          ring_barrier();   // ... for every wave; and slot (ci + 3) % 4 is free
+          const int nx = ci + kRing - 1;
+          u32x4* sn = s_ring + (nx & (kRing - 1)) * kSlotU4;
+          issue_chunk16(kb, vb, nx < nck ? s_koff[nx] : (int64_t)-1, nx < nck ? Leff - s_key0[nx] : 0, p.zero_page, sn,
+                        sn + kChunkU4);
+          const int64_t off = s_koff[ci];
+          if (wave_has && off >= 0) {
+            const int key0 = s_key0[ci];
+            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
+            const u32x4* sK = s_ring + (ci & (kRing - 1)) * kSlotU4;
+            rows_chunk<CT>(rt, sK, sK + kChunkU4, key0, Leff, s, !full, p.scale_log2);
+          }
+        }
+        wait_vmcnt<0>();  // the trailing (zero-page) loads are done before the ring is reused
+      }
+    }
+
+    // merge with the unit partials of the row's residual slots, then write
+    const float l_tot = rows_total(rt);
+    if (valid) {
+      const size_t tg = (size_t)tok * Hkv + g;
+      float M = rt.m;
+      const int nres = p.tok_nres[tg];
+      const int ntot = p.counters[kCntResidual];  // positions are below this
+      const uint8_t* flags = p.slot_flag + tg * K;
+      const int32_t* spos = p.slot_pos + tg * K;
+      if (nres > 0) {
+        for (int k = 0; k < K; ++k) {
+          const int sp = spos[k];
+          if (flags[k] == 2 && sp >= 0 && sp < ntot) M = fmaxf(M, p.lpart[(size_t)sp * G + hr]);
+        }
+      }
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float fc = rt.m == -INFINITY ? 0.f : exp2f(rt.m - Mu);
+      float W = l_tot * fc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rt.o[t] *= fc;
+      if (nres > 0) {
+        for (int k = 0; k < K; ++k) {
+          const int sp = spos[k];
+          if (flags[k] != 2 || sp < 0 || sp >= ntot) continue;
+          const size_t pidx = (size_t)sp * G + hr;
+          const float li = p.lpart[pidx];
+          const float fi = li == -INFINITY ? 0.f : exp2f(li - Mu);
+          W += fi;
+          const uint16_t* src = (const uint16_t*)p.opart + pidx * kD + 4 * h;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const u32x2 w = *(const u32x2*)(src + 32 * t + 8 * a);
+              rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
+              rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
+              rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
+              rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
+            }
+        }
+      }
+      const float inv = W > 0.f ? 1.f / W : 0.f;
+      store_row16<CT>((uint16_t*)p.out + ((size_t)tok * p.Hq + head) * kD, rt, inv);
+      if (h == 0 && p.lse) p.lse[(size_t)head * p.Tq + tok] = W > 0.f ? (Mu + log2f(W)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();  // the chunk table and ring are free for the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename CT, typename KVT>
+static hipError_t launch_units_t(const Params& p, int num_cu, hipStream_t st) {
+  hipLaunchKernelGGL((k_units<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename CT, typename KVT>
+static hipError_t launch_tiles_t(const Params& p, int num_cu, hipStream_t st) {
+  hipLaunchKernelGGL((k_tiles<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_units(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
+  profile_mark(kKUnits, true, st);
+  hipError_t e;
+  if (q_elem == kElemBF16)
+    e = kv_elem == kElemFP8 ? launch_units_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
+                            : launch_units_t<bf16_t, bf16_t>(p, num_cu, st);
+  else
+    e = kv_elem == kElemFP8 ? launch_units_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
+                            : launch_units_t<f16_t, f16_t>(p, num_cu, st);
+  profile_mark(kKUnits, false, st);
+  return e;
+}
+
+hipError_t launch_tiles(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
+  profile_mark(kKTiles, true, st);
+  hipError_t e;
+  if (q_elem == kElemBF16)
+    e = kv_elem == kElemFP8 ? launch_tiles_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
+                            : launch_tiles_t<bf16_t, bf16_t>(p, num_cu, st);
+  else
+    e = kv_elem == kElemFP8 ? launch_tiles_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
+                            : launch_tiles_t<f16_t, f16_t>(p, num_cu, st);
+  profile_mark(kKTiles, false, st);
+  return e;
+}
+
+}  // namespace msa

@@ -136,17 +136,17 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  * slots are inverted into rows r = b*Hkv + g: row_off is the exclusive scan
  * of the row counts, ent lists each row's slot ids in ascending order, and
  * slot_pos[slot] is the slot's index in ent (-1 if not residual). unit_off is
- * the exclusive scan of ceil(row count / unit_tokens). Chains of tiles with
- * more than 16 query rows (tokens in the tile * Hq/Hkv), or every chain when
- * list_all_chains is 1, are listed in wide_items as t_leader*Hkv + g (the
- * two settings are the two launch shapes of the classifier: one workgroup
- * per token, or one per tile); pairs (t, g) whose output is produced by
- * merging partial results (a residual slot, or no chain) are listed in
- * combine_items as t*Hkv + g. Both lists are in unspecified order.
+ * the exclusive scan of ceil(row count / unit_tokens). A tile is listed in
+ * tile_items as t_leader*Hkv + g, per KV head g, unless list_all_tiles is 0,
+ * the tile has at most 16 query rows (tokens in the tile * Hq/Hkv) and none
+ * of its slots is residual: such tiles are finished by the classifier itself
+ * in the attention pass (the two settings are the classifier's two launch
+ * shapes: one workgroup per token, or one per tile). With tile_tokens == 0
+ * tiles are single tokens. The list is in unspecified order.
  *
  * All output buffers are caller-owned device memory of the sizes given;
  * chain_blk holds valid entries only at leader tokens (first tok_chain
- * entries). counters[0..3] = residual slots, combine items, wide items, units.
+ * entries). counters[0..2] = residual slots, tile items, units.
  * Inputs as in msa_kvouter_attention; nb_max = ceil(max_pages*page_size/128).
  */
 typedef struct msa_index_out {
@@ -158,15 +158,14 @@ typedef struct msa_index_out {
   int32_t* unit_off;     /* [nb_max*Hkv + 1] */
   int32_t* ent;          /* [Tq*Hkv*topk] capacity */
   int32_t* slot_pos;     /* [Tq*Hkv*topk] */
-  int32_t* combine_items; /* [Tq*Hkv] capacity */
-  int32_t* wide_items;   /* [Tq*Hkv] capacity */
+  int32_t* tile_items;   /* [Tq*Hkv] capacity */
   int32_t* counters;     /* [8] */
 } msa_index_out;
 
 int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
                         const msa_tensor* used_kv_lens, int32_t Hq, int32_t nb_max,
                         int32_t causal, int32_t tile_tokens, int32_t unit_tokens,
-                        int32_t list_all_chains, const msa_index_out* out, void* stream);
+                        int32_t list_all_tiles, const msa_index_out* out, void* stream);
 
 /*
  * msa_widen_fp8 -- widen n e4m3fn values (device bytes `in`) to bf16 or fp16
@@ -200,9 +199,9 @@ int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache,
  */
 enum {
   MSA_KERNEL_INDEX = 0, /* residual inversion: row counts and scan */
-  MSA_KERNEL_FRONT = 1, /* classification + streaming of tiles of <= 16 rows */
-  MSA_KERNEL_WORK = 2,  /* wide tiles and KV-outer units (LDS-staged) */
-  MSA_KERNEL_MERGE = 3, /* LSE merges of partial results */
+  MSA_KERNEL_FRONT = 1, /* classification + residual-free tiles of <= 16 rows */
+  MSA_KERNEL_UNITS = 2, /* KV-outer units: partial O and LSE per residual slot */
+  MSA_KERNEL_TILES = 3, /* listed tiles: chain blocks, LSE merge of the partials */
 };
 int32_t msa_profile_enable(uint32_t kernel_mask);
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches);

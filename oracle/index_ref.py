@@ -15,7 +15,8 @@ Tiles: the tokens of each sequence are cut into runs of ``tile_tokens``
 consecutive tokens (the last run may be shorter); the first token of a run
 is its leader. For a tile and KV head g, the CHAIN is the list of blocks
 that every token of the tile selected validly, in the order of the leader's
-picks. ``tile_tokens == 0`` disables chains.
+picks. ``tile_tokens == 0`` disables chains (tiles are then single tokens
+with empty chains).
 
 A valid slot whose block is in its tile's chain is COVERED (flag 1); any
 other valid slot is RESIDUAL (flag 2); invalid slots have flag 0.
@@ -28,11 +29,10 @@ into units of at most ``unit_tokens`` entries; ``unit_off`` is the
 exclusive scan of ceil(count/unit_tokens).
 
 Per (t, g): ``tok_chain`` is the chain length of t's tile and ``tok_nres``
-the number of residual slots of (t, g). Chains of tiles with more than 16
-query rows (tile tokens x G) form the wide work list (every chain when
-``list_all_chains`` is set); pairs whose output is
-merged from partial results (a residual slot, or no chain) form the combine
-list.
+the number of residual slots of (t, g). Tiles (t_leader, g) form the tile
+work list, except -- unless ``list_all_tiles`` is set -- tiles of at most 16
+query rows (tile tokens x G) none of whose slots is residual: the
+classifier finishes those itself.
 """
 from __future__ import annotations
 
@@ -54,8 +54,7 @@ class Plan:
     ent: np.ndarray            # [nres] int32
     slot_pos: np.ndarray       # [Tq, Hkv, K] int32
     unit_off: np.ndarray       # [nb_max*Hkv + 1] int32
-    wide_items: set            # {t0*Hkv + g} chains with tile rows > 16
-    combine_items: set         # {t*Hkv + g} outputs merged from partials
+    tile_items: set            # {t0*Hkv + g} tiles left to the tile kernel
 
 
 def token_sequence(cu: np.ndarray, Tq: int) -> np.ndarray:
@@ -88,7 +87,7 @@ def slot_validity(selected, cu, used, causal, nb_max):
 
 
 def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
-          nb_max: int, G: int, list_all_chains: bool = False) -> Plan:
+          nb_max: int, G: int, list_all_tiles: bool = False) -> Plan:
     selected = np.asarray(selected, dtype=np.int32)
     Tq, Hkv, K = selected.shape
     cu = np.asarray(cu, dtype=np.int64)
@@ -107,33 +106,32 @@ def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
     slot_flag = np.where(valid, 2, 0).astype(np.uint8)
     tok_chain = np.zeros((Tq, Hkv), dtype=np.int32)
     chain_blk = {}
-    wide = set()
-    if tile_tokens > 0:
-        for s in range(len(cu) - 1):
-            q0, q1 = int(cu[s]), int(cu[s + 1])
-            for t0 in range(q0, q1, tile_tokens):
-                t1 = min(t0 + tile_tokens, q1)
-                toks = np.arange(t0, t1)
-                for g in range(Hkv):
-                    chain = []
-                    for k in range(K):
-                        if not valid[t0, g, k]:
-                            continue
-                        bb = int(b64[t0, g, k])
-                        if bb in chain:
-                            continue
-                        if np.all(has_pick(toks, g, bb)):
-                            chain.append(bb)
-                    chain_blk[(t0, g)] = chain
-                    tok_chain[t0:t1, g] = len(chain)
-                    if chain:
-                        cover = valid[t0:t1, g, :] & np.isin(b64[t0:t1, g, :], chain)
-                        slot_flag[t0:t1, g, :][cover] = 1
-                        if list_all_chains or (t1 - t0) * G > 16:
-                            wide.add(t0 * Hkv + g)
+    tiles = set()
+    T = max(tile_tokens, 1)
+    for s in range(len(cu) - 1):
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        for t0 in range(q0, q1, T):
+            t1 = min(t0 + T, q1)
+            toks = np.arange(t0, t1)
+            for g in range(Hkv):
+                chain = []
+                for k in range(K if tile_tokens > 0 else 0):
+                    if not valid[t0, g, k]:
+                        continue
+                    bb = int(b64[t0, g, k])
+                    if bb in chain:
+                        continue
+                    if np.all(has_pick(toks, g, bb)):
+                        chain.append(bb)
+                chain_blk[(t0, g)] = chain
+                tok_chain[t0:t1, g] = len(chain)
+                if chain:
+                    cover = valid[t0:t1, g, :] & np.isin(b64[t0:t1, g, :], chain)
+                    slot_flag[t0:t1, g, :][cover] = 1
+                has_res = bool(np.any(slot_flag[t0:t1, g, :] == 2))
+                if list_all_tiles or (t1 - t0) * G > 16 or has_res:
+                    tiles.add(t0 * Hkv + g)
     tok_nres = (slot_flag == 2).sum(axis=2).astype(np.int32)
-    need = (tok_nres > 0) | (tok_chain == 0)
-    combine = set(int(x) for x in np.nonzero(need.reshape(-1))[0])
 
     NR = nb_max * Hkv
     slot_ids = np.arange(Tq * Hkv * K, dtype=np.int64).reshape(Tq, Hkv, K)
@@ -155,5 +153,5 @@ def build(selected, cu, used, causal: bool, tile_tokens: int, unit_tokens: int,
         slot_flag=slot_flag, tok_chain=tok_chain, tok_nres=tok_nres, chain_blk=chain_blk,
         row_off=row_off.astype(np.int32), ent=ids.astype(np.int32),
         slot_pos=slot_pos.reshape(Tq, Hkv, K).astype(np.int32),
-        unit_off=unit_off.astype(np.int32), wide_items=wide, combine_items=combine,
+        unit_off=unit_off.astype(np.int32), tile_items=tiles,
     )

@@ -139,7 +139,7 @@ def test_widen_argument_checks():
 
 def test_build_index_argument_checks():
     lib = msa.load()
-    o = _lib.MsaIndexOut(*([FAKE] * 11))
+    o = _lib.MsaIndexOut(*([FAKE] * 10))
     sel = desc([4, 2, 4], msa.MSA_INT32)
     cu = desc([3], msa.MSA_INT64)
     used = desc([2], msa.MSA_INT32)

@@ -59,10 +59,10 @@ def _index_case(wl, T, Tu, list_all=False):
 
     nb_max = (wl.block_tables.shape[1] * wl.page_size + 127) // 128
     ref = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G,
-                          list_all_chains=list_all)
+                          list_all_tiles=list_all)
     got = msa.build_index(torch.from_numpy(wl.selected).cuda(), torch.from_numpy(wl.cu_seqlens_q).cuda(),
                           torch.from_numpy(wl.used_kv_lens).cuda(), Hq=wl.Hq, nb_max=nb_max,
-                          causal=wl.causal, tile_tokens=T, unit_tokens=Tu, list_all_chains=list_all)
+                          causal=wl.causal, tile_tokens=T, unit_tokens=Tu, list_all_tiles=list_all)
     got = {k: v.cpu().numpy() for k, v in got.items()}
     Tq, Hkv, K = wl.selected.shape
     assert np.array_equal(got["slot_flag"], ref.slot_flag.reshape(-1))
@@ -74,13 +74,12 @@ def _index_case(wl, T, Tu, list_all=False):
     assert got["counters"][0] == n
     assert np.array_equal(got["ent"][:n], ref.ent)
     assert np.array_equal(got["slot_pos"], ref.slot_pos.reshape(-1))
-    assert got["counters"][3] == ref.unit_off[-1]
+    assert got["counters"][2] == ref.unit_off[-1]
     cb = got["chain_blk"].reshape(Tq, Hkv, K)
     for (t0, g), ch in ref.chain_blk.items():
         assert list(cb[t0, g, :len(ch)]) == ch, (t0, g)
-    nc, nw = got["counters"][1], got["counters"][2]
-    assert sorted(got["combine_items"][:nc].tolist()) == sorted(ref.combine_items)
-    assert sorted(got["wide_items"][:nw].tolist()) == sorted(ref.wide_items)
+    nt = got["counters"][1]
+    assert sorted(got["tile_items"][:nt].tolist()) == sorted(ref.tile_items)
 
 
 @pytest.mark.parametrize("list_all", [False, True])

@@ -117,7 +117,7 @@ def test_invariants_on_named_workloads(name):
     if name == "decode_gqa":
         # one token per sequence: every tile is a single token, all slots covered
         assert plan.ent.size == 0
-        assert not plan.combine_items and not plan.wide_items
+        assert not plan.tile_items
 
 
 @pytest.mark.slow
