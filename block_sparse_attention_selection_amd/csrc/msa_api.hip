@@ -145,7 +145,7 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
   d->NR = d->nb_max * d->Hkv;
   d->W = (int)((Tq + 31) / 32);
   d->T = std::max(1, 128 / d->G);
-  d->Tu = d->T;
+  d->Tu = std::min(8 * d->T, msa::kUnitWindowTokens);  // a unit kernel work item: up to 8 tiles' worth
   d->q_elem = elem_of(q->dtype);
   d->kv_elem = elem_of(k->dtype);
   return MSA_OK;

@@ -186,6 +186,24 @@ __device__ __forceinline__ int wave_seq_of(const int64_t* __restrict__ cu, int B
   return (cu[s] <= t && t < cu[s + 1]) ? s : -1;
 }
 
+// Largest i in [0, n) with a[i] <= x, for a non-decreasing a with
+// a[0] <= x (one wave; every lane gets the answer). Each round of 64 sampled
+// loads narrows the range 64-fold, so n <= 4096 takes two dependent loads.
+__device__ __forceinline__ int wave_last_le(const int32_t* __restrict__ a, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;  // the answer lies in [lo, hi)
+  while (hi - lo > 64) {
+    const int stride = (hi - lo + 63) / 64;
+    const int i = lo + lane * stride;
+    const bool le = i < hi && a[i] <= x;
+    lo = lo + (__popcll(__ballot(le)) - 1) * stride;
+    hi = min(lo + stride, hi);
+  }
+  const int i = lo + lane;
+  const bool le = i < hi && a[i] <= x;
+  return lo + __popcll(__ballot(le)) - 1;
+}
+
 // Tile j of the batch, tiles being runs of T consecutive tokens numbered
 // sequence by sequence: returns its sequence and sets its first token, or
 // returns -1 beyond the last tile. Token ranges are clamped to [0, Tq).

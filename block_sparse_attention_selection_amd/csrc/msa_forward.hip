@@ -333,6 +333,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   __shared__ int s_page[128];     // pages of the leader's picks (ppb per pick)
   __shared__ int s_nch;
   __shared__ int s_tile_res;      // residual slots of the tile
+  __shared__ int s_miss[64];      // leader picks missing from some token of the tile
   const int g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = p.K, Hkv = p.Hkv;
@@ -401,22 +402,31 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     s_sel[idx] = valid ? b : -1;
   }
   for (int tau = tid; tau < nt; tau += 256) s_nres[tau] = 0;
+  if (tid < 64) s_miss[tid] = 0;
   if (stream && tid < K * ppb) s_page[tid] = my_page;
   __syncthreads();
 
-  // the chain: the leader's valid picks present in every token of the tile
+  // the chain: the leader's valid picks present in every token of the tile.
+  // One thread per (token, leader pick) looks for the pick in the token's
+  // list; a miss marks the pick.
+  if (p.T > 0) {
+    for (int idx = tid + K; idx < nt * K; idx += 256) {  // tokens 1 .. nt-1
+      const int tau = idx / K, k = idx - tau * K;
+      const int bl = s_sel[k];
+      if (bl < 0) continue;
+      bool found = false;
+      for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
+      if (!found) s_miss[k] = 1;
+    }
+  }
+  __syncthreads();
   if (wave == 0) {
     bool in_chain = false;
     int bl = -1;
     if (p.T > 0 && lane < K) {
       bl = s_sel[lane];
-      in_chain = bl >= 0;
-      for (int k2 = 0; k2 < lane && in_chain; ++k2) in_chain = s_sel[k2] != bl;
-      for (int tau = 1; tau < nt && in_chain; ++tau) {
-        bool found = false;
-        for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
-        in_chain = found;
-      }
+      in_chain = bl >= 0 && s_miss[lane] == 0;
+      for (int k2 = 0; k2 < lane && in_chain; ++k2) in_chain = s_sel[k2] != bl;  // first occurrence only
     }
     const uint64_t mask = __ballot(in_chain);
     if (in_chain) {
@@ -463,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     for (int off = 32; off > 0; off >>= 1) res += __shfl_xor(res, off, 64);
     if (lane == 0) {
       s_tile_res = res;
-      if (res > 0) atomicAdd(&p.counters[kCntResidual], res);
+      if (res > 0) p.counters[kCntResidual] = 1;  // "some"; the index kernel writes the total
       const bool here = p.stream_narrow && rows <= 16 && res == 0;
       if (!here && p.list_tiles) p.tile_items[atomicAdd(&p.counters[kCntTiles], 1)] = (int)tg;
     }

@@ -94,6 +94,7 @@ __device__ __forceinline__ void rowscan_all(const Params& p, int* smem) {
     p.row_off[NR] = tot_cnt;
     p.unit_off[NR] = tot_units;
     p.counters[kCntUnits] = tot_units;
+    p.counters[kCntResidual] = tot_cnt;  // every workgroup of this kernel has read the flag by now
   }
 }
 

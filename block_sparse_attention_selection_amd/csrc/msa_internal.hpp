@@ -8,7 +8,8 @@ namespace msa {
 
 // counters[] slots in the workspace
 enum Counter {
-  kCntResidual = 0,   // residual slots in the batch
+  kCntResidual = 0,   // residual slots in the batch (the front kernel sets it to 1 if
+                      // there are any; the index kernel replaces that with the total)
   kCntTiles = 1,      // tile items (tiles the front kernel does not finish itself)
   kCntUnits = 2,      // KV-outer units
   kCntDoneR = 5,      // finished row groups of the index kernel
@@ -26,6 +27,9 @@ constexpr size_t kZeroPageBytes = 16384;
 constexpr size_t kZsHeaderBytes = 2 * kCntSlots * sizeof(int32_t) + kZeroPageBytes;
 
 enum ElemCode { kElemBF16 = 0, kElemF16 = 1, kElemFP8 = 2 };
+
+// tokens of one KV-outer work item (the unit kernel's LDS token list)
+constexpr int kUnitWindowTokens = 512;
 
 struct Params {
   // inputs

@@ -3,12 +3,12 @@
 // Two kernels of the prefill-shaped path (fw-ai/minimax-kernels README,
 // intro: a selected KV block is loaded once and every query that selected it
 // is processed against it):
-//   k_units  KV-outer units. A unit is up to Tu tokens that picked block b of
-//            KV head g outside their tile's chain; its rows are the tokens x
-//            the G query heads of g. A workgroup takes a run of consecutive
-//            units, keeps the block staged in LDS while the row stays the
-//            same, and writes one normalised bf16/fp16 partial O and one LSE
-//            per (residual slot, head).
+//   k_units  KV-outer units. A unit (window) is up to Tu tokens that picked
+//            block b of KV head g outside their tile's chain; its rows are
+//            the tokens x the G query heads of g. The block is staged once
+//            in LDS per sequence and every piece of at most 128 rows is
+//            multiplied against it, writing one normalised bf16/fp16
+//            partial O and one LSE per (residual slot, head).
 //   k_tiles  one tile per item: the chain (blocks picked by every token of
 //            the tile) streams through a ring of LDS chunk slots while the
 //            tile's rows stay in registers; the unit partials of the tile's
@@ -69,7 +69,7 @@ struct Mma32<f16_t> {
 constexpr int kChunkU4 = 512;       // one 32-key tile of K or V (16-bit): 8 KB
 constexpr int kSlotU4 = 1024;       // one ring slot: the K tile, then the V tile
 constexpr int kRing = 4;            // ring slots (bf16/fp16 caches)
-constexpr int kUnitsPerSeg = 4;     // consecutive units per k_units work item
+constexpr int kUnitWindow = kUnitWindowTokens;
 constexpr float kRescale32 = 8.0f;  // lazy rescale threshold (powers of two)
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
@@ -90,8 +90,13 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// swizzled 16-byte piece of a 32 x 128 16-bit tile
-__device__ __forceinline__ int piece(int row, int lc) { return row * 16 + (lc ^ (row & 15)); }
+// Swizzled 16-byte pieces of a 32 x 128 16-bit tile (row = key). The K tile
+// XORs the piece index with row & 15: a K-operand read has lane c reading
+// row c, so 16 consecutive lanes hit 16 different pieces. The V tile XORs it
+// with 4 (row & 3): a transposing read has 32 lanes reading 4 rows x 4
+// pieces of one d-tile, which then land on 16 different pieces.
+__device__ __forceinline__ int pieceK(int row, int lc) { return row * 16 + (lc ^ (row & 15)); }
+__device__ __forceinline__ int pieceV(int row, int lc) { return row * 16 + (lc ^ ((row & 3) << 2)); }
 
 // ---------------------------------------------------------------------------
 // the wave's 32 query rows
@@ -139,22 +144,20 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
 #pragma unroll
   for (int j = 0; j < 16; ++j) sa[j] = 0.f;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) sa = Mma32<CT>::run(sK[piece(c, 2 * s + h)], rt.qb[s], sa);
+  for (int s = 0; s < 8; ++s) sa = Mma32<CT>::run(sK[pieceK(c, 2 * s + h)], rt.qb[s], sa);
 
-  float x[16];
-  float cmax = -INFINITY;
+  if (mask) {
+    // key (key0 + 4h + the element's offset) is visible iff it is <= bound
+    const int bound = rt.seq == run_seq ? min(rt.pos, lim - 1) : -1;
+    const int rel = bound - key0 - 4 * h;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float v = sa[j] * sl2;
-    if (mask) {
-      const int key = key0 + 8 * (j >> 2) + 4 * h + (j & 3);
-      const bool ok = rt.seq == run_seq && key < lim && key <= rt.pos;
-      v = ok ? v : -INFINITY;
-    }
-    x[j] = v;
-    cmax = fmaxf(cmax, v);
+    for (int j = 0; j < 16; ++j) sa[j] = (8 * (j >> 2) + (j & 3)) <= rel ? sa[j] : -INFINITY;
   }
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  // the row max of the raw scores; sl2 > 0 commutes with max
+  float cmax = sa[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) cmax = fmaxf(cmax, sa[j]);
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64)) * sl2;
   if (__any(cmax > rt.m + kRescale32)) {
     const float m_new = fmaxf(rt.m, cmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(rt.m - m_new);
@@ -163,22 +166,24 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
     for (int t = 0; t < 4; ++t) rt.o[t] *= alpha;
     rt.m = m_new;
   }
-  const float mu = (rt.m == -INFINITY) ? 0.f : rt.m;
+  const float nmu = (rt.m == -INFINITY) ? 0.f : -rt.m;
   u32x4 pb[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float p0 = __builtin_amdgcn_exp2f(x[2 * i] - mu);
-    const float p1 = __builtin_amdgcn_exp2f(x[2 * i + 1] - mu);
-    rt.l += p0 + p1;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * i], sl2, nmu));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * i + 1], sl2, nmu));
     pb[i >> 2][i & 3] = pack2<CT>(p0, p1);
+    rt.l += p0 + p1;  // fp32 sum of the unrounded probabilities (the LSE needs it)
   }
 
   // V^T fragments by transposing reads: lane (h, c) receives V[key][32t + c]
   // for the four keys 16s' + 8r + 4h + i (i = 0..3); its source lanes read 8
-  // bytes each at row 16s' + 8r + 4h + ((l >> 2) & 3), dims 32t + 16((l >> 4) & 1)
-  // + 4(l & 3) .. +3.
-  const int rsub = 4 * h + ((lane >> 2) & 3);          // 0..7
-  const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // logical piece within the d-tile: 0..3
+  // bytes each at row 16s' + 8r + 4h + i (i = (l >> 2) & 3), logical piece
+  // 4t + 2((l >> 4) & 1) + ((l & 3) >> 1), half l & 1. With the V swizzle the
+  // physical piece is 4(t ^ i) + the low two bits.
+  const int i4 = (lane >> 2) & 3;
+  const int rsub = 4 * h + i4;                                 // 0..7
+  const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // 0..3
   const int half = 8 * (lane & 1);
   const char* vbytes = (const char*)sV;
 #pragma unroll
@@ -189,7 +194,7 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int row = 16 * sp + 8 * r + rsub;
-        const int off = row * 256 + (((4 * t + psub) ^ (row & 15)) << 4) + half;
+        const int off = row * 256 + ((4 * (t ^ i4) + psub) << 4) + half;
         const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbytes + off));
         const u32x2 w = __builtin_bit_cast(u32x2, v);
         a[2 * r] = w[0];
@@ -222,27 +227,53 @@ __device__ __forceinline__ void store_row16(uint16_t* row, const Rows32& rt, flo
 // ---------------------------------------------------------------------------
 // chunk staging
 // ---------------------------------------------------------------------------
-// 16-bit caches: direct-to-LDS 16-byte loads. One chunk is 32 key rows of K
-// and of V (8 KB each); each thread issues two loads per tensor. Lane i of
-// wave w's j-th load fills LDS piece (2w + j) * 64 + i; the global piece it
-// reads is chosen so that LDS holds the swizzled layout. Absent chunks
-// (off < 0) and rows at or beyond `nrows` (keys past the used length, whose
-// cache rows may hold anything) read the zero page: a masked probability is
-// exactly zero, but 0 * NaN is not.
-__device__ __forceinline__ void issue_chunk16(const uint16_t* kb, const uint16_t* vb, int64_t off, int nrows,
-                                              const void* zero, u32x4* sK, u32x4* sV) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int pc = (2 * wave + j) * 64 + lane;
-    const int row = pc >> 4, phys = pc & 15;
-    const int64_t e = (int64_t)row * kD + 8 * (phys ^ (row & 15));
-    const bool ok = off >= 0 && row < nrows;
-    const void* gk = ok ? (const void*)(kb + off + e) : (const void*)((const char*)zero + 16 * lane);
-    const void* gv = ok ? (const void*)(vb + off + e) : (const void*)((const char*)zero + 16 * lane);
-    __builtin_amdgcn_global_load_lds(gk, (lds_void*)(sK + (2 * wave + j) * 64), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gv, (lds_void*)(sV + (2 * wave + j) * 64), 16, 0, 0);
+// 16-bit caches: direct-to-LDS 16-byte buffer loads. One chunk is 32 key
+// rows of K and of V (8 KB each); each thread issues two loads per tensor.
+// Lane i of wave w's j-th load fills LDS piece (2w + j) * 64 + i; the piece
+// of global memory it reads (a per-lane constant, DmaLane) is chosen so that
+// LDS holds the swizzled layout. The chunk's address and extent go into the
+// buffer descriptor (scalar registers): rows at or beyond `nrows` (keys past
+// the used length, whose cache rows may hold anything) and absent chunks
+// (off < 0) fall outside the descriptor's range, and out-of-range buffer
+// loads return zeros -- a masked probability is exactly zero, but 0 * NaN is
+// not.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+struct DmaLane {
+  int k0, k1, v0, v1;  // byte offsets within a chunk of the lane's two K and two V loads
+  __device__ __forceinline__ void init() {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pc0 = (2 * wave) * 64 + lane, pc1 = pc0 + 64;
+    const int r0 = pc0 >> 4, f0 = pc0 & 15, r1 = pc1 >> 4, f1 = pc1 & 15;
+    k0 = r0 * 256 + ((f0 ^ (r0 & 15)) << 4);
+    k1 = r1 * 256 + ((f1 ^ (r1 & 15)) << 4);
+    v0 = r0 * 256 + ((f0 ^ ((r0 & 3) << 2)) << 4);
+    v1 = r1 * 256 + ((f1 ^ ((r1 & 3) << 2)) << 4);
   }
+};
+
+// wave-uniform value, held in a scalar register
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// off and nrows must be the same in every lane of the wave
+__device__ __forceinline__ void issue_chunk16(const void* kb, const void* vb, int64_t off_any, int nrows_any,
+                                              const DmaLane& dl, u32x4* sK, u32x4* sV) {
+  const int wave = threadIdx.x >> 6;
+  const int64_t off = uniform64(off_any);
+  const int nrows = __builtin_amdgcn_readfirstlane(nrows_any);
+  const bool present = off >= 0 && nrows > 0;
+  const int64_t ob = present ? off * 2 : 0;
+  const int nrec = present ? min(nrows, 32) * 256 : 0;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kb + ob), (short)0, nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vb + ob), (short)0, nrec, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + (2 * wave) * 64), 16, dl.k0, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + (2 * wave + 1) * 64), 16, dl.k1, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + (2 * wave) * 64), 16, dl.v0, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + (2 * wave + 1) * 64), 16, dl.v1, 0, 0, 0);
 }
 
 // e4m3fn caches: each thread loads 16 raw bytes of K and of V (16 dims of
@@ -266,10 +297,10 @@ __device__ __forceinline__ Raw8 load_chunk8(const uint8_t* kb, const uint8_t* vb
 template <typename CT>
 __device__ __forceinline__ void store_chunk8(const Raw8& r, u32x4* sK, u32x4* sV) {
   const int row = threadIdx.x >> 3, lc = threadIdx.x & 7;
-  sK[piece(row, 2 * lc)] = widen8<CT>(u32x2{r.k[0], r.k[1]});
-  sK[piece(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.k[2], r.k[3]});
-  sV[piece(row, 2 * lc)] = widen8<CT>(u32x2{r.v[0], r.v[1]});
-  sV[piece(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.v[2], r.v[3]});
+  sK[pieceK(row, 2 * lc)] = widen8<CT>(u32x2{r.k[0], r.k[1]});
+  sK[pieceK(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.k[2], r.k[3]});
+  sV[pieceV(row, 2 * lc)] = widen8<CT>(u32x2{r.v[0], r.v[1]});
+  sV[pieceV(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.v[2], r.v[3]});
 }
 
 // ---------------------------------------------------------------------------
@@ -354,144 +385,152 @@ struct XcdQueue {
 };
 
 // ---------------------------------------------------------------------------
-// k_units: KV-outer units, KV-stationary. Work item = kUnitsPerSeg
-// consecutive units of the residual order (units of one row are adjacent,
-// so the staged block is reused until the row or the sequence changes).
+// k_units: KV-outer units, KV-stationary. Work item = one window of the
+// residual order: up to Tu consecutive entries (tokens) of one row (block b,
+// KV head g). The window is cut into pieces -- runs of tokens of one
+// sequence, at most 128 / G tokens each, i.e. at most 128 query rows -- and
+// the pieces are multiplied one after another against the block, which stays
+// staged in LDS until the sequence or the row changes. The next piece's Q is
+// loaded while the current one is multiplied.
 // ---------------------------------------------------------------------------
+constexpr int kSeqLds = 256;  // cu_seqlens / used_kv_lens cached in LDS up to this many sequences
+
+__device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok, int head, int h) {
+  if (tok < 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const uint16_t* base = (const uint16_t*)p.q + ((size_t)tok * p.Hq + head) * kD + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qb[s] = *(const u32x4*)(base + 16 * s);
+}
+
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(256, 2) void k_units(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
   __shared__ u32x4 s_blk[kRing * kSlotU4];  // the staged block: chunk q at q * kSlotU4 (K), + kChunkU4 (V)
-  __shared__ int s_tok[128];
-  __shared__ int s_seq[128];
+  __shared__ int s_tok[kUnitWindow];
+  __shared__ int s_seq[kUnitWindow];
+  __shared__ int64_t s_cu[kSeqLds + 1];
+  __shared__ int s_used[kSeqLds];
   __shared__ int s_item;
   const int nU = p.counters[kCntUnits];
   if (nU == 0) return;
-  const int nseg = (nU + kUnitsPerSeg - 1) / kUnitsPerSeg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int G = p.G, Hkv = p.Hkv, K = p.K;
+  const int Tp = max(1, 128 / G);  // tokens per piece
+  const bool seq_lds = p.B <= kSeqLds;
+  if (seq_lds) {
+    for (int i = tid; i <= p.B; i += 256) s_cu[i] = p.cu[i];
+    for (int i = tid; i < p.B; i += 256) s_used[i] = p.used[i];
+  }
+  const int64_t* cu = seq_lds ? s_cu : p.cu;
+  const int* used = seq_lds ? s_used : p.used;
   int st_s = -1, st_b = -1, st_g = -1;  // staged block (uniform)
+  DmaLane dl;
+  dl.init();
   XcdQueue wq;
-  wq.init(nseg, p.counters + kCntXcdU);
+  wq.init(nU, p.counters + kCntXcdU);
   for (bool first = true;; first = false) {
     if (tid == 0) s_item = wq.next(first);
     __syncthreads();
-    const int id = s_item;
-    if (id < 0) break;
-    const int u0 = id * kUnitsPerSeg, u1 = min(u0 + kUnitsPerSeg, nU);
-    int r = 0;
-    {
-      int lo = 0, hi = p.NR;  // largest r with unit_off[r] <= u0
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.unit_off[mid] <= u0)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      r = lo;
+    const int u = s_item;
+    if (u < 0) break;
+    const int r = wave_last_le(p.unit_off, p.NR, u);
+    const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
+    const int rank0 = (u - p.unit_off[r]) * p.Tu;
+    const int e0 = p.row_off[r] + rank0;
+    const int n = min(p.Tu, p.row_off[r + 1] - e0);
+    for (int i = tid; i < n; i += 256) s_tok[i] = -1;
+    __syncthreads();
+    if (wave == 0) unit_tokens(p, r, rank0, n, s_tok);
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) s_seq[i] = s_tok[i] >= 0 ? seq_of(cu, p.B, s_tok[i]) : -1;
+    // the residual order of each entry, by slot (read by the tile merges)
+    for (int idx = tid; idx < n * K; idx += 256) {
+      const int tau = idx / K, k = idx - tau * K;
+      if (s_tok[tau] < 0) continue;
+      const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
+      if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.slot_pos[slot] = e0 + tau;
     }
-    for (int u = u0; u < u1; ++u) {
-      while (p.unit_off[r + 1] <= u) ++r;
-      const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
-      const int rank0 = (u - p.unit_off[r]) * p.Tu;
-      const int e0 = p.row_off[r] + rank0;
-      const int ntok = min(p.Tu, p.row_off[r + 1] - e0);
-      __syncthreads();  // the previous unit's readers of s_tok / s_seq are done
-      if (tid < 128) s_tok[tid] = -1;
-      __syncthreads();
-      if (wave == 0) unit_tokens(p, r, rank0, ntok, s_tok);
-      __syncthreads();
-      if (tid < ntok) s_seq[tid] = s_tok[tid] >= 0 ? seq_of(p.cu, p.B, s_tok[tid]) : -1;
-      // the residual order of each entry, by slot (read by the tile merges)
-      for (int idx = tid; idx < ntok * K; idx += 256) {
-        const int tau = idx / K, k = idx - tau * K;
-        if (s_tok[tau] < 0) continue;
-        const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
-        if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.slot_pos[slot] = e0 + tau;
-      }
-      __syncthreads();
-      const int rows = ntok * G;
-      const int rho = 32 * wave + c;
-      const bool valid = rho < rows;
-      const int tau = valid ? rho / G : 0;
-      const int hr = rho - tau * G;
-      Rows32 rt;
+    __syncthreads();
+
+    // pieces [a0, a1): a run of one sequence, at most Tp tokens
+    auto piece_end = [&](int a0) {
+      const int sq = s_seq[a0];
+      const int lim = min(n, a0 + Tp);
+      int e = a0 + 1;
+      while (e < lim && s_seq[e] == sq) ++e;
+      return e;
+    };
+    const int rho = 32 * wave + c;
+    const int head = g * G + (rho % G);
+    const int hr = rho % G;
+    auto row_token = [&](int a0, int a1) {  // the lane's token in piece [a0, a1), or -1
+      const int tau = rho / G;
+      return (a0 + tau < a1 && s_seq[a0 + tau] >= 0) ? s_tok[a0 + tau] : -1;
+    };
+    int a0 = 0, a1 = piece_end(0);
+    Rows32 rt;
+    load_q8(rt.qb, p, row_token(a0, a1), head, h);
+    for (;;) {
+      const int s_run = s_seq[a0];
+      const int a2 = a1 < n ? piece_end(a1) : a1;
+      u32x4 qn[8];
+      load_q8(qn, p, a1 < n ? row_token(a1, a2) : -1, head, h);  // the next piece's Q, in flight
       rows_reset(rt);
-      rt.seq = -1;
+      const int rows = (a1 - a0) * G;
+      const bool valid = rho < rows;
+      const int tok = valid ? s_tok[a0 + rho / G] : -1;
+      rt.seq = s_run;
       rt.pos = INT_MAX;
-      int tok = -1;
-      if (valid) {
-        tok = s_tok[tau];
-        const int s = s_seq[tau];
-        rt.seq = s;
-        if (s >= 0 && p.causal) {
-          const int64_t q0 = p.cu[s];
-          rt.pos = (int)(p.used[s] - (p.cu[s + 1] - q0) + (tok - q0));
+      if (s_run >= 0) {
+        const int L = used[s_run];
+        const int Leff = min(L, p.MP * p.P);
+        const int base = (int)(L - (cu[s_run + 1] - cu[s_run]) - cu[s_run]);  // pos = base + token
+        if (p.causal && tok >= 0) rt.pos = base + tok;
+        if (s_run != st_s || b != st_b || g != st_g) {
+          ring_barrier();  // every wave is done with the previous block
+          if constexpr (kFp8) {
+            Raw8 raw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v,
+                                   chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
+                                   p.zero_page);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+            __syncthreads();
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              issue_chunk16(p.k, p.v, chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff),
+                            Leff - (kBlk * b + 32 * q), dl, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+            wait_vmcnt<0>();
+            ring_barrier();
+          }
+          st_s = s_run;
+          st_b = b;
+          st_g = g;
         }
-      }
-      rows_load_q(rt, p, valid && rt.seq >= 0 ? tok : -1, g * G + hr, h);
-      const bool wave_has = 32 * wave < rows;
-
-      for (int run0 = 0; run0 < ntok;) {
-        const int s_run = s_seq[run0];
-        int run1 = run0 + 1;
-        while (run1 < ntok && s_seq[run1] == s_run) ++run1;
-        if (s_run >= 0) {
-          const int L = p.used[s_run];
-          const int Leff = min(L, p.MP * p.P);
-          if (s_run != st_s || b != st_b || g != st_g) {
-            ring_barrier();  // every wave is done with the previous block
-            if constexpr (kFp8) {
-              Raw8 raw[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v,
-                                     chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
-                                     p.zero_page);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
-              __syncthreads();
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                issue_chunk16((const uint16_t*)p.k, (const uint16_t*)p.v,
-                              chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
-                              p.zero_page, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
-              wait_vmcnt<0>();
-              ring_barrier();
-            }
-            st_s = s_run;
-            st_b = b;
-            st_g = g;
-          }
-          // visibility bounds of the run's rows
-          const bool single = run0 == 0 && run1 == ntok;
-          int pmin = INT_MAX, pmax = INT_MAX;
-          if (p.causal) {
-            const int64_t q0 = p.cu[s_run];
-            const int base = (int)(L - (p.cu[s_run + 1] - q0) - q0);
-            pmin = base + s_tok[run0];
-            pmax = base + s_tok[run1 - 1];
-          }
-          if (wave_has) {
+        const int pmin = p.causal ? base + s_tok[a0] : INT_MAX;
+        const int pmax = p.causal ? base + s_tok[a1 - 1] : INT_MAX;
+        if (32 * wave < rows) {
 #pragma unroll 1
-            for (int q = 0; q < 4; ++q) {
-              const int key0 = kBlk * b + 32 * q;
-              if (key0 >= Leff || key0 > pmax) break;
-              const bool full = single && key0 + 31 < Leff && key0 + 31 <= pmin;
-              rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, Leff, s_run, !full,
-                                 p.scale_log2);
-            }
+          for (int q = 0; q < 4; ++q) {
+            const int key0 = kBlk * b + 32 * q;
+            if (key0 >= Leff || key0 > pmax) break;
+            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
+            rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, Leff, s_run, !full,
+                           p.scale_log2);
           }
         }
-        run0 = run1;
       }
-
-      // partial result of the unit's rows: normalised O and log2 LSE
+      // partial result of the piece's rows: normalised O and log2 LSE
       const float l_row = rows_total(rt);
       if (valid) {
-        const size_t pidx = (size_t)(e0 + tau) * G + hr;
+        const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
         store_row16<CT>((uint16_t*)p.opart + pidx * kD, rt, inv);
         if (h == 0) {
@@ -499,7 +538,13 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
           p.lpart[pidx] = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
         }
       }
+      if (a1 >= n) break;
+      a0 = a1;
+      a1 = a2;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) rt.qb[s] = qn[s];
     }
+    __syncthreads();  // the window's readers of s_tok / s_seq are done
   }
 }
 
@@ -527,6 +572,8 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
   const int ntiles = (p.Tq + Teff - 1) / Teff + p.B;  // bound on the tile count
   const int total = listed ? p.counters[kCntTiles] : ntiles * Hkv;
   if (total == 0) return;
+  DmaLane dl;
+  dl.init();
   XcdQueue wq;
   wq.init(total, p.counters + kCntXcd);
   for (bool first = true;; first = false) {
@@ -605,19 +652,17 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
           __syncthreads();
         }
       } else {
-        const uint16_t* kb = (const uint16_t*)p.k;
-        const uint16_t* vb = (const uint16_t*)p.v;
         asm volatile("" ::: "memory");  // the Q loads above are older than the ring loads
 #pragma unroll
         for (int ci = 0; ci < kRing - 1; ++ci)
-          issue_chunk16(kb, vb, ci < nck ? s_koff[ci] : (int64_t)-1, ci < nck ? Leff - s_key0[ci] : 0, p.zero_page,
+          issue_chunk16(p.k, p.v, ci < nck ? s_koff[ci] : (int64_t)-1, ci < nck ? Leff - s_key0[ci] : 0, dl,
                         s_ring + ci * kSlotU4, s_ring + ci * kSlotU4 + kChunkU4);
         for (int ci = 0; ci < nck; ++ci) {
           wait_vmcnt<8>();  // chunk ci has landed (two newer chunks may be in flight)
           ring_barrier();   // ... for every wave; and slot (ci + 3) % 4 is free
           const int nx = ci + kRing - 1;
           u32x4* sn = s_ring + (nx & (kRing - 1)) * kSlotU4;
-          issue_chunk16(kb, vb, nx < nck ? s_koff[nx] : (int64_t)-1, nx < nck ? Leff - s_key0[nx] : 0, p.zero_page, sn,
+          issue_chunk16(p.k, p.v, nx < nck ? s_koff[nx] : (int64_t)-1, nx < nck ? Leff - s_key0[nx] : 0, dl, sn,
                         sn + kChunkU4);
           const int64_t off = s_koff[ci];
           if (wave_has && off >= 0) {
