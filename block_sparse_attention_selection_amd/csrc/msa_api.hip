@@ -186,9 +186,11 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->ent = c.take<int32_t>(base, nslots);
   p->slot_pos = c.take<int32_t>(base, nslots);
   if (with_partials) {
+    p->res_list = c.take<int32_t>(base, nslots);
     p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
+    p->res_list = nullptr;
     p->opart = nullptr;
     p->lpart = nullptr;
   }

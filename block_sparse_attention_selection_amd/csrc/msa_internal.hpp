@@ -70,7 +70,8 @@ struct Params {
   int32_t* row_off;
   int32_t* unit_off;
   int32_t* ent;
-  int32_t* slot_pos;
+  int32_t* slot_pos;   // staged index entry: residual order of each slot
+  int32_t* res_list;   // attention: per (t, g), the residual order of its residual slots, in slot order
   // partial results of the KV-outer units
   void* opart;   // [residual slots, G, 128] normalised O, in q's 16-bit type
   float* lpart;  // [residual slots, G] LSE (log2 units)

@@ -447,12 +447,19 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
     if (wave == 0) unit_tokens(p, r, rank0, n, s_tok);
     __syncthreads();
     for (int i = tid; i < n; i += 256) s_seq[i] = s_tok[i] >= 0 ? seq_of(cu, p.B, s_tok[i]) : -1;
-    // the residual order of each entry, by slot (read by the tile merges)
+    // the residual order of each entry, listed per (token, KV head) in slot
+    // order (read by the tile merges)
     for (int idx = tid; idx < n * K; idx += 256) {
       const int tau = idx / K, k = idx - tau * K;
       if (s_tok[tau] < 0) continue;
       const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
-      if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.slot_pos[slot] = e0 + tau;
+      if (p.selected[slot] == b && p.slot_flag[slot] == 2) {
+        // rank of the slot among the residual slots of (token, g)
+        const uint8_t* f = p.slot_flag + (slot - k);
+        int rank = 0;
+        for (int k2 = 0; k2 < k; ++k2) rank += f[k2] == 2;
+        p.res_list[slot - k + rank] = e0 + tau;
+      }
     }
     __syncthreads();
 
@@ -676,50 +683,67 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
       }
     }
 
-    // merge with the unit partials of the row's residual slots, then write
+    // merge with the unit partials of the row's residual slots, then write.
+    // The partials' positions are listed per (token, KV head); partial i+1
+    // is loaded while partial i is merged. The reference max M moves only
+    // when a partial's LSE exceeds it by more than 2^kRescale32.
     const float l_tot = rows_total(rt);
     if (valid) {
       const size_t tg = (size_t)tok * Hkv + g;
-      float M = rt.m;
-      const int nres = p.tok_nres[tg];
+      const int nres = min(p.tok_nres[tg], K);
       const int ntot = p.counters[kCntResidual];  // positions are below this
-      const uint8_t* flags = p.slot_flag + tg * K;
-      const int32_t* spos = p.slot_pos + tg * K;
+      const int32_t* rl = p.res_list + tg * K;
+      float M = rt.m;  // O and W are relative to 2^M
+      float W = l_tot;
+      const uint16_t* obase = (const uint16_t*)p.opart + 4 * h;
+      auto fetch = [&](int i, float& li, u32x2 (&d)[16]) {
+        const int pos = i < nres ? rl[i] : -1;
+        const bool ok = pos >= 0 && pos < ntot;
+        const size_t pidx = ok ? (size_t)pos * G + hr : 0;
+        li = ok ? p.lpart[pidx] : -INFINITY;
+        const uint16_t* src = obase + pidx * kD;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) d[4 * t + a] = *(const u32x2*)(src + 32 * t + 8 * a);
+      };
       if (nres > 0) {
-        for (int k = 0; k < K; ++k) {
-          const int sp = spos[k];
-          if (flags[k] == 2 && sp >= 0 && sp < ntot) M = fmaxf(M, p.lpart[(size_t)sp * G + hr]);
-        }
-      }
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float fc = rt.m == -INFINITY ? 0.f : exp2f(rt.m - Mu);
-      float W = l_tot * fc;
+        float lc;
+        u32x2 dc[16];
+        fetch(0, lc, dc);
+        for (int i = 0; i < nres; ++i) {
+          float ln;
+          u32x2 dn[16];
+          fetch(i + 1, ln, dn);  // in flight while partial i is merged
+          if (lc != -INFINITY) {
+            if (M == -INFINITY || lc > M + kRescale32) {
+              const float sc = M == -INFINITY ? 0.f : exp2f(M - lc);
+              W *= sc;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rt.o[t] *= fc;
-      if (nres > 0) {
-        for (int k = 0; k < K; ++k) {
-          const int sp = spos[k];
-          if (flags[k] != 2 || sp < 0 || sp >= ntot) continue;
-          const size_t pidx = (size_t)sp * G + hr;
-          const float li = p.lpart[pidx];
-          const float fi = li == -INFINITY ? 0.f : exp2f(li - Mu);
-          W += fi;
-          const uint16_t* src = (const uint16_t*)p.opart + pidx * kD + 4 * h;
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const u32x2 w = *(const u32x2*)(src + 32 * t + 8 * a);
-              rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
-              rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
-              rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
-              rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
+              for (int t = 0; t < 4; ++t) rt.o[t] *= sc;
+              M = lc;
             }
+            const float fi = exp2f(lc - M);
+            W += fi;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+              for (int a = 0; a < 4; ++a) {
+                const u32x2 w = dc[4 * t + a];
+                rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
+                rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
+                rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
+                rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
+              }
+          }
+          lc = ln;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) dc[j] = dn[j];
         }
       }
       const float inv = W > 0.f ? 1.f / W : 0.f;
       store_row16<CT>((uint16_t*)p.out + ((size_t)tok * p.Hq + head) * kD, rt, inv);
-      if (h == 0 && p.lse) p.lse[(size_t)head * p.Tq + tok] = W > 0.f ? (Mu + log2f(W)) * kLn2 : -INFINITY;
+      if (h == 0 && p.lse) p.lse[(size_t)head * p.Tq + tok] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
     }
     __syncthreads();  // the chunk table and ring are free for the next item
   }
