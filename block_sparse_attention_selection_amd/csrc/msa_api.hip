@@ -187,10 +187,14 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->slot_pos = c.take<int32_t>(base, nslots);
   if (with_partials) {
     p->res_list = c.take<int32_t>(base, nslots);
+    p->res_rank = c.take<uint8_t>(base, nslots);
+    p->win_desc = c.take<int4>(base, nslots);
     p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
     p->res_list = nullptr;
+    p->res_rank = nullptr;
+    p->win_desc = nullptr;
     p->opart = nullptr;
     p->lpart = nullptr;
   }

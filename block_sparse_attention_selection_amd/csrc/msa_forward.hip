@@ -33,6 +33,9 @@
 
 namespace msa {
 
+// marks a residual slot in the classifiers' LDS pick lists (block ids are < 2^30)
+constexpr int kResidualMark = 1 << 30;
+
 // element offset of k-step s (0..3, 32 dims each) for lane group q: pairs of
 // k-steps share one 64-dim slab, so an fp8 lane reads 16 contiguous bytes
 __device__ __forceinline__ int kmap(int s, int q) { return 64 * (s >> 1) + 16 * q + 8 * (s & 1); }
@@ -456,8 +459,18 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
       }
     }
     p.slot_flag[((size_t)(t + tau) * Hkv + g) * K + (idx - tau * K)] = flag;
+    if (flag == 2) s_sel[idx] = b | kResidualMark;
   }
   __syncthreads();
+  if (p.res_rank) {  // rank of each residual slot among its token's residual slots
+    for (int idx = tid; idx < nt * K; idx += 256) {
+      if (!(s_sel[idx] & kResidualMark) || s_sel[idx] < 0) continue;
+      const int tau = idx / K;
+      int rank = 0;
+      for (int i = tau * K; i < idx; ++i) rank += (s_sel[i] >= 0 && (s_sel[i] & kResidualMark)) ? 1 : 0;
+      p.res_rank[((size_t)(t + tau) * Hkv + g) * K + (idx - tau * K)] = (uint8_t)rank;
+    }
+  }
 
   // per-token results; the tile is finished here or listed
   if (wave == 0) {
@@ -482,6 +495,124 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     __syncthreads();
     if (stream && s_tile_res == 0)
       stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// wave-per-tile classification (tiles of at most kWaveSlots slots): the same
+// rules as k_front's classification, with each wave handling one tile on its
+// own, so a workgroup carries four tiles and no workgroup barrier. Used
+// outside decode mode, where the front kernel only classifies.
+// ---------------------------------------------------------------------------
+constexpr int kWaveSlots = 512;  // tile tokens x topk handled by one wave
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
+  __shared__ int s_sel[4][kWaveSlots];  // valid picks, -1 where the slot is invalid
+  __shared__ int s_chain[4][64];
+  __shared__ int s_nres[4][128];
+  __shared__ unsigned long long s_miss[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.y;
+  const int j = blockIdx.x * 4 + wave;
+  const int K = p.K, Hkv = p.Hkv;
+  const int Teff = p.T > 0 ? p.T : 1;
+  if (j >= ntiles) return;
+  int64_t t0l;
+  const int s = wave_tile_of(p.cu, p.B, p.Tq, Teff, j, &t0l);
+  if (s < 0) return;
+  const int t = (int)t0l;
+  const size_t tg = (size_t)t * Hkv + g;
+  const int64_t q0 = p.cu[s], qe = p.cu[s + 1];
+  const int nt = (int)min((int64_t)Teff, min(qe, (int64_t)p.Tq) - t);
+  const int L = p.used[s];
+  const int Tq_s = (int)(qe - q0);
+  const int i0 = (int)(t - q0);
+  const int nblk = L > 0 ? min((L + kBlk - 1) / kBlk, p.nb_max) : 0;
+  int* sel = s_sel[wave];
+  for (int idx = lane; idx < nt * K; idx += 64) {
+    const int tau = idx / K;
+    const int b = p.selected[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)];
+    const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
+    const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
+    sel[idx] = valid ? b : -1;
+  }
+  for (int tau = lane; tau < nt; tau += 64) s_nres[wave][tau] = 0;
+  if (lane == 0) s_miss[wave] = 0ull;
+  wave_lds_sync();
+  // the chain: the leader's valid picks present in every token of the tile
+  if (p.T > 0) {
+    unsigned long long miss = 0ull;
+    for (int idx = lane + K; idx < nt * K; idx += 64) {
+      const int tau = idx / K, k = idx - tau * K;
+      const int bl = sel[k];
+      if (bl < 0) continue;
+      bool found = false;
+      for (int k2 = 0; k2 < K; ++k2) found |= (sel[tau * K + k2] == bl);
+      if (!found) miss |= 1ull << k;
+    }
+    if (miss) atomicOr(&s_miss[wave], miss);
+  }
+  wave_lds_sync();
+  bool in_chain = false;
+  int bl = -1;
+  if (p.T > 0 && lane < K) {
+    bl = sel[lane];
+    in_chain = bl >= 0 && !((s_miss[wave] >> lane) & 1ull);
+    for (int k2 = 0; k2 < lane && in_chain; ++k2) in_chain = sel[k2] != bl;  // first occurrence only
+  }
+  const uint64_t mask = __ballot(in_chain);
+  const int n_ch = __popcll(mask);
+  if (in_chain) {
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    s_chain[wave][rank] = bl;
+    p.chain_blk[tg * K + rank] = bl;
+  }
+  wave_lds_sync();
+  // flags, residual bits, residual counts
+  int res = 0;
+  for (int idx = lane; idx < nt * K; idx += 64) {
+    const int tau = idx / K;
+    const int b = sel[idx];
+    uint8_t flag = 0;
+    if (b >= 0) {
+      bool cov = false;
+      for (int c = 0; c < n_ch; ++c) cov |= (s_chain[wave][c] == b);
+      flag = cov ? 1 : 2;
+      if (!cov) {
+        const int tt = t + tau;
+        atomicOr(&p.bitmap[((size_t)b * Hkv + g) * p.W + (tt >> 5)], 1u << (tt & 31));
+        atomicAdd(&s_nres[wave][tau], 1);
+        ++res;
+      }
+    }
+    p.slot_flag[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)] = flag;
+    if (flag == 2) sel[idx] = b | kResidualMark;
+  }
+  wave_lds_sync();
+  if (p.res_rank) {  // rank of each residual slot among its token's residual slots
+    for (int idx = lane; idx < nt * K; idx += 64) {
+      if (sel[idx] < 0 || !(sel[idx] & kResidualMark)) continue;
+      const int tau = idx / K;
+      int rank = 0;
+      for (int i = tau * K; i < idx; ++i) rank += (sel[i] >= 0 && (sel[i] & kResidualMark)) ? 1 : 0;
+      p.res_rank[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)] = (uint8_t)rank;
+    }
+  }
+  for (int tau = lane; tau < nt; tau += 64) {
+    const size_t tg2 = tg + (size_t)tau * Hkv;
+    p.tok_chain[tg2] = n_ch;
+    p.tok_nres[tg2] = s_nres[wave][tau];
+  }
+  const bool any_res = __any(res > 0);
+  if (lane == 0) {
+    if (any_res) p.counters[kCntResidual] = 1;  // "some"; the index kernel writes the total
+    if (p.list_tiles) p.tile_items[atomicAdd(&p.counters[kCntTiles], 1)] = (int)tg;
   }
 }
 
@@ -522,7 +653,13 @@ hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st
   hipError_t e;
   // outside decode mode the front kernel only classifies: the light
   // instantiation (no attention registers or LDS) keeps many workgroups per CU
-  if (q_elem < 0 || !p.stream_narrow)
+  const int Teff = p.T > 0 ? p.T : 1;
+  if (!p.stream_narrow && Teff * p.K <= kWaveSlots) {
+    // every tile is listed or enumerated: one wave per tile
+    const int ntiles = (p.Tq + Teff - 1) / Teff + p.B;
+    hipLaunchKernelGGL(k_classify_waves, dim3((ntiles + 3) / 4, p.Hkv), dim3(256), 0, st, p, ntiles);
+    e = hipGetLastError();
+  } else if (q_elem < 0 || !p.stream_narrow)
     e = launch_front_t<bf16_t, bf16_t, false>(p, st);
   else if (q_elem == kElemBF16)
     e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(p, st)

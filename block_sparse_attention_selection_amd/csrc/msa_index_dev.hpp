@@ -87,8 +87,15 @@ __device__ __forceinline__ void rowscan_all(const Params& p, int* smem) {
     const int c = __hip_atomic_load(&p.row_cnt[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     p.row_off[r] = run_c;
     p.unit_off[r] = run_u;
+    const int nu = (c + p.Tu - 1) / p.Tu;
+    if (p.win_desc) {  // (row, first rank, first entry, entries) of each of the row's windows
+      for (int i = 0; i < nu; ++i) {
+        const int rank0 = i * p.Tu;
+        p.win_desc[run_u + i] = int4{r, rank0, run_c + rank0, min(p.Tu, c - rank0)};
+      }
+    }
     run_c += c;
-    run_u += (c + p.Tu - 1) / p.Tu;
+    run_u += nu;
   }
   if (threadIdx.x == 0) {
     p.row_off[NR] = tot_cnt;

@@ -72,6 +72,8 @@ struct Params {
   int32_t* ent;
   int32_t* slot_pos;   // staged index entry: residual order of each slot
   int32_t* res_list;   // attention: per (t, g), the residual order of its residual slots, in slot order
+  uint8_t* res_rank;   // attention: rank of a residual slot among the residual slots of its (t, g)
+  int4* win_desc;      // attention: per unit-kernel window (row, first rank, first entry, entries)
   // partial results of the KV-outer units
   void* opart;   // [residual slots, G, 128] normalised O, in q's 16-bit type
   float* lpart;  // [residual slots, G] LSE (log2 units)

@@ -437,11 +437,9 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
     __syncthreads();
     const int u = s_item;
     if (u < 0) break;
-    const int r = wave_last_le(p.unit_off, p.NR, u);
+    const int4 wd = p.win_desc[u];  // (row, first rank, first entry, entries)
+    const int r = wd.x, rank0 = wd.y, e0 = wd.z, n = min(wd.w, p.Tu);
     const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
-    const int rank0 = (u - p.unit_off[r]) * p.Tu;
-    const int e0 = p.row_off[r] + rank0;
-    const int n = min(p.Tu, p.row_off[r + 1] - e0);
     for (int i = tid; i < n; i += 256) s_tok[i] = -1;
     __syncthreads();
     if (wave == 0) unit_tokens(p, r, rank0, n, s_tok);
@@ -453,13 +451,7 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
       const int tau = idx / K, k = idx - tau * K;
       if (s_tok[tau] < 0) continue;
       const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
-      if (p.selected[slot] == b && p.slot_flag[slot] == 2) {
-        // rank of the slot among the residual slots of (token, g)
-        const uint8_t* f = p.slot_flag + (slot - k);
-        int rank = 0;
-        for (int k2 = 0; k2 < k; ++k2) rank += f[k2] == 2;
-        p.res_list[slot - k + rank] = e0 + tau;
-      }
+      if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.res_list[slot - k + p.res_rank[slot]] = e0 + tau;
     }
     __syncthreads();
 
