@@ -189,12 +189,17 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
     p->res_list = c.take<int32_t>(base, nslots);
     p->res_rank = c.take<uint8_t>(base, nslots);
     p->win_desc = c.take<int4>(base, nslots);
+    const size_t items = ((size_t)(d.Tq + d.T - 1) / d.T + d.B) * d.Hkv;  // tile items, listed or enumerated
+    p->tdesc = c.take<int4>(base, 2 * items);
+    p->ctab = c.take<int4>(base, items * 4 * d.K);
     p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
     p->res_list = nullptr;
     p->res_rank = nullptr;
     p->win_desc = nullptr;
+    p->tdesc = nullptr;
+    p->ctab = nullptr;
     p->opart = nullptr;
     p->lpart = nullptr;
   }
@@ -413,6 +418,7 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   WsLease ws;
   if ((rc = get_workspace(need, (size_t)d.NR * d.W, &ws))) return rc;
   layout(d, (char*)ws.scratch, &p, true);
+  p.slot_pos = nullptr;  // the per-token residual lists replace it here
   fill_inputs(&p, d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
   // decode-shaped batches (few queries per sequence, at most 16 query rows
   // per token) finish their residual-free tiles in the front kernel, one
@@ -434,7 +440,11 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   hipError_t e = hipSuccess;
   if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
   if (e == hipSuccess) e = msa::launch_front(p, d.q_elem, d.kv_elem, st);
-  if (e == hipSuccess) e = msa::launch_index(p, false, st);
+  // decode-shaped batches rarely have residual slots: there the unit kernel
+  // derives the residual order itself and the materialising pass (one more
+  // launch) is skipped
+  p.ent_ready = p.stream_narrow ? 0 : 1;
+  if (e == hipSuccess) e = msa::launch_index(p, p.ent_ready != 0, st);
   if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, ws.num_cu, st);
   if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, ws.num_cu, st);
   {

@@ -336,6 +336,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   __shared__ int s_page[128];     // pages of the leader's picks (ppb per pick)
   __shared__ int s_nch;
   __shared__ int s_tile_res;      // residual slots of the tile
+  __shared__ int s_item_idx;      // the tile kernel's item for this tile (-1: none)
   __shared__ int s_miss[64];      // leader picks missing from some token of the tile
   const int g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -370,7 +371,10 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     // one workgroup per tile
     int64_t t0;
     s = wave_tile_of(p.cu, p.B, p.Tq, Teff, blockIdx.x, &t0);
-    if (s < 0) return;
+    if (s < 0) {  // no tile: the tile kernel's item (g, blockIdx.x) has nothing to do
+      if (p.tdesc && tid == 0) p.tdesc[2 * ((size_t)g * gridDim.x + blockIdx.x)] = int4{0, 0, 0, 0};
+      return;
+    }
     t = (int)t0;
     if (tid < K) b_raw = p.selected[((size_t)t * Hkv + g) * K + tid];
   }
@@ -488,11 +492,19 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
       s_tile_res = res;
       if (res > 0) p.counters[kCntResidual] = 1;  // "some"; the index kernel writes the total
       const bool here = p.stream_narrow && rows <= 16 && res == 0;
-      if (!here && p.list_tiles) p.tile_items[atomicAdd(&p.counters[kCntTiles], 1)] = (int)tg;
+      int item = -1;  // the tile kernel's item for this tile
+      if (!here && p.list_tiles) {
+        item = atomicAdd(&p.counters[kCntTiles], 1);
+        p.tile_items[item] = (int)tg;
+      }
+      if (!p.stream_narrow) item = (int)(g * gridDim.x + blockIdx.x);
+      s_item_idx = item;
     }
   }
+  __syncthreads();
+  if (p.tdesc && s_item_idx >= 0)
+    write_tile_desc(p, s_item_idx, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain, tid, 256);
   if constexpr (ATTN) {
-    __syncthreads();
     if (stream && s_tile_res == 0)
       stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
   }
@@ -525,7 +537,11 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   if (j >= ntiles) return;
   int64_t t0l;
   const int s = wave_tile_of(p.cu, p.B, p.Tq, Teff, j, &t0l);
-  if (s < 0) return;
+  const int item = g * ntiles + j;  // the tile kernel's item (KV head, tile number)
+  if (s < 0) {
+    if (p.tdesc && lane == 0) p.tdesc[2 * (size_t)item] = int4{0, 0, 0, 0};  // no tile: nothing to do
+    return;
+  }
   const int t = (int)t0l;
   const size_t tg = (size_t)t * Hkv + g;
   const int64_t q0 = p.cu[s], qe = p.cu[s + 1];
@@ -574,6 +590,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     p.chain_blk[tg * K + rank] = bl;
   }
   wave_lds_sync();
+  if (p.tdesc) write_tile_desc(p, item, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain[wave], lane, 64);
   // flags, residual bits, residual counts
   int res = 0;
   for (int idx = lane; idx < nt * K; idx += 64) {

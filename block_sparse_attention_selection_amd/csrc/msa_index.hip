@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_index(Params p, int rows_per_task, int 
   if (s_last) rowscan_all<256>(p, smem);
 }
 
-// staged entry only: materialise ent / slot_pos from the implicit order
+// materialise the residual order (ent, and slot_pos or the per-token lists)
 __global__ __launch_bounds__(256) void k_emit(Params p) {
   if (p.counters[kCntResidual] == 0) return;
   const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;

@@ -4,6 +4,8 @@
 #pragma once
 
 #include "msa_device.hpp"
+#include <limits.h>
+
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -105,6 +107,40 @@ __device__ __forceinline__ void rowscan_all(const Params& p, int* smem) {
   }
 }
 
+// element offset of the 32-key chunk starting at key0 of sequence s, KV head
+// g, or -1 when the chunk lies beyond the keys the page table can reach or
+// its page is out of range (its keys are then treated as absent)
+__device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, int key0, int Leff) {
+  if (key0 >= Leff) return -1;
+  const int page = p.block_tables[(size_t)s * p.MP + key0 / p.P];
+  if (page < 0 || page >= p.NP) return -1;
+  return (((int64_t)page * p.Hkv + g) * p.P + (key0 % p.P)) * 128;
+}
+
+// Descriptor and chunk table of tile item `item` (tile leader t0 of sequence
+// s, nt tokens, KV head g, chain of n_ch blocks): tdesc[2 item] = (t0, s, nt,
+// n_ch), tdesc[2 item + 1] = (reachable keys Leff, base position: pos =
+// base + token, g), ctab[item * 4 topk + ci] = (element offset low, high, first
+// key, keys present) of chunk ci, offset -1 for a chunk no row can see.
+// Threads first, first + stride, ... share the chunks.
+__device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t0, int s, int nt, int n_ch, int L,
+                                                int Tq_s, int64_t q0, int g, const int* chain, int first,
+                                                int stride) {
+  const int Leff = min(L, p.MP * p.P);
+  const int base = (int)(L - Tq_s - q0);
+  const int pmax = p.causal ? base + t0 + nt - 1 : INT_MAX;
+  const size_t K4 = 4 * (size_t)p.K;
+  for (int ci = first; ci < 4 * n_ch; ci += stride) {
+    const int key0 = 128 * chain[ci >> 2] + 32 * (ci & 3);
+    const int64_t off = key0 > pmax ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
+    p.ctab[(size_t)item * K4 + ci] = int4{(int)(uint32_t)(uint64_t)off, (int)(off >> 32), key0, min(32, Leff - key0)};
+  }
+  if (first == 0) {
+    p.tdesc[2 * (size_t)item] = int4{t0, s, nt, n_ch};
+    p.tdesc[2 * (size_t)item + 1] = int4{Leff, base, g, 0};
+  }
+}
+
 // Index of residual slot (t, g) -> block b in the residual order: the row's
 // offset plus the token's rank among the row's set bits. The row data were
 // written by an earlier kernel.
@@ -115,10 +151,11 @@ __device__ __forceinline__ int residual_pos(const Params& p, int t, int g, int b
   return p.row_off[r] + (int)p.wordpre[w] + __popc(below);
 }
 
-// Materialises the residual order for one slot (ent, slot_pos); used by the
-// staged index entry point, which returns these arrays for testing. Flags of
-// tokens this call did not classify (only with malformed cu_seqlens) are
-// ignored: their bit is not set.
+// Materialises the residual order for one slot: ent[pos] = slot, and, when
+// present, slot_pos[slot] = pos (staged index entry point) and the slot's
+// entry in its (t, g) residual list, res_list[tg * K + rank] = pos (attention;
+// rank from res_rank). Flags of tokens this call did not classify (only with
+// malformed cu_seqlens) are ignored: their bit is not set.
 __device__ __forceinline__ void emit_slot(const Params& p, int64_t slot) {
   if (p.slot_flag[slot] != 2) return;
   const int t = (int)(slot / ((int64_t)p.Hkv * p.K));
@@ -129,7 +166,11 @@ __device__ __forceinline__ void emit_slot(const Params& p, int64_t slot) {
   if (!((p.wordbits[w] >> (t & 31)) & 1u)) return;
   const int pos = residual_pos(p, t, g, b);
   p.ent[pos] = (int)slot;
-  p.slot_pos[slot] = pos;
+  if (p.slot_pos) p.slot_pos[slot] = pos;
+  if (p.res_list) {
+    const int64_t k = slot % p.K;
+    p.res_list[slot - k + p.res_rank[slot]] = pos;
+  }
 }
 
 }  // namespace msa

@@ -53,6 +53,7 @@ struct Params {
   int causal;
   int stream_narrow;  // front kernel finishes residual-free tiles of <= 16 rows (decode mode)
   int list_tiles;     // front kernel appends the tiles it does not finish to tile_items
+  int ent_ready;      // the index step materialised ent and res_list (else the unit kernel derives them)
   float scale_log2;   // softmax scale * log2(e)
   // planning arrays
   int32_t* counters;       // this call's counter set (zero on entry)
@@ -74,6 +75,8 @@ struct Params {
   int32_t* res_list;   // attention: per (t, g), the residual order of its residual slots, in slot order
   uint8_t* res_rank;   // attention: rank of a residual slot among the residual slots of its (t, g)
   int4* win_desc;      // attention: per unit-kernel window (row, first rank, first entry, entries)
+  int4* tdesc;         // attention: per tile item, 2 x int4 (see write_tile_desc)
+  int4* ctab;          // attention: per tile item, 4 topk chunk entries
   // partial results of the KV-outer units
   void* opart;   // [residual slots, G, 128] normalised O, in q's 16-bit type
   float* lpart;  // [residual slots, G] LSE (log2 units)
@@ -85,8 +88,8 @@ extern volatile uint32_t g_profile_mask;
 void profile_mark(int kernel, bool begin, hipStream_t st);
 
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
-// residual inversion: row counts and row scan; `materialise` also writes
-// ent / slot_pos (staged entry point only) (msa_index.hip)
+// residual inversion: row counts and row scan; `materialise` also writes the
+// residual order (ent, and slot_pos or the per-token residual lists) (msa_index.hip)
 hipError_t launch_index(const Params& p, bool materialise, hipStream_t st);
 // front kernel: classification, plus the residual-free narrow tiles when
 // attention is requested (msa_forward.hip); q_elem < 0 classifies only

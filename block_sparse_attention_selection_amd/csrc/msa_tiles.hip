@@ -345,16 +345,6 @@ __device__ __forceinline__ void unit_tokens(const Params& p, int r, int rank0, i
   }
 }
 
-// element offset of the 32-key chunk starting at key0 of sequence s, KV head
-// g, or -1 when the chunk lies beyond the keys the page table can reach or
-// its page is out of range (its keys are then treated as absent)
-__device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, int key0, int Leff) {
-  if (key0 >= Leff) return -1;
-  const int page = p.block_tables[(size_t)s * p.MP + key0 / p.P];
-  if (page < 0 || page >= p.NP) return -1;
-  return (((int64_t)page * p.Hkv + g) * p.P + (key0 % p.P)) * kD;
-}
-
 // ---------------------------------------------------------------------------
 // XCD-aware work queue. Workgroups of a launch are dispatched round-robin
 // over the 8 XCDs, each with its own L2, so workgroup i runs on XCD i % 8.
@@ -432,28 +422,57 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
   dl.init();
   XcdQueue wq;
   wq.init(nU, p.counters + kCntXcdU);
-  for (bool first = true;; first = false) {
-    if (tid == 0) s_item = wq.next(first);
-    __syncthreads();
-    const int u = s_item;
-    if (u < 0) break;
-    const int4 wd = p.win_desc[u];  // (row, first rank, first entry, entries)
-    const int r = wd.x, rank0 = wd.y, e0 = wd.z, n = min(wd.w, p.Tu);
-    const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
-    for (int i = tid; i < n; i += 256) s_tok[i] = -1;
-    __syncthreads();
-    if (wave == 0) unit_tokens(p, r, rank0, n, s_tok);
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) s_seq[i] = s_tok[i] >= 0 ? seq_of(cu, p.B, s_tok[i]) : -1;
-    // the residual order of each entry, listed per (token, KV head) in slot
-    // order (read by the tile merges)
-    for (int idx = tid; idx < n * K; idx += 256) {
-      const int tau = idx / K, k = idx - tau * K;
-      if (s_tok[tau] < 0) continue;
-      const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
-      if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.res_list[slot - k + p.res_rank[slot]] = e0 + tau;
+  const int64_t slots_per_tok = (int64_t)Hkv * K;
+  // the window's descriptor and tokens (two per thread) are loaded one window ahead
+  // (with ent materialised; otherwise the tokens come from the row's bitmap
+  // words when the window starts, and the window writes its own residual
+  // list entries)
+  const bool have_ent = p.ent_ready != 0;
+  auto load_tokens = [&](int4 wd, int (&tk)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      tk[i] = (have_ent && e < min(wd.w, p.Tu)) ? (int)(p.ent[wd.z + e] / slots_per_tok) : -1;
     }
+  };
+  if (tid == 0) s_item = wq.next(true);
+  __syncthreads();
+  int u = s_item;
+  __syncthreads();  // s_item is rewritten inside the loop
+  int4 wd = u >= 0 ? p.win_desc[u] : int4{0, 0, 0, 0};
+  int tk[2];
+  load_tokens(wd, tk);
+  while (u >= 0) {
+    const int r = wd.x, e0 = wd.z, n = min(wd.w, p.Tu);
+    const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
+    if (!have_ent) {
+      for (int i = tid; i < n; i += 256) s_tok[i] = -1;
+      __syncthreads();
+      if (wave == 0) unit_tokens(p, r, wd.y, n, s_tok);
+      __syncthreads();
+      for (int idx = tid; idx < n * K; idx += 256) {
+        const int tau = idx / K, k = idx - tau * K;
+        if (s_tok[tau] < 0) continue;
+        const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
+        if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.res_list[slot - k + p.res_rank[slot]] = e0 + tau;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      if (e < n) {
+        const int tok = have_ent ? tk[i] : s_tok[e];
+        s_tok[e] = tok;
+        s_seq[e] = tok >= 0 ? seq_of(cu, p.B, tok) : -1;
+      }
+    }
+    if (tid == 0) s_item = wq.next(false);
     __syncthreads();
+    // the next window, in flight while this one is multiplied
+    const int un = s_item;
+    const int4 wdn = un >= 0 ? p.win_desc[un] : int4{0, 0, 0, 0};
+    int tkn[2];
+    load_tokens(wdn, tkn);
 
     // pieces [a0, a1): a run of one sequence, at most Tp tokens
     auto piece_end = [&](int a0) {
@@ -543,26 +562,33 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) rt.qb[s] = qn[s];
     }
-    __syncthreads();  // the window's readers of s_tok / s_seq are done
+    __syncthreads();  // the window's readers of s_tok / s_seq / s_item are done
+    u = un;
+    wd = wdn;
+    tk[0] = tkn[0];
+    tk[1] = tkn[1];
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_tiles: one tile (t0, g) per item. The chain's chunks stream through the
+// k_tiles: one tile per item. The classifier wrote each item's descriptor
+// and chunk table (write_tile_desc). The chain's chunks stream through the
 // ring; then the residual partials of each row are merged and O / LSE are
-// written. Workgroup 0 also clears the counter set of the next call.
+// written. The next item's descriptor and table are loaded while the current
+// item's chunks are multiplied, and its Q and (16-bit caches) its first
+// three chunks are in flight while the current item's merge runs. Workgroup
+// 0 also clears the counter set of the next call.
 // ---------------------------------------------------------------------------
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
   __shared__ u32x4 s_ring[kRing * kSlotU4];
-  __shared__ int64_t s_koff[4 * 64];
-  __shared__ int s_key0[4 * 64];
+  __shared__ int4 s_ctab[4 * 64];  // the current item's chunk table
   __shared__ int s_item;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   if (blockIdx.x == 0 && p.counters_next)
     for (int i = tid; i < kCntSlots; i += 256) p.counters_next[i] = 0;
-  const int G = p.G, Hkv = p.Hkv, K = p.K;
+  const int G = p.G, Hkv = p.Hkv, K = p.K, K4 = 4 * p.K;
   const int Teff = p.T > 0 ? p.T : 1;
   // decode mode: the listed tiles; otherwise every tile, enumerated as
   // (KV head, tile number) so that an XCD's range holds neighbouring tiles
@@ -575,104 +601,124 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
   dl.init();
   XcdQueue wq;
   wq.init(total, p.counters + kCntXcd);
-  for (bool first = true;; first = false) {
-    if (tid == 0) s_item = wq.next(first);
-    __syncthreads();
-    const int id = s_item;
-    if (id < 0) break;
-    int t0, g, s;
-    if (listed) {
-      const int code = p.tile_items[id];
-      t0 = code / Hkv;
-      g = code - t0 * Hkv;
-      s = wave_seq_of(p.cu, p.B, t0);
+  auto load_item = [&](int i, int4& d0, int4& d1, int4& ce) {
+    d0 = p.tdesc[2 * (size_t)i];
+    d1 = p.tdesc[2 * (size_t)i + 1];
+    ce = tid < K4 ? p.ctab[(size_t)i * K4 + tid] : int4{-1, -1, 0, 0};
+  };
+  // chunk ci of the LDS table: element offset (-1: skip) and rows present
+  auto chunk_of = [&](int ci, int nck, int64_t& off, int& nrows) {
+    if (ci < nck) {
+      const int4 e = s_ctab[ci];
+      off = (int64_t)(((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x);
+      nrows = e.w;
     } else {
-      g = id / ntiles;
-      int64_t t0l;
-      s = wave_tile_of(p.cu, p.B, p.Tq, Teff, id - g * ntiles, &t0l);
-      t0 = (int)t0l;
+      off = -1;
+      nrows = 0;
     }
-    if (s < 0) {  // beyond the last tile
-      __syncthreads();
-      continue;
+  };
+  auto issue_first = [&](int nck) {  // the first three chunks of an item
+    asm volatile("" ::: "memory");     // older loads stay older than the ring loads
+#pragma unroll
+    for (int ci = 0; ci < kRing - 1; ++ci) {
+      int64_t off;
+      int nr;
+      chunk_of(ci, nck, off, nr);
+      issue_chunk16(p.k, p.v, off, nr, dl, s_ring + ci * kSlotU4, s_ring + ci * kSlotU4 + kChunkU4);
     }
-    const int code = t0 * Hkv + g;
-    const int64_t q0 = p.cu[s];
-    const int64_t q1 = min(p.cu[s + 1], (int64_t)p.Tq);
-    const int nt = (int)min((int64_t)Teff, q1 - t0);
+  };
+
+  if (tid == 0) s_item = wq.next(true);
+  __syncthreads();
+  const int id0 = s_item;
+  __syncthreads();  // s_item is rewritten inside the loop
+  if (id0 < 0) return;
+  int4 d0, d1, ce;
+  load_item(id0, d0, d1, ce);
+  if (tid < K4) s_ctab[tid] = ce;
+  const int rho = 32 * wave + c;  // the lane's row within the tile
+  Rows32 rt;
+  {
+    const int rows0 = d0.z * G;
+    load_q8(rt.qb, p, rho < rows0 ? d0.x + rho / G : -1, d1.z * G + rho % G, h);
+  }
+  bool ahead = false;  // the item's first chunks were issued by the previous iteration
+  for (;;) {
+    // the current item
+    const int t0 = d0.x, s = d0.y, nt = d0.z;
+    const int nck = nt > 0 ? 4 * d0.w : 0;
+    const int Leff = d1.x, base = d1.y, g = d1.z;
     const int rows = nt * G;
-    const int L = p.used[s];
-    const int Leff = min(L, p.MP * p.P);
-    const int base_pos = (int)(L - (p.cu[s + 1] - q0) - q0);  // pos = base_pos + token
-    const int pmin = p.causal ? base_pos + t0 : INT_MAX;
-    const int pmax = p.causal ? base_pos + t0 + nt - 1 : INT_MAX;
-    const int n_ch = p.tok_chain[code];
-    const int nck = 4 * n_ch;
-    // chunk table: element offset (-1: skip) and first key
-    for (int ci = tid; ci < nck; ci += 256) {
-      const int key0 = kBlk * p.chain_blk[(size_t)code * K + (ci >> 2)] + 32 * (ci & 3);
-      int64_t off = chunk_offset(p, s, g, key0, Leff);
-      if (key0 > pmax) off = -1;  // causally invisible to every row of the tile
-      s_koff[ci] = off;
-      s_key0[ci] = key0;
-    }
-    // the wave's rows
-    const int rho = 32 * wave + c;
     const bool valid = rho < rows;
     const int tau = valid ? rho / G : 0;
     const int hr = rho - tau * G;
     const int tok = t0 + tau;
     const int head = g * G + hr;
-    Rows32 rt;
+    const int pmin = p.causal ? base + t0 : INT_MAX;
+    const bool wave_has = 32 * wave < rows;
     rows_reset(rt);
     rt.seq = s;
-    rt.pos = (valid && p.causal) ? base_pos + tok : INT_MAX;
-    rows_load_q(rt, p, valid ? tok : -1, head, h);
-    const bool wave_has = 32 * wave < rows;
-    __syncthreads();  // chunk table visible
+    rt.pos = (valid && p.causal) ? base + tok : INT_MAX;
+    if (tid == 0) s_item = wq.next(false);
+    __syncthreads();  // s_ctab and s_item visible
+    const int nid = s_item;
+    int4 nd0 = {0, 0, 0, 0}, nd1 = {0, 0, 0, 0}, nce = {-1, -1, 0, 0};
+    if (nid >= 0) load_item(nid, nd0, nd1, nce);  // in flight during the chunk loop
 
     if (nck > 0) {
       if constexpr (kFp8) {
         // register-staged double buffer: chunk ci+1 loads while ci is multiplied
-        Raw8 raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, s_koff[0], Leff - s_key0[0], p.zero_page);
+        int64_t off;
+        int nr;
+        chunk_of(0, nck, off, nr);
+        Raw8 raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
         store_chunk8<CT>(raw, s_ring, s_ring + kChunkU4);
         __syncthreads();
         for (int ci = 0; ci < nck; ++ci) {
-          const int nxt = ci + 1 < nck ? ci + 1 : ci;
-          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, s_koff[nxt], Leff - s_key0[nxt], p.zero_page);
+          chunk_of(ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
+          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
           const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
-          const int64_t off = s_koff[ci];
-          if (wave_has && off >= 0) {
-            const int key0 = s_key0[ci];
-            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
-            rows_chunk<CT>(rt, sK, sK + kChunkU4, key0, Leff, s, !full, p.scale_log2);
+          const int4 e = s_ctab[ci];
+          if (wave_has && !(e.x == -1 && e.y == -1)) {
+            const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
+            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
           }
-          if (ci + 1 < nck) store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+          if (ci + 1 < nck)
+            store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
           __syncthreads();
         }
       } else {
-        asm volatile("" ::: "memory");  // the Q loads above are older than the ring loads
-#pragma unroll
-        for (int ci = 0; ci < kRing - 1; ++ci)
-          issue_chunk16(p.k, p.v, ci < nck ? s_koff[ci] : (int64_t)-1, ci < nck ? Leff - s_key0[ci] : 0, dl,
-                        s_ring + ci * kSlotU4, s_ring + ci * kSlotU4 + kChunkU4);
+        if (!ahead) issue_first(nck);
         for (int ci = 0; ci < nck; ++ci) {
           wait_vmcnt<8>();  // chunk ci has landed (two newer chunks may be in flight)
           ring_barrier();   // ... for every wave; and slot (ci + 3) % 4 is free
           const int nx = ci + kRing - 1;
           u32x4* sn = s_ring + (nx & (kRing - 1)) * kSlotU4;
-          issue_chunk16(p.k, p.v, nx < nck ? s_koff[nx] : (int64_t)-1, nx < nck ? Leff - s_key0[nx] : 0, dl, sn,
-                        sn + kChunkU4);
-          const int64_t off = s_koff[ci];
-          if (wave_has && off >= 0) {
-            const int key0 = s_key0[ci];
-            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
+          int64_t off;
+          int nr;
+          chunk_of(nx, nck, off, nr);
+          issue_chunk16(p.k, p.v, off, nr, dl, sn, sn + kChunkU4);
+          const int4 e = s_ctab[ci];
+          if (wave_has && !(e.x == -1 && e.y == -1)) {
+            const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
             const u32x4* sK = s_ring + (ci & (kRing - 1)) * kSlotU4;
-            rows_chunk<CT>(rt, sK, sK + kChunkU4, key0, Leff, s, !full, p.scale_log2);
+            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
           }
         }
-        wait_vmcnt<0>();  // the trailing (zero-page) loads are done before the ring is reused
       }
+    }
+
+    // the next item: its table replaces this one's; its Q and (16-bit
+    // caches) its first chunks are issued before this item's merge
+    ring_barrier();  // every wave is done with s_ctab and the ring
+    if (nid >= 0) {
+      if (tid < K4) s_ctab[tid] = nce;
+      const int nrows = nd0.z * G;
+      load_q8(rt.qb, p, rho < nrows ? nd0.x + rho / G : -1, nd1.z * G + rho % G, h);
+    }
+    ring_barrier();
+    if constexpr (!kFp8) {
+      if (nid >= 0) issue_first(nd0.z > 0 ? 4 * nd0.w : 0);
     }
 
     // merge with the unit partials of the row's residual slots, then write.
@@ -737,8 +783,12 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
       store_row16<CT>((uint16_t*)p.out + ((size_t)tok * p.Hq + head) * kD, rt, inv);
       if (h == 0 && p.lse) p.lse[(size_t)head * p.Tq + tok] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
     }
-    __syncthreads();  // the chunk table and ring are free for the next item
+    if (nid < 0) break;
+    d0 = nd0;
+    d1 = nd1;
+    ahead = !kFp8;
   }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
 // ---------------------------------------------------------------------------
