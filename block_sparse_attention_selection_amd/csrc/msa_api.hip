@@ -186,6 +186,7 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->ent = c.take<int32_t>(base, nslots);
   p->slot_pos = c.take<int32_t>(base, nslots);
   if (with_partials) {
+    p->scratch_row = c.take<char>(base, 1024);
     p->res_list = c.take<int32_t>(base, nslots);
     p->res_rank = c.take<uint8_t>(base, nslots);
     p->win_desc = c.take<int4>(base, nslots);
@@ -195,6 +196,7 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
     p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
+    p->scratch_row = nullptr;
     p->res_list = nullptr;
     p->res_rank = nullptr;
     p->win_desc = nullptr;

@@ -77,6 +77,7 @@ struct Params {
   int4* win_desc;      // attention: per unit-kernel window (row, first rank, first entry, entries)
   int4* tdesc;         // attention: per tile item, 2 x int4 (see write_tile_desc)
   int4* ctab;          // attention: per tile item, 4 topk chunk entries
+  void* scratch_row;  // 1 KB that stores of rows outside a tile or piece may land in
   // partial results of the KV-outer units
   void* opart;   // [residual slots, G, 128] normalised O, in q's 16-bit type
   float* lpart;  // [residual slots, G] LSE (log2 units)

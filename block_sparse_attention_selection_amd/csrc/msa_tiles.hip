@@ -521,10 +521,13 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
             for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
             __syncthreads();
           } else {
+            int64_t offs[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) offs[q] = chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              issue_chunk16(p.k, p.v, chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff),
-                            Leff - (kBlk * b + 32 * q), dl, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+              issue_chunk16(p.k, p.v, offs[q], Leff - (kBlk * b + 32 * q), dl, s_blk + q * kSlotU4,
+                            s_blk + q * kSlotU4 + kChunkU4);
             wait_vmcnt<0>();
             ring_barrier();
           }
@@ -545,16 +548,19 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
           }
         }
       }
-      // partial result of the piece's rows: normalised O and log2 LSE
+      // partial result of the piece's rows: normalised O and log2 LSE. Every
+      // lane stores (rows outside the piece into a scratch row), so that no
+      // branch separates these stores from the next piece's use of its Q and
+      // the compiler's wait for that Q need not include them.
       const float l_row = rows_total(rt);
-      if (valid) {
+      {
         const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-        store_row16<CT>((uint16_t*)p.opart + pidx * kD, rt, inv);
-        if (h == 0) {
-          const float mu = rt.m == -INFINITY ? 0.f : rt.m;
-          p.lpart[pidx] = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
-        }
+        uint16_t* orow = valid ? (uint16_t*)p.opart + pidx * kD : (uint16_t*)p.scratch_row;
+        float* lrow = (valid && h == 0) ? p.lpart + pidx : (float*)p.scratch_row + 64 + lane;
+        store_row16<CT>(orow, rt, inv);
+        const float mu = rt.m == -INFINITY ? 0.f : rt.m;
+        *lrow = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
       }
       if (a1 >= n) break;
       a0 = a1;
@@ -722,66 +728,89 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
     }
 
     // merge with the unit partials of the row's residual slots, then write.
-    // The partials' positions are listed per (token, KV head); partial i+1
-    // is loaded while partial i is merged. The reference max M moves only
-    // when a partial's LSE exceeds it by more than 2^kRescale32.
+    // The partials' positions are listed per (token, KV head). Two partials
+    // are in flight while one is merged, and each position is loaded two
+    // partials before its data, so every load waits on one round trip at
+    // most. The reference max M moves only when a partial's LSE exceeds it by
+    // more than 2^kRescale32.
+    // Every lane runs the same number of iterations and stores (rows outside
+    // the tile into a scratch row): with no branch around loads or stores,
+    // the compiler's waits count exactly the loads they need.
     const float l_tot = rows_total(rt);
-    if (valid) {
-      const size_t tg = (size_t)tok * Hkv + g;
-      const int nres = min(p.tok_nres[tg], K);
+    {
+      const size_t tg = valid ? (size_t)tok * Hkv + g : 0;
+      const int nres = valid ? min(p.tok_nres[tg], K) : 0;
+      int nres_w = nres;  // the wave's largest count
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) nres_w = max(nres_w, __shfl_xor(nres_w, off, 64));
       const int ntot = p.counters[kCntResidual];  // positions are below this
       const int32_t* rl = p.res_list + tg * K;
       float M = rt.m;  // O and W are relative to 2^M
       float W = l_tot;
       const uint16_t* obase = (const uint16_t*)p.opart + 4 * h;
-      auto fetch = [&](int i, float& li, u32x2 (&d)[16]) {
-        const int pos = i < nres ? rl[i] : -1;
+      struct Part {
+        float l;
+        u32x2 d[16];
+      };
+      auto pos_of = [&](int i) {  // an unconditional load: no branch around it
+        const int v = rl[min(i, K - 1)];
+        return i < nres ? v : -1;
+      };
+      auto fetch = [&](int pos, Part& pt) {
         const bool ok = pos >= 0 && pos < ntot;
         const size_t pidx = ok ? (size_t)pos * G + hr : 0;
-        li = ok ? p.lpart[pidx] : -INFINITY;
+        const float lv = p.lpart[pidx];
+        pt.l = ok ? lv : -INFINITY;
         const uint16_t* src = obase + pidx * kD;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) d[4 * t + a] = *(const u32x2*)(src + 32 * t + 8 * a);
+          for (int a = 0; a < 4; ++a) pt.d[4 * t + a] = *(const u32x2*)(src + 32 * t + 8 * a);
       };
-      if (nres > 0) {
-        float lc;
-        u32x2 dc[16];
-        fetch(0, lc, dc);
-        for (int i = 0; i < nres; ++i) {
-          float ln;
-          u32x2 dn[16];
-          fetch(i + 1, ln, dn);  // in flight while partial i is merged
-          if (lc != -INFINITY) {
-            if (M == -INFINITY || lc > M + kRescale32) {
-              const float sc = M == -INFINITY ? 0.f : exp2f(M - lc);
-              W *= sc;
+      auto merge = [&](const Part& pt) {
+        const float lc = pt.l;
+        const bool use = lc != -INFINITY;
+        const bool lift = use && (M == -INFINITY || lc > M + kRescale32);
+        const float m_new = lift ? lc : M;
+        const float sc = (lift && M != -INFINITY) ? exp2f(M - lc) : (lift ? 0.f : 1.f);
+        if (__any(lift)) {
+          W *= sc;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) rt.o[t] *= sc;
-              M = lc;
-            }
-            const float fi = exp2f(lc - M);
-            W += fi;
+          for (int t = 0; t < 4; ++t) rt.o[t] *= sc;
+        }
+        M = m_new;
+        const float fi = use ? exp2f(lc - M) : 0.f;
+        W += fi;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-              for (int a = 0; a < 4; ++a) {
-                const u32x2 w = dc[4 * t + a];
-                rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
-                rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
-                rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
-                rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
-              }
+          for (int a = 0; a < 4; ++a) {
+            const u32x2 w = pt.d[4 * t + a];
+            rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
+            rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
+            rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
+            rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
           }
-          lc = ln;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) dc[j] = dn[j];
+      };
+      if (nres_w > 0) {
+        Part pa, pb;
+        fetch(pos_of(0), pa);
+        fetch(pos_of(1), pb);
+        int qa = pos_of(2), qb = pos_of(3);
+        for (int i = 0; i < nres_w; i += 2) {
+          merge(pa);
+          fetch(qa, pa);
+          qa = pos_of(i + 4);
+          merge(pb);
+          fetch(qb, pb);
+          qb = pos_of(i + 5);
         }
       }
       const float inv = W > 0.f ? 1.f / W : 0.f;
-      store_row16<CT>((uint16_t*)p.out + ((size_t)tok * p.Hq + head) * kD, rt, inv);
-      if (h == 0 && p.lse) p.lse[(size_t)head * p.Tq + tok] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
+      uint16_t* orow = valid ? (uint16_t*)p.out + ((size_t)tok * p.Hq + head) * kD : (uint16_t*)p.scratch_row;
+      store_row16<CT>(orow, rt, inv);
+      float* lrow = (valid && h == 0 && p.lse) ? p.lse + (size_t)head * p.Tq + tok : (float*)p.scratch_row + 64 + lane;
+      *lrow = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
     }
     if (nid < 0) break;
     d0 = nd0;
