@@ -93,6 +93,43 @@ def accounting(wl):
     return dict(unique_kv_bytes=unique_kv, effective_flops=flops, qo_bytes=qo)
 
 
+def kernel_sources_sha256():
+    """Digest of the HIP sources of the library (any change voids recorded counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_selection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernels):
+    """HBM bytes per launch of `kernels` from the recorded counter runs, or None.
+
+    profiles/traffic_<workload>.txt holds a JSON object written from two
+    rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, per
+    kernel) and the same counters for a plain 1 GiB copy (bench.py
+    --calibrate-copy), which give the KiB-to-bytes factors. The figure is
+    reported only while the kernel sources are the ones it was taken on.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        ff, fw = rec["fetch_factor"], rec["write_factor"]
+        return int(sum(rec["kernels"][k]["fetch_kib"] * ff + rec["kernels"][k]["write_kib"] * fw
+                       for k in kernels))
+    except (KeyError, TypeError):
+        return None
+
+
 def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
 
@@ -140,6 +177,9 @@ def main():
     ap.add_argument("--workload", default="decode_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=None, help="oracle sample size in (token, kv-head) pairs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference kernel for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and print its size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -155,9 +195,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    msa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
+    msa.load()
     seed0 = W.CONFIGS[args.workload]["seed"]
 
     batches = []
@@ -231,6 +280,7 @@ def main():
         achieved = flops / (k_avg_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+    roof["traffic"] = measured_traffic(args.workload, dom)
     roof["kernel"] = "+".join(dom)
     roof["kernel_avg_us"] = round(k_avg_ms * 1e3, 2)
     roof["per_kernel_avg_us"] = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in per_kernel.items()}

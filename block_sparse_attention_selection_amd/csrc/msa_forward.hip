@@ -349,7 +349,11 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     // sequence, so their loads are issued before the search
     t = blockIdx.x;
     if (tid < K) b_raw = p.selected[((size_t)t * Hkv + g) * K + tid];
-    s = wave_seq_of(p.cu, p.B, t);
+    // a batch of one-token sequences has token t in sequence t: try that
+    // first (one round of loads, issued with the picks), search otherwise
+    const int sg = min(t, p.B - 1);
+    const bool hit = p.B > 0 && p.cu[sg] <= t && t < p.cu[sg + 1];
+    s = hit ? sg : wave_seq_of(p.cu, p.B, t);
     if (s < 0) {  // outside every sequence: no keys
       const size_t tg = (size_t)t * Hkv + g;
       if (tid < K) p.slot_flag[tg * K + tid] = 0;
@@ -391,7 +395,14 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
 
   // pages of the leader's picks, looked up while the sequence length loads
   int my_page = -1;
-  if (stream && tid < K * ppb) {
+  if (stream && K * ppb <= 64) {
+    // picks are already in lanes 0..K-1 of wave 0 (b_raw)
+    const int k = lane / ppb, j = lane - (lane / ppb) * ppb;
+    const int b = __shfl(b_raw, k, 64);
+    const int lp = b * ppb + j;
+    if (wave == 0 && lane < K * ppb && b >= 0 && b < p.nb_max && lp < p.MP)
+      my_page = p.block_tables[(size_t)s * p.MP + lp];
+  } else if (stream && tid < K * ppb) {
     const int k = tid / ppb, j = tid - (tid / ppb) * ppb;
     const int b = p.selected[tg * K + k];
     const int lp = b * ppb + j;
