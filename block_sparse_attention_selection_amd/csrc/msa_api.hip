@@ -144,8 +144,11 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
   d->nb_max = (int)std::max<int64_t>(nb_max, 1);
   d->NR = d->nb_max * d->Hkv;
   d->W = (int)((Tq + 31) / 32);
-  d->T = std::max(1, 128 / d->G);
-  d->Tu = std::min(8 * d->T, msa::kUnitWindowTokens);  // a unit kernel work item: up to 8 tiles' worth
+  // tiles of up to 256 query rows (the tile kernel's 8 waves x 32 rows), at
+  // most 128 tokens; unit kernel pieces of up to 128 rows, windows of up to
+  // 8 pieces' worth of tokens
+  d->T = std::min(128, std::max(1, 256 / d->G));
+  d->Tu = std::min(8 * std::max(1, 128 / d->G), msa::kUnitWindowTokens);
   d->q_elem = elem_of(q->dtype);
   d->kv_elem = elem_of(k->dtype);
   return MSA_OK;

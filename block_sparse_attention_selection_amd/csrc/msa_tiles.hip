@@ -130,24 +130,32 @@ __device__ __forceinline__ void rows_load_q(Rows32& rt, const Params& p, int tok
   for (int s = 0; s < 8; ++s) rt.qb[s] = *(const u32x4*)(base + 16 * s);
 }
 
-// One 32-key chunk staged in LDS (sK: K tile, sV: V tile): scores, online
-// softmax (lazy rescale), P V. Keys at or beyond lim, keys after a row's
-// causal position and rows of another sequence are removed by select when
-// `mask` is set; the caller clears it only for chunks fully visible to every
-// row. (One instantiation for both cases keeps the register allocation
-// within 256 VGPRs.)
+// The three stages of one 32-key chunk staged in LDS (sK: K tile, sV: V
+// tile). rows_scores: S^T = K Q^T. rows_probs: online-softmax step (lazy
+// rescale) giving the P^T B fragments; keys at or beyond lim, keys after a
+// row's causal position and rows of another sequence are removed by select
+// when `mask` is set (the caller clears it only for chunks fully visible to
+// every row). It moves a row's reference max only when the chunk's max
+// exceeds it by more than 2^kRescale32 and returns the factor the
+// accumulators must be scaled by (1 when it did not move); the row sum is
+// already scaled. rows_pv: O^T += V^T P^T.
 template <typename CT>
-__device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u32x4* sV, int key0, int lim,
-                                           int run_seq, bool mask, float sl2) {
+__device__ __forceinline__ f32x16 rows_scores(const Rows32& rt, const u32x4* sK) {
   const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
   f32x16 sa;
 #pragma unroll
   for (int j = 0; j < 16; ++j) sa[j] = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) sa = Mma32<CT>::run(sK[pieceK(c, 2 * s + h)], rt.qb[s], sa);
+  return sa;
+}
 
+template <typename CT>
+__device__ __forceinline__ float rows_probs(Rows32& rt, f32x16 sa, int key0, int lim, int run_seq, bool mask,
+                                            float sl2, u32x4 (&pb)[2]) {
   if (mask) {
     // key (key0 + 4h + the element's offset) is visible iff it is <= bound
+    const int h = (threadIdx.x & 63) >> 5;
     const int bound = rt.seq == run_seq ? min(rt.pos, lim - 1) : -1;
     const int rel = bound - key0 - 4 * h;
 #pragma unroll
@@ -157,30 +165,43 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
   float cmax = sa[0];
 #pragma unroll
   for (int j = 1; j < 16; ++j) cmax = fmaxf(cmax, sa[j]);
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64)) * sl2;
-  if (__any(cmax > rt.m + kRescale32)) {
-    const float m_new = fmaxf(rt.m, cmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(rt.m - m_new);
-    rt.l *= alpha;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) rt.o[t] *= alpha;
-    rt.m = m_new;
+  {
+    // with the other half-wave's value (lane l ^ 32): the swap leaves one of
+    // the two in each output, so their max is the pair's max in every lane
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cmax), __float_as_uint(cmax), false, false);
+    cmax = __builtin_amdgcn_fmed3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), INFINITY) * sl2;
   }
-  const float nmu = (rt.m == -INFINITY) ? 0.f : -rt.m;
-  u32x4 pb[2];
+  const float m_new = cmax > rt.m + kRescale32 ? cmax : rt.m;
+  const float alpha = m_new == rt.m ? 1.f : exp2f(rt.m - m_new);  // 0 when the old max was -inf
+  rt.m = m_new;
+  const float nmu = (m_new == -INFINITY) ? 0.f : -m_new;
+  float ls = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * i], sl2, nmu));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * i + 1], sl2, nmu));
     pb[i >> 2][i & 3] = pack2<CT>(p0, p1);
-    rt.l += p0 + p1;  // fp32 sum of the unrounded probabilities (the LSE needs it)
+    ls += p0 + p1;  // fp32 sum of the unrounded probabilities (the LSE needs it)
   }
+  rt.l = __builtin_fmaf(rt.l, alpha, ls);
+  return alpha;
+}
 
-  // V^T fragments by transposing reads: lane (h, c) receives V[key][32t + c]
-  // for the four keys 16s' + 8r + 4h + i (i = 0..3); its source lanes read 8
-  // bytes each at row 16s' + 8r + 4h + i (i = (l >> 2) & 3), logical piece
-  // 4t + 2((l >> 4) & 1) + ((l & 3) >> 1), half l & 1. With the V swizzle the
-  // physical piece is 4(t ^ i) + the low two bits.
+__device__ __forceinline__ void rows_rescale(Rows32& rt, float alpha) {
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rt.o[t] *= alpha;
+  }
+}
+
+// V^T fragments by transposing reads: lane (h, c) receives V[key][32t + c]
+// for the four keys 16s' + 8r + 4h + i (i = 0..3); its source lanes read 8
+// bytes each at row 16s' + 8r + 4h + i (i = (l >> 2) & 3), logical piece
+// 4t + 2((l >> 4) & 1) + ((l & 3) >> 1), half l & 1. With the V swizzle the
+// physical piece is 4(t ^ i) + the low two bits.
+template <typename CT>
+__device__ __forceinline__ void rows_pv(Rows32& rt, const u32x4 (&pb)[2], const u32x4* sV) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
   const int i4 = (lane >> 2) & 3;
   const int rsub = 4 * h + i4;                                 // 0..7
   const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // 0..3
@@ -203,6 +224,109 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
       rt.o[t] = Mma32<CT>::run(a, pb[sp], rt.o[t]);
     }
   }
+}
+
+// One chunk, the three stages in order.
+template <typename CT>
+__device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u32x4* sV, int key0, int lim,
+                                           int run_seq, bool mask, float sl2) {
+  const f32x16 sa = rows_scores<CT>(rt, sK);
+  u32x4 pb[2];
+  rows_rescale(rt, rows_probs<CT>(rt, sa, key0, lim, run_seq, mask, sl2, pb));
+  rows_pv<CT>(rt, pb, sV);
+}
+
+// One iteration of the tile kernel's chunk pipeline, scheduled by hand:
+// O^T += V(prev)^T P(prev)^T, sn = S of the next chunk, and the softmax step
+// of sc (this chunk's scores) giving pn. The work is cut into eight stages,
+// each one P V product, one Q K product, the LDS reads of the products two
+// stages later and a slice of the vector work; sched_barrier keeps the
+// compiler from regrouping them, so the vector ALU runs while the matrix
+// core is busy and every LDS read has two stages to land. Returns the
+// accumulator rescale factor (see rows_probs).
+template <typename CT, bool kMask>
+__device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u32x4 (&pp)[2], const char* vprev,
+                                           const u32x4* knext, int key0, int lim, float sl2, f32x16& sn,
+                                           u32x4 (&pn)[2]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+  const int i4 = (lane >> 2) & 3;
+  const int rsub = 4 * h + i4;
+  const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int half = 8 * (lane & 1);
+  auto vfrag = [&](int t, int sp) {
+    u32x4 a;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 16 * sp + 8 * r + rsub;
+      const int off = row * 256 + ((4 * (t ^ i4) + psub) << 4) + half;
+      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vprev + off)));
+      a[2 * r] = w[0];
+      a[2 * r + 1] = w[1];
+    }
+    return a;
+  };
+  auto kfrag = [&](int st) { return knext[pieceK(c, 2 * st + h)]; };
+
+  f32x16 sa = sc;
+  u32x4 va[8], ka[8];
+  va[0] = vfrag(0, 0);
+  ka[0] = kfrag(0);
+  va[1] = vfrag(1, 0);
+  ka[1] = kfrag(1);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sn[j] = 0.f;
+  float cmax = 0.f, alpha = 1.f, nmu = 0.f, ls = 0.f;
+  int rel = 0;
+  if (kMask) {
+    const int bound = min(rt.pos, lim - 1);
+    rel = bound - key0 - 4 * h;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 2 < 8) {
+      va[i + 2] = vfrag((i + 2) & 3, (i + 2) >> 2);
+      ka[i + 2] = kfrag(i + 2);
+    }
+    rt.o[i & 3] = Mma32<CT>::run(va[i], pp[i >> 2], rt.o[i & 3]);
+    sn = Mma32<CT>::run(ka[i], rt.qb[i], sn);
+    if (i == 0) {
+      // masking, then the row max of the raw scores (sl2 > 0 commutes with max)
+      if (kMask) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sa[j] = (8 * (j >> 2) + (j & 3)) <= rel ? sa[j] : -INFINITY;
+      }
+      cmax = sa[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sa[j]);
+    } else if (i == 1) {
+#pragma unroll
+      for (int j = 8; j < 16; ++j) cmax = fmaxf(cmax, sa[j]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cmax), __float_as_uint(cmax), false, false);
+      cmax = __builtin_amdgcn_fmed3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), INFINITY) * sl2;
+      const float m_new = cmax > rt.m + kRescale32 ? cmax : rt.m;
+      alpha = m_new == rt.m ? 1.f : exp2f(rt.m - m_new);
+      rt.m = m_new;
+      nmu = (m_new == -INFINITY) ? 0.f : -m_new;
+    } else {
+      // pairs of probabilities: stage 2 takes pairs 0-1, stage 3 pair 2, ...
+      const int q0 = i == 2 ? 0 : (i == 3 ? 2 : (i == 4 ? 3 : (i == 5 ? 4 : (i == 6 ? 6 : 7))));
+      const int q1 = i == 2 ? 2 : (i == 3 ? 3 : (i == 4 ? 4 : (i == 5 ? 6 : (i == 6 ? 7 : 8))));
+#pragma unroll
+      for (int q = q0; q < q1; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q], sl2, nmu));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q + 1], sl2, nmu));
+        pn[q >> 2][q & 3] = pack2<CT>(p0, p1);
+        ls += p0 + p1;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // used here, so that the vector work is not sunk past the caller's
+  // rarely taken rescale branch
+  asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(ls));
+  rt.l = __builtin_fmaf(rt.l, alpha, ls);
+  return alpha;
 }
 
 // Final row state: total sum over the lane pair, reference max, log2 LSE.
@@ -252,6 +376,7 @@ struct DmaLane {
   }
 };
 
+// off and nrows must be the same in every lane of the wave
 // wave-uniform value, held in a scalar register
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
@@ -259,7 +384,55 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// off and nrows must be the same in every lane of the wave
+// The tile kernel's 512 threads: one K piece and one V piece each per chunk.
+struct DmaLane512 {
+  int k0, v0;
+  __device__ __forceinline__ void init() {
+    const int pc = threadIdx.x;  // 0..511
+    const int r = pc >> 4, f = pc & 15;
+    k0 = r * 256 + ((f ^ (r & 15)) << 4);
+    v0 = r * 256 + ((f ^ ((r & 3) << 2)) << 4);
+  }
+};
+
+// One 16-byte direct-to-LDS buffer load per lane: lane i's bytes land at LDS
+// byte address lds + 16 i. Issued from inline assembly so that the compiler
+// does not treat every later LDS read as a possible reader of the load (it
+// would wait for all loads in flight before the first one): the ring's
+// protocol orders these loads with wait_vmcnt and barriers instead.
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t lds, int voff) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// raw buffer descriptor of nrec bytes at base (stride 0)
+__device__ __forceinline__ i32x4v make_rsrc(const void* base, int nrec) {
+  const uint64_t b = (uint64_t)base;
+  i32x4v r;
+  r.x = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
+  r.z = (int)__builtin_amdgcn_readfirstlane((uint32_t)nrec);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
+// chunk into the ring slot at LDS byte address slot (K tile, then V tile)
+__device__ __forceinline__ void issue_chunk16_512(const void* kb, const void* vb, int64_t off_any, int nrows_any,
+                                                  const DmaLane512& dl, uint32_t slot) {
+  const int wave = threadIdx.x >> 6;
+  const int64_t off = uniform64(off_any);
+  const int nrows = __builtin_amdgcn_readfirstlane(nrows_any);
+  const bool present = off >= 0 && nrows > 0;
+  const int64_t ob = present ? off * 2 : 0;
+  const int nrec = present ? min(nrows, 32) * 256 : 0;
+  dma16(make_rsrc((const char*)kb + ob, nrec), slot + 1024 * wave, dl.k0);
+  dma16(make_rsrc((const char*)vb + ob, nrec), slot + 16 * kChunkU4 + 1024 * wave, dl.v0);
+}
+
 __device__ __forceinline__ void issue_chunk16(const void* kb, const void* vb, int64_t off_any, int nrows_any,
                                               const DmaLane& dl, u32x4* sK, u32x4* sV) {
   const int wave = threadIdx.x >> 6;
@@ -585,15 +758,19 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
 // three chunks are in flight while the current item's merge runs. Workgroup
 // 0 also clears the counter set of the next call.
 // ---------------------------------------------------------------------------
+constexpr int kTileThreads = 512;  // 8 waves: 256 query rows per tile
+constexpr int kRingT = 8;          // ring slots of the tile kernel (seven chunks ahead)
+
 template <typename CT, typename KVT>
-__global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
+__global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
-  __shared__ u32x4 s_ring[kRing * kSlotU4];
+  __shared__ u32x4 s_ring[kRingT * kSlotU4];
   __shared__ int4 s_ctab[4 * 64];  // the current item's chunk table
+  __shared__ int s_cnt[2 * (kTileThreads / 64)];
   __shared__ int s_item;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   if (blockIdx.x == 0 && p.counters_next)
-    for (int i = tid; i < kCntSlots; i += 256) p.counters_next[i] = 0;
+    for (int i = tid; i < kCntSlots; i += kTileThreads) p.counters_next[i] = 0;
   const int G = p.G, Hkv = p.Hkv, K = p.K, K4 = 4 * p.K;
   const int Teff = p.T > 0 ? p.T : 1;
   // decode mode: the listed tiles; otherwise every tile, enumerated as
@@ -603,8 +780,9 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
   const int ntiles = (p.Tq + Teff - 1) / Teff + p.B;  // bound on the tile count
   const int total = listed ? p.counters[kCntTiles] : ntiles * Hkv;
   if (total == 0) return;
-  DmaLane dl;
+  DmaLane512 dl;
   dl.init();
+  const uint32_t ring0 = lds_addr(s_ring);
   XcdQueue wq;
   wq.init(total, p.counters + kCntXcd);
   auto load_item = [&](int i, int4& d0, int4& d1, int4& ce) {
@@ -623,15 +801,44 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
       nrows = 0;
     }
   };
-  auto issue_first = [&](int nck) {  // the first three chunks of an item
+  auto issue_first = [&](int nck) {  // the first kRingT - 2 chunks of an item
     asm volatile("" ::: "memory");     // older loads stay older than the ring loads
 #pragma unroll
-    for (int ci = 0; ci < kRing - 1; ++ci) {
+    for (int ci = 0; ci < kRingT - 2; ++ci) {
       int64_t off;
       int nr;
       chunk_of(ci, nck, off, nr);
-      issue_chunk16(p.k, p.v, off, nr, dl, s_ring + ci * kSlotU4, s_ring + ci * kSlotU4 + kChunkU4);
+      issue_chunk16_512(p.k, p.v, off, nr, dl, ring0 + 16 * kSlotU4 * ci);
     }
+  };
+
+  // An item's chunk table into LDS, the chunks fully visible to every row of
+  // the tile first (table order within each class), so that the chunk loop
+  // runs unmasked up to the returned count. Two barriers; the caller makes
+  // the table visible with a third.
+  auto put_table = [&](int4 e, int4 i0, int4 i1) {
+    const int n = i0.z > 0 ? 4 * i0.w : 0;
+    const int Lv = i1.x, pmn = p.causal ? i1.y + i0.x : INT_MAX;
+    const bool in = tid < n;
+    const bool full = in && e.z + 31 < Lv && e.z + 31 <= pmn;
+    const uint64_t bf = __ballot(full), bp = __ballot(in && !full);
+    if (lane == 0) {
+      s_cnt[wave] = __popcll(bf);
+      s_cnt[kTileThreads / 64 + wave] = __popcll(bp);
+    }
+    ring_barrier();
+    int nf = 0, fb = 0, pbf = 0;
+#pragma unroll
+    for (int w = 0; w < kTileThreads / 64; ++w) {
+      const int cf = s_cnt[w], cp = s_cnt[kTileThreads / 64 + w];
+      nf += cf;
+      fb += w < wave ? cf : 0;
+      pbf += w < wave ? cp : 0;
+    }
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int at = full ? fb + __popcll(bf & lt) : nf + pbf + __popcll(bp & lt);
+    if (in) s_ctab[at] = e;
+    return nf;
   };
 
   if (tid == 0) s_item = wq.next(true);
@@ -641,7 +848,7 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
   if (id0 < 0) return;
   int4 d0, d1, ce;
   load_item(id0, d0, d1, ce);
-  if (tid < K4) s_ctab[tid] = ce;
+  int nfull = put_table(ce, d0, d1);
   const int rho = 32 * wave + c;  // the lane's row within the tile
   Rows32 rt;
   {
@@ -666,7 +873,7 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
     rt.seq = s;
     rt.pos = (valid && p.causal) ? base + tok : INT_MAX;
     if (tid == 0) s_item = wq.next(false);
-    __syncthreads();  // s_ctab and s_item visible
+    ring_barrier();  // s_ctab and s_item visible (LDS only: ring loads stay in flight)
     const int nid = s_item;
     int4 nd0 = {0, 0, 0, 0}, nd1 = {0, 0, 0, 0}, nce = {-1, -1, 0, 0};
     if (nid >= 0) load_item(nid, nd0, nd1, nce);  // in flight during the chunk loop
@@ -676,41 +883,63 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
         // register-staged double buffer: chunk ci+1 loads while ci is multiplied
         int64_t off;
         int nr;
+        const bool stager = tid < 256;  // 32 rows x 8 pieces of K and of V
         chunk_of(0, nck, off, nr);
-        Raw8 raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
-        store_chunk8<CT>(raw, s_ring, s_ring + kChunkU4);
+        Raw8 raw{};
+        if (stager) {
+          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
+          store_chunk8<CT>(raw, s_ring, s_ring + kChunkU4);
+        }
         __syncthreads();
         for (int ci = 0; ci < nck; ++ci) {
           chunk_of(ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
-          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
+          if (stager) raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
           const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
           const int4 e = s_ctab[ci];
           if (wave_has && !(e.x == -1 && e.y == -1)) {
             const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
             rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
           }
-          if (ci + 1 < nck)
+          if (stager && ci + 1 < nck)
             store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
           __syncthreads();
         }
       } else {
+        // software pipeline over the chunks: iteration ci multiplies V(ci-1)
+        // by P(ci-1), computes the scores S(ci+1) and the probabilities of
+        // S(ci); the three are independent, so the matrix cores and the
+        // vector ALU overlap within the wave. Iteration ci reads chunks
+        // ci-1 and ci+1, so once every wave has passed its barrier the slot
+        // of chunk ci-2 takes chunk ci + kRingT - 2.
         if (!ahead) issue_first(nck);
-        for (int ci = 0; ci < nck; ++ci) {
-          wait_vmcnt<8>();  // chunk ci has landed (two newer chunks may be in flight)
-          ring_barrier();   // ... for every wave; and slot (ci + 3) % 4 is free
-          const int nx = ci + kRing - 1;
-          u32x4* sn = s_ring + (nx & (kRing - 1)) * kSlotU4;
+        wait_vmcnt<2 * (kRingT - 3)>();  // chunk 0 has landed
+        ring_barrier();
+        f32x16 sc = rows_scores<CT>(rt, s_ring);
+        u32x4 pp[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};  // P of chunk -1 (nothing)
+        auto step = [&](int ci, bool mask) {
+          wait_vmcnt<2 * (kRingT - 4)>();  // chunk ci+1 has landed
+          ring_barrier();                  // ... for every wave; and slot (ci - 2) % kRingT is free
+          const int nx = ci + kRingT - 2;
           int64_t off;
           int nr;
           chunk_of(nx, nck, off, nr);
-          issue_chunk16(p.k, p.v, off, nr, dl, sn, sn + kChunkU4);
-          const int4 e = s_ctab[ci];
-          if (wave_has && !(e.x == -1 && e.y == -1)) {
-            const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
-            const u32x4* sK = s_ring + (ci & (kRing - 1)) * kSlotU4;
-            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
-          }
-        }
+          issue_chunk16_512(p.k, p.v, off, nr, dl, ring0 + 16 * kSlotU4 * (nx & (kRingT - 1)));
+          const int key0 = s_ctab[ci].z;
+          const char* vprev = (const char*)(s_ring + ((ci > 0 ? ci - 1 : 0) & (kRingT - 1)) * kSlotU4 + kChunkU4);
+          const u32x4* knext = s_ring + ((ci + 1 < nck ? ci + 1 : ci) & (kRingT - 1)) * kSlotU4;
+          f32x16 sn;
+          u32x4 pn[2];
+          const float alpha = mask ? tile_iter<CT, true>(rt, sc, pp, vprev, knext, key0, Leff, p.scale_log2, sn, pn)
+                                   : tile_iter<CT, false>(rt, sc, pp, vprev, knext, key0, Leff, p.scale_log2, sn, pn);
+          rows_rescale(rt, alpha);
+          sc = sn;
+          pp[0] = pn[0];
+          pp[1] = pn[1];
+        };
+        int ci = 0;
+        for (; ci < nfull; ++ci) step(ci, false);
+        for (; ci < nck; ++ci) step(ci, true);
+        rows_pv<CT>(rt, pp, s_ring + ((nck - 1) & (kRingT - 1)) * kSlotU4 + kChunkU4);
       }
     }
 
@@ -718,9 +947,9 @@ __global__ __launch_bounds__(256, 2) void k_tiles(Params p) {
     // caches) its first chunks are issued before this item's merge
     ring_barrier();  // every wave is done with s_ctab and the ring
     if (nid >= 0) {
-      if (tid < K4) s_ctab[tid] = nce;
       const int nrows = nd0.z * G;
       load_q8(rt.qb, p, rho < nrows ? nd0.x + rho / G : -1, nd1.z * G + rho % G, h);
+      nfull = put_table(nce, nd0, nd1);
     }
     ring_barrier();
     if constexpr (!kFp8) {
@@ -831,7 +1060,7 @@ static hipError_t launch_units_t(const Params& p, int num_cu, hipStream_t st) {
 
 template <typename CT, typename KVT>
 static hipError_t launch_tiles_t(const Params& p, int num_cu, hipStream_t st) {
-  hipLaunchKernelGGL((k_tiles<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((k_tiles<CT, KVT>), dim3(num_cu), dim3(kTileThreads), 0, st, p);
   return hipGetLastError();
 }
 
