@@ -513,8 +513,8 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     }
   }
   __syncthreads();
-  if (p.tdesc && s_item_idx >= 0)
-    write_tile_desc(p, s_item_idx, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain, tid, 256);
+  if (p.tdesc && s_item_idx >= 0 && tid < 64)
+    write_tile_desc(p, s_item_idx, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain, tid);
   if constexpr (ATTN) {
     if (stream && s_tile_res == 0)
       stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   const int s = wave_tile_of(p.cu, p.B, p.Tq, Teff, j, &t0l);
   const int item = g * ntiles + j;  // the tile kernel's item (KV head, tile number)
   if (s < 0) {
-    if (p.tdesc && lane == 0) p.tdesc[2 * (size_t)item] = int4{0, 0, 0, 0};  // no tile: nothing to do
+    if (p.tdesc && lane < 2) p.tdesc[2 * (size_t)item + lane] = int4{0, 0, 0, 0};  // no tile: nothing to do
     return;
   }
   const int t = (int)t0l;
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     p.chain_blk[tg * K + rank] = bl;
   }
   wave_lds_sync();
-  if (p.tdesc) write_tile_desc(p, item, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain[wave], lane, 64);
+  if (p.tdesc) write_tile_desc(p, item, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain[wave], lane);
   // flags, residual bits, residual counts
   int res = 0;
   for (int idx = lane; idx < nt * K; idx += 64) {

@@ -120,24 +120,47 @@ __device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, i
 // Descriptor and chunk table of tile item `item` (tile leader t0 of sequence
 // s, nt tokens, KV head g, chain of n_ch blocks): tdesc[2 item] = (t0, s, nt,
 // n_ch), tdesc[2 item + 1] = (reachable keys Leff, base position: pos =
-// base + token, g), ctab[item * 4 topk + ci] = (element offset low, high, first
-// key, keys present) of chunk ci, offset -1 for a chunk no row can see.
-// Threads first, first + stride, ... share the chunks.
+// base + token, g, nfull), and the table ctab[item * 4 topk + ...] of
+// (element offset low, high, first key, keys present) per chunk, offset -1
+// for a chunk no row can see. The table lists first the nfull chunks every
+// row of the tile sees whole (all keys below Leff and at or before the first
+// row's position), then the others, each class in chain order, so that the
+// tile kernel runs its unmasked loop up to nfull. One wave calls this (lane
+// 0..63).
 __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t0, int s, int nt, int n_ch, int L,
-                                                int Tq_s, int64_t q0, int g, const int* chain, int first,
-                                                int stride) {
+                                                int Tq_s, int64_t q0, int g, const int* chain, int lane) {
   const int Leff = min(L, p.MP * p.P);
   const int base = (int)(L - Tq_s - q0);
   const int pmax = p.causal ? base + t0 + nt - 1 : INT_MAX;
+  const int pmin = p.causal ? base + t0 : INT_MAX;
   const size_t K4 = 4 * (size_t)p.K;
-  for (int ci = first; ci < 4 * n_ch; ci += stride) {
-    const int key0 = 128 * chain[ci >> 2] + 32 * (ci & 3);
-    const int64_t off = key0 > pmax ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
-    p.ctab[(size_t)item * K4 + ci] = int4{(int)(uint32_t)(uint64_t)off, (int)(off >> 32), key0, min(32, Leff - key0)};
+  const int n = 4 * n_ch;
+  auto key_of = [&](int ci) { return 128 * chain[ci >> 2] + 32 * (ci & 3); };
+  auto whole = [&](int ci) {
+    const int k0 = key_of(ci);
+    return k0 + 31 < Leff && k0 + 31 <= pmin;
+  };
+  int nfull = 0;
+  for (int b = 0; b < n; b += 64) nfull += __popcll(__ballot(b + lane < n && whole(b + lane)));
+  const uint64_t below = (1ull << lane) - 1ull;
+  int fb = 0, pb = 0;  // whole / other chunks of earlier batches
+  for (int b = 0; b < n; b += 64) {
+    const int ci = b + lane;
+    const bool in = ci < n;
+    const bool f = in && whole(ci);
+    const uint64_t bf = __ballot(f), bo = __ballot(in && !f);
+    if (in) {
+      const int at = f ? fb + __popcll(bf & below) : nfull + pb + __popcll(bo & below);
+      const int key0 = key_of(ci);
+      const int64_t off = key0 > pmax ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
+      p.ctab[(size_t)item * K4 + at] = int4{(int)(uint32_t)(uint64_t)off, (int)(off >> 32), key0, min(32, Leff - key0)};
+    }
+    fb += __popcll(bf);
+    pb += __popcll(bo);
   }
-  if (first == 0) {
+  if (lane == 0) {
     p.tdesc[2 * (size_t)item] = int4{t0, s, nt, n_ch};
-    p.tdesc[2 * (size_t)item + 1] = int4{Leff, base, g, 0};
+    p.tdesc[2 * (size_t)item + 1] = int4{Leff, base, g, nfull};
   }
 }
 

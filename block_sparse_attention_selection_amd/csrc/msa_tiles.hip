@@ -751,22 +751,55 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
 
 // ---------------------------------------------------------------------------
 // k_tiles: one tile per item. The classifier wrote each item's descriptor
-// and chunk table (write_tile_desc). The chain's chunks stream through the
-// ring; then the residual partials of each row are merged and O / LSE are
-// written. The next item's descriptor and table are loaded while the current
-// item's chunks are multiplied, and its Q and (16-bit caches) its first
-// three chunks are in flight while the current item's merge runs. Workgroup
-// 0 also clears the counter set of the next call.
+// and chunk table (write_tile_desc: the chunks fully visible to every row of
+// the tile first). The chain's chunks stream through a ring of LDS slots
+// that runs on from one item into the next: once the current item's chunks
+// are all issued, the next item's first chunks follow in the same slots, so
+// the next item starts with its data in place. Then the residual partials of
+// each row are merged and O / LSE are written.
+//
+// Everything an item needs besides Q and the partials reaches LDS by
+// direct-to-LDS loads issued early and ordered by the ring's own waits: the
+// next item's descriptor and chunk table and the current item's residual
+// counts and positions, at the start of the current item; the item after
+// next is requested from the work queue at the same time. No load the
+// compiler tracks is waited for inside the chunk loop, so the ring's loads
+// stay in flight across the item boundary. Workgroup 0 also clears the
+// counter set of the next call.
 // ---------------------------------------------------------------------------
 constexpr int kTileThreads = 512;  // 8 waves: 256 query rows per tile
-constexpr int kRingT = 8;          // ring slots of the tile kernel (seven chunks ahead)
+constexpr int kAhead = 6;           // chunks in flight ahead of the one being multiplied
+constexpr int kRingT = kAhead + 2;  // ring slots: chunks ci-1 .. ci+1 in use, kAhead - 1 more landing
+constexpr int kTabMax = 4 * 64;     // chunk table entries (top-k <= 64)
+constexpr int kPosMax = 4096;       // residual positions of one item held in LDS
+constexpr int kTokMax = 256;        // tokens of one tile
+
+// 4-byte direct-to-LDS buffer load per lane (lane i's bytes at lds + 4 i)
+__device__ __forceinline__ void dma4(i32x4v rsrc, uint32_t lds, int voff) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Returning atomic add whose result is waited for explicitly (wait_vmcnt,
+// then settle()): the compiler does not see it as a load in flight.
+__device__ __forceinline__ int atomic_add_nowait(int32_t* ptr, int val) {
+  int r;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(r) : "v"(ptr), "v"(val) : "memory");
+  return r;
+}
+__device__ __forceinline__ int settle(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
   __shared__ u32x4 s_ring[kRingT * kSlotU4];
-  __shared__ int4 s_ctab[4 * 64];  // the current item's chunk table
-  __shared__ int s_cnt[2 * (kTileThreads / 64)];
+  __shared__ int4 s_tab[2][kTabMax];  // chunk tables of the current and the next item
+  __shared__ int4 s_desc[2][2];       // their descriptors
+  __shared__ int s_pos[kPosMax];      // the current item's residual positions, [token][rank]
+  __shared__ int s_nres[kTokMax];     // and residual counts
   __shared__ int s_item;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   if (blockIdx.x == 0 && p.counters_next)
@@ -785,15 +818,35 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   const uint32_t ring0 = lds_addr(s_ring);
   XcdQueue wq;
   wq.init(total, p.counters + kCntXcd);
-  auto load_item = [&](int i, int4& d0, int4& d1, int4& ce) {
-    d0 = p.tdesc[2 * (size_t)i];
-    d1 = p.tdesc[2 * (size_t)i + 1];
-    ce = tid < K4 ? p.ctab[(size_t)i * K4 + tid] : int4{-1, -1, 0, 0};
+
+  // descriptor and chunk table of item i into buffer bf (direct-to-LDS:
+  // lane l of wave w < 4 brings table entry 64 w + l; wave 0 also the
+  // descriptor)
+  auto fetch_meta = [&](int i, int bf) {
+    if (wave < kTabMax / 64)
+      dma16(make_rsrc(p.ctab + (size_t)i * K4, K4 * 16), lds_addr(&s_tab[bf][64 * wave]), 16 * (64 * wave + lane));
+    if (wave == 0 && lane < 2) dma16(make_rsrc(p.tdesc + 2 * (size_t)i, 32), lds_addr(&s_desc[bf][0]), 16 * lane);
   };
-  // chunk ci of the LDS table: element offset (-1: skip) and rows present
-  auto chunk_of = [&](int ci, int nck, int64_t& off, int& nrows) {
-    if (ci < nck) {
-      const int4 e = s_ctab[ci];
+  // residual counts and positions of the item's tokens (nt tokens from t0,
+  // KV head g), the positions when they fit
+  auto fetch_res = [&](int t0, int nt, int g) {
+    const size_t tg0 = (size_t)t0 * Hkv + g;
+    if (wave * 64 < nt) {
+      const i32x4v rn = make_rsrc(p.tok_nres + tg0, ((nt - 1) * Hkv + 1) * 4);
+      dma4(rn, lds_addr(&s_nres[64 * wave]), 4 * (64 * wave + lane) * Hkv);
+    }
+    if (nt * K <= kPosMax) {
+      const i32x4v rp = make_rsrc(p.res_list + tg0 * K, ((nt - 1) * Hkv + 1) * K * 4);
+      for (int j = 64 * wave; j < nt * K; j += kTileThreads) {
+        const int e = j + lane, tau = e / K;
+        dma4(rp, lds_addr(&s_pos[j]), 4 * (tau * Hkv * K + (e - tau * K)));
+      }
+    }
+  };
+  // chunk ci of table bf (n chunks): element offset (-1: skip) and rows present
+  auto chunk_of = [&](int bf, int ci, int n, int64_t& off, int& nrows) {
+    if (ci < n) {
+      const int4 e = s_tab[bf][ci];
       off = (int64_t)(((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x);
       nrows = e.w;
     } else {
@@ -801,90 +854,62 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
       nrows = 0;
     }
   };
-  auto issue_first = [&](int nck) {  // the first kRingT - 2 chunks of an item
-    asm volatile("" ::: "memory");     // older loads stay older than the ring loads
-#pragma unroll
-    for (int ci = 0; ci < kRingT - 2; ++ci) {
-      int64_t off;
-      int nr;
-      chunk_of(ci, nck, off, nr);
-      issue_chunk16_512(p.k, p.v, off, nr, dl, ring0 + 16 * kSlotU4 * ci);
-    }
-  };
+  auto slot_addr = [&](int x) { return ring0 + 16 * kSlotU4 * (x & (kRingT - 1)); };
+  auto slot_ptr = [&](int x) { return s_ring + (x & (kRingT - 1)) * kSlotU4; };
 
-  // An item's chunk table into LDS, the chunks fully visible to every row of
-  // the tile first (table order within each class), so that the chunk loop
-  // runs unmasked up to the returned count. Two barriers; the caller makes
-  // the table visible with a third.
-  auto put_table = [&](int4 e, int4 i0, int4 i1) {
-    const int n = i0.z > 0 ? 4 * i0.w : 0;
-    const int Lv = i1.x, pmn = p.causal ? i1.y + i0.x : INT_MAX;
-    const bool in = tid < n;
-    const bool full = in && e.z + 31 < Lv && e.z + 31 <= pmn;
-    const uint64_t bf = __ballot(full), bp = __ballot(in && !full);
-    if (lane == 0) {
-      s_cnt[wave] = __popcll(bf);
-      s_cnt[kTileThreads / 64 + wave] = __popcll(bp);
-    }
-    ring_barrier();
-    int nf = 0, fb = 0, pbf = 0;
-#pragma unroll
-    for (int w = 0; w < kTileThreads / 64; ++w) {
-      const int cf = s_cnt[w], cp = s_cnt[kTileThreads / 64 + w];
-      nf += cf;
-      fb += w < wave ? cf : 0;
-      pbf += w < wave ? cp : 0;
-    }
-    const uint64_t lt = (1ull << lane) - 1ull;
-    const int at = full ? fb + __popcll(bf & lt) : nf + pbf + __popcll(bp & lt);
-    if (in) s_ctab[at] = e;
-    return nf;
-  };
-
-  if (tid == 0) s_item = wq.next(true);
-  __syncthreads();
-  const int id0 = s_item;
-  __syncthreads();  // s_item is rewritten inside the loop
-  if (id0 < 0) return;
-  int4 d0, d1, ce;
-  load_item(id0, d0, d1, ce);
-  int nfull = put_table(ce, d0, d1);
   const int rho = 32 * wave + c;  // the lane's row within the tile
   Rows32 rt;
-  {
-    const int rows0 = d0.z * G;
-    load_q8(rt.qb, p, rho < rows0 ? d0.x + rho / G : -1, d1.z * G + rho % G, h);
-  }
-  bool ahead = false;  // the item's first chunks were issued by the previous iteration
+  auto load_q_item = [&](int4 i0, int4 i1) {
+    const int nrows = i0.z * G;
+    load_q8(rt.qb, p, rho < nrows ? i0.x + rho / G : -1, i1.z * G + rho % G, h);
+  };
+
+  // start: the first item (a fixed one per workgroup) and the next
+  int cur = wq.next(true);
+  if (cur < 0) return;
+  if (tid == 0) s_item = wq.next(false);
+  fetch_meta(cur, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  int nxt = s_item;
+  int bf = 0;               // table buffer of the current item
+  int rbase = 0;            // ring slot of the current item's chunk 0
+  int first_real = kAhead;  // the current item's chunks below this are not in flight yet
+  load_q_item(s_desc[0][0], s_desc[0][1]);
+
   for (;;) {
-    // the current item
+    const int4 d0 = s_desc[bf][0], d1 = s_desc[bf][1];
     const int t0 = d0.x, s = d0.y, nt = d0.z;
     const int nck = nt > 0 ? 4 * d0.w : 0;
+    const int nfull = min(d1.w, nck);
     const int Leff = d1.x, base = d1.y, g = d1.z;
     const int rows = nt * G;
+    const int pmin = p.causal ? base + t0 : INT_MAX;
+    const bool lds_res = nt * K <= kPosMax;
     const bool valid = rho < rows;
     const int tau = valid ? rho / G : 0;
     const int hr = rho - tau * G;
     const int tok = t0 + tau;
     const int head = g * G + hr;
-    const int pmin = p.causal ? base + t0 : INT_MAX;
-    const bool wave_has = 32 * wave < rows;
     rows_reset(rt);
     rt.seq = s;
     rt.pos = (valid && p.causal) ? base + tok : INT_MAX;
-    if (tid == 0) s_item = wq.next(false);
-    ring_barrier();  // s_ctab and s_item visible (LDS only: ring loads stay in flight)
-    const int nid = s_item;
-    int4 nd0 = {0, 0, 0, 0}, nd1 = {0, 0, 0, 0}, nce = {-1, -1, 0, 0};
-    if (nid >= 0) load_item(nid, nd0, nd1, nce);  // in flight during the chunk loop
+    // early loads: this item's residual data, the next item's table, the
+    // item after next
+    if (nt > 0) fetch_res(t0, nt, g);
+    if (nxt >= 0) fetch_meta(nxt, bf ^ 1);
+    int nn = 0;
+    if (tid == 0) nn = atomic_add_nowait(wq.head, 1);  // XcdQueue::next(false), not waited for here
 
     if (nck > 0) {
       if constexpr (kFp8) {
+        wait_vmcnt<0>();
+        __syncthreads();
         // register-staged double buffer: chunk ci+1 loads while ci is multiplied
         int64_t off;
         int nr;
         const bool stager = tid < 256;  // 32 rows x 8 pieces of K and of V
-        chunk_of(0, nck, off, nr);
+        chunk_of(bf, 0, nck, off, nr);
         Raw8 raw{};
         if (stager) {
           raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
@@ -892,11 +917,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         }
         __syncthreads();
         for (int ci = 0; ci < nck; ++ci) {
-          chunk_of(ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
+          chunk_of(bf, ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
           if (stager) raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
           const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
-          const int4 e = s_ctab[ci];
-          if (wave_has && !(e.x == -1 && e.y == -1)) {
+          const int4 e = s_tab[bf][ci];
+          if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
             const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
             rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
           }
@@ -905,28 +930,44 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           __syncthreads();
         }
       } else {
+        // chunks not brought in by the previous item's loop
+        if (first_real > 0) {
+          for (int ci = 0; ci < first_real; ++ci) {
+            int64_t off;
+            int nr;
+            chunk_of(bf, ci, nck, off, nr);
+            issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + ci));
+          }
+          wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<2 * (kAhead - 1)>();  // chunk 0 has landed (chunks 1 .. kAhead-1 may be in flight)
+        }
+        ring_barrier();
+        f32x16 sc = rows_scores<CT>(rt, slot_ptr(rbase));
+        u32x4 pp[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};  // P of chunk -1 (nothing)
         // software pipeline over the chunks: iteration ci multiplies V(ci-1)
         // by P(ci-1), computes the scores S(ci+1) and the probabilities of
-        // S(ci); the three are independent, so the matrix cores and the
-        // vector ALU overlap within the wave. Iteration ci reads chunks
-        // ci-1 and ci+1, so once every wave has passed its barrier the slot
-        // of chunk ci-2 takes chunk ci + kRingT - 2.
-        if (!ahead) issue_first(nck);
-        wait_vmcnt<2 * (kRingT - 3)>();  // chunk 0 has landed
-        ring_barrier();
-        f32x16 sc = rows_scores<CT>(rt, s_ring);
-        u32x4 pp[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};  // P of chunk -1 (nothing)
+        // S(ci) (tile_iter). Iteration ci reads chunks ci-1 and ci+1, so
+        // once every wave has passed its barrier the slot of chunk ci-2
+        // takes chunk ci + kAhead: this item's, else the next item's.
         auto step = [&](int ci, bool mask) {
-          wait_vmcnt<2 * (kRingT - 4)>();  // chunk ci+1 has landed
+          wait_vmcnt<2 * (kAhead - 2)>();  // chunk ci+1 has landed
           ring_barrier();                  // ... for every wave; and slot (ci - 2) % kRingT is free
-          const int nx = ci + kRingT - 2;
-          int64_t off;
-          int nr;
-          chunk_of(nx, nck, off, nr);
-          issue_chunk16_512(p.k, p.v, off, nr, dl, ring0 + 16 * kSlotU4 * (nx & (kRingT - 1)));
-          const int key0 = s_ctab[ci].z;
-          const char* vprev = (const char*)(s_ring + ((ci > 0 ? ci - 1 : 0) & (kRingT - 1)) * kSlotU4 + kChunkU4);
-          const u32x4* knext = s_ring + ((ci + 1 < nck ? ci + 1 : ci) & (kRingT - 1)) * kSlotU4;
+          const int nx = ci + kAhead;
+          int64_t off = -1;
+          int nr = 0;
+          if (nx < nck) {
+            chunk_of(bf, nx, nck, off, nr);
+          } else if (nxt >= 0 && (ci >= kAhead - 1 || first_real > 0)) {
+            // the next item's table was issued before chunk kAhead of this
+            // item (or drained with the top-up), so it has landed by now
+            const int4 dn = s_desc[bf ^ 1][0];
+            chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? 4 * dn.w : 0, off, nr);
+          }
+          issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + nx));
+          const int key0 = s_tab[bf][ci].z;
+          const char* vprev = (const char*)(slot_ptr(rbase + (ci > 0 ? ci - 1 : 0)) + kChunkU4);
+          const u32x4* knext = slot_ptr(rbase + (ci + 1 < nck ? ci + 1 : ci));
           f32x16 sn;
           u32x4 pn[2];
           const float alpha = mask ? tile_iter<CT, true>(rt, sc, pp, vprev, knext, key0, Leff, p.scale_log2, sn, pn)
@@ -939,41 +980,50 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         int ci = 0;
         for (; ci < nfull; ++ci) step(ci, false);
         for (; ci < nck; ++ci) step(ci, true);
-        rows_pv<CT>(rt, pp, s_ring + ((nck - 1) & (kRingT - 1)) * kSlotU4 + kChunkU4);
+        rows_pv<CT>(rt, pp, slot_ptr(rbase + nck - 1) + kChunkU4);
       }
     }
-
-    // the next item: its table replaces this one's; its Q and (16-bit
-    // caches) its first chunks are issued before this item's merge
-    ring_barrier();  // every wave is done with s_ctab and the ring
-    if (nid >= 0) {
-      const int nrows = nd0.z * G;
-      load_q8(rt.qb, p, rho < nrows ? nd0.x + rho / G : -1, nd1.z * G + rho % G, h);
-      nfull = put_table(nce, nd0, nd1);
+    // The next item's chunks j < kAhead that this loop issued: those of
+    // iterations from kAhead - 1 on (all of them, after a top-up), i.e.
+    // j >= 2 kAhead - 1 - nck (j >= kAhead - nck); the rest is issued when
+    // the next item starts.
+    int next_first_real = kAhead;
+    if (!kFp8 && nck > 0)
+      next_first_real = first_real > 0 ? max(0, kAhead - nck) : min(kAhead, max(0, 2 * kAhead - 1 - nck));
+    // This item's residual data, the next item's table and the queue slot
+    // taken at the start were issued before chunk kAhead of this item: they
+    // have landed once the loop has waited for that chunk, else (short
+    // items, and the 8-bit path, which issues no ring loads) they are
+    // drained here.
+    if (!kFp8 && nck >= kAhead) {
+      wait_vmcnt<2 * kAhead>();
+    } else {
+      wait_vmcnt<0>();
     }
-    ring_barrier();
-    if constexpr (!kFp8) {
-      if (nid >= 0) issue_first(nd0.z > 0 ? 4 * nd0.w : 0);
+    if (tid == 0) {
+      const int v = settle(nn);
+      s_item = nxt >= 0 && wq.lo + wq.nwg + v < wq.hi ? wq.lo + wq.nwg + v : -1;
     }
+    ring_barrier();  // every wave is done with the ring slots of this item and s_tab[bf]
+    if (nxt >= 0) load_q_item(s_desc[bf ^ 1][0], s_desc[bf ^ 1][1]);
 
     // merge with the unit partials of the row's residual slots, then write.
-    // The partials' positions are listed per (token, KV head). Two partials
-    // are in flight while one is merged, and each position is loaded two
-    // partials before its data, so every load waits on one round trip at
-    // most. The reference max M moves only when a partial's LSE exceeds it by
-    // more than 2^kRescale32.
+    // Two partials are in flight while one is merged (their positions are in
+    // LDS). The reference max M moves only when a partial's LSE exceeds it
+    // by more than 2^kRescale32.
     // Every lane runs the same number of iterations and stores (rows outside
     // the tile into a scratch row): with no branch around loads or stores,
     // the compiler's waits count exactly the loads they need.
     const float l_tot = rows_total(rt);
     {
       const size_t tg = valid ? (size_t)tok * Hkv + g : 0;
-      const int nres = valid ? min(p.tok_nres[tg], K) : 0;
+      const int nr_ = lds_res ? s_nres[tau] : p.tok_nres[tg];
+      const int nres = valid ? min(nr_, K) : 0;
       int nres_w = nres;  // the wave's largest count
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) nres_w = max(nres_w, __shfl_xor(nres_w, off, 64));
+      nres_w = __builtin_amdgcn_readfirstlane(nres_w);
       const int ntot = p.counters[kCntResidual];  // positions are below this
-      const int32_t* rl = p.res_list + tg * K;
       float M = rt.m;  // O and W are relative to 2^M
       float W = l_tot;
       const uint16_t* obase = (const uint16_t*)p.opart + 4 * h;
@@ -981,8 +1031,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         float l;
         u32x2 d[16];
       };
-      auto pos_of = [&](int i) {  // an unconditional load: no branch around it
-        const int v = rl[min(i, K - 1)];
+      auto pos_of = [&](int i) {
+        const int ii = min(i, K - 1);
+        const int v = lds_res ? s_pos[tau * K + ii] : p.res_list[tg * K + ii];
         return i < nres ? v : -1;
       };
       auto fetch = [&](int pos, Part& pt) {
@@ -1025,14 +1076,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         Part pa, pb;
         fetch(pos_of(0), pa);
         fetch(pos_of(1), pb);
-        int qa = pos_of(2), qb = pos_of(3);
         for (int i = 0; i < nres_w; i += 2) {
           merge(pa);
-          fetch(qa, pa);
-          qa = pos_of(i + 4);
+          fetch(pos_of(i + 2), pa);
           merge(pb);
-          fetch(qb, pb);
-          qb = pos_of(i + 5);
+          fetch(pos_of(i + 3), pb);
         }
       }
       const float inv = W > 0.f ? 1.f / W : 0.f;
@@ -1041,10 +1089,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
       float* lrow = (valid && h == 0 && p.lse) ? p.lse + (size_t)head * p.Tq + tok : (float*)p.scratch_row + 64 + lane;
       *lrow = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
     }
-    if (nid < 0) break;
-    d0 = nd0;
-    d1 = nd1;
-    ahead = !kFp8;
+    ring_barrier();  // s_item visible; every wave is done with s_pos / s_nres
+    if (nxt < 0) break;
+    rbase = (rbase + nck) & (kRingT - 1);
+    first_real = next_first_real;
+    bf ^= 1;
+    cur = nxt;
+    nxt = s_item;
   }
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
