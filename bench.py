@@ -130,6 +130,91 @@ def measured_traffic(workload, kernels):
         return None
 
 
+# rocprofv3 runs whose outputs write_profile_summaries() turns into the
+# text summaries under profiles/ ($ROOT: the repository root on the GPU machine)
+PROF_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $ROOT/gpurun_out/prof/{w} -o run "
+                  "-- python3 $ROOT/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
+PROF_PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/traffic/{w}_{c} -o run "
+                "-- python3 $ROOT/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline")
+PROF_COPY_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/traffic/copy_{c} -o run "
+                 "-- python3 $ROOT/bench.py --calibrate-copy")
+KERNEL_KEYS = {"front": "k_front", "units": "k_units", "tiles": "k_tiles", "classify": "k_classify_waves",
+               "index": "k_index", "emit": "k_emit"}
+
+
+def write_profile_summaries(src):
+    """profiles/kernels_<w>.md and profiles/traffic_<w>.txt from rocprofv3 outputs under src.
+
+    src/prof/<w>/**/run_kernel_stats.csv: the kernel-trace statistics of
+    PROF_TRACE_CMD; src/traffic/{copy,<w>}_{FETCH_SIZE,WRITE_SIZE}/**/
+    run_counter_collection.csv: the counter runs of PROF_PMC_CMD and
+    PROF_COPY_CMD. FETCH_SIZE and WRITE_SIZE are KiB-like units per dispatch;
+    the plain 1 GiB copy gives the factors to bytes.
+    """
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def one(pattern):
+        f = sorted(glob.glob(os.path.join(src, pattern), recursive=True))
+        return f[0] if f else None
+
+    def counters(d):
+        f = one(os.path.join("traffic", d, "**", "*counter_collection.csv"))
+        acc = defaultdict(list)
+        if f:
+            for r in csv.DictReader(open(f)):
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    factors = None
+    cf, cw = counters("copy_FETCH_SIZE"), counters("copy_WRITE_SIZE")
+    if cf and cw:
+        (f_kib, _), f_name = max((v, k) for k, v in cf.items() if "copy" in k.lower())
+        (w_kib, _), _ = max((v, k) for k, v in cw.items() if "copy" in k.lower())
+        factors = ((1 << 30) / f_kib, (1 << 30) / w_kib, f_kib, w_kib, f_name)
+    sha = kernel_sources_sha256()
+    for w in DESCRIPTIONS:
+        stats = one(os.path.join("prof", w, "**", "*kernel_stats.csv"))
+        if stats:
+            rows = [r for r in csv.DictReader(open(stats)) if "msa" in r["Name"]]
+            lines = [f"# {w}: rocprofv3 kernel statistics", "",
+                     f"Workload: {DESCRIPTIONS[w]}.", "",
+                     "Command (from the repository root on an MI355X; `$ROOT` is that root):", "",
+                     "```", PROF_TRACE_CMD.format(w=w), "```", "",
+                     f"Kernel sources: sha256 {sha}.", "",
+                     "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share of GPU time |",
+                     "|---|---|---|---|---|---|"]
+            for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+                lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                             f"{float(r['Percentage']):.1f}% |")
+            lines += ["", "The benchmark's own input generation kernels (torch fills, copies) are omitted; "
+                      "their share is part of the last column's remainder."]
+            with open(os.path.join(ROOT, "profiles", f"kernels_{w}.md"), "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print("wrote", f"profiles/kernels_{w}.md")
+        fk, wk = counters(f"{w}_FETCH_SIZE"), counters(f"{w}_WRITE_SIZE")
+        if factors and fk and wk:
+            ff, fw, f_kib, w_kib, f_name = factors
+            rec = {"workload": w, "sources_sha256": sha, "fetch_factor": ff, "write_factor": fw,
+                   "copy_reference": {"bytes": 1 << 30, "fetch_size": f_kib, "write_size": w_kib,
+                                      "kernel": f_name[:120]},
+                   "commands": [PROF_COPY_CMD.format(c="FETCH_SIZE"), PROF_COPY_CMD.format(c="WRITE_SIZE"),
+                                PROF_PMC_CMD.format(w=w, c="FETCH_SIZE"), PROF_PMC_CMD.format(w=w, c="WRITE_SIZE")],
+                   "kernels": {}}
+            for short, pat in KERNEL_KEYS.items():
+                a = [v for k, v in fk.items() if pat in k]
+                b = [v for k, v in wk.items() if pat in k]
+                if a and b:
+                    rec["kernels"][short] = {"fetch_kib": a[0][0], "write_kib": b[0][0], "dispatches": a[0][1],
+                                             "hbm_bytes": a[0][0] * ff + b[0][0] * fw}
+            with open(os.path.join(ROOT, "profiles", f"traffic_{w}.txt"), "w") as f:
+                json.dump(rec, f, indent=1)
+            print("wrote", f"profiles/traffic_{w}.txt",
+                  {k: round(v["hbm_bytes"] / 1e6, 1) for k, v in rec["kernels"].items()}, "MB per launch")
+
+
 def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
 
@@ -177,11 +262,17 @@ def main():
     ap.add_argument("--workload", default="decode_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=None, help="oracle sample size in (token, kv-head) pairs")
+    ap.add_argument("--profile-summaries", metavar="DIR", default=None,
+                    help="only write profiles/kernels_<w>.md and profiles/traffic_<w>.txt from the rocprofv3 "
+                         "outputs under DIR (see PROF_TRACE_CMD, PROF_PMC_CMD, PROF_COPY_CMD); needs no GPU")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference kernel for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and print its size")
     args = ap.parse_args()
 
+    if args.profile_summaries:
+        write_profile_summaries(args.profile_summaries)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
