@@ -90,6 +90,16 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier of the tile kernel's chunk loop: every LDS read the loop issues
+// is consumed within its iteration (or, for the next iteration's first V
+// fragments, reads a slot no load overwrites before the following
+// iteration), so no LDS wait is needed before it.
+__device__ __forceinline__ void loop_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Swizzled 16-byte pieces of a 32 x 128 16-bit tile (row = key). The K tile
 // XORs the piece index with row & 15: a K-operand read has lane c reading
 // row c, so 16 consecutive lanes hit 16 different pieces. The V tile XORs it
@@ -236,43 +246,54 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
   rows_pv<CT>(rt, pb, sV);
 }
 
-// One iteration of the tile kernel's chunk pipeline, scheduled by hand:
-// O^T += V(prev)^T P(prev)^T, sn = S of the next chunk, and the softmax step
-// of sc (this chunk's scores) giving pn. The work is cut into eight stages,
-// each one P V product, one Q K product, the LDS reads of the products two
-// stages later and a slice of the vector work; sched_barrier keeps the
-// compiler from regrouping them, so the vector ALU runs while the matrix
-// core is busy and every LDS read has two stages to land. Returns the
-// accumulator rescale factor (see rows_probs).
-template <typename CT, bool kMask>
-__device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u32x4 (&pp)[2], const char* vprev,
-                                           const u32x4* knext, int key0, int lim, float sl2, f32x16& sn,
-                                           u32x4 (&pn)[2]) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+// V^T fragment of d-tile t and key step sp of a staged V tile (transposing
+// reads): lane (h, c) receives V[key][32t + c] for the four keys
+// 16sp + 8r + 4h + i; its source lanes read 8 bytes each at row
+// 16sp + 8r + 4h + i (i = (l >> 2) & 3), logical piece 4t + 2((l >> 4) & 1)
+// + ((l & 3) >> 1), half l & 1. With the V swizzle the physical piece is
+// 4(t ^ i) + the low two bits.
+__device__ __forceinline__ u32x4 vfrag_at(const char* vtile, int t, int sp) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
   const int i4 = (lane >> 2) & 3;
   const int rsub = 4 * h + i4;
   const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int half = 8 * (lane & 1);
-  auto vfrag = [&](int t, int sp) {
-    u32x4 a;
+  u32x4 a;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 16 * sp + 8 * r + rsub;
-      const int off = row * 256 + ((4 * (t ^ i4) + psub) << 4) + half;
-      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vprev + off)));
-      a[2 * r] = w[0];
-      a[2 * r + 1] = w[1];
-    }
-    return a;
-  };
+  for (int r = 0; r < 2; ++r) {
+    const int row = 16 * sp + 8 * r + rsub;
+    const int off = row * 256 + ((4 * (t ^ i4) + psub) << 4) + half;
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtile + off)));
+    a[2 * r] = w[0];
+    a[2 * r + 1] = w[1];
+  }
+  return a;
+}
+
+// One iteration of the tile kernel's chunk pipeline, scheduled by hand:
+// O^T += V(prev)^T P(prev)^T, sn = S of the next chunk, and the softmax step
+// of sc (this chunk's scores) giving pn. The work is cut into eight stages:
+// stage i holds the P V product i, the Q K product i - 1, the LDS reads of
+// the products two stages later and a slice of the vector work;
+// sched_barrier keeps the compiler from regrouping them, so the vector ALU
+// runs while the matrix core is busy and every LDS read has two stages to
+// land. The first two V fragments (vpre) were read by the previous
+// iteration, before the barrier; this one reads those of the current
+// chunk's V for the next iteration (vnext). The K reads start one stage
+// after the barrier that makes the next chunk visible. Returns the
+// accumulator rescale factor (see rows_probs).
+template <typename CT, bool kMask>
+__device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u32x4 (&pp)[2], const char* vprev,
+                                           const u32x4 (&vpre)[2], const char* vcur, const u32x4* knext, int key0,
+                                           int lim, float sl2, f32x16& sn, u32x4 (&pn)[2], u32x4 (&vnext)[2]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
   auto kfrag = [&](int st) { return knext[pieceK(c, 2 * st + h)]; };
 
   f32x16 sa = sc;
   u32x4 va[8], ka[8];
-  va[0] = vfrag(0, 0);
+  va[0] = vpre[0];
+  va[1] = vpre[1];
   ka[0] = kfrag(0);
-  va[1] = vfrag(1, 0);
-  ka[1] = kfrag(1);
 #pragma unroll
   for (int j = 0; j < 16; ++j) sn[j] = 0.f;
   float cmax = 0.f, alpha = 1.f, nmu = 0.f, ls = 0.f;
@@ -284,12 +305,10 @@ __device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (i + 2 < 8) {
-      va[i + 2] = vfrag((i + 2) & 3, (i + 2) >> 2);
-      ka[i + 2] = kfrag(i + 2);
-    }
+    if (i + 2 < 8) va[i + 2] = vfrag_at(vprev, (i + 2) & 3, (i + 2) >> 2);
+    if (i + 1 < 8) ka[i + 1] = kfrag(i + 1);
     rt.o[i & 3] = Mma32<CT>::run(va[i], pp[i >> 2], rt.o[i & 3]);
-    sn = Mma32<CT>::run(ka[i], rt.qb[i], sn);
+    if (i > 0) sn = Mma32<CT>::run(ka[i - 1], rt.qb[i - 1], sn);
     if (i == 0) {
       // masking, then the row max of the raw scores (sl2 > 0 commutes with max)
       if (kMask) {
@@ -322,6 +341,9 @@ __device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  sn = Mma32<CT>::run(ka[7], rt.qb[7], sn);
+  vnext[0] = vfrag_at(vcur, 0, 0);
+  vnext[1] = vfrag_at(vcur, 1, 0);
   // used here, so that the vector work is not sunk past the caller's
   // rarely taken rescale branch
   asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(ls));
@@ -943,44 +965,68 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           wait_vmcnt<2 * (kAhead - 1)>();  // chunk 0 has landed (chunks 1 .. kAhead-1 may be in flight)
         }
         ring_barrier();
-        f32x16 sc = rows_scores<CT>(rt, slot_ptr(rbase));
-        u32x4 pp[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};  // P of chunk -1 (nothing)
+        // the state carried from one iteration to the next: the scores of
+        // the current chunk, the probabilities of the previous one and the
+        // first two V fragments of the next products. The loops run two
+        // iterations per trip with the roles of A and B swapped, so the
+        // state is never copied.
+        struct Pipe {
+          f32x16 sc;
+          u32x4 pp[2];
+          u32x4 vpre[2];
+        } A, B;
+        A.sc = rows_scores<CT>(rt, slot_ptr(rbase));
+        A.pp[0] = u32x4{0u, 0u, 0u, 0u};  // P of chunk -1 (nothing)
+        A.pp[1] = u32x4{0u, 0u, 0u, 0u};
+        A.vpre[0] = vfrag_at((const char*)(slot_ptr(rbase) + kChunkU4), 0, 0);  // chunk 0 stands in for chunk -1
+        A.vpre[1] = vfrag_at((const char*)(slot_ptr(rbase) + kChunkU4), 1, 0);
         // software pipeline over the chunks: iteration ci multiplies V(ci-1)
         // by P(ci-1), computes the scores S(ci+1) and the probabilities of
-        // S(ci) (tile_iter). Iteration ci reads chunks ci-1 and ci+1, so
+        // S(ci) (tile_iter). Iteration ci reads chunks ci-1 .. ci+1, so
         // once every wave has passed its barrier the slot of chunk ci-2
         // takes chunk ci + kAhead: this item's, else the next item's.
-        auto step = [&](int ci, bool mask) {
-          wait_vmcnt<2 * (kAhead - 2)>();  // chunk ci+1 has landed
-          ring_barrier();                  // ... for every wave; and slot (ci - 2) % kRingT is free
+        auto step = [&](int ci, bool mask, const Pipe& in, Pipe& out) {
           const int nx = ci + kAhead;
           int64_t off = -1;
           int nr = 0;
-          if (nx < nck) {
-            chunk_of(bf, nx, nck, off, nr);
-          } else if (nxt >= 0 && (ci >= kAhead - 1 || first_real > 0)) {
+          if (nx < nck) chunk_of(bf, nx, nck, off, nr);  // this item's table: visible since the item began
+          wait_vmcnt<2 * (kAhead - 2)>();                 // chunk ci+1 has landed
+          loop_barrier();                                 // ... for every wave; and slot (ci - 2) % kRingT is free
+          if (nx >= nck && nxt >= 0 && (ci >= kAhead - 1 || first_real > 0)) {
             // the next item's table was issued before chunk kAhead of this
             // item (or drained with the top-up), so it has landed by now
             const int4 dn = s_desc[bf ^ 1][0];
             chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? 4 * dn.w : 0, off, nr);
           }
           issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + nx));
-          const int key0 = s_tab[bf][ci].z;
+          const int key0 = mask ? s_tab[bf][ci].z : 0;
           const char* vprev = (const char*)(slot_ptr(rbase + (ci > 0 ? ci - 1 : 0)) + kChunkU4);
+          const char* vcur = (const char*)(slot_ptr(rbase + ci) + kChunkU4);
           const u32x4* knext = slot_ptr(rbase + (ci + 1 < nck ? ci + 1 : ci));
-          f32x16 sn;
-          u32x4 pn[2];
-          const float alpha = mask ? tile_iter<CT, true>(rt, sc, pp, vprev, knext, key0, Leff, p.scale_log2, sn, pn)
-                                   : tile_iter<CT, false>(rt, sc, pp, vprev, knext, key0, Leff, p.scale_log2, sn, pn);
+          const float alpha = mask ? tile_iter<CT, true>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, Leff,
+                                                         p.scale_log2, out.sc, out.pp, out.vpre)
+                                   : tile_iter<CT, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, Leff,
+                                                          p.scale_log2, out.sc, out.pp, out.vpre);
           rows_rescale(rt, alpha);
-          sc = sn;
-          pp[0] = pn[0];
-          pp[1] = pn[1];
         };
         int ci = 0;
-        for (; ci < nfull; ++ci) step(ci, false);
-        for (; ci < nck; ++ci) step(ci, true);
-        rows_pv<CT>(rt, pp, slot_ptr(rbase + nck - 1) + kChunkU4);
+        for (; ci + 2 <= nfull; ci += 2) {
+          step(ci, false, A, B);
+          step(ci + 1, false, B, A);
+        }
+        if (ci < nfull) {
+          step(ci++, false, A, B);
+          A = B;
+        }
+        for (; ci + 2 <= nck; ci += 2) {
+          step(ci, true, A, B);
+          step(ci + 1, true, B, A);
+        }
+        if (ci < nck) {
+          step(ci++, true, A, B);
+          A = B;
+        }
+        rows_pv<CT>(rt, A.pp, slot_ptr(rbase + nck - 1) + kChunkU4);
       }
     }
     // The next item's chunks j < kAhead that this loop issued: those of
