@@ -45,13 +45,16 @@ DESCRIPTIONS = {
                   "Hq=32, Hkv=1, d=128, page 128, top-32, causal, fp16",
     "decode_fp8": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
                   "K/V fp8 e4m3fn, q bf16, causal",
+    "dense_causal": "1 seq, Tq=L=8192, Hq=64, Hkv=8, d=128, page 128, every visible block selected "
+                    "(top-64), causal, bf16: dense causal attention through the sparse path",
 }
 # Kernels whose summed average launch time the roofline is taken over. In
 # the prefill-shaped workloads the attention's MFMA work is split between
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
 DOMINANT = {"tiny": ["tiles"], "decode_gqa": ["front"], "decode_fp8": ["front"],
-            "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"]}
+            "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
+            "dense_causal": ["tiles"]}
 
 
 def log(*a):

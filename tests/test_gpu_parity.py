@@ -179,6 +179,25 @@ def test_parity_varlen_mqa_sampled():
     assert not torch.isnan(out.float()).any()
 
 
+def test_parity_dense_causal_sampled():
+    # every visible block selected: dense causal attention through the sparse path
+    wl = W.make("dense_causal")
+    out, lse = run_gpu(wl)
+    pairs = sample_pairs(wl, 128)
+    ref_o, ref_l = oracle_pairs(wl, pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+    assert not torch.isnan(out.float()).any()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_parity_dense_small(causal):
+    # all blocks selected at a size the oracle checks in full, several tiles
+    # and a ragged last block
+    wl = W.make_custom(620 + int(causal), [200, 77], [900, 77 if causal else 333], 16, 2, 64, topk=8,
+                       causal=causal, pick="all")
+    _full(wl)
+
+
 # ---------------------------------------------------------------------------
 # properties
 # ---------------------------------------------------------------------------

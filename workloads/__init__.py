@@ -46,6 +46,7 @@ CONFIGS = {
     "prefill_shared": dict(seed=1003),
     "varlen_mqa": dict(seed=1004),
     "decode_fp8": dict(seed=1005),
+    "dense_causal": dict(seed=1006),
 }
 
 
@@ -281,12 +282,30 @@ def make_decode_fp8(seed=1005, poison=True, batch=256):
                     np.arange(batch + 1), used, bt, sel, NP, poison)
 
 
+def make_dense_causal(seed=1006, poison=True, seqlen=8192):
+    """Dense causal attention as the case where every visible block is
+    selected: 1 sequence, Tq = L = seqlen, Hq 64, Hkv 8, page 128, top-64
+    (every block a token can see), bf16."""
+    rng = np.random.default_rng(seed)
+    P, Hkv, K = 128, 8, 64
+    T = L = seqlen
+    assert (L + BLOCK - 1) // BLOCK <= K, "every block must fit in the top-k"
+    bt, NP = _page_tables(rng, [L], P)
+    sel = np.full((T, Hkv, K), -1, dtype=np.int32)
+    for t in range(T):
+        vis = t // BLOCK + 1
+        sel[t, :, :vis] = np.arange(vis, dtype=np.int32)
+    return assemble("dense_causal", seed, 64, Hkv, P, K, True, torch.bfloat16, torch.bfloat16,
+                    [0, T], [L], bt, sel, NP, poison, all_pages=True)
+
+
 MAKERS = {
     "tiny": make_tiny,
     "decode_gqa": make_decode_gqa,
     "prefill_shared": make_prefill_shared,
     "varlen_mqa": make_varlen_mqa,
     "decode_fp8": make_decode_fp8,
+    "dense_causal": make_dense_causal,
 }
 
 
