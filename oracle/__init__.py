@@ -16,6 +16,8 @@ Contents
   * ``index_ref``      -- integer CPU reference of the selection inversion and
                           the work split that the GPU index builder must match
                           bit for bit.
+  * ``store_ref``      -- reference of the paged K/V store with its fp8 e4m3fn
+                          cast (the step before the pass).
 """
 from __future__ import annotations
 
