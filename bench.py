@@ -47,14 +47,17 @@ DESCRIPTIONS = {
                   "K/V fp8 e4m3fn, q bf16, causal",
     "dense_causal": "1 seq, Tq=L=8192, Hq=64, Hkv=8, d=128, page 128, every visible block selected "
                     "(top-64), causal, bf16: dense causal attention through the sparse path",
+    "kv_store_fp8": "paged K/V store (the step before the pass): 32768 new tokens x Hkv=8 x d=128, "
+                    "bf16 -> fp8 e4m3fn cache, page 64, slots shuffled over the cache",
 }
+STORE_METRIC = "paged K/V store GB/s (bytes read + written), bf16 -> fp8 e4m3fn"
 # Kernels whose summed average launch time the roofline is taken over. In
 # the prefill-shaped workloads the attention's MFMA work is split between
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
 DOMINANT = {"tiny": ["tiles"], "decode_gqa": ["front"], "decode_fp8": ["front"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
-            "dense_causal": ["tiles"]}
+            "dense_causal": ["tiles"], "kv_store_fp8": ["store"]}
 
 
 def log(*a):
@@ -218,6 +221,76 @@ def write_profile_summaries(src):
                   {k: round(v["hbm_bytes"] / 1e6, 1) for k, v in rec["kernels"].items()}, "MB per launch")
 
 
+def bench_store(args, torch, msa):
+    """The paged K/V store benchmark: one step is one msa_store_kv call."""
+    from oracle import store_ref  # the CPU baseline leg only
+
+    dev = torch.device("cuda:0")
+    N, Hkv, P = 32768, 8, 64
+    NP = N // P + 64
+    sets = []
+    for i in range(2):
+        g = torch.Generator().manual_seed(4242 + i)
+        k = torch.randn((N, Hkv, 128), generator=g).to(torch.bfloat16)
+        v = torch.randn((N, Hkv, 128), generator=g).to(torch.bfloat16)
+        loc = torch.randperm(NP * P, generator=g)[:N].to(torch.int64)
+        sets.append(dict(k=k.to(dev), v=v.to(dev), loc=loc.to(dev), k_cpu=k, v_cpu=v, loc_cpu=loc))
+    kc = torch.zeros((NP, Hkv, P, 128), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+    vc = torch.zeros_like(kc)
+    moved = N * Hkv * 128 * 2 * (2 + 1) + N * 8  # read K and V (16-bit) and the slots, write K and V (fp8)
+
+    def step(i):
+        d = sets[i % 2]
+        msa.store_kv(d["k"], d["v"], d["loc"], kc, vc, page_size=P)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    stop.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    msa.profile_enable(["store"])
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    k_ms, k_n = msa.profile_collect("store")
+    msa.profile_enable([])
+    k_avg = k_ms / max(k_n, 1)
+    achieved = moved / (k_avg * 1e-3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(args.workload, ["store"]),
+                kernel="store", kernel_avg_us=round(k_avg * 1e3, 2), launches=k_n)
+    cpu = None
+    if not args.no_cpu_baseline:
+        d = sets[0]
+        n_s = 2048
+        kh = np.zeros((NP, Hkv, P, 128), np.uint8)
+        vh = np.zeros((NP, Hkv, P, 128), np.uint8)
+        kf, vf, lf = d["k_cpu"][:n_s].float().numpy(), d["v_cpu"][:n_s].float().numpy(), d["loc_cpu"][:n_s].numpy()
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < 5.0:
+            store_ref.store_kv(kf, vf, lf, kh, vh, P)
+            reps += 1
+        el = time.time() - t0
+        cpu = {"value": round(moved * n_s / N * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_s} of {N} new tokens, repeated {reps}x ({el:.1f} s of oracle time); "
+                         f"bytes scaled by the sampled fraction"}
+    res = {"metric": STORE_METRIC, "value": round(moved / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8",
+           "data": "synthetic",
+           "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "new_tokens": N,
+                      "bytes_per_step": moved, "parallelism": "single GPU", "input_sets": 2},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
 
@@ -301,6 +374,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return
     msa.load()
+    if args.workload == "kv_store_fp8":
+        bench_store(args, torch, msa)
+        return
     seed0 = W.CONFIGS[args.workload]["seed"]
 
     batches = []

@@ -27,6 +27,7 @@ from ._lib import (
     load,
     profile_collect,
     profile_enable,
+    store_kv,
     validate_inputs,
     version,
     widen_fp8,
@@ -36,6 +37,7 @@ __all__ = [
     "kvouter_attention",
     "build_index",
     "widen_fp8",
+    "store_kv",
     "validate_inputs",
     "version",
     "load",

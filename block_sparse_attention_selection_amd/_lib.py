@@ -77,6 +77,8 @@ def load():
         lib.msa_build_index.argtypes = [T, T, T, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MsaIndexOut), vp]
         lib.msa_widen_fp8.restype = i32
         lib.msa_widen_fp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
+        lib.msa_store_kv.restype = i32
+        lib.msa_store_kv.argtypes = [T, T, T, T, T, i32, vp]
         lib.msa_validate_inputs.restype = i32
         lib.msa_validate_inputs.argtypes = [T, T, T, T, T, T, T, i32, i32, vp]
         lib.msa_profile_enable.restype = i32
@@ -156,6 +158,18 @@ def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens
     return (out, lse) if return_lse else out
 
 
+def store_kv(k_new, v_new, loc, k_cache, v_cache, *, page_size: int):
+    """Store new tokens' K and V rows into the paged caches (in place); see
+    include/msa_kvouter.h (msa_store_kv) for the contract."""
+    lib = load()
+    _device_check(k_new, v_new, loc, k_cache, v_cache)
+    ds = [describe(x) for x in (k_new, v_new, loc, k_cache, v_cache)]
+    with torch.cuda.device(k_new.device):
+        rc = lib.msa_store_kv(*[_ref(d) for d in ds], int(page_size), _stream(k_new.device))
+    _check(rc)
+    return k_cache, v_cache
+
+
 def validate_inputs(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
                     page_size: int, causal: bool = False):
     """Synchronous check of the data-dependent preconditions; raises MsaError."""
@@ -199,7 +213,7 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
     return res
 
 
-KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3}
+KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3, "store": 4}
 
 
 def profile_enable(kernels=()):

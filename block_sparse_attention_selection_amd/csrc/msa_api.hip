@@ -333,7 +333,7 @@ struct ProfRec {
 std::mutex g_prof_mutex;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
-hipEvent_t g_open[4] = {nullptr, nullptr, nullptr, nullptr};
+hipEvent_t g_open[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
 
 hipEvent_t pooled_event() {
   if (!g_event_pool.empty()) {
@@ -373,12 +373,12 @@ int32_t msa_profile_enable(uint32_t kernel_mask) {
     g_event_pool.push_back(r.b);
   }
   g_prof.clear();
-  msa::g_profile_mask = kernel_mask & 0xFu;
+  msa::g_profile_mask = kernel_mask & 0x1Fu;
   return ok();
 }
 
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (!total_ms || !launches || kernel < 0 || kernel > 3) return fail(MSA_ERR_INVALID_ARGUMENT, "bad profile query");
+  if (!total_ms || !launches || kernel < 0 || kernel > 4) return fail(MSA_ERR_INVALID_ARGUMENT, "bad profile query");
   std::lock_guard<std::mutex> lk(g_prof_mutex);
   double tot = 0.0;
   int64_t n = 0;
@@ -546,6 +546,50 @@ int32_t msa_widen_fp8(const void* in, int64_t n, int32_t out_dtype, void* out, v
   if (((uintptr_t)in) % 16 || ((uintptr_t)out) % 16) return fail(MSA_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
   if (out_dtype != MSA_BF16 && out_dtype != MSA_FP16) return fail(MSA_ERR_INVALID_ARGUMENT, "out dtype must be bf16 or fp16");
   hipError_t e = msa::launch_widen_fp8(in, n, elem_of(out_dtype), out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa_tensor* loc,
+                     msa_tensor* k_cache, msa_tensor* v_cache, int32_t page_size, void* stream) {
+  int32_t rc;
+  if ((rc = check_tensor(k_new, "k_new", 3, -1, 16))) return rc;
+  if (k_new->dtype != MSA_BF16 && k_new->dtype != MSA_FP16)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_new: dtype must be bf16 or fp16, got %s", dname(k_new->dtype));
+  if ((rc = check_tensor(v_new, "v_new", 3, k_new->dtype, 16))) return rc;
+  if ((rc = check_tensor(loc, "loc", 1, MSA_INT64, 8))) return rc;
+  if ((rc = check_tensor(k_cache, "k_cache", 4, -1, 16))) return rc;
+  if ((rc = check_tensor(v_cache, "v_cache", 4, k_cache->dtype, 16))) return rc;
+  if (k_cache->dtype != k_new->dtype && k_cache->dtype != MSA_FP8_E4M3FN)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: dtype %s must equal k_new's (%s) or be fp8_e4m3fn",
+                dname(k_cache->dtype), dname(k_new->dtype));
+  if (page_size != 64 && page_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "page_size %d: only 64 and 128 are supported", page_size);
+  for (int i = 0; i < 3; ++i)
+    if (v_new->shape[i] != k_new->shape[i]) return fail(MSA_ERR_INVALID_ARGUMENT, "v_new: shape differs from k_new");
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i])
+      return fail(MSA_ERR_INVALID_ARGUMENT, "v_cache: shape differs from k_cache");
+  if (k_new->shape[2] != 128 || k_cache->shape[3] != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "head dim must be 128");
+  if (k_cache->shape[2] != page_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: page dimension %lld != page_size %d",
+                (long long)k_cache->shape[2], page_size);
+  if (k_cache->shape[1] != k_new->shape[1])
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: %lld KV heads, k_new has %lld", (long long)k_cache->shape[1],
+                (long long)k_new->shape[1]);
+  if (loc->shape[0] != k_new->shape[0])
+    return fail(MSA_ERR_INVALID_ARGUMENT, "loc: %lld slots for %lld new tokens", (long long)loc->shape[0],
+                (long long)k_new->shape[0]);
+  const int64_t N = k_new->shape[0], Hkv = k_new->shape[1], NP = k_cache->shape[0];
+  if (N * Hkv * 32 >= (1ll << 31) || NP * Hkv * page_size >= (1ll << 40))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large");
+  if (N == 0) return ok();
+  msa::profile_mark(msa::kKStore, true, (hipStream_t)stream);
+  hipError_t e = msa::launch_store_kv(k_new->data, v_new->data, (const int64_t*)loc->data, k_cache->data,
+                                      v_cache->data, (int)N, (int)Hkv, page_size, NP, elem_of(k_new->dtype),
+                                      k_cache->dtype == MSA_FP8_E4M3FN, (hipStream_t)stream);
+  msa::profile_mark(msa::kKStore, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -84,7 +84,7 @@ struct Params {
 };
 
 // kernel timing hooks (msa_api.hip): no-ops unless msa_profile_enable set the bit
-enum KernelId { kKIndex = 0, kKFront = 1, kKUnits = 2, kKTiles = 3 };
+enum KernelId { kKIndex = 0, kKFront = 1, kKUnits = 2, kKTiles = 3, kKStore = 4 };
 extern volatile uint32_t g_profile_mask;
 void profile_mark(int kernel, bool begin, hipStream_t st);
 
@@ -99,5 +99,7 @@ hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st
 hipError_t launch_units(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st);
 hipError_t launch_tiles(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st);
 hipError_t launch_widen_fp8(const void* in, int64_t n, int out_elem, void* out, hipStream_t st);
+hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, void* kc, void* vc, int N, int Hkv,
+                           int P, int64_t num_pages, int in_elem, bool fp8_cache, hipStream_t st);
 
 }  // namespace msa

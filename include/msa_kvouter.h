@@ -176,6 +176,35 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
 int32_t msa_widen_fp8(const void* in, int64_t n, int32_t out_dtype, void* out, void* stream);
 
 /*
+ * msa_store_kv -- the paged K/V store, the step before the attention pass
+ * (sglang pull request "Speed up MiniMax-M3 sparse attention on Hopper",
+ * summary and "Verification": the fused K/V store with an unscaled cast of
+ * 16-bit values to fp8 e4m3fn, bit-exact with
+ * x.float().clamp(-448, 448).to(float8_e4m3fn)).
+ *
+ *   k_new, v_new  [N, Hkv, 128] bf16 or fp16 (the same dtype), the new
+ *                 tokens' keys and values
+ *   loc           [N] int64, the flat cache slot of each new token:
+ *                 page * page_size + offset. A negative slot, or one at or
+ *                 beyond num_pages * page_size, stores nothing.
+ *   k_cache, v_cache  [num_pages, Hkv, page_size, 128], the layout the
+ *                 attention pass reads, in the new values' dtype (copied
+ *                 unchanged) or fp8_e4m3fn (each value clamped to [-448, 448]
+ *                 and rounded to nearest even; NaN keeps its sign and becomes
+ *                 the NaN code)
+ *   page_size     64 or 128
+ *
+ * Row (i, g) of k_new / v_new goes to cache[loc[i] / page_size, g,
+ * loc[i] % page_size, :]. Two new tokens with the same slot race (the result
+ * is one of them). All buffers are caller-owned device memory, 16-byte
+ * aligned; the call enqueues one kernel on `stream` and returns; the caches
+ * are modified in place. Errors as for msa_kvouter_attention; N == 0
+ * enqueues nothing.
+ */
+int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa_tensor* loc,
+                     msa_tensor* k_cache, msa_tensor* v_cache, int32_t page_size, void* stream);
+
+/*
  * msa_validate_inputs -- synchronous check of the data-dependent
  * preconditions of msa_kvouter_attention (copies the small index arrays to
  * the host and waits for `stream`). Returns MSA_OK or MSA_ERR_PRECONDITION
@@ -190,7 +219,7 @@ int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache,
 
 /*
  * Kernel timing for benchmarks. msa_profile_enable(mask) makes every later
- * msa_kvouter_attention call record a pair of HIP events on its stream
+ * msa_kvouter_attention (and msa_store_kv) call record a pair of HIP events on its stream
  * around each launch of the kernels whose bit is set in `mask`
  * (1 << MSA_KERNEL_*); mask 0 turns recording off. Enabling discards
  * earlier records. msa_profile_collect waits for the recorded events of one
@@ -202,6 +231,7 @@ enum {
   MSA_KERNEL_FRONT = 1, /* classification + residual-free tiles of <= 16 rows */
   MSA_KERNEL_UNITS = 2, /* KV-outer units: partial O and LSE per residual slot */
   MSA_KERNEL_TILES = 3, /* listed tiles: chain blocks, LSE merge of the partials */
+  MSA_KERNEL_STORE = 4, /* msa_store_kv */
 };
 int32_t msa_profile_enable(uint32_t kernel_mask);
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches);

@@ -150,3 +150,30 @@ def test_build_index_argument_checks():
     assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 0, 0, 8, 8, 0, r(o), None) == INV    # nb_max 0
     assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, 2, r(o), None) == INV    # flag
     assert lib.msa_build_index(r(sel), r(cu), r(used), 16, 4, 0, 8, 8, 0, None, None) == INV
+
+
+def test_store_kv_argument_checks():
+    lib = msa.load()
+    r = ctypes.byref
+
+    def args(N=8, Hkv=2, NP=4, P=64, in_dt=msa.MSA_BF16, cache_dt=msa.MSA_FP8_E4M3FN, nloc=None, vshape=None):
+        k = desc([N, Hkv, 128], in_dt)
+        v = desc(vshape or [N, Hkv, 128], in_dt)
+        loc = desc([N if nloc is None else nloc], msa.MSA_INT64)
+        kc = desc([NP, Hkv, P, 128], cache_dt)
+        vc = desc([NP, Hkv, P, 128], cache_dt)
+        return k, v, loc, kc, vc
+
+    def call_store(a, P=64):
+        k, v, loc, kc, vc = a
+        return lib.msa_store_kv(r(k), r(v), r(loc), r(kc), r(vc), P, None)
+
+    assert call_store(args(in_dt=msa.MSA_FP32)) == INV                          # input dtype
+    assert call_store(args(cache_dt=msa.MSA_FP16)) == INV                       # bf16 into fp16 cache
+    assert call_store(args(nloc=7)) == INV                                      # one slot per token
+    assert call_store(args(vshape=[8, 2, 64])) != 0                             # K and V differ
+    assert call_store(args(P=128)) == INV                                       # page dim != page_size
+    assert call_store(args(), P=32) != 0                                        # unsupported page size
+    k, v, loc, kc, vc = args()
+    assert lib.msa_store_kv(None, r(v), r(loc), r(kc), r(vc), 64, None) == INV
+    assert call_store(args(N=0)) == 0                                           # nothing to store
