@@ -145,7 +145,7 @@ PROF_PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/tra
 PROF_COPY_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/traffic/copy_{c} -o run "
                  "-- python3 $ROOT/bench.py --calibrate-copy")
 KERNEL_KEYS = {"front": "k_front", "units": "k_units", "tiles": "k_tiles", "classify": "k_classify_waves",
-               "index": "k_index", "emit": "k_emit"}
+               "index": "k_index", "emit": "k_emit", "store": "k_store_kv"}
 
 
 def write_profile_summaries(src):
