@@ -18,6 +18,10 @@ Contents
                           bit for bit.
   * ``store_ref``      -- reference of the paged K/V store with its fp8 e4m3fn
                           cast (the step before the pass).
+  * ``select_ref``     -- reference of block selection (index-key block scores,
+                          then top-k), the step that produces ``selected``; its
+                          scoring rule is a reading, parity unpinned against
+                          the pages.
 """
 from __future__ import annotations
 
