@@ -51,13 +51,22 @@ DESCRIPTIONS = {
                     "bf16 -> fp8 e4m3fn cache, page 64, slots shuffled over the cache",
 }
 STORE_METRIC = "paged K/V store GB/s (bytes read + written), bf16 -> fp8 e4m3fn"
+DESCRIPTIONS.update({
+    "select_decode": "block selection for 64 decode tokens (one per sequence), L~U[8192,32768], Hkv=8, d=128, "
+                     "page 64, fp8 e4m3fn index keys, bf16 index queries, top-16, causal, own block forced",
+    "select_prefill": "block selection for 1 seq, Tq=L=8192, Hkv=8, d=128, page 128, bf16 index keys and "
+                      "queries, top-16, causal, own block forced",
+})
+SELECT_METRIC = {"select_decode": ("index-key HBM GB/s, block selection (scores + top-k)", "GB/s"),
+                 "select_prefill": ("effective TFLOP/s, block selection (scores + top-k)", "TFLOP/s")}
 # Kernels whose summed average launch time the roofline is taken over. In
 # the prefill-shaped workloads the attention's MFMA work is split between
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
 DOMINANT = {"tiny": ["tiles"], "decode_gqa": ["front"], "decode_fp8": ["front"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
-            "dense_causal": ["tiles"], "kv_store_fp8": ["store"]}
+            "dense_causal": ["tiles"], "kv_store_fp8": ["store"], "select_decode": ["select"],
+            "select_prefill": ["select"]}
 
 
 def log(*a):
@@ -145,7 +154,7 @@ PROF_PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/tra
 PROF_COPY_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/traffic/copy_{c} -o run "
                  "-- python3 $ROOT/bench.py --calibrate-copy")
 KERNEL_KEYS = {"front": "k_front", "units": "k_units", "tiles": "k_tiles", "classify": "k_classify_waves",
-               "index": "k_index", "emit": "k_emit", "store": "k_store_kv"}
+               "index": "k_index", "emit": "k_emit", "store": "k_store_kv", "select": "k_select"}
 
 
 def write_profile_summaries(src):
@@ -291,6 +300,104 @@ def bench_store(args, torch, msa):
     print(json.dumps(res), flush=True)
 
 
+def bench_select(args, torch, msa):
+    """The block-selection benchmark: one step is one msa_select_blocks call."""
+    import workloads as W
+    from oracle import decode as odecode  # the CPU baseline leg only
+    from oracle import select_ref
+
+    dev = torch.device("cuda:0")
+    seed0 = W.SELECT_CONFIGS[args.workload]["seed"]
+    sets = []
+    for i in range(2):
+        si = W.SELECT_MAKERS[args.workload](seed=seed0 + 1000 * i, poison=False)
+        sets.append(dict(si=si, q=si.q_idx.to(dev), k=si.k_idx.to(dev),
+                         bt=torch.from_numpy(si.block_tables).to(dev),
+                         cu=torch.from_numpy(si.cu_seqlens_q).to(dev),
+                         used=torch.from_numpy(si.used_kv_lens).to(dev)))
+    si0 = sets[0]["si"]
+    kelem = si0.k_idx.element_size()
+    # algorithmic work of one step (set 0; set 1 is drawn the same way):
+    # every visible index key is read once per (sequence, KV head) and
+    # multiplied with each query token of the sequence that sees it
+    seq, pos = select_ref._positions(si0.cu_seqlens_q, si0.used_kv_lens, si0.Tq, si0.causal)
+    keys_read = sum(int(L) for s, L in enumerate(si0.used_kv_lens) if np.any(seq == s)) * si0.Hkv
+    pairs = int(np.sum(np.where(seq >= 0, pos + 1, 0))) * si0.Hkv
+    bytes_step = keys_read * 128 * kelem + si0.Tq * si0.Hkv * (256 + 4 * si0.topk)
+    flops_step = 2 * 128 * pairs
+    sel = torch.empty((si0.Tq, si0.Hkv, si0.topk), dtype=torch.int32, device=dev)
+
+    def step(i):
+        d = sets[i % 2]
+        msa.select_blocks(d["q"], d["k"], d["bt"], cu_seqlens_q=d["cu"], used_kv_lens=d["used"],
+                          page_size=si0.page_size, topk=si0.topk, causal=si0.causal, selected=sel)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    stop.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    msa.profile_enable(["select"])
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    k_ms, k_n = msa.profile_collect("select")
+    msa.profile_enable([])
+    k_avg = k_ms / max(k_n, 1)
+    decode = args.workload == "select_decode"
+    if decode:
+        achieved, peak, unit, bound = bytes_step / (k_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        value = bytes_step / (ms_step * 1e-3) / 1e9
+    else:
+        achieved, peak, unit, bound = flops_step / (k_avg * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        value = flops_step / (ms_step * 1e-3) / 1e12
+    roof = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                traffic=measured_traffic(args.workload, ["select"]), kernel="select",
+                kernel_avg_us=round(k_avg * 1e3, 2), launches=k_n)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on whole (token, KV head) rows of set 0, one sequence's
+        # pages de-paged per row, until 5 s have passed
+        rng = np.random.default_rng(11)
+        t_start, done_bytes, done_flops, n_rows = time.time(), 0, 0, 0
+        while time.time() - t_start < 5.0:
+            t = int(rng.integers(si0.Tq))
+            g = int(rng.integers(si0.Hkv))
+            s = int(seq[t])
+            L = int(si0.used_kv_lens[s])
+            n = -(-L // si0.page_size)
+            pages = torch.from_numpy(si0.block_tables[s, :n].astype(np.int64))
+            a = int(si0.cu_seqlens_q[s])
+            sub_k = odecode(si0.k_idx[pages][:, g:g + 1])
+            sub_q = odecode(si0.q_idx[a:int(si0.cu_seqlens_q[s + 1]), g:g + 1])
+            sc = select_ref.block_scores(sub_q, sub_k, np.arange(n, dtype=np.int32)[None, :], [0, sub_q.shape[0]],
+                                         [L], si0.page_size, si0.causal, tokens=[t - a])
+            select_ref.select_topk(sc[t - a:t - a + 1], si0.topk, [0, 1], [L], False, True)
+            done_bytes += L * 128 * kelem
+            done_flops += 2 * 128 * (int(pos[t]) + 1)
+            n_rows += 1
+        el = time.time() - t_start
+        cpu_val = done_bytes / el / 1e9 if decode else done_flops / el / 1e12
+        cpu = {"value": round(cpu_val, 5), "unit": unit, "cores": 1, "kind": "oracle",
+               "sample": f"{n_rows} random (token, KV head) rows of one input set, each scored over its "
+                         f"sequence's keys ({el:.1f} s of oracle time)"}
+    res = {"metric": SELECT_METRIC[args.workload][0], "value": round(value, 2), "unit": unit,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 x " + ("fp8" if kelem == 1 else "bf16") + " -> fp32", "data": "synthetic",
+           "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "query_tokens": si0.Tq,
+                      "index_key_bytes_per_step": bytes_step, "flops_per_step": flops_step,
+                      "parallelism": "single GPU", "input_sets": 2},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
 
@@ -376,6 +483,9 @@ def main():
     msa.load()
     if args.workload == "kv_store_fp8":
         bench_store(args, torch, msa)
+        return
+    if args.workload in SELECT_METRIC:
+        bench_select(args, torch, msa)
         return
     seed0 = W.CONFIGS[args.workload]["seed"]
 

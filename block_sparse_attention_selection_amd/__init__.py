@@ -28,6 +28,7 @@ from ._lib import (
     profile_collect,
     profile_enable,
     store_kv,
+    select_blocks,
     validate_inputs,
     version,
     widen_fp8,
@@ -38,6 +39,7 @@ __all__ = [
     "build_index",
     "widen_fp8",
     "store_kv",
+    "select_blocks",
     "validate_inputs",
     "version",
     "load",

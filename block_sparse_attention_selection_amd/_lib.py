@@ -79,6 +79,8 @@ def load():
         lib.msa_widen_fp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
         lib.msa_store_kv.restype = i32
         lib.msa_store_kv.argtypes = [T, T, T, T, T, i32, vp]
+        lib.msa_select_blocks.restype = i32
+        lib.msa_select_blocks.argtypes = [T, T, T, T, T, i32, i32, i32, i32, T, T, vp]
         lib.msa_validate_inputs.restype = i32
         lib.msa_validate_inputs.argtypes = [T, T, T, T, T, T, T, i32, i32, vp]
         lib.msa_profile_enable.restype = i32
@@ -170,6 +172,32 @@ def store_kv(k_new, v_new, loc, k_cache, v_cache, *, page_size: int):
     return k_cache, v_cache
 
 
+def select_blocks(q_idx, k_idx_cache, block_tables, *, cu_seqlens_q, used_kv_lens, page_size: int,
+                  topk: int, causal: bool = False, force_local: bool = True, selected=None,
+                  return_scores: bool = False, scores=None):
+    """Top-k block selection from index queries and the paged index K cache.
+
+    Returns ``selected [Tq, Hkv, topk]`` int32, or ``(selected, scores)`` with
+    ``scores [Tq, Hkv, ceil(max_pages * page_size / 128)]`` fp32. The scoring
+    rule and the order of the list are in include/msa_kvouter.h
+    (msa_select_blocks)."""
+    lib = load()
+    _device_check(q_idx, k_idx_cache, block_tables, cu_seqlens_q, used_kv_lens)
+    Tq, Hkv = q_idx.shape[0], q_idx.shape[1]
+    if selected is None:
+        selected = torch.empty((Tq, Hkv, int(topk)), dtype=torch.int32, device=q_idx.device)
+    if return_scores and scores is None:
+        nb = -(-block_tables.shape[1] * int(page_size) // 128)
+        scores = torch.empty((Tq, Hkv, nb), dtype=torch.float32, device=q_idx.device)
+    ds = [describe(x) for x in (q_idx, k_idx_cache, block_tables, cu_seqlens_q, used_kv_lens)]
+    dsel, dsc = describe(selected), describe(scores)
+    with torch.cuda.device(q_idx.device):
+        rc = lib.msa_select_blocks(*[_ref(d) for d in ds], int(page_size), int(bool(causal)), int(topk),
+                                   int(bool(force_local)), _ref(dsel), _ref(dsc), _stream(q_idx.device))
+    _check(rc)
+    return (selected, scores) if return_scores else selected
+
+
 def validate_inputs(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
                     page_size: int, causal: bool = False):
     """Synchronous check of the data-dependent preconditions; raises MsaError."""
@@ -213,7 +241,7 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
     return res
 
 
-KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3, "store": 4}
+KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3, "store": 4, "select": 5}
 
 
 def profile_enable(kernels=()):

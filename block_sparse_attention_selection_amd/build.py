@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmsa_kvouter.so")
 OBJDIR = os.path.join(ROOT, "_build", "msa")
-SOURCES = ["msa_api.hip", "msa_index.hip", "msa_forward.hip", "msa_tiles.hip", "msa_store.hip"]
+SOURCES = ["msa_api.hip", "msa_index.hip", "msa_forward.hip", "msa_tiles.hip", "msa_store.hip", "msa_select.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

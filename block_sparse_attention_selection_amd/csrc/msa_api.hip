@@ -333,7 +333,7 @@ struct ProfRec {
 std::mutex g_prof_mutex;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
-hipEvent_t g_open[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+hipEvent_t g_open[msa::kNumKernelIds] = {};
 
 hipEvent_t pooled_event() {
   if (!g_event_pool.empty()) {
@@ -373,12 +373,12 @@ int32_t msa_profile_enable(uint32_t kernel_mask) {
     g_event_pool.push_back(r.b);
   }
   g_prof.clear();
-  msa::g_profile_mask = kernel_mask & 0x1Fu;
+  msa::g_profile_mask = kernel_mask & ((1u << msa::kNumKernelIds) - 1u);
   return ok();
 }
 
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (!total_ms || !launches || kernel < 0 || kernel > 4) return fail(MSA_ERR_INVALID_ARGUMENT, "bad profile query");
+  if (!total_ms || !launches || kernel < 0 || kernel >= msa::kNumKernelIds) return fail(MSA_ERR_INVALID_ARGUMENT, "bad profile query");
   std::lock_guard<std::mutex> lk(g_prof_mutex);
   double tot = 0.0;
   int64_t n = 0;
@@ -590,6 +590,85 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
                                       v_cache->data, (int)N, (int)Hkv, page_size, NP, elem_of(k_new->dtype),
                                       k_cache->dtype == MSA_FP8_E4M3FN, (hipStream_t)stream);
   msa::profile_mark(msa::kKStore, false, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache, const msa_tensor* block_tables,
+                          const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens, int32_t page_size,
+                          int32_t causal, int32_t topk, int32_t force_local, msa_tensor* selected,
+                          msa_tensor* scores, void* stream) {
+  int32_t rc;
+  if ((rc = check_tensor(q_idx, "q_idx", 3, -1, 16))) return rc;
+  if (q_idx->dtype != MSA_BF16 && q_idx->dtype != MSA_FP16)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q_idx: dtype must be bf16 or fp16, got %s", dname(q_idx->dtype));
+  if ((rc = check_tensor(k_idx_cache, "k_idx_cache", 4, -1, 16))) return rc;
+  if (k_idx_cache->dtype != q_idx->dtype && k_idx_cache->dtype != MSA_FP8_E4M3FN)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_idx_cache: dtype %s must equal q_idx's (%s) or be fp8_e4m3fn",
+                dname(k_idx_cache->dtype), dname(q_idx->dtype));
+  if ((rc = check_tensor(block_tables, "block_tables", 2, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(cu_seqlens_q, "cu_seqlens_q", 1, MSA_INT64, 8))) return rc;
+  if ((rc = check_tensor(used_kv_lens, "used_kv_lens", 1, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(selected, "selected", 3, MSA_INT32, 4))) return rc;
+  if (scores && (rc = check_tensor(scores, "scores", 3, MSA_FP32, 4))) return rc;
+  if (page_size != 64 && page_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "page_size %d: only 64 and 128 are supported", page_size);
+  if ((causal != 0 && causal != 1) || (force_local != 0 && force_local != 1))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "causal and force_local must be 0 or 1");
+  const int64_t Tq = q_idx->shape[0], Hkv = q_idx->shape[1], B = used_kv_lens->shape[0];
+  const int64_t NP = k_idx_cache->shape[0], MP = block_tables->shape[1];
+  if (q_idx->shape[2] != 128 || k_idx_cache->shape[3] != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim must be 128");
+  if (k_idx_cache->shape[1] != Hkv)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_idx_cache: %lld KV heads, q_idx has %lld",
+                (long long)k_idx_cache->shape[1], (long long)Hkv);
+  if (k_idx_cache->shape[2] != page_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_idx_cache: page dimension %lld != page_size %d",
+                (long long)k_idx_cache->shape[2], page_size);
+  if (block_tables->shape[0] != B || cu_seqlens_q->shape[0] != B + 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "block_tables, cu_seqlens_q and used_kv_lens disagree on the batch size");
+  if (topk < 1 || topk > msa::kSelMaxBlocks)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "topk %d outside [1, %d]", topk, msa::kSelMaxBlocks);
+  if (selected->shape[0] != Tq || selected->shape[1] != Hkv || selected->shape[2] != topk)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "selected: expected [%lld, %lld, %d]", (long long)Tq, (long long)Hkv, topk);
+  const int64_t nb_cap = (MP * page_size + 127) / 128;
+  if (nb_cap > msa::kSelMaxBlocks)
+    return fail(MSA_ERR_UNSUPPORTED, "page tables reach %lld blocks; the selection scores at most %d per sequence",
+                (long long)nb_cap, msa::kSelMaxBlocks);
+  if (scores && (scores->shape[0] != Tq || scores->shape[1] != Hkv || scores->shape[2] != nb_cap))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "scores: expected [%lld, %lld, %lld]", (long long)Tq, (long long)Hkv,
+                (long long)nb_cap);
+  if (Tq >= (1ll << 31) / 16 || Hkv > 65535 || NP >= (1ll << 31) || B >= (1ll << 30) ||
+      Tq * Hkv * (int64_t)topk >= (1ll << 40))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large");
+  if (Tq == 0 || Hkv == 0) return ok();
+  if (B == 0) return fail(MSA_ERR_INVALID_ARGUMENT, "Tq > 0 with an empty batch");
+  msa::SelectParams p{};
+  p.q = q_idx->data;
+  p.k = k_idx_cache->data;
+  p.bt = (const int32_t*)block_tables->data;
+  p.cu = (const int64_t*)cu_seqlens_q->data;
+  p.used = (const int32_t*)used_kv_lens->data;
+  p.selected = (int32_t*)selected->data;
+  p.scores = scores ? (float*)scores->data : nullptr;
+  p.Tq = (int)Tq;
+  p.Hkv = (int)Hkv;
+  p.B = (int)B;
+  p.MP = (int)MP;
+  p.P = page_size;
+  p.num_pages = (int)NP;
+  p.nb_cap = (int)nb_cap;
+  p.topk = topk;
+  p.causal = causal;
+  p.force_local = force_local;
+  // 64-token tiles share each key row among four 16-token row blocks; they
+  // need 64 * nb_cap floats of LDS, so they serve page tables of at most 256
+  // blocks, and decode-shaped batches (a few queries per sequence) use
+  // 16-token tiles
+  const int nrb = (Tq > 4 * B && nb_cap <= 256) ? 4 : 1;
+  msa::profile_mark(msa::kKSelect, true, (hipStream_t)stream);
+  hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, nrb,
+                                    (hipStream_t)stream);
+  msa::profile_mark(msa::kKSelect, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -84,7 +84,8 @@ struct Params {
 };
 
 // kernel timing hooks (msa_api.hip): no-ops unless msa_profile_enable set the bit
-enum KernelId { kKIndex = 0, kKFront = 1, kKUnits = 2, kKTiles = 3, kKStore = 4 };
+enum KernelId { kKIndex = 0, kKFront = 1, kKUnits = 2, kKTiles = 3, kKStore = 4, kKSelect = 5 };
+constexpr int kNumKernelIds = 6;
 extern volatile uint32_t g_profile_mask;
 void profile_mark(int kernel, bool begin, hipStream_t st);
 
@@ -101,5 +102,20 @@ hipError_t launch_tiles(const Params& p, int q_elem, int kv_elem, int num_cu, hi
 hipError_t launch_widen_fp8(const void* in, int64_t n, int out_elem, void* out, hipStream_t st);
 hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, void* kc, void* vc, int N, int Hkv,
                            int P, int64_t num_pages, int in_elem, bool fp8_cache, hipStream_t st);
+
+// block selection (msa_select.hip)
+constexpr int kSelMaxBlocks = 1024;  // blocks per sequence the selection can score (131072 tokens)
+struct SelectParams {
+  const void* q;          // [Tq, Hkv, 128] index queries, 16-bit
+  const void* k;          // [num_pages, Hkv, P, 128] index keys, q's type or e4m3fn
+  const int32_t* bt;      // [B, MP]
+  const int64_t* cu;      // [B + 1]
+  const int32_t* used;    // [B]
+  int32_t* selected;      // [Tq, Hkv, topk]
+  float* scores;          // [Tq, Hkv, nb_cap] or null
+  int Tq, Hkv, B, MP, P, num_pages, nb_cap, topk, causal, force_local;
+};
+// nrb: row blocks of 16 tokens per workgroup (1 or 4)
+hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, int nrb, hipStream_t st);
 
 }  // namespace msa

@@ -205,6 +205,47 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
                      msa_tensor* k_cache, msa_tensor* v_cache, int32_t page_size, void* stream);
 
 /*
+ * msa_select_blocks -- block selection, the step that produces `selected`
+ * (the MSA README, "How It Works" and "Highlighted Details": sparse top-k
+ * selection; sglang pull request "Speed up MiniMax-M3 sparse attention on
+ * Hopper", "Changes to existing code": the sparse index K cache, fp8 with an
+ * fp8 KV cache). The pages do not give the scoring; this call implements:
+ *
+ *   score(t, g, b) = max over visible tokens j of block b (tokens
+ *                    [128 b, 128 b + 128)) of q_idx[t, g, :] . k_idx(s, g, j, :)
+ *
+ * with j visible when j < used_kv_lens[s] and, when causal,
+ * j <= pos(t) = used_kv_lens[s] - Tq_s + (t - cu_seqlens_q[s]) (the
+ * attention pass's alignment). selected[t, g, :] lists the token's own block
+ * first when force_local is 1 (the block of pos(t) when causal, the last
+ * block when not), then the other blocks by descending score, equal scores by
+ * ascending block id; -1 pads the rest. Blocks without a visible token and
+ * NaN scores are never selected. Scores are accumulated in fp32 by MFMA.
+ *
+ *   q_idx         [Tq, Hkv, 128] bf16 or fp16, one index query per (token,
+ *                 KV head)
+ *   k_idx_cache   [num_pages, Hkv, page_size, 128] index keys in q_idx's
+ *                 dtype or fp8_e4m3fn (scale 1), read through block_tables
+ *   block_tables, cu_seqlens_q, used_kv_lens, page_size, causal: as for
+ *                 msa_kvouter_attention (the same preconditions)
+ *   topk          1 .. 1024, the width of `selected`
+ *   selected      [Tq, Hkv, topk] int32, written
+ *   scores        NULL, or [Tq, Hkv, nb] fp32 with nb = ceil(max_pages *
+ *                 page_size / 128): written with every block's score (-inf
+ *                 for blocks without a visible token)
+ *
+ * Sequences may reach at most 1024 blocks (nb <= 1024, else
+ * MSA_ERR_UNSUPPORTED). All buffers are caller-owned device memory; the call
+ * validates descriptors on the host, enqueues one kernel on `stream` and
+ * returns. Errors as for msa_kvouter_attention; Tq == 0 enqueues nothing.
+ */
+int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache,
+                          const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                          const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                          int32_t topk, int32_t force_local, msa_tensor* selected,
+                          msa_tensor* scores, void* stream);
+
+/*
  * msa_validate_inputs -- synchronous check of the data-dependent
  * preconditions of msa_kvouter_attention (copies the small index arrays to
  * the host and waits for `stream`). Returns MSA_OK or MSA_ERR_PRECONDITION
@@ -232,6 +273,7 @@ enum {
   MSA_KERNEL_UNITS = 2, /* KV-outer units: partial O and LSE per residual slot */
   MSA_KERNEL_TILES = 3, /* listed tiles: chain blocks, LSE merge of the partials */
   MSA_KERNEL_STORE = 4, /* msa_store_kv */
+  MSA_KERNEL_SELECT = 5, /* msa_select_blocks */
 };
 int32_t msa_profile_enable(uint32_t kernel_mask);
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches);

@@ -53,12 +53,14 @@ def _positions(cu, used, Tq, causal):
     return seq, pos
 
 
-def block_scores(q_idx, k_cache, block_tables, cu, used, page_size, causal, nb_cap=None):
+def block_scores(q_idx, k_cache, block_tables, cu, used, page_size, causal, nb_cap=None, tokens=None):
     """float64 scores [Tq, Hkv, nb_cap] of the rule in the module docstring.
 
     q_idx: [Tq, Hkv, 128] and k_cache: [NP, Hkv, P, 128], float arrays holding
     the stored values exactly; block_tables: [B, MP]; cu: [B + 1]; used: [B].
     nb_cap defaults to ceil(MP * P / 128), the most blocks a sequence can hold.
+    With ``tokens`` (query token ids) only those rows are computed; the
+    others stay -inf.
     """
     q = np.asarray(q_idx, dtype=np.float64)
     kc = np.asarray(k_cache, dtype=np.float64)
@@ -69,9 +71,10 @@ def block_scores(q_idx, k_cache, block_tables, cu, used, page_size, causal, nb_c
         nb_cap = -(-bt.shape[1] * P // BLK)
     out = np.full((Tq, Hkv, nb_cap), -np.inf)
     seq, pos = _positions(cu, used, Tq, causal)
+    wanted = np.ones(Tq, dtype=bool) if tokens is None else np.isin(np.arange(Tq), np.asarray(tokens))
     for s in range(len(used)):
         L = int(used[s])
-        toks = np.nonzero(seq == s)[0]
+        toks = np.nonzero((seq == s) & wanted)[0]
         if L <= 0 or toks.size == 0:
             continue
         j = np.arange(L)

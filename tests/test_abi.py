@@ -177,3 +177,30 @@ def test_store_kv_argument_checks():
     k, v, loc, kc, vc = args()
     assert lib.msa_store_kv(None, r(v), r(loc), r(kc), r(vc), 64, None) == INV
     assert call_store(args(N=0)) == 0                                           # nothing to store
+
+
+def test_select_blocks_argument_checks():
+    lib = msa.load()
+    r = ctypes.byref
+
+    def args(Tq=4, Hkv=2, NP=8, P=64, B=2, MP=4, topk=4, q_dt=msa.MSA_BF16, k_dt=msa.MSA_FP8_E4M3FN, sel=None,
+             sc=None):
+        return [desc([Tq, Hkv, 128], q_dt), desc([NP, Hkv, P, 128], k_dt), desc([B, MP], msa.MSA_INT32),
+                desc([B + 1], msa.MSA_INT64), desc([B], msa.MSA_INT32), desc(sel or [Tq, Hkv, topk], msa.MSA_INT32),
+                None if sc is None else desc(sc, msa.MSA_FP32)]
+
+    def call_sel(a, P=64, causal=1, topk=4, force=1):
+        q, k, bt, cu, used, sel, sc = a
+        return lib.msa_select_blocks(r(q), r(k), r(bt), r(cu), r(used), P, causal, topk, force, r(sel),
+                                     r(sc) if sc is not None else None, None)
+
+    assert call_sel(args(q_dt=msa.MSA_FP8_E4M3FN)) == INV                  # fp8 index queries
+    assert call_sel(args(k_dt=msa.MSA_FP16)) == INV                        # keys of another 16-bit type
+    assert call_sel(args(), topk=0) == INV                                 # topk outside [1, 1024]
+    assert call_sel(args(topk=5)) == INV                                   # selected width != topk
+    assert call_sel(args(sc=[4, 2, 3])) == INV                             # scores: nb = 4*64/128 = 2
+    assert call_sel(args(MP=2100)) == UNS                                  # beyond 1024 blocks
+    assert call_sel(args(P=128)) == INV                                    # page dim != page_size
+    assert call_sel(args(), causal=2) == INV
+    assert call_sel(args(Tq=0)) == 0                                       # nothing to select
+    assert call_sel(args(sc=[4, 2, 2]), P=32) == UNS                       # page size

@@ -422,3 +422,83 @@ def compact_cache(wl: Workload, heads=None):
     bt = wl.block_tables.astype(np.int64)
     bt_c = np.where(bt >= 0, remap[np.clip(bt, 0, None)], -1).astype(np.int32)
     return k, v, bt_c
+
+
+# ----------------------------------------------------------------------------
+# block selection inputs: index queries and a paged index K cache
+# ----------------------------------------------------------------------------
+@dataclass
+class SelectionInputs:
+    name: str
+    seed: int
+    page_size: int
+    causal: bool
+    topk: int
+    cu_seqlens_q: np.ndarray     # [B+1] int64
+    used_kv_lens: np.ndarray     # [B] int32
+    block_tables: np.ndarray     # [B, max_pages] int32 (-1 = unused)
+    q_idx: torch.Tensor          # [Tq, Hkv, 128] cpu, 16-bit
+    k_idx: torch.Tensor          # [num_pages, Hkv, P, 128] cpu, q's dtype or e4m3fn
+
+    @property
+    def Tq(self):
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def Hkv(self):
+        return int(self.q_idx.shape[1])
+
+
+SELECT_CONFIGS = {
+    "select_decode": dict(seed=1008),
+    "select_prefill": dict(seed=1009),
+}
+
+
+def make_selection(seed, tq_per_seq, kv_lens, Hkv, page_size, topk, causal=True, q_dtype=torch.bfloat16,
+                   key_dtype=None, poison=True, extra_pages=2, name="custom"):
+    """Index queries and keys, N(0,1), for sequences of the given query and key counts.
+
+    Every page a sequence needs is drawn (the selection reads all of its
+    keys), one seeded stream per sequence; rows at or beyond a sequence's
+    length, and the extra pages no table lists, hold NaN poison (zeros when
+    ``poison`` is off).
+    """
+    key_dtype = key_dtype or q_dtype
+    rng = np.random.default_rng([seed, 0])
+    used = np.asarray(kv_lens, dtype=np.int32)
+    tq = np.asarray(tq_per_seq, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(tq)]).astype(np.int64)
+    bt, NP = _page_tables(rng, used, page_size, extra_pages=extra_pages)
+    k_idx = filled((NP, Hkv, page_size, HEAD_DIM), key_dtype, poison)
+    for s, L in enumerate(used):
+        n = (int(L) + page_size - 1) // page_size
+        if n == 0:
+            continue
+        gen = torch.Generator().manual_seed(int(seed) * 1_000_003 + 7919 * (s + 1))
+        vals = torch.randn((int(L), Hkv, HEAD_DIM), generator=gen)
+        rows = vals.clamp(-448, 448).to(key_dtype) if key_dtype == torch.float8_e4m3fn else vals.to(key_dtype)
+        full = filled((n * page_size, Hkv, HEAD_DIM), key_dtype, poison)
+        full[:L] = rows
+        k_idx[torch.from_numpy(bt[s, :n].astype(np.int64))] = full.view(n, page_size, Hkv, HEAD_DIM).transpose(1, 2)
+    q = np.random.default_rng([seed, 2]).standard_normal((int(cu[-1]), Hkv, HEAD_DIM), dtype=np.float32)
+    return SelectionInputs(name, seed, page_size, causal, topk, cu, used, bt, to_dtype(q, q_dtype), k_idx)
+
+
+def make_select_decode(seed=1008, poison=True, batch=64):
+    """64 decode tokens (one per sequence), L ~ U{8192..32768}, Hkv 8, page 64,
+    fp8 e4m3fn index keys, bf16 index queries, top-16, causal."""
+    rng = np.random.default_rng([seed, 9])
+    used = rng.integers(8192, 32769, size=batch)
+    return make_selection(seed, np.ones(batch, np.int64), used, 8, 64, 16, True, torch.bfloat16,
+                          torch.float8_e4m3fn, poison, name="select_decode")
+
+
+def make_select_prefill(seed=1009, poison=True, seqlen=8192):
+    """One sequence of seqlen tokens, all of them queries, Hkv 8, page 128, bf16
+    index keys and queries, top-16, causal."""
+    return make_selection(seed, [seqlen], [seqlen], 8, 128, 16, True, torch.bfloat16, torch.bfloat16,
+                          poison, name="select_prefill")
+
+
+SELECT_MAKERS = {"select_decode": make_select_decode, "select_prefill": make_select_prefill}
