@@ -638,7 +638,7 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
     return fail(MSA_ERR_INVALID_ARGUMENT, "scores: expected [%lld, %lld, %lld]", (long long)Tq, (long long)Hkv,
                 (long long)nb_cap);
   if (Tq >= (1ll << 31) / 16 || Hkv > 65535 || NP >= (1ll << 31) || B >= (1ll << 30) ||
-      Tq * Hkv * (int64_t)topk >= (1ll << 40))
+      Tq * Hkv * (int64_t)topk >= (1ll << 40) || (Tq / 16 + B + 1) * Hkv >= (1ll << 31))
     return fail(MSA_ERR_UNSUPPORTED, "problem too large");
   if (Tq == 0 || Hkv == 0) return ok();
   if (B == 0) return fail(MSA_ERR_INVALID_ARGUMENT, "Tq > 0 with an empty batch");

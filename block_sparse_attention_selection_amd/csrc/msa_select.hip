@@ -15,8 +15,9 @@
 // scores by ascending block id, padded with -1. Blocks without a visible
 // token, and NaN scores, are never selected.
 //
-// Work: one workgroup of 4 waves per (tile of 16 or 64 consecutive tokens of
-// one sequence, KV head). The waves split the tile's blocks; each computes
+// Work: one workgroup per (tile of consecutive tokens of one sequence, KV
+// head): 64-token tiles of 4 waves, or 16-token tiles of 8 or 16 waves for
+// decode-shaped batches. The waves split the tile's blocks; each computes
 // S^T = K . Q^T with 16x16x32 MFMA for 16 keys at a time, K read from the
 // paged cache straight into operand registers (a lane reads 32 contiguous
 // dims of one key row), and max-pools it into a [tokens][blocks] fp32 table
@@ -27,8 +28,6 @@
 
 namespace msa {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelPerLane = kSelMaxBlocks / 64;  // score registers per lane in the top-k phase
 
 // 32 consecutive index-key dims of one row, as four 8-value MFMA fragments
 template <typename QT, typename KT>
@@ -78,14 +77,20 @@ __device__ __forceinline__ bool sel_better(float v, int b, float v2, int b2) {
   return v > v2 || (v == v2 && b < b2);
 }
 
-template <typename QT, typename KT, int NRB>
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectParams p) {
+// NRB: 16-token row blocks per tile; NW: waves; NPL: score registers per
+// lane in the top-k phase (64 * NPL >= nb_cap)
+template <typename QT, typename KT, int NRB, int NW, int NPL>
+__global__ __launch_bounds__(64 * NW) void k_select(SelectParams p) {
   constexpr int T = 16 * NRB;  // tokens per tile
   extern __shared__ float s_sc[];  // [T][nb_cap]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.y;
+  // workgroup i runs on XCD i % 8: KV head i % Hkv keeps each head's keys in
+  // the L2 of the same XCDs; tiles go last to first, so the tiles that see
+  // the most blocks (late in a causal sequence) start first
+  const int g = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int tile = (int)(gridDim.x / (unsigned)p.Hkv) - 1 - (int)(blockIdx.x / (unsigned)p.Hkv);
   int64_t t0 = 0;
-  const int s = wave_tile_of(p.cu, p.B, p.Tq, T, blockIdx.x, &t0);
+  const int s = wave_tile_of(p.cu, p.B, p.Tq, T, tile, &t0);
   if (s < 0) return;
   const int64_t c0 = p.cu[s], c1 = p.cu[s + 1];
   const int64_t tq_end = min(c1, (int64_t)p.Tq);
@@ -116,74 +121,97 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectParams p) {
         for (int st = 0; st < 4; ++st) qf[rb][st] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    int64_t posr[NRB];
+    // positions as int32 (below L < 2^31; -1 stands for "sees nothing")
+    int posr[NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) posr[rb] = pos_of(rb * 16 + col);
+    for (int rb = 0; rb < NRB; ++rb) posr[rb] = (int)max(pos_of(rb * 16 + col), (int64_t)-1);
+    const int pos_lo = (int)max(pos_of(0), (int64_t)-1);  // the tile's first row sees the fewest keys
     const int32_t* bt = p.bt + (int64_t)s * p.MP;
-    // the key row this lane reads for group gi of this wave's blocks
-    auto key_ptr = [&](int j) -> const void* {
-      if (j >= L) return nullptr;  // L <= MP * P, so the table read below stays inside the row
-      const int page = bt[j / p.P];
-      if (page < 0 || page >= p.num_pages) return nullptr;
-      const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + (j % p.P);
-      return (const uint8_t*)p.k + row * KeyBytes<KT>::kRow;
+    // physical pages of block b's two 64-token halves (the same page when P
+    // is 128); wave-uniform, -1 where the half holds no token below L
+    auto pages_of = [&](int b, int& pa, int& pb) {
+      const int j0 = 128 * b;
+      pa = j0 < L ? bt[j0 / p.P] : -1;
+      pb = p.P == 64 ? (j0 + 64 < L ? bt[(j0 + 64) / p.P] : -1) : pa;
     };
-    const int nblk_w = nscan > wave ? (nscan - wave + 3) / 4 : 0;  // blocks wave, wave + 4, ...
-    const int ngroups = nblk_w * 8;
-    KeyRow<QT, KT> cur, nxt;
-    nxt.zero();
-    auto fetch = [&](KeyRow<QT, KT>& kr, int gi) {
-      const int b = wave + 4 * (gi >> 3);
-      const int j = 128 * b + 16 * (gi & 7) + col;
-      const void* ptr = key_ptr(j);
-      if (ptr)
-        kr.load(ptr, h);
-      else
+    // group kg of block b: keys 128 b + 16 kg + [0, 16); a lane reads key
+    // (lane & 15), dims 32 (lane >> 4) + [0, 32)
+    auto fetch = [&](KeyRow<QT, KT>& kr, int b, int kg, int pa, int pb) {
+      const int j = 128 * b + 16 * kg + col;
+      const int page = kg >= 4 ? pb : pa;
+      if (j < L && page >= 0 && page < p.num_pages) {
+        const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + ((16 * kg + col) & (p.P - 1));
+        kr.load((const uint8_t*)p.k + row * KeyBytes<KT>::kRow, h);
+      } else {
         kr.zero();
-    };
-    if (ngroups > 0) fetch(cur, 0);
-    float m[NRB];
-    for (int gi = 0; gi < ngroups; ++gi) {
-      if (gi + 1 < ngroups) fetch(nxt, gi + 1);
-      const int b = wave + 4 * (gi >> 3);
-      if ((gi & 7) == 0) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) m[rb] = -INFINITY;
       }
-      const int jbase = 128 * b + 16 * (gi & 7) + 4 * h;  // keys of this lane's accumulator rows
+    };
+    const int nblk_w = nscan > wave ? (nscan - wave + NW - 1) / NW : 0;  // blocks wave, wave + NW, ...
+    // three groups in flight: the one in use and the next two
+    KeyRow<QT, KT> k0, k1, k2;
+    k2.zero();
+    int pa = -1, pb = -1, na = -1, nb2 = -1;
+    if (nblk_w > 0) {
+      pages_of(wave, pa, pb);
+      fetch(k0, wave, 0, pa, pb);
+      fetch(k1, wave, 1, pa, pb);
+    }
+    for (int bi = 0, b = wave; bi < nblk_w; ++bi, b += NW) {
+      const bool has_next = bi + 1 < nblk_w;
+      if (has_next) pages_of(b + NW, na, nb2);
+      // a block every key of which every row of the tile sees needs no mask
+      const bool full = 128 * b + 127 < L && 128 * b + 127 <= pos_lo;
+      float m[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) m[rb] = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < 8; ++kg) {
+        if (kg < 6)
+          fetch(k2, b, kg + 2, pa, pb);
+        else if (has_next)
+          fetch(k2, b + NW, kg - 6, na, nb2);
+        const int jbase = 128 * b + 16 * kg + 4 * h;  // keys of this lane's accumulator rows
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(k0.frag(st), qf[rb][st], acc);
+          float v;
+          if (full) {
+            v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+          } else {
+            v = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = jbase + i;
+              v = fmaxf(v, (j < L && j <= posr[rb]) ? acc[i] : -INFINITY);
+            }
+          }
+          m[rb] = fmaxf(m[rb], v);  // this lane's keys; the lane groups are combined once per block
+        }
+        k0 = k1;
+        k1 = k2;
+      }
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(cur.frag(st), qf[rb][st], acc);
-        float v = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = jbase + i;
-          const bool vis = j < L && (int64_t)j <= posr[rb];
-          v = fmaxf(v, vis ? acc[i] : -INFINITY);
-        }
-        m[rb] = fmaxf(m[rb], max_over_groups(v));
+        const float mb = max_over_groups(m[rb]);
+        if (h == 0 && rb * 16 + col < ntok) s_sc[(rb * 16 + col) * p.nb_cap + b] = mb;
       }
-      if ((gi & 7) == 7 && h == 0) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          if (rb * 16 + col < ntok) s_sc[(rb * 16 + col) * p.nb_cap + b] = m[rb];
-      }
-      cur = nxt;
+      pa = na;
+      pb = nb2;
     }
   }
   __syncthreads();
 
-  // top-k per row: rows wave, wave + 4, ...
-  for (int r = wave; r < ntok; r += 4) {
+  // top-k per row: rows wave, wave + NW, ...
+  for (int r = wave; r < ntok; r += NW) {
     const int64_t t = t0 + r;
     const int64_t pos = pos_of(r);
     const int nr = (L <= 0 || pos < 0) ? 0 : (int)min((int64_t)nb, pos / 128 + 1);
     int32_t* out = p.selected + (t * p.Hkv + g) * (int64_t)p.topk;
-    float v[kSelPerLane];
+    float v[NPL];
 #pragma unroll
-    for (int i = 0; i < kSelPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
       const int b = lane + 64 * i;
       float x = b < nr ? s_sc[r * p.nb_cap + b] : -INFINITY;
       if (p.scores && b < p.nb_cap) p.scores[(t * p.Hkv + g) * (int64_t)p.nb_cap + b] = x;
@@ -194,25 +222,50 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectParams p) {
       const int lb = (int)(pos / 128);  // the token's own block (the last one when not causal)
       float own = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kSelPerLane; ++i)
+      for (int i = 0; i < NPL; ++i)
         if (lane + 64 * i == lb) own = v[i];
       if (__shfl(own, lb & 63, 64) > -INFINITY) {  // it holds the token itself: only a NaN score fails
 #pragma unroll
-        for (int i = 0; i < kSelPerLane; ++i)
+        for (int i = 0; i < NPL; ++i)
           if (lane + 64 * i == lb) v[i] = -INFINITY;
         if (lane == 0) out[0] = lb;
         k = 1;
       }
     }
-    for (; k < p.topk; ++k) {
-      float bv = -INFINITY;
-      int bb = 0x7FFFFFFF;
+    if constexpr (NPL == 1) {
+      // at most 64 blocks, one per lane: every block's rank among the others
+      // in one pass of wave broadcasts, then the blocks ranked below the
+      // free places write themselves
+      int rank = 0;
+      for (int m = 0; m < 64; ++m) {
+        const float vm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), m));
+        rank += sel_better(vm, m, v[0], lane) ? 1 : 0;
+      }
+      const int free_places = p.topk - k;
+      if (v[0] > -INFINITY && rank < free_places) out[k + rank] = lane;
+      int nvalid = __popcll(__ballot(v[0] > -INFINITY));
+      k += min(nvalid, free_places);
+      for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
+      continue;
+    }
+    // each lane keeps its own best (value, block); a round reduces them over
+    // the wave and only the winning lane rescans its registers
+    auto lane_best = [&](float& bv, int& bb) {
+      bv = -INFINITY;
+      bb = 0x7FFFFFFF;
 #pragma unroll
-      for (int i = 0; i < kSelPerLane; ++i)
+      for (int i = 0; i < NPL; ++i)
         if (sel_better(v[i], lane + 64 * i, bv, bb)) {
           bv = v[i];
           bb = lane + 64 * i;
         }
+    };
+    float lv;
+    int lbk;
+    lane_best(lv, lbk);
+    for (; k < p.topk; ++k) {
+      float bv = lv;
+      int bb = lbk;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float ov = __shfl_xor(bv, off, 64);
@@ -224,24 +277,48 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectParams p) {
       }
       if (bv == -INFINITY) break;  // every lane agrees: nothing left to select
       if (lane == 0) out[k] = bb;
+      if ((bb & 63) == lane) {
 #pragma unroll
-      for (int i = 0; i < kSelPerLane; ++i)
-        if (lane + 64 * i == bb) v[i] = -INFINITY;
+        for (int i = 0; i < NPL; ++i)
+          if (lane + 64 * i == bb) v[i] = -INFINITY;
+        lane_best(lv, lbk);
+      }
     }
     for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
   }
 }
 
+template <typename QT, typename KT, int NRB, int NW>
+static void launch_select_npl(const SelectParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  const dim3 block(64 * NW);
+  if (p.nb_cap <= 64)
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 1>), grid, block, lds, st, p);
+  else if (p.nb_cap <= 128)
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 2>), grid, block, lds, st, p);
+  else if (p.nb_cap <= 256)
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 4>), grid, block, lds, st, p);
+  else if (p.nb_cap <= 512)
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 8>), grid, block, lds, st, p);
+  else
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, kSelMaxBlocks / 64>), grid, block, lds, st, p);
+}
+
+// nrb 4: 64-token tiles of 4 waves (prefill-shaped batches); nrb 1: 16-token
+// tiles of 16 (fp8 keys) or 8 waves, which split a long sequence's blocks
+// among more loads in flight (decode-shaped batches)
 template <typename QT, typename KT>
 static hipError_t launch_select_t(const SelectParams& p, int nrb, hipStream_t st) {
   const int T = 16 * nrb;
   const int64_t tiles = ((int64_t)p.Tq + T - 1) / T + p.B;  // each sequence adds at most one partial tile
-  const dim3 grid((unsigned)tiles, (unsigned)p.Hkv), block(kSelThreads);
+  const dim3 grid((unsigned)(tiles * p.Hkv));
   const size_t lds = (size_t)T * p.nb_cap * sizeof(float);
+  // 16-bit keys need twice the registers in flight: 8 waves keep them
+  // within a 1024-thread workgroup's share
+  constexpr int kNarrowWaves = sizeof(KT) == 1 ? 16 : 8;
   if (nrb == 4)
-    hipLaunchKernelGGL((k_select<QT, KT, 4>), grid, block, lds, st, p);
+    launch_select_npl<QT, KT, 4, 4>(p, grid, lds, st);
   else
-    hipLaunchKernelGGL((k_select<QT, KT, 1>), grid, block, lds, st, p);
+    launch_select_npl<QT, KT, 1, kNarrowWaves>(p, grid, lds, st);
   return hipGetLastError();
 }
 

@@ -95,6 +95,8 @@ CASES = [
     ([200, 130], [1500, 4100], 1, 128, 12, True, torch.bfloat16),           # 64-token tiles (Tq > 4B)
     ([200, 130], [1500, 4100], 3, 64, 5, True, torch.float8_e4m3fn),
     ([3, 0, 5, 1], [129, 700, 0, 64], 2, 64, 40, True, torch.bfloat16),     # empty seqs, topk > blocks
+    ([2, 3], [10000, 9000], 1, 64, 8, True, torch.float8_e4m3fn),          # 65..128 blocks a row
+    ([1, 2], [100000, 20000], 1, 128, 16, True, torch.bfloat16),           # up to 782 blocks a row
 ]
 
 
