@@ -162,9 +162,10 @@ def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens
 
 def store_kv(k_new, v_new, loc, k_cache, v_cache, *, page_size: int):
     """Store new tokens' K and V rows into the paged caches (in place); see
-    include/msa_kvouter.h (msa_store_kv) for the contract."""
+    include/msa_kvouter.h (msa_store_kv) for the contract. v_new and v_cache
+    may both be None (K rows only, e.g. an index key cache)."""
     lib = load()
-    _device_check(k_new, v_new, loc, k_cache, v_cache)
+    _device_check(*[x for x in (k_new, v_new, loc, k_cache, v_cache) if x is not None])
     ds = [describe(x) for x in (k_new, v_new, loc, k_cache, v_cache)]
     with torch.cuda.device(k_new.device):
         rc = lib.msa_store_kv(*[_ref(d) for d in ds], int(page_size), _stream(k_new.device))

@@ -556,18 +556,20 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
   if ((rc = check_tensor(k_new, "k_new", 3, -1, 16))) return rc;
   if (k_new->dtype != MSA_BF16 && k_new->dtype != MSA_FP16)
     return fail(MSA_ERR_INVALID_ARGUMENT, "k_new: dtype must be bf16 or fp16, got %s", dname(k_new->dtype));
-  if ((rc = check_tensor(v_new, "v_new", 3, k_new->dtype, 16))) return rc;
+  if (!v_new != !v_cache) return fail(MSA_ERR_INVALID_ARGUMENT, "v_new and v_cache: pass both or neither");
+  const bool has_v = v_new != nullptr;
+  if (has_v && (rc = check_tensor(v_new, "v_new", 3, k_new->dtype, 16))) return rc;
   if ((rc = check_tensor(loc, "loc", 1, MSA_INT64, 8))) return rc;
   if ((rc = check_tensor(k_cache, "k_cache", 4, -1, 16))) return rc;
-  if ((rc = check_tensor(v_cache, "v_cache", 4, k_cache->dtype, 16))) return rc;
+  if (has_v && (rc = check_tensor(v_cache, "v_cache", 4, k_cache->dtype, 16))) return rc;
   if (k_cache->dtype != k_new->dtype && k_cache->dtype != MSA_FP8_E4M3FN)
     return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: dtype %s must equal k_new's (%s) or be fp8_e4m3fn",
                 dname(k_cache->dtype), dname(k_new->dtype));
   if (page_size != 64 && page_size != 128)
     return fail(MSA_ERR_UNSUPPORTED, "page_size %d: only 64 and 128 are supported", page_size);
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; has_v && i < 3; ++i)
     if (v_new->shape[i] != k_new->shape[i]) return fail(MSA_ERR_INVALID_ARGUMENT, "v_new: shape differs from k_new");
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; has_v && i < 4; ++i)
     if (v_cache->shape[i] != k_cache->shape[i])
       return fail(MSA_ERR_INVALID_ARGUMENT, "v_cache: shape differs from k_cache");
   if (k_new->shape[2] != 128 || k_cache->shape[3] != 128)
@@ -586,8 +588,9 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
     return fail(MSA_ERR_UNSUPPORTED, "problem too large");
   if (N == 0) return ok();
   msa::profile_mark(msa::kKStore, true, (hipStream_t)stream);
-  hipError_t e = msa::launch_store_kv(k_new->data, v_new->data, (const int64_t*)loc->data, k_cache->data,
-                                      v_cache->data, (int)N, (int)Hkv, page_size, NP, elem_of(k_new->dtype),
+  hipError_t e = msa::launch_store_kv(k_new->data, has_v ? v_new->data : nullptr, (const int64_t*)loc->data,
+                                      k_cache->data, has_v ? v_cache->data : nullptr, (int)N, (int)Hkv, page_size,
+                                      NP, elem_of(k_new->dtype),
                                       k_cache->dtype == MSA_FP8_E4M3FN, (hipStream_t)stream);
   msa::profile_mark(msa::kKStore, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

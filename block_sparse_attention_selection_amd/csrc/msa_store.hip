@@ -35,9 +35,9 @@ constexpr int kStoreUnroll = 4;  // 32-byte pieces per thread, all loads issued 
 template <typename IT, bool kFp8>
 __global__ __launch_bounds__(kStoreThreads) void k_store_kv(const uint16_t* kn, const uint16_t* vn,
                                                             const int64_t* loc, void* kc, void* vc, int N,
-                                                            int Hkv, int P, int64_t nslots) {
+                                                            int Hkv, int P, int64_t nslots, int ntensors) {
   // piece p of a tensor: row p >> 3 = (token, KV head), 16 values at 16 * (p & 7);
-  // pieces [0, per) are K's, [per, 2 per) V's
+  // pieces [0, per) are K's, [per, 2 per) V's (ntensors = 2)
   const int per = N * Hkv * 8;
   const int base = blockIdx.x * (kStoreThreads * kStoreUnroll) + threadIdx.x;
   u32x4 in[kStoreUnroll][2];
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kStoreThreads) void k_store_kv(const uint16_t* kn, 
   for (int j = 0; j < kStoreUnroll; ++j) {
     dst[j] = -1;
     const int gp = base + j * kStoreThreads;
-    if (gp >= 2 * per) continue;
+    if (gp >= ntensors * per) continue;
     const bool is_v = gp >= per;
     const int r = is_v ? gp - per : gp;
     const int row = r >> 3, piece = r & 7;
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kStoreThreads) void k_store_kv(const uint16_t* kn, 
 
 hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, void* kc, void* vc, int N, int Hkv,
                            int P, int64_t num_pages, int in_elem, bool fp8_cache, hipStream_t st) {
-  const int64_t pieces = 2 * (int64_t)N * Hkv * 8;
+  const int ntensors = vn ? 2 : 1;  // no V: the K rows only (an index key cache)
+  const int64_t pieces = ntensors * (int64_t)N * Hkv * 8;
   if (pieces == 0) return hipSuccess;
   const int64_t per_block = kStoreThreads * kStoreUnroll;
   const dim3 grid((unsigned)((pieces + per_block - 1) / per_block)), block(kStoreThreads);
@@ -94,14 +95,14 @@ hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, v
   const uint16_t* v16 = (const uint16_t*)vn;
   if (in_elem == kElemBF16) {
     if (fp8_cache)
-      hipLaunchKernelGGL((k_store_kv<bf16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots);
+      hipLaunchKernelGGL((k_store_kv<bf16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
     else
-      hipLaunchKernelGGL((k_store_kv<bf16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots);
+      hipLaunchKernelGGL((k_store_kv<bf16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
   } else {
     if (fp8_cache)
-      hipLaunchKernelGGL((k_store_kv<f16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots);
+      hipLaunchKernelGGL((k_store_kv<f16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
     else
-      hipLaunchKernelGGL((k_store_kv<f16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots);
+      hipLaunchKernelGGL((k_store_kv<f16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
   }
   return hipGetLastError();
 }

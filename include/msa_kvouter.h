@@ -195,7 +195,9 @@ int32_t msa_widen_fp8(const void* in, int64_t n, int32_t out_dtype, void* out, v
  *   page_size     64 or 128
  *
  * Row (i, g) of k_new / v_new goes to cache[loc[i] / page_size, g,
- * loc[i] % page_size, :]. Two new tokens with the same slot race (the result
+ * loc[i] % page_size, :]. v_new and v_cache may both be NULL: then only the
+ * K rows are stored, which is how the sparse index K cache read by
+ * msa_select_blocks (same layout) is written. Two new tokens with the same slot race (the result
  * is one of them). All buffers are caller-owned device memory, 16-byte
  * aligned; the call enqueues one kernel on `stream` and returns; the caches
  * are modified in place. Errors as for msa_kvouter_attention; N == 0

@@ -177,6 +177,8 @@ def test_store_kv_argument_checks():
     k, v, loc, kc, vc = args()
     assert lib.msa_store_kv(None, r(v), r(loc), r(kc), r(vc), 64, None) == INV
     assert call_store(args(N=0)) == 0                                           # nothing to store
+    assert lib.msa_store_kv(r(k), None, r(loc), r(kc), r(vc), 64, None) == INV   # V half given
+    assert lib.msa_store_kv(r(k), None, r(loc), r(kc), None, 128, None) == INV   # K only: checks still run
 
 
 def test_select_blocks_argument_checks():

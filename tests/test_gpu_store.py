@@ -128,3 +128,22 @@ def test_store_then_attention_reads_the_stored_tokens():
                                    causal=True, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_store_keys_only_into_an_index_cache():
+    # no V: only the K rows are written (the sparse index K cache), same bytes
+    # as the oracle's K cache
+    import block_sparse_attention_selection_amd as msa
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(31)
+    N, Hkv, NP, P = 200, 2, 6, 64
+    k_new = torch.from_numpy(rng.standard_normal((N, Hkv, 128)).astype(np.float32) * 30).to(torch.bfloat16)
+    loc = torch.from_numpy(rng.permutation(NP * P)[:N].astype(np.int64))
+    kc = torch.full((NP, Hkv, P, 128), 0x21, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+    msa.store_kv(k_new.to(dev), None, loc.to(dev), kc, None, page_size=P)
+    torch.cuda.synchronize()
+    ek = np.full((NP, Hkv, P, 128), 0x21, np.uint8)
+    ev = np.full((NP, Hkv, P, 128), 0x21, np.uint8)
+    S.store_kv(k_new.float().numpy(), k_new.float().numpy(), loc.numpy(), ek, ev, P)
+    assert np.array_equal(kc.view(torch.uint8).cpu().numpy(), ek)
