@@ -641,7 +641,8 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
     return fail(MSA_ERR_INVALID_ARGUMENT, "scores: expected [%lld, %lld, %lld]", (long long)Tq, (long long)Hkv,
                 (long long)nb_cap);
   if (Tq >= (1ll << 31) / 16 || Hkv > 65535 || NP >= (1ll << 31) || B >= (1ll << 30) ||
-      Tq * Hkv * (int64_t)topk >= (1ll << 40) || (Tq / 16 + B + 1) * Hkv >= (1ll << 31))
+      Tq * Hkv * (int64_t)topk >= (1ll << 40) ||
+      (Tq / 16 + B + 1) * Hkv * ((nb_cap + msa::kSelSplitBlocks - 1) / msa::kSelSplitBlocks) >= (1ll << 31))
     return fail(MSA_ERR_UNSUPPORTED, "problem too large");
   if (Tq == 0 || Hkv == 0) return ok();
   if (B == 0) return fail(MSA_ERR_INVALID_ARGUMENT, "Tq > 0 with an empty batch");
@@ -663,13 +664,24 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
   p.topk = topk;
   p.causal = causal;
   p.force_local = force_local;
-  // 64-token tiles share each key row among four 16-token row blocks; they
-  // need 64 * nb_cap floats of LDS, so they serve page tables of at most 256
-  // blocks, and decode-shaped batches (a few queries per sequence) use
-  // 16-token tiles
-  const int nrb = (Tq > 4 * B && nb_cap <= 256) ? 4 : 1;
+  // Prefill-shaped batches: 64-token tiles share each key row among four
+  // 16-token row blocks and keep their scores in LDS (64 * nb_cap floats, so
+  // page tables of at most 256 blocks). Decode-shaped batches (a few queries
+  // per long sequence) and longer tables: the split path, whose score table
+  // is the caller's `scores` or the library workspace.
+  const bool fused = Tq > 4 * B && nb_cap <= 256;
+  float* table = nullptr;
+  if (!fused) {
+    if (scores) {
+      table = (float*)scores->data;
+    } else {
+      WsLease ws;
+      if ((rc = get_workspace((size_t)Tq * Hkv * nb_cap * sizeof(float), 0, &ws))) return rc;
+      table = (float*)ws.scratch;
+    }
+  }
   msa::profile_mark(msa::kKSelect, true, (hipStream_t)stream);
-  hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, nrb,
+  hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, table,
                                     (hipStream_t)stream);
   msa::profile_mark(msa::kKSelect, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

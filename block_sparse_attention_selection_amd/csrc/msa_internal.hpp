@@ -115,7 +115,10 @@ struct SelectParams {
   float* scores;          // [Tq, Hkv, nb_cap] or null
   int Tq, Hkv, B, MP, P, num_pages, nb_cap, topk, causal, force_local;
 };
-// nrb: row blocks of 16 tokens per workgroup (1 or 4)
-hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, int nrb, hipStream_t st);
+constexpr int kSelSplitBlocks = 16;  // blocks per workgroup of the split (decode-shaped) path
+constexpr int kSelSplitWaves = 4;
+// table == null: the fused path (64-token tiles, scores in LDS, nb_cap <= 256);
+// else the split path, whose score table [Tq, Hkv, nb_cap] fp32 is `table`
+hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, hipStream_t st);
 
 }  // namespace msa

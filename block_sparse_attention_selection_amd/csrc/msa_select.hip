@@ -15,14 +15,15 @@
 // scores by ascending block id, padded with -1. Blocks without a visible
 // token, and NaN scores, are never selected.
 //
-// Work: one workgroup per (tile of consecutive tokens of one sequence, KV
-// head): 64-token tiles of 4 waves, or 16-token tiles of 8 or 16 waves for
-// decode-shaped batches. The waves split the tile's blocks; each computes
+// Work, prefill-shaped batches: one workgroup of 4 waves per (64-token tile
+// of one sequence, KV head). The waves split the tile's blocks; each computes
 // S^T = K . Q^T with 16x16x32 MFMA for 16 keys at a time, K read from the
 // paged cache straight into operand registers (a lane reads 32 contiguous
 // dims of one key row), and max-pools it into a [tokens][blocks] fp32 table
-// in LDS. Then each wave takes rows of the table and extracts the top-k with
-// wave-wide arg-max rounds.
+// in LDS. Then each wave takes rows of the table and lists their top-k.
+// Decode-shaped batches (a few tokens per long sequence) split each
+// sequence's blocks over several workgroups that write a global score table,
+// and a second launch lists every row from it.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -77,177 +78,190 @@ __device__ __forceinline__ bool sel_better(float v, int b, float v2, int b2) {
   return v > v2 || (v == v2 && b < b2);
 }
 
-// NRB: 16-token row blocks per tile; NW: waves; NPL: score registers per
-// lane in the top-k phase (64 * NPL >= nb_cap)
-template <typename QT, typename KT, int NRB, int NW, int NPL>
-__global__ __launch_bounds__(64 * NW) void k_select(SelectParams p) {
-  constexpr int T = 16 * NRB;  // tokens per tile
-  extern __shared__ float s_sc[];  // [T][nb_cap]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // workgroup i runs on XCD i % 8: KV head i % Hkv keeps each head's keys in
-  // the L2 of the same XCDs; tiles go last to first, so the tiles that see
-  // the most blocks (late in a causal sequence) start first
-  const int g = (int)(blockIdx.x % (unsigned)p.Hkv);
-  const int tile = (int)(gridDim.x / (unsigned)p.Hkv) - 1 - (int)(blockIdx.x / (unsigned)p.Hkv);
+// The tile of workgroup-level work: token rows [t0, t0 + ntok) of sequence s
+// for KV head g, with the sequence's clamped length and the block range
+// [0, nscan) that some row of the tile sees.
+struct SelTile {
+  int s, g, ntok, L, nb, nscan;
+  int64_t t0, c0, tq_s;
+  bool causal;
+  // position of tile row r (bottom-right causal alignment); L - 1 when not causal
+  __device__ __forceinline__ int64_t pos(int r) const { return causal ? (int64_t)L - tq_s + (t0 + r - c0) : (int64_t)L - 1; }
+};
+
+__device__ __forceinline__ bool sel_tile(const SelectParams& p, int tile, int g, int T, SelTile* st) {
   int64_t t0 = 0;
   const int s = wave_tile_of(p.cu, p.B, p.Tq, T, tile, &t0);
-  if (s < 0) return;
-  const int64_t c0 = p.cu[s], c1 = p.cu[s + 1];
-  const int64_t tq_end = min(c1, (int64_t)p.Tq);
-  const int ntok = (int)min((int64_t)T, tq_end - t0);
-  int L = p.used[s];
-  L = min(L, p.MP * p.P);  // a sequence reaches no further than its page table
-  const int64_t tq_s = c1 - c0;
-  // position of tile row r (bottom-right causal alignment); L - 1 when not causal
-  auto pos_of = [&](int r) -> int64_t { return p.causal ? (int64_t)L - tq_s + (t0 + r - c0) : (int64_t)L - 1; };
-  const int nb = min((L + 127) / 128, p.nb_cap);
-  const int64_t pos_max = pos_of(ntok - 1);
-  const int nscan = (L <= 0 || pos_max < 0) ? 0 : (int)min((int64_t)nb, pos_max / 128 + 1);
+  if (s < 0) return false;
+  SelTile& x = *st;
+  x.s = s;
+  x.g = g;
+  x.t0 = t0;
+  x.c0 = p.cu[s];
+  const int64_t c1 = p.cu[s + 1];
+  x.tq_s = c1 - x.c0;
+  x.ntok = (int)min((int64_t)T, min(c1, (int64_t)p.Tq) - t0);
+  x.L = min(p.used[s], p.MP * p.P);  // a sequence reaches no further than its page table
+  x.causal = p.causal != 0;
+  x.nb = min((x.L + 127) / 128, p.nb_cap);
+  const int64_t pos_max = x.pos(x.ntok - 1);
+  x.nscan = (x.L <= 0 || pos_max < 0) ? 0 : (int)min((int64_t)x.nb, pos_max / 128 + 1);
+  return true;
+}
 
-  if (nscan > 0) {
-    // index queries of the tile as MFMA B operands: lane holds token row
-    // (lane & 15) of row block rb, dims 32 (lane >> 4) + 8 st + [0, 8)
-    const int h = lane >> 4, col = lane & 15;
-    u32x4 qf[NRB][4];
+// Block scores of the tile's rows for blocks [b0, b1) (b1 <= nscan): wave w
+// takes blocks b0 + w, b0 + w + NW, ...; row r's score of block b goes to
+// dst[r * row_stride + b].
+template <typename QT, typename KT, int NRB, int NW>
+__device__ __forceinline__ void score_blocks(const SelectParams& p, const SelTile& x, int b0, int b1, float* dst,
+                                             int64_t row_stride) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = x.g, L = x.L;
+  // index queries of the tile as MFMA B operands: lane holds token row
+  // (lane & 15) of row block rb, dims 32 (lane >> 4) + 8 st + [0, 8)
+  const int h = lane >> 4, col = lane & 15;
+  u32x4 qf[NRB][4];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int r = rb * 16 + col;
-      if (r < ntok) {
-        const u32x4* q = (const u32x4*)((const uint16_t*)p.q + ((t0 + r) * p.Hkv + g) * (int64_t)kD + 32 * h);
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = rb * 16 + col;
+    if (r < x.ntok) {
+      const u32x4* q = (const u32x4*)((const uint16_t*)p.q + ((x.t0 + r) * p.Hkv + g) * (int64_t)kD + 32 * h);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) qf[rb][st] = q[st];
-      } else {
+      for (int st = 0; st < 4; ++st) qf[rb][st] = q[st];
+    } else {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) qf[rb][st] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    // positions as int32 (below L < 2^31; -1 stands for "sees nothing")
-    int posr[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) posr[rb] = (int)max(pos_of(rb * 16 + col), (int64_t)-1);
-    const int pos_lo = (int)max(pos_of(0), (int64_t)-1);  // the tile's first row sees the fewest keys
-    const int32_t* bt = p.bt + (int64_t)s * p.MP;
-    // physical pages of block b's two 64-token halves (the same page when P
-    // is 128); wave-uniform, -1 where the half holds no token below L
-    auto pages_of = [&](int b, int& pa, int& pb) {
-      const int j0 = 128 * b;
-      pa = j0 < L ? bt[j0 / p.P] : -1;
-      pb = p.P == 64 ? (j0 + 64 < L ? bt[(j0 + 64) / p.P] : -1) : pa;
-    };
-    // group kg of block b: keys 128 b + 16 kg + [0, 16); a lane reads key
-    // (lane & 15), dims 32 (lane >> 4) + [0, 32)
-    auto fetch = [&](KeyRow<QT, KT>& kr, int b, int kg, int pa, int pb) {
-      const int j = 128 * b + 16 * kg + col;
-      const int page = kg >= 4 ? pb : pa;
-      if (j < L && page >= 0 && page < p.num_pages) {
-        const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + ((16 * kg + col) & (p.P - 1));
-        kr.load((const uint8_t*)p.k + row * KeyBytes<KT>::kRow, h);
-      } else {
-        kr.zero();
-      }
-    };
-    const int nblk_w = nscan > wave ? (nscan - wave + NW - 1) / NW : 0;  // blocks wave, wave + NW, ...
-    // three groups in flight: the one in use and the next two
-    KeyRow<QT, KT> k0, k1, k2;
-    k2.zero();
-    int pa = -1, pb = -1, na = -1, nb2 = -1;
-    if (nblk_w > 0) {
-      pages_of(wave, pa, pb);
-      fetch(k0, wave, 0, pa, pb);
-      fetch(k1, wave, 1, pa, pb);
-    }
-    for (int bi = 0, b = wave; bi < nblk_w; ++bi, b += NW) {
-      const bool has_next = bi + 1 < nblk_w;
-      if (has_next) pages_of(b + NW, na, nb2);
-      // a block every key of which every row of the tile sees needs no mask
-      const bool full = 128 * b + 127 < L && 128 * b + 127 <= pos_lo;
-      float m[NRB];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) m[rb] = -INFINITY;
-#pragma unroll
-      for (int kg = 0; kg < 8; ++kg) {
-        if (kg < 6)
-          fetch(k2, b, kg + 2, pa, pb);
-        else if (has_next)
-          fetch(k2, b + NW, kg - 6, na, nb2);
-        const int jbase = 128 * b + 16 * kg + 4 * h;  // keys of this lane's accumulator rows
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(k0.frag(st), qf[rb][st], acc);
-          float v;
-          if (full) {
-            v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-          } else {
-            v = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = jbase + i;
-              v = fmaxf(v, (j < L && j <= posr[rb]) ? acc[i] : -INFINITY);
-            }
-          }
-          m[rb] = fmaxf(m[rb], v);  // this lane's keys; the lane groups are combined once per block
-        }
-        k0 = k1;
-        k1 = k2;
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float mb = max_over_groups(m[rb]);
-        if (h == 0 && rb * 16 + col < ntok) s_sc[(rb * 16 + col) * p.nb_cap + b] = mb;
-      }
-      pa = na;
-      pb = nb2;
+      for (int st = 0; st < 4; ++st) qf[rb][st] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();
-
-  // top-k per row: rows wave, wave + NW, ...
-  for (int r = wave; r < ntok; r += NW) {
-    const int64_t t = t0 + r;
-    const int64_t pos = pos_of(r);
-    const int nr = (L <= 0 || pos < 0) ? 0 : (int)min((int64_t)nb, pos / 128 + 1);
-    int32_t* out = p.selected + (t * p.Hkv + g) * (int64_t)p.topk;
-    float v[NPL];
+  // positions as int32 (below L < 2^31; -1 stands for "sees nothing")
+  int posr[NRB];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int b = lane + 64 * i;
-      float x = b < nr ? s_sc[r * p.nb_cap + b] : -INFINITY;
-      if (p.scores && b < p.nb_cap) p.scores[(t * p.Hkv + g) * (int64_t)p.nb_cap + b] = x;
-      v[i] = (x != x) ? -INFINITY : x;  // a NaN score is never selected
+  for (int rb = 0; rb < NRB; ++rb) posr[rb] = (int)max(x.pos(rb * 16 + col), (int64_t)-1);
+  const int pos_lo = (int)max(x.pos(0), (int64_t)-1);  // the tile's first row sees the fewest keys
+  const int32_t* bt = p.bt + (int64_t)x.s * p.MP;
+  // physical pages of block b's two 64-token halves (the same page when P
+  // is 128); wave-uniform, -1 where the half holds no token below L
+  auto pages_of = [&](int b, int& pa, int& pb) {
+    const int j0 = 128 * b;
+    pa = j0 < L ? bt[j0 / p.P] : -1;
+    pb = p.P == 64 ? (j0 + 64 < L ? bt[(j0 + 64) / p.P] : -1) : pa;
+  };
+  // group kg of block b: keys 128 b + 16 kg + [0, 16); a lane reads key
+  // (lane & 15), dims 32 (lane >> 4) + [0, 32)
+  auto fetch = [&](KeyRow<QT, KT>& kr, int b, int kg, int pa, int pb) {
+    const int j = 128 * b + 16 * kg + col;
+    const int page = kg >= 4 ? pb : pa;
+    if (j < L && page >= 0 && page < p.num_pages) {
+      const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + ((16 * kg + col) & (p.P - 1));
+      kr.load((const uint8_t*)p.k + row * KeyBytes<KT>::kRow, h);
+    } else {
+      kr.zero();
     }
-    int k = 0;
-    if (p.force_local && nr > 0 && p.topk > 0) {
-      const int lb = (int)(pos / 128);  // the token's own block (the last one when not causal)
-      float own = -INFINITY;
+  };
+  const int first = b0 + wave;
+  const int nblk_w = b1 > first ? (b1 - first + NW - 1) / NW : 0;
+  // three groups in flight: the one in use and the next two
+  KeyRow<QT, KT> k0, k1, k2;
+  k2.zero();
+  int pa = -1, pb = -1, na = -1, nb2 = -1;
+  if (nblk_w > 0) {
+    pages_of(first, pa, pb);
+    fetch(k0, first, 0, pa, pb);
+    fetch(k1, first, 1, pa, pb);
+  }
+  for (int bi = 0, b = first; bi < nblk_w; ++bi, b += NW) {
+    const bool has_next = bi + 1 < nblk_w;
+    if (has_next) pages_of(b + NW, na, nb2);
+    // a block every key of which every row of the tile sees needs no mask
+    const bool full = 128 * b + 127 < L && 128 * b + 127 <= pos_lo;
+    float m[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) m[rb] = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      if (kg < 6)
+        fetch(k2, b, kg + 2, pa, pb);
+      else if (has_next)
+        fetch(k2, b + NW, kg - 6, na, nb2);
+      const int jbase = 128 * b + 16 * kg + 4 * h;  // keys of this lane's accumulator rows
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(k0.frag(st), qf[rb][st], acc);
+        float v;
+        if (full) {
+          v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        } else {
+          v = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = jbase + i;
+            v = fmaxf(v, (j < L && j <= posr[rb]) ? acc[i] : -INFINITY);
+          }
+        }
+        m[rb] = fmaxf(m[rb], v);  // this lane's keys; the lane groups are combined once per block
+      }
+      k0 = k1;
+      k1 = k2;
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mb = max_over_groups(m[rb]);
+      if (h == 0 && rb * 16 + col < x.ntok) dst[(rb * 16 + col) * row_stride + b] = mb;
+    }
+    pa = na;
+    pb = nb2;
+  }
+}
+
+// The list of one (token t, KV head g) row whose token sits at position pos
+// and sees blocks [0, nr), from its scores row[0, nr) (LDS or global). One
+// wave. Also writes the row to p.scores when requested (unless the row is
+// already there: in_place).
+template <int NPL>
+__device__ __forceinline__ void topk_row(const SelectParams& p, int64_t t, int g, int64_t pos, int nr,
+                                         const float* row, bool in_place) {
+  const int lane = threadIdx.x & 63;
+  int32_t* out = p.selected + (t * p.Hkv + g) * (int64_t)p.topk;
+  float* srow = p.scores ? p.scores + (t * p.Hkv + g) * (int64_t)p.nb_cap : nullptr;
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int b = lane + 64 * i;
+    float x = b < nr ? row[b] : -INFINITY;
+    if (srow && b < p.nb_cap && !(in_place && b < nr)) srow[b] = x;
+    v[i] = (x != x) ? -INFINITY : x;  // a NaN score is never selected
+  }
+  int k = 0;
+  if (p.force_local && nr > 0 && p.topk > 0) {
+    const int lb = (int)(pos / 128);  // the token's own block (the last one when not causal)
+    float own = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i == lb) own = v[i];
+    if (__shfl(own, lb & 63, 64) > -INFINITY) {  // it holds the token itself: only a NaN score fails
 #pragma unroll
       for (int i = 0; i < NPL; ++i)
-        if (lane + 64 * i == lb) own = v[i];
-      if (__shfl(own, lb & 63, 64) > -INFINITY) {  // it holds the token itself: only a NaN score fails
-#pragma unroll
-        for (int i = 0; i < NPL; ++i)
-          if (lane + 64 * i == lb) v[i] = -INFINITY;
-        if (lane == 0) out[0] = lb;
-        k = 1;
-      }
+        if (lane + 64 * i == lb) v[i] = -INFINITY;
+      if (lane == 0) out[0] = lb;
+      k = 1;
     }
-    if constexpr (NPL == 1) {
-      // at most 64 blocks, one per lane: every block's rank among the others
-      // in one pass of wave broadcasts, then the blocks ranked below the
-      // free places write themselves
-      int rank = 0;
-      for (int m = 0; m < 64; ++m) {
-        const float vm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), m));
-        rank += sel_better(vm, m, v[0], lane) ? 1 : 0;
-      }
-      const int free_places = p.topk - k;
-      if (v[0] > -INFINITY && rank < free_places) out[k + rank] = lane;
-      int nvalid = __popcll(__ballot(v[0] > -INFINITY));
-      k += min(nvalid, free_places);
-      for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
-      continue;
+  }
+  if constexpr (NPL == 1) {
+    // at most 64 blocks, one per lane: every block's rank among the others
+    // in one pass of wave broadcasts, then the blocks ranked below the free
+    // places write themselves
+    int rank = 0;
+    for (int m = 0; m < 64; ++m) {
+      const float vm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), m));
+      rank += sel_better(vm, m, v[0], lane) ? 1 : 0;
     }
+    const int free_places = p.topk - k;
+    if (v[0] > -INFINITY && rank < free_places) out[k + rank] = lane;
+    const int nvalid = __popcll(__ballot(v[0] > -INFINITY));
+    k += min(nvalid, free_places);
+  } else {
     // each lane keeps its own best (value, block); a round reduces them over
     // the wave and only the winning lane rescans its registers
     auto lane_best = [&](float& bv, int& bb) {
@@ -284,49 +298,119 @@ __global__ __launch_bounds__(64 * NW) void k_select(SelectParams p) {
         lane_best(lv, lbk);
       }
     }
-    for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
+  }
+  for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
+}
+
+// Fused path (prefill-shaped batches): one workgroup of NW waves per (64-token
+// tile, KV head) scores every block into LDS, then lists each row. Workgroup
+// i runs on XCD i % 8: KV head i % Hkv keeps each head's keys in the L2 of
+// the same XCDs; tiles go last to first, so the tiles that see the most blocks
+// (late in a causal sequence) start first.
+template <typename QT, typename KT, int NRB, int NW, int NPL>
+__global__ __launch_bounds__(64 * NW) void k_select(SelectParams p) {
+  constexpr int T = 16 * NRB;
+  extern __shared__ float s_sc[];  // [T][nb_cap]
+  const int wave = threadIdx.x >> 6;
+  const int g = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int tile = (int)(gridDim.x / (unsigned)p.Hkv) - 1 - (int)(blockIdx.x / (unsigned)p.Hkv);
+  SelTile x;
+  if (!sel_tile(p, tile, g, T, &x)) return;
+  if (x.nscan > 0) score_blocks<QT, KT, NRB, NW>(p, x, 0, x.nscan, s_sc, p.nb_cap);
+  __syncthreads();
+  for (int r = wave; r < x.ntok; r += NW) {
+    const int64_t pos = x.pos(r);
+    const int nr = (x.L <= 0 || pos < 0) ? 0 : (int)min((int64_t)x.nb, pos / 128 + 1);
+    topk_row<NPL>(p, x.t0 + r, g, pos, nr, s_sc + r * p.nb_cap, false);
   }
 }
 
+// Split path (decode-shaped batches), first pass: one workgroup per (16-token
+// tile, KV head, slice of kSelSplitBlocks blocks) writes its blocks' scores
+// to the global table sc [Tq, Hkv, nb_cap]; the slices of a long sequence run
+// side by side.
+template <typename QT, typename KT>
+__global__ __launch_bounds__(64 * kSelSplitWaves) void k_select_scores(SelectParams p, float* sc, int nsplit) {
+  const int g = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int rest = (int)(blockIdx.x / (unsigned)p.Hkv);
+  const int split = rest % nsplit;
+  const int tile = (int)(gridDim.x / (unsigned)(p.Hkv * nsplit)) - 1 - rest / nsplit;
+  SelTile x;
+  if (!sel_tile(p, tile, g, 16, &x)) return;
+  const int b0 = split * kSelSplitBlocks, b1 = min(b0 + kSelSplitBlocks, x.nscan);
+  if (b0 >= b1) return;
+  score_blocks<QT, KT, 1, kSelSplitWaves>(p, x, b0, b1, sc + (x.t0 * p.Hkv + g) * (int64_t)p.nb_cap,
+                                          (int64_t)p.Hkv * p.nb_cap);
+}
+
+// Split path, second pass: one wave per (token, KV head) row lists it from
+// the global table.
+template <int NPL>
+__global__ __launch_bounds__(256) void k_select_lists(SelectParams p, const float* sc) {
+  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * Hkv + g
+  if (rid >= (int64_t)p.Tq * p.Hkv) return;
+  const int64_t t = rid / p.Hkv;
+  const int g = (int)(rid - t * p.Hkv);
+  const int s = wave_seq_of(p.cu, p.B, t);
+  int nr = 0;
+  int64_t pos = -1;
+  if (s >= 0) {
+    const int L = min(p.used[s], p.MP * p.P);
+    const int64_t c0 = p.cu[s], tq_s = p.cu[s + 1] - c0;
+    pos = p.causal ? (int64_t)L - tq_s + (t - c0) : (int64_t)L - 1;
+    const int nb = min((L + 127) / 128, p.nb_cap);
+    nr = (L <= 0 || pos < 0) ? 0 : (int)min((int64_t)nb, pos / 128 + 1);
+  }
+  topk_row<NPL>(p, t, g, pos, nr, sc + rid * p.nb_cap, sc == p.scores);
+}
+
 template <typename QT, typename KT, int NRB, int NW>
-static void launch_select_npl(const SelectParams& p, dim3 grid, size_t lds, hipStream_t st) {
+static void launch_fused_npl(const SelectParams& p, dim3 grid, size_t lds, hipStream_t st) {
   const dim3 block(64 * NW);
   if (p.nb_cap <= 64)
     hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 1>), grid, block, lds, st, p);
   else if (p.nb_cap <= 128)
     hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 2>), grid, block, lds, st, p);
-  else if (p.nb_cap <= 256)
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 4>), grid, block, lds, st, p);
-  else if (p.nb_cap <= 512)
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 8>), grid, block, lds, st, p);
   else
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, kSelMaxBlocks / 64>), grid, block, lds, st, p);
+    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 4>), grid, block, lds, st, p);
 }
 
-// nrb 4: 64-token tiles of 4 waves (prefill-shaped batches); nrb 1: 16-token
-// tiles of 16 (fp8 keys) or 8 waves, which split a long sequence's blocks
-// among more loads in flight (decode-shaped batches)
-template <typename QT, typename KT>
-static hipError_t launch_select_t(const SelectParams& p, int nrb, hipStream_t st) {
-  const int T = 16 * nrb;
-  const int64_t tiles = ((int64_t)p.Tq + T - 1) / T + p.B;  // each sequence adds at most one partial tile
-  const dim3 grid((unsigned)(tiles * p.Hkv));
-  const size_t lds = (size_t)T * p.nb_cap * sizeof(float);
-  // 16-bit keys need twice the registers in flight: 8 waves keep them
-  // within a 1024-thread workgroup's share
-  constexpr int kNarrowWaves = sizeof(KT) == 1 ? 16 : 8;
-  if (nrb == 4)
-    launch_select_npl<QT, KT, 4, 4>(p, grid, lds, st);
+static void launch_lists(const SelectParams& p, const float* sc, hipStream_t st) {
+  const dim3 grid((unsigned)(((int64_t)p.Tq * p.Hkv + 3) / 4)), block(256);
+  if (p.nb_cap <= 64)
+    hipLaunchKernelGGL((k_select_lists<1>), grid, block, 0, st, p, sc);
+  else if (p.nb_cap <= 128)
+    hipLaunchKernelGGL((k_select_lists<2>), grid, block, 0, st, p, sc);
+  else if (p.nb_cap <= 256)
+    hipLaunchKernelGGL((k_select_lists<4>), grid, block, 0, st, p, sc);
+  else if (p.nb_cap <= 512)
+    hipLaunchKernelGGL((k_select_lists<8>), grid, block, 0, st, p, sc);
   else
-    launch_select_npl<QT, KT, 1, kNarrowWaves>(p, grid, lds, st);
+    hipLaunchKernelGGL((k_select_lists<kSelMaxBlocks / 64>), grid, block, 0, st, p, sc);
+}
+
+template <typename QT, typename KT>
+static hipError_t launch_select_t(const SelectParams& p, float* table, hipStream_t st) {
+  if (!table) {
+    // fused: 64-token tiles of 4 waves, every score in LDS (nb_cap <= 256)
+    const int64_t tiles = ((int64_t)p.Tq + 63) / 64 + p.B;  // each sequence adds at most one partial tile
+    const size_t lds = (size_t)64 * p.nb_cap * sizeof(float);
+    launch_fused_npl<QT, KT, 4, 4>(p, dim3((unsigned)(tiles * p.Hkv)), lds, st);
+  } else {
+    const int64_t tiles = ((int64_t)p.Tq + 15) / 16 + p.B;
+    const int nsplit = (p.nb_cap + kSelSplitBlocks - 1) / kSelSplitBlocks;
+    hipLaunchKernelGGL((k_select_scores<QT, KT>), dim3((unsigned)(tiles * p.Hkv * nsplit)),
+                       dim3(64 * kSelSplitWaves), 0, st, p, table, nsplit);
+    launch_lists(p, table, st);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, int nrb, hipStream_t st) {
+hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, hipStream_t st) {
   if (p.Tq == 0 || p.Hkv == 0) return hipSuccess;
   if (q_elem == kElemBF16)
-    return fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(p, nrb, st) : launch_select_t<bf16_t, bf16_t>(p, nrb, st);
-  return fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(p, nrb, st) : launch_select_t<f16_t, f16_t>(p, nrb, st);
+    return fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(p, table, st) : launch_select_t<bf16_t, bf16_t>(p, table, st);
+  return fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(p, table, st) : launch_select_t<f16_t, f16_t>(p, table, st);
 }
 
 }  // namespace msa

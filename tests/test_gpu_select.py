@@ -41,7 +41,14 @@ def _run(si: W.SelectionInputs, force_local=True, topk=None):
                                 used_kv_lens=torch.from_numpy(si.used_kv_lens).to(dev),
                                 page_size=si.page_size, topk=topk or si.topk, causal=si.causal,
                                 force_local=force_local, return_scores=True)
+    # without a score output the library keeps the table in its workspace
+    sel2 = msa.select_blocks(si.q_idx.to(dev), si.k_idx.to(dev), torch.from_numpy(si.block_tables).to(dev),
+                             cu_seqlens_q=torch.from_numpy(si.cu_seqlens_q).to(dev),
+                             used_kv_lens=torch.from_numpy(si.used_kv_lens).to(dev),
+                             page_size=si.page_size, topk=topk or si.topk, causal=si.causal,
+                             force_local=force_local)
     torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
     return sel.cpu().numpy(), sc.cpu().numpy()
 
 
