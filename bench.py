@@ -219,11 +219,15 @@ def write_profile_summaries(src):
                                 PROF_PMC_CMD.format(w=w, c="FETCH_SIZE"), PROF_PMC_CMD.format(w=w, c="WRITE_SIZE")],
                    "kernels": {}}
             for short, pat in KERNEL_KEYS.items():
+                # every kernel of the family (e.g. the selection's score and list
+                # launches), each launched once per call: their per-dispatch
+                # averages add up to one call's traffic
                 a = [v for k, v in fk.items() if pat in k]
                 b = [v for k, v in wk.items() if pat in k]
                 if a and b:
-                    rec["kernels"][short] = {"fetch_kib": a[0][0], "write_kib": b[0][0], "dispatches": a[0][1],
-                                             "hbm_bytes": a[0][0] * ff + b[0][0] * fw}
+                    f_sum, w_sum = sum(x[0] for x in a), sum(x[0] for x in b)
+                    rec["kernels"][short] = {"fetch_kib": f_sum, "write_kib": w_sum, "dispatches": a[0][1],
+                                             "kernels_in_family": len(a), "hbm_bytes": f_sum * ff + w_sum * fw}
             with open(os.path.join(ROOT, "profiles", f"traffic_{w}.txt"), "w") as f:
                 json.dump(rec, f, indent=1)
             print("wrote", f"profiles/traffic_{w}.txt",
