@@ -104,6 +104,7 @@ CASES = [
     ([3, 0, 5, 1], [129, 700, 0, 64], 2, 64, 40, True, torch.bfloat16),     # empty seqs, topk > blocks
     ([2, 3], [10000, 9000], 1, 64, 8, True, torch.float8_e4m3fn),          # 65..128 blocks a row
     ([1, 2], [100000, 20000], 1, 128, 16, True, torch.bfloat16),           # up to 782 blocks a row
+    ([1, 1, 1, 1, 1], [3000, 200, 129, 128, 5000], 16, 128, 1, False, torch.float8_e4m3fn),  # 16 heads, top-1
 ]
 
 
@@ -115,8 +116,9 @@ def test_select_matches_oracle(case):
     _check(si, sel, sc, _oracle_scores(si), topk, True)
 
 
-def test_select_without_forced_local_and_fp16():
-    si = W.make_selection(320, [5, 90], [900, 3000], 2, 64, 6, True, torch.float16, torch.float16)
+@pytest.mark.parametrize("tq, lens", [([5, 90], [900, 3000]), ([2, 1], [4000, 700])])  # fused, split
+def test_select_without_forced_local_and_fp16(tq, lens):
+    si = W.make_selection(320, tq, lens, 2, 64, 6, True, torch.float16, torch.float16)
     sel, sc = _run(si, force_local=False)
     _check(si, sel, sc, _oracle_scores(si), 6, False)
 
