@@ -101,7 +101,8 @@ __device__ __forceinline__ bool sel_tile(const SelectParams& p, int tile, int g,
   const int64_t c1 = p.cu[s + 1];
   x.tq_s = c1 - x.c0;
   x.ntok = (int)min((int64_t)T, min(c1, (int64_t)p.Tq) - t0);
-  x.L = min(p.used[s], p.MP * p.P);  // a sequence reaches no further than its page table
+  // a sequence reaches no further than its page table (and nowhere without a cache)
+  x.L = p.num_pages > 0 ? min(p.used[s], p.MP * p.P) : 0;
   x.causal = p.causal != 0;
   x.nb = min((x.L + 127) / 128, p.nb_cap);
   const int64_t pos_max = x.pos(x.ntok - 1);
@@ -148,26 +149,25 @@ __device__ __forceinline__ void score_blocks(const SelectParams& p, const SelTil
   };
   // group kg of block b: keys 128 b + 16 kg + [0, 16); a lane reads key
   // (lane & 15), dims 32 (lane >> 4) + [0, 32)
+  // Every fetch loads: a half without a page (beyond L) or with a page id
+  // outside the cache reads page 0 instead (num_pages >= 1 here), and the
+  // mask removes keys at or beyond L, so no branch zeroes registers.
   auto fetch = [&](KeyRow<QT, KT>& kr, int b, int kg, int pa, int pb) {
-    const int j = 128 * b + 16 * kg + col;
-    const int page = kg >= 4 ? pb : pa;
-    if (j < L && page >= 0 && page < p.num_pages) {
-      const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + ((16 * kg + col) & (p.P - 1));
-      kr.load((const uint8_t*)p.k + row * KeyBytes<KT>::kRow, h);
-    } else {
-      kr.zero();
-    }
+    int page = kg >= 4 ? pb : pa;
+    page = (page >= 0 && page < p.num_pages) ? page : 0;
+    const int64_t row = ((int64_t)page * p.Hkv + g) * p.P + ((16 * kg + col) & (p.P - 1));
+    kr.load((const uint8_t*)p.k + row * KeyBytes<KT>::kRow, h);
   };
   const int first = b0 + wave;
   const int nblk_w = b1 > first ? (b1 - first + NW - 1) / NW : 0;
-  // three groups in flight: the one in use and the next two
-  KeyRow<QT, KT> k0, k1, k2;
-  k2.zero();
+  // a ring of four key groups, two in flight ahead of the one in use; with
+  // the group loop unrolled by 8 every slot index is a constant
+  KeyRow<QT, KT> kr[4];
   int pa = -1, pb = -1, na = -1, nb2 = -1;
   if (nblk_w > 0) {
     pages_of(first, pa, pb);
-    fetch(k0, first, 0, pa, pb);
-    fetch(k1, first, 1, pa, pb);
+    fetch(kr[0], first, 0, pa, pb);
+    fetch(kr[1], first, 1, pa, pb);
   }
   for (int bi = 0, b = first; bi < nblk_w; ++bi, b += NW) {
     const bool has_next = bi + 1 < nblk_w;
@@ -180,15 +180,15 @@ __device__ __forceinline__ void score_blocks(const SelectParams& p, const SelTil
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
       if (kg < 6)
-        fetch(k2, b, kg + 2, pa, pb);
+        fetch(kr[(kg + 2) & 3], b, kg + 2, pa, pb);
       else if (has_next)
-        fetch(k2, b + NW, kg - 6, na, nb2);
+        fetch(kr[(kg + 2) & 3], b + NW, kg - 6, na, nb2);
       const int jbase = 128 * b + 16 * kg + 4 * h;  // keys of this lane's accumulator rows
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(k0.frag(st), qf[rb][st], acc);
+        for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(kr[kg & 3].frag(st), qf[rb][st], acc);
         float v;
         if (full) {
           v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
@@ -202,8 +202,6 @@ __device__ __forceinline__ void score_blocks(const SelectParams& p, const SelTil
         }
         m[rb] = fmaxf(m[rb], v);  // this lane's keys; the lane groups are combined once per block
       }
-      k0 = k1;
-      k1 = k2;
     }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -249,18 +247,36 @@ __device__ __forceinline__ void topk_row(const SelectParams& p, int64_t t, int g
     }
   }
   if constexpr (NPL == 1) {
-    // at most 64 blocks, one per lane: every block's rank among the others
-    // in one pass of wave broadcasts, then the blocks ranked below the free
-    // places write themselves
-    int rank = 0;
-    for (int m = 0; m < 64; ++m) {
-      const float vm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), m));
-      rank += sel_better(vm, m, v[0], lane) ? 1 : 0;
+    // At most 64 blocks, one per lane. The values map to order-preserving
+    // integers u; the need-th largest u (need = the free places, or fewer
+    // valid blocks) is found bit by bit with wave ballots; the blocks above
+    // it and the lowest-numbered ones equal to it are the list, and each
+    // chosen block's place is the count of chosen blocks ahead of it.
+    const float x0 = v[0] == 0.f ? 0.f : v[0];  // -0 and +0 are one value
+    const uint32_t bits = __float_as_uint(x0);
+    const uint32_t u = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    const bool valid = x0 > -INFINITY;
+    const int need = min(__popcll(__ballot(valid)), p.topk - k);
+    if (need > 0) {
+      uint32_t T = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        if (__popcll(__ballot(valid && u >= cand)) >= need) T = cand;
+      }
+      const uint64_t gt = __ballot(valid && u > T);
+      const uint64_t eq = __ballot(valid && u == T);
+      const int take = need - __popcll(gt);
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes under this one
+      const bool chosen = ((gt >> lane) & 1ull) || (((eq >> lane) & 1ull) && __popcll(eq & below) < take);
+      int place = 0;
+      for (uint64_t m = __ballot(chosen); m; m &= m - 1) {
+        const int o = __ffsll((unsigned long long)m) - 1;
+        const uint32_t uo = (uint32_t)__builtin_amdgcn_readlane((int)u, o);
+        place += (uo > u || (uo == u && o < lane)) ? 1 : 0;
+      }
+      if (chosen) out[k + place] = lane;
+      k += need;
     }
-    const int free_places = p.topk - k;
-    if (v[0] > -INFINITY && rank < free_places) out[k + rank] = lane;
-    const int nvalid = __popcll(__ballot(v[0] > -INFINITY));
-    k += min(nvalid, free_places);
   } else {
     // each lane keeps its own best (value, block); a round reduces them over
     // the wave and only the winning lane rescans its registers
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(256) void k_select_lists(SelectParams p, const floa
   int nr = 0;
   int64_t pos = -1;
   if (s >= 0) {
-    const int L = min(p.used[s], p.MP * p.P);
+    const int L = p.num_pages > 0 ? min(p.used[s], p.MP * p.P) : 0;
     const int64_t c0 = p.cu[s], tq_s = p.cu[s + 1] - c0;
     pos = p.causal ? (int64_t)L - tq_s + (t - c0) : (int64_t)L - 1;
     const int nb = min((L + 127) / 128, p.nb_cap);
