@@ -356,17 +356,27 @@ __device__ __forceinline__ float rows_total(const Rows32& rt) { return rt.l + __
 
 // 16-bit row stores/loads in the D layout: for d-tile t and group a the lane
 // holds d = 32t + 8a + 4h + (0..3), i.e. 8 contiguous bytes.
+//
+// The store pairs the two half-waves first: for groups a = 2u and 2u + 1,
+// v_permlane32_swap hands the upper half's group-2u words to the lower half
+// and the lower half's group-(2u+1) words to the upper half, so lane (h, c)
+// then holds d = 32t + 16u + 8h + (0..7) of its row and writes 16 contiguous
+// bytes: half the store instructions, each covering 32 bytes of every row.
 template <typename CT>
 __device__ __forceinline__ void store_row16(uint16_t* row, const Rows32& rt, float scale) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      u32x2 w;
-      w[0] = pack2<CT>(rt.o[t][4 * a] * scale, rt.o[t][4 * a + 1] * scale);
-      w[1] = pack2<CT>(rt.o[t][4 * a + 2] * scale, rt.o[t][4 * a + 3] * scale);
-      *(u32x2*)(row + 32 * t + 8 * a + 4 * h) = w;
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t x0 = pack2<CT>(rt.o[t][8 * u] * scale, rt.o[t][8 * u + 1] * scale);
+      const uint32_t x1 = pack2<CT>(rt.o[t][8 * u + 2] * scale, rt.o[t][8 * u + 3] * scale);
+      const uint32_t y0 = pack2<CT>(rt.o[t][8 * u + 4] * scale, rt.o[t][8 * u + 5] * scale);
+      const uint32_t y1 = pack2<CT>(rt.o[t][8 * u + 6] * scale, rt.o[t][8 * u + 7] * scale);
+      // upper lanes of the first operand <-> lower lanes of the second
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      *(u32x4*)(row + 32 * t + 16 * u + 8 * h) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     }
 }
 
