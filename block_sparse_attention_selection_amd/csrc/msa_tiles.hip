@@ -1082,10 +1082,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
       const int ntot = p.counters[kCntResidual];  // positions are below this
       float M = rt.m;  // O and W are relative to 2^M
       float W = l_tot;
-      const uint16_t* obase = (const uint16_t*)p.opart + 4 * h;
+      // a partial row is read as 16-byte pieces (lane (h, c): d = 32t + 16u +
+      // 8h + (0..7)) and put into the D layout by the same half-wave swap as
+      // store_row16, just before it is merged
+      const uint16_t* obase = (const uint16_t*)p.opart + 8 * h;
       struct Part {
         float l;
-        u32x2 d[16];
+        u32x4 d[8];
       };
       auto pos_of = [&](int i) {
         const int ii = min(i, K - 1);
@@ -1101,7 +1104,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) pt.d[4 * t + a] = *(const u32x2*)(src + 32 * t + 8 * a);
+          for (int u = 0; u < 2; ++u) pt.d[2 * t + u] = *(const u32x4*)(src + 32 * t + 16 * u);
       };
       auto merge = [&](const Part& pt) {
         const float lc = pt.l;
@@ -1120,12 +1123,18 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const u32x2 w = pt.d[4 * t + a];
-            rt.o[t][4 * a] += fi * from_bits16<CT>(w[0] & 0xFFFFu);
-            rt.o[t][4 * a + 1] += fi * from_bits16<CT>(w[0] >> 16);
-            rt.o[t][4 * a + 2] += fi * from_bits16<CT>(w[1] & 0xFFFFu);
-            rt.o[t][4 * a + 3] += fi * from_bits16<CT>(w[1] >> 16);
+          for (int u = 0; u < 2; ++u) {
+            const u32x4 v = pt.d[2 * t + u];
+            const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {  // group a = 2u + e: words s0[e], s1[e]
+              const int a = 2 * u + e;
+              rt.o[t][4 * a] += fi * from_bits16<CT>(s0[e] & 0xFFFFu);
+              rt.o[t][4 * a + 1] += fi * from_bits16<CT>(s0[e] >> 16);
+              rt.o[t][4 * a + 2] += fi * from_bits16<CT>(s1[e] & 0xFFFFu);
+              rt.o[t][4 * a + 3] += fi * from_bits16<CT>(s1[e] >> 16);
+            }
           }
       };
       if (nres_w > 0) {
