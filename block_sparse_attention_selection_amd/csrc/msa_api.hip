@@ -189,14 +189,14 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->ent = c.take<int32_t>(base, nslots);
   p->slot_pos = c.take<int32_t>(base, nslots);
   if (with_partials) {
-    p->scratch_row = c.take<char>(base, 1024);
+    p->scratch_row = c.take<char>(base, 8192);
     p->res_list = c.take<int32_t>(base, nslots);
     p->res_rank = c.take<uint8_t>(base, nslots);
     p->win_desc = c.take<int4>(base, nslots);
     const size_t items = ((size_t)(d.Tq + d.T - 1) / d.T + d.B) * d.Hkv;  // tile items, listed or enumerated
     p->tdesc = c.take<int4>(base, 2 * items);
     p->ctab = c.take<int4>(base, items * 4 * d.K);
-    p->opart = c.take<uint16_t>(base, nslots * d.G * 128);
+    p->opart = c.take<uint16_t>(base, (nslots * d.G + 31) / 32 * 32 * 128);  // whole 32-row blocks
     p->lpart = c.take<float>(base, nslots * d.G);
   } else {
     p->scratch_row = nullptr;

@@ -357,27 +357,49 @@ __device__ __forceinline__ float rows_total(const Rows32& rt) { return rt.l + __
 // 16-bit row stores/loads in the D layout: for d-tile t and group a the lane
 // holds d = 32t + 8a + 4h + (0..3), i.e. 8 contiguous bytes.
 //
-// The store pairs the two half-waves first: for groups a = 2u and 2u + 1,
+// Stores pair the two half-waves first: for groups a = 2u and 2u + 1,
 // v_permlane32_swap hands the upper half's group-2u words to the lower half
 // and the lower half's group-(2u+1) words to the upper half, so lane (h, c)
-// then holds d = 32t + 16u + 8h + (0..7) of its row and writes 16 contiguous
-// bytes: half the store instructions, each covering 32 bytes of every row.
+// then holds the 16 contiguous bytes d = 32t + 16u + 8h + (0..7) of its row,
+// i.e. 16-byte chunk 4t + 2u + h. The same swap undoes it after a load.
+template <typename CT>
+__device__ __forceinline__ u32x4 paired16(const Rows32& rt, int t, int u, float scale) {
+  const uint32_t x0 = pack2<CT>(rt.o[t][8 * u] * scale, rt.o[t][8 * u + 1] * scale);
+  const uint32_t x1 = pack2<CT>(rt.o[t][8 * u + 2] * scale, rt.o[t][8 * u + 3] * scale);
+  const uint32_t y0 = pack2<CT>(rt.o[t][8 * u + 4] * scale, rt.o[t][8 * u + 5] * scale);
+  const uint32_t y1 = pack2<CT>(rt.o[t][8 * u + 6] * scale, rt.o[t][8 * u + 7] * scale);
+  // upper lanes of the first operand <-> lower lanes of the second
+  const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
+// a row-major 16-bit row of 128
 template <typename CT>
 __device__ __forceinline__ void store_row16(uint16_t* row, const Rows32& rt, float scale) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t x0 = pack2<CT>(rt.o[t][8 * u] * scale, rt.o[t][8 * u + 1] * scale);
-      const uint32_t x1 = pack2<CT>(rt.o[t][8 * u + 2] * scale, rt.o[t][8 * u + 3] * scale);
-      const uint32_t y0 = pack2<CT>(rt.o[t][8 * u + 4] * scale, rt.o[t][8 * u + 5] * scale);
-      const uint32_t y1 = pack2<CT>(rt.o[t][8 * u + 6] * scale, rt.o[t][8 * u + 7] * scale);
-      // upper lanes of the first operand <-> lower lanes of the second
-      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-      *(u32x4*)(row + 32 * t + 16 * u + 8 * h) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-    }
+    for (int u = 0; u < 2; ++u) *(u32x4*)(row + 32 * t + 16 * u + 8 * h) = paired16<CT>(rt, t, u, scale);
+}
+
+// Residual partials are stored in blocks of 32 rows (row = residual position
+// x G + query head within the group): for each 16-byte chunk k of a row
+// (d = 8k .. 8k + 7) the block holds the chunk of its 32 rows side by side,
+// row r's chunk k at byte (r >> 5) * 8192 + k * 512 + (r & 31) * 16. A wave
+// storing 32 consecutive rows writes 512 contiguous bytes per chunk (two runs
+// when its rows cross a block), and a residual slot's G query heads share
+// one line per chunk when the merge reads them back.
+__device__ __forceinline__ size_t part_offset(size_t row) { return (row >> 5) * 8192 + (row & 31) * 16; }
+
+// base: the row's part_offset plus 512 h (chunk 4t + 2u + h at base + (4t + 2u) * 512)
+template <typename CT>
+__device__ __forceinline__ void store_part(char* base, const Rows32& rt, float scale) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *(u32x4*)(base + (4 * t + 2 * u) * 512) = paired16<CT>(rt, t, u, scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -761,9 +783,9 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
       {
         const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-        uint16_t* orow = valid ? (uint16_t*)p.opart + pidx * kD : (uint16_t*)p.scratch_row;
+        char* pbase = (valid ? (char*)p.opart + part_offset(pidx) : (char*)p.scratch_row + 16 * c) + 512 * h;
         float* lrow = (valid && h == 0) ? p.lpart + pidx : (float*)p.scratch_row + 64 + lane;
-        store_row16<CT>(orow, rt, inv);
+        store_part<CT>(pbase, rt, inv);
         const float mu = rt.m == -INFINITY ? 0.f : rt.m;
         *lrow = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
       }
@@ -1082,10 +1104,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
       const int ntot = p.counters[kCntResidual];  // positions are below this
       float M = rt.m;  // O and W are relative to 2^M
       float W = l_tot;
-      // a partial row is read as 16-byte pieces (lane (h, c): d = 32t + 16u +
-      // 8h + (0..7)) and put into the D layout by the same half-wave swap as
-      // store_row16, just before it is merged
-      const uint16_t* obase = (const uint16_t*)p.opart + 8 * h;
+      // a partial row is read as 16-byte chunks (lane (h, c): chunk 4t + 2u +
+      // h, d = 32t + 16u + 8h + (0..7)) and put into the D layout by the same
+      // half-wave swap as paired16, just before it is merged
+      const char* obase = (const char*)p.opart + 512 * h;
       struct Part {
         float l;
         u32x4 d[8];
@@ -1100,11 +1122,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         const size_t pidx = ok ? (size_t)pos * G + hr : 0;
         const float lv = p.lpart[pidx];
         pt.l = ok ? lv : -INFINITY;
-        const uint16_t* src = obase + pidx * kD;
+        const char* src = obase + part_offset(pidx);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) pt.d[2 * t + u] = *(const u32x4*)(src + 32 * t + 16 * u);
+          for (int u = 0; u < 2; ++u) pt.d[2 * t + u] = *(const u32x4*)(src + (4 * t + 2 * u) * 512);
       };
       auto merge = [&](const Part& pt) {
         const float lc = pt.l;
