@@ -108,13 +108,22 @@ def accounting(wl):
     return dict(unique_kv_bytes=unique_kv, effective_flops=flops, qo_bytes=qo)
 
 
-def kernel_sources_sha256():
-    """Digest of the HIP sources of the library (any change voids recorded counters)."""
+# the source file each kernel family is compiled from
+KERNEL_SOURCES = {"front": "msa_forward.hip", "classify": "msa_forward.hip", "units": "msa_tiles.hip",
+                  "tiles": "msa_tiles.hip", "index": "msa_index.hip", "emit": "msa_index.hip",
+                  "store": "msa_store.hip", "select": "msa_select.hip"}
+
+
+def kernel_sources_sha256(workload):
+    """Digest of the sources behind a workload's dominant kernels: their own
+    .hip files, every shared header and the host file that sizes and launches
+    them. A change to any of these voids the workload's recorded counters."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_selection_amd", "csrc")
+    own = {KERNEL_SOURCES[k] for k in DOMINANT[workload]} | {"msa_api.hip"}
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith(".hpp") or name in own:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -135,7 +144,7 @@ def measured_traffic(workload, kernels):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != kernel_sources_sha256():
+    if rec.get("sources_sha256") != kernel_sources_sha256(workload):
         return None
     try:
         ff, fw = rec["fetch_factor"], rec["write_factor"]
@@ -188,8 +197,8 @@ def write_profile_summaries(src):
         (f_kib, _), f_name = max((v, k) for k, v in cf.items() if "copy" in k.lower())
         (w_kib, _), _ = max((v, k) for k, v in cw.items() if "copy" in k.lower())
         factors = ((1 << 30) / f_kib, (1 << 30) / w_kib, f_kib, w_kib, f_name)
-    sha = kernel_sources_sha256()
     for w in DESCRIPTIONS:
+        sha = kernel_sources_sha256(w)
         stats = one(os.path.join("prof", w, "**", "*kernel_stats.csv"))
         if stats:
             rows = [r for r in csv.DictReader(open(stats)) if "msa" in r["Name"]]
