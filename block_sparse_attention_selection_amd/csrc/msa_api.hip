@@ -418,6 +418,12 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
                         causal, out, lse, &d);
   if (rc) return rc;
   if (d.Tq == 0) return ok();
+  // One query token per sequence slot (Tq == B) with at most 16 query rows
+  // per token is decode: tiles of one token each make every tile's chain its
+  // token's whole selection, so no slot is residual and the front kernel
+  // finishes every tile; the index, unit and tile kernels are not launched.
+  const bool front_only = d.G <= 16 && d.Tq == d.B;
+  if (front_only) d.T = 1;
   msa::Params p{};
   const size_t need = layout(d, nullptr, &p, true);
   WsLease ws;
@@ -431,6 +437,7 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   // tile and lists every tile for the tile kernel
   p.stream_narrow = (d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B) ? 1 : 0;
   p.list_tiles = p.stream_narrow;  // otherwise the tile kernel enumerates every tile itself
+  p.front_only = front_only ? 1 : 0;
   int32_t* sets = (int32_t*)ws.zs;
   p.counters = sets + ws.parity * msa::kCntSlots;
   p.counters_next = sets + (1 - ws.parity) * msa::kCntSlots;
@@ -449,9 +456,11 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   // derives the residual order itself and the materialising pass (one more
   // launch) is skipped
   p.ent_ready = p.stream_narrow ? 0 : 1;
-  if (e == hipSuccess) e = msa::launch_index(p, p.ent_ready != 0, st);
-  if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, ws.num_cu, st);
-  if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+  if (!front_only) {
+    if (e == hipSuccess) e = msa::launch_index(p, p.ent_ready != 0, st);
+    if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+    if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+  }
   {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     if (e != hipSuccess) {

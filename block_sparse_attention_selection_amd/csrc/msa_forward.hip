@@ -342,6 +342,10 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = p.K, Hkv = p.Hkv;
   const int Teff = p.T > 0 ? p.T : 1;
+  // the last kernel of a call leaves the next call's counter set zeroed (it
+  // was used by the previous call, whose kernels have all finished)
+  if (p.front_only && blockIdx.x == 0 && blockIdx.y == 0 && p.counters_next && tid < kCntSlots)
+    p.counters_next[tid] = 0;
   int t, s;
   int b_raw = -1;
   if (p.stream_narrow) {

@@ -54,6 +54,8 @@ struct Params {
   int stream_narrow;  // front kernel finishes residual-free tiles of <= 16 rows (decode mode)
   int list_tiles;     // front kernel appends the tiles it does not finish to tile_items
   int ent_ready;      // the index step materialised ent and res_list (else the unit kernel derives them)
+  int front_only;     // one-token tiles, all finished by the front kernel: no later kernel runs, and
+                      // the front kernel clears counters_next (otherwise the tile kernel does)
   float scale_log2;   // softmax scale * log2(e)
   // planning arrays
   int32_t* counters;       // this call's counter set (zero on entry)

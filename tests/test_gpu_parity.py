@@ -129,6 +129,8 @@ EDGE = [
     ([5, 3], [700, 350], 8, 2, 64, 4, True, "random", (torch.bfloat16, torch.float8_e4m3fn)),
     ([5, 3], [700, 350], 8, 2, 128, 4, False, "random", (torch.float16, torch.float8_e4m3fn)),
     ([2, 1], [64, 190], 64, 8, 64, 3, True, "all", None),                        # G=8, small
+    ([2, 0, 1], [900, 300, 700], 16, 2, 64, 4, True, "random", None),            # Tq == B, one 2-token seq
+    ([3, 0, 0, 1], [1200, 64, 64, 500], 8, 1, 128, 6, False, "all", None),       # Tq == B, non-causal
 ]
 
 
@@ -209,6 +211,33 @@ def test_deterministic_bits():
     o2, l2 = run_gpu(wl, inputs)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+def test_decode_and_prefill_calls_interleaved():
+    # Batches with one query token per sequence skip the index, unit and tile
+    # kernels; the front kernel then resets the counter set of the next call.
+    # Calls of both kinds, back to back on one stream, must each match the
+    # oracle, whatever kind of call ran before them.
+    dec = [W.make_custom(720 + i, [1] * 6, [900, 3000, 129, 4000, 640, 2000], 16, 2, 64, topk=6,
+                         causal=True, pick="random") for i in range(2)]
+    pre = [W.make_custom(730 + i, [40, 17], [2000, 700], 16, 2, 64, topk=8, causal=True, pick="diag",
+                         shared_chunk=16, shared_picks=4) for i in range(2)]
+    import block_sparse_attention_selection_amd as msa
+
+    inputs = {id(w): device_inputs(w) for w in dec + pre}
+    order = [pre[0], dec[0], dec[1], pre[1], dec[0], pre[0], pre[1], dec[1]]
+    results = []
+    for wl in order:  # enqueued back to back, one synchronisation at the end
+        d = inputs[id(wl)]
+        results.append(msa.kvouter_attention(
+            d["q"], d["k_cache"], d["v_cache"], d["selected"], d["block_tables"],
+            cu_seqlens_q=d["cu_seqlens_q"], used_kv_lens=d["used_kv_lens"],
+            page_size=wl.page_size, causal=wl.causal, return_lse=True))
+    torch.cuda.synchronize()
+    for wl, (out, lse) in zip(order, results):
+        pairs = all_pairs(wl)
+        ref_o, ref_l = oracle_pairs(wl, pairs)
+        compare(wl, out, lse, pairs, ref_o, ref_l)
 
 
 def test_tq_zero_is_a_no_op():
