@@ -63,7 +63,7 @@ SELECT_METRIC = {"select_decode": ("index-key HBM GB/s, block selection (scores 
 # the prefill-shaped workloads the attention's MFMA work is split between
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
-DOMINANT = {"tiny": ["tiles"], "decode_gqa": ["front"], "decode_fp8": ["front"],
+DOMINANT = {"tiny": ["front"], "decode_gqa": ["front"], "decode_fp8": ["front"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
             "dense_causal": ["tiles"], "kv_store_fp8": ["store"], "select_decode": ["select"],
             "select_prefill": ["select"]}

@@ -235,18 +235,35 @@ struct WsLease {
 
 // Scratch of `need` bytes and a zero-state buffer holding `bitmap_words`.
 // Growing either synchronises the device; a new zero-state buffer is zeroed.
-int32_t get_workspace(size_t need, size_t bitmap_words, WsLease* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
-  std::lock_guard<std::mutex> lk(g_ws_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  DeviceWs& w = g_ws[dev];
+// the compute-unit count of device dev, queried once (g_ws_mutex held)
+int32_t ensure_cu_count(DeviceWs& w, int dev) {
   if (w.num_cu == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return fail(MSA_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
     w.num_cu = n;
   }
+  return 0;
+}
+
+// compute units of the current device
+int32_t current_cu_count(int* n) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  const int32_t rc = ensure_cu_count(g_ws[dev], dev);
+  *n = g_ws[dev].num_cu;
+  return rc;
+}
+
+int32_t get_workspace(size_t need, size_t bitmap_words, WsLease* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DeviceWs& w = g_ws[dev];
+  if (int32_t rc = ensure_cu_count(w, dev)) return rc;
   const size_t zs_need = msa::kZsHeaderBytes + bitmap_words * 4;
   if (w.bytes < need || w.zs_bytes < zs_need) {
     if (w.ptr || w.zs) {
@@ -418,11 +435,17 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
                         causal, out, lse, &d);
   if (rc) return rc;
   if (d.Tq == 0) return ok();
-  // One query token per sequence slot (Tq == B) with at most 16 query rows
-  // per token is decode: tiles of one token each make every tile's chain its
-  // token's whole selection, so no slot is residual and the front kernel
-  // finishes every tile; the index, unit and tile kernels are not launched.
-  const bool front_only = d.G <= 16 && d.Tq == d.B;
+  // Tiles of one token each make every tile's chain its token's whole
+  // selection, so no slot is residual and the front kernel finishes every
+  // tile (at most 16 query rows per token); the index, unit and tile kernels
+  // are then not launched. Used for decode (one query token per sequence
+  // slot, Tq == B) and for small decode-shaped batches (Tq <= 4B) whose
+  // tokens all fit in one round of front workgroups, where launches cost
+  // more than the KV a sequence's tokens would otherwise share.
+  int ncu = 0;
+  if ((rc = current_cu_count(&ncu))) return rc;
+  const bool narrow = d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B;
+  const bool front_only = narrow && (d.Tq == d.B || (int64_t)d.Tq * d.Hkv <= 2 * (int64_t)ncu);
   if (front_only) d.T = 1;
   msa::Params p{};
   const size_t need = layout(d, nullptr, &p, true);

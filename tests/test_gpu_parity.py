@@ -131,16 +131,33 @@ EDGE = [
     ([2, 1], [64, 190], 64, 8, 64, 3, True, "all", None),                        # G=8, small
     ([2, 0, 1], [900, 300, 700], 16, 2, 64, 4, True, "random", None),            # Tq == B, one 2-token seq
     ([3, 0, 0, 1], [1200, 64, 64, 500], 8, 1, 128, 6, False, "all", None),       # Tq == B, non-causal
+    ([77, 30], [3000, 1100], 4, 2, 64, 7, True, "random", None),                 # G=2: partial rows cross blocks
 ]
+
+
+def _edge(case, tile_path=False):
+    tq, lens, Hq, Hkv, P, K, causal, pick, dt = EDGE[case]
+    if tile_path:  # one more sequence of 40 tokens makes the batch too long for per-token streaming
+        tq, lens = list(tq) + [40], list(lens) + [296]
+    qd, kvd = dt if dt else (torch.bfloat16, None)
+    return W.make_custom(500 + case, tq, lens, Hq, Hkv, P, topk=K, causal=causal, pick=pick,
+                         q_dtype=qd, kv_dtype=kvd, shared_chunk=16 if case == 6 else 0,
+                         shared_picks=5 if case == 6 else 0, pad_every=7 if pick == "oob" else 0)
 
 
 @pytest.mark.parametrize("case", range(len(EDGE)))
 def test_parity_edge_cases(case):
-    tq, lens, Hq, Hkv, P, K, causal, pick, dt = EDGE[case]
-    qd, kvd = dt if dt else (torch.bfloat16, None)
-    wl = W.make_custom(500 + case, tq, lens, Hq, Hkv, P, topk=K, causal=causal, pick=pick,
-                       q_dtype=qd, kv_dtype=kvd, shared_chunk=16 if case == 6 else 0,
-                       shared_picks=5 if case == 6 else 0, pad_every=7 if pick == "oob" else 0)
+    _full(_edge(case))
+
+
+# Small decode-shaped batches (Tq <= 4B, G <= 16) stream every token in the
+# front kernel; these cases again with a longer batch, so that the unit and
+# tile kernels see the same shapes.
+@pytest.mark.parametrize("case", [i for i, e in enumerate(EDGE)
+                                  if sum(e[0]) <= 4 * len(e[0]) and e[2] // e[3] <= 16 and sum(e[0]) != len(e[0])])
+def test_parity_edge_cases_tile_path(case):
+    wl = _edge(case, tile_path=True)
+    assert wl.Tq > 4 * len(wl.used_kv_lens)
     _full(wl)
 
 
