@@ -132,6 +132,8 @@ EDGE = [
     ([2, 0, 1], [900, 300, 700], 16, 2, 64, 4, True, "random", None),            # Tq == B, one 2-token seq
     ([3, 0, 0, 1], [1200, 64, 64, 500], 8, 1, 128, 6, False, "all", None),       # Tq == B, non-causal
     ([77, 30], [3000, 1100], 4, 2, 64, 7, True, "random", None),                 # G=2: partial rows cross blocks
+    ([12, 3], [2000, 900], 64, 1, 128, 5, False, "random", None),                # G=64: 4-token tiles
+    ([9, 5], [1500, 700], 128, 1, 64, 6, True, "random", None),                  # G=128: 2-token tiles, 1-token pieces
 ]
 
 
