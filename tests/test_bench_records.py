@@ -1,0 +1,60 @@
+"""Host logic of bench.py: which source changes void a workload's recorded
+HBM-traffic counters (CPU only)."""
+import os
+import shutil
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.fixture()
+def tree(tmp_path, monkeypatch):
+    src = os.path.join(ROOT, "block_sparse_attention_selection_amd", "csrc")
+    dst = tmp_path / "block_sparse_attention_selection_amd" / "csrc"
+    shutil.copytree(src, dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    return dst
+
+
+def _touch(path):
+    with open(path, "a") as f:
+        f.write("\n// edited\n")
+
+
+def _hashes():
+    return {w: bench.kernel_sources_sha256(w) for w in bench.DOMINANT}
+
+
+def test_every_dominant_kernel_has_a_source_file():
+    for w, kernels in bench.DOMINANT.items():
+        for k in kernels:
+            assert k in bench.KERNEL_SOURCES, (w, k)
+
+
+def test_a_kernel_file_voids_only_the_workloads_it_serves(tree):
+    before = _hashes()
+    _touch(tree / "msa_store.hip")
+    after = _hashes()
+    changed = {w for w in before if before[w] != after[w]}
+    assert changed == {"kv_store_fp8"}
+
+
+def test_the_tile_file_voids_the_prefill_workloads(tree):
+    before = _hashes()
+    _touch(tree / "msa_tiles.hip")
+    after = _hashes()
+    changed = {w for w in before if before[w] != after[w]}
+    assert changed == {w for w, ks in bench.DOMINANT.items() if {"units", "tiles"} & set(ks)}
+
+
+def test_shared_headers_and_the_host_file_void_everything(tree):
+    for name in ("msa_internal.hpp", "msa_api.hip"):
+        before = _hashes()
+        _touch(tree / name)
+        after = _hashes()
+        assert all(before[w] != after[w] for w in before), name
