@@ -32,10 +32,12 @@ from ._lib import (
     validate_inputs,
     version,
     widen_fp8,
+    workspace_bytes,
 )
 
 __all__ = [
     "kvouter_attention",
+    "workspace_bytes",
     "build_index",
     "widen_fp8",
     "store_kv",

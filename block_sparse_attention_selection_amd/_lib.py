@@ -73,6 +73,10 @@ def load():
         i32, vp = ctypes.c_int32, ctypes.c_void_p
         lib.msa_kvouter_attention.restype = i32
         lib.msa_kvouter_attention.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
+        lib.msa_kvouter_workspace_bytes.restype = i32
+        lib.msa_kvouter_workspace_bytes.argtypes = [T, T, T, T, T, T, T, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.msa_kvouter_attention_ws.restype = i32
+        lib.msa_kvouter_attention_ws.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp, ctypes.c_size_t, vp]
         lib.msa_build_index.restype = i32
         lib.msa_build_index.argtypes = [T, T, T, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MsaIndexOut), vp]
         lib.msa_widen_fp8.restype = i32
@@ -139,14 +143,18 @@ def _stream(dev) -> int:
 
 def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
                       page_size: int, causal: bool = False, return_lse: bool = False,
-                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
     """Block-sparse attention forward; see include/msa_kvouter.h for the contract.
 
     Returns ``out`` ``[Tq, Hq, 128]`` (q's dtype), or ``(out, lse)`` with
-    ``lse`` fp32 ``[Hq, Tq]`` when ``return_lse`` is set.
+    ``lse`` fp32 ``[Hq, Tq]`` when ``return_lse`` is set. With ``workspace``
+    (a contiguous device tensor of at least :func:`workspace_bytes` bytes) the
+    call uses it as scratch (msa_kvouter_attention_ws) and allocates nothing;
+    otherwise the library's own per-device workspace is used.
     """
     lib = load()
-    _device_check(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, out, lse)
+    _device_check(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, out, lse, workspace)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:
@@ -154,10 +162,31 @@ def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens
     ds = [describe(x) for x in (q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)]
     do, dl = describe(out), describe(lse if return_lse or lse is not None else None)
     with torch.cuda.device(q.device):
-        rc = lib.msa_kvouter_attention(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
-                                       _ref(do), _ref(dl), _stream(q.device))
+        if workspace is None:
+            rc = lib.msa_kvouter_attention(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                           _ref(do), _ref(dl), _stream(q.device))
+        else:
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
+            nbytes = workspace.numel() * workspace.element_size()
+            rc = lib.msa_kvouter_attention_ws(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                              _ref(do), _ref(dl), workspace.data_ptr() if nbytes else None,
+                                              nbytes, _stream(q.device))
     _check(rc)
     return (out, lse) if return_lse else out
+
+
+def workspace_bytes(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
+                    page_size: int, causal: bool = False) -> int:
+    """Bytes of the caller-owned workspace a call with these shapes needs
+    (msa_kvouter_workspace_bytes). Reads shapes and dtypes only; the tensors
+    may live on any device."""
+    lib = load()
+    ds = [describe(x) for x in (q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)]
+    n = ctypes.c_size_t()
+    _check(lib.msa_kvouter_workspace_bytes(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                           ctypes.byref(n)))
+    return int(n.value)
 
 
 def store_kv(k_new, v_new, loc, k_cache, v_cache, *, page_size: int):

@@ -20,20 +20,20 @@
 
 namespace {
 
-thread_local std::string g_err;
+// message of the last failing call on this thread (a fixed buffer: no call
+// path allocates host memory)
+thread_local char g_err[512];
 
 int32_t fail(int32_t code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return code;
 }
 
 int32_t ok() {
-  g_err.clear();
+  g_err[0] = '\0';
   return MSA_OK;
 }
 
@@ -56,14 +56,16 @@ int64_t numel(const msa_tensor* t) {
   return n;
 }
 
-int32_t check_tensor(const msa_tensor* t, const char* name, int ndim, int32_t dtype, size_t align) {
+// need_data: the buffer must be present and aligned (off for shape-only queries)
+int32_t check_tensor(const msa_tensor* t, const char* name, int ndim, int32_t dtype, size_t align,
+                     bool need_data = true) {
   if (!t) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: null descriptor", name);
   if (t->ndim != ndim) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: expected rank %d, got %d", name, ndim, t->ndim);
   for (int i = 0; i < ndim; ++i)
     if (t->shape[i] < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: negative extent", name);
   if (dtype >= 0 && t->dtype != dtype)
     return fail(MSA_ERR_INVALID_ARGUMENT, "%s: expected %s, got %s", name, dname(dtype), dname(t->dtype));
-  if (numel(t) > 0) {
+  if (need_data && numel(t) > 0) {
     if (!t->data) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: null data pointer", name);
     if (((uintptr_t)t->data) % align) return fail(MSA_ERR_INVALID_ARGUMENT, "%s: data not %zu-byte aligned", name, align);
   }
@@ -81,15 +83,15 @@ int elem_of(int32_t d) {
 
 int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, const msa_tensor* sel,
                  const msa_tensor* bt, const msa_tensor* cu, const msa_tensor* used, int32_t page_size,
-                 int32_t causal, const msa_tensor* out, const msa_tensor* lse, Dims* d) {
+                 int32_t causal, const msa_tensor* out, const msa_tensor* lse, Dims* d, bool nd = true) {
   int32_t rc;
-  if ((rc = check_tensor(q, "q", 3, -1, 16))) return rc;
+  if ((rc = check_tensor(q, "q", 3, -1, 16, nd))) return rc;
   if (q->dtype == MSA_FP8_E4M3FN) return fail(MSA_ERR_UNSUPPORTED, "q: fp8 queries are not supported");
   if (q->dtype != MSA_BF16 && q->dtype != MSA_FP16)
     return fail(MSA_ERR_INVALID_ARGUMENT, "q: dtype must be bf16 or fp16, got %s", dname(q->dtype));
   if (q->shape[2] != 128) return fail(MSA_ERR_UNSUPPORTED, "q: head dim %lld, only 128 is supported", (long long)q->shape[2]);
-  if ((rc = check_tensor(k, "k_cache", 4, -1, 16))) return rc;
-  if ((rc = check_tensor(v, "v_cache", 4, -1, 16))) return rc;
+  if ((rc = check_tensor(k, "k_cache", 4, -1, 16, nd))) return rc;
+  if ((rc = check_tensor(v, "v_cache", 4, -1, 16, nd))) return rc;
   if (k->dtype != q->dtype && k->dtype != MSA_FP8_E4M3FN)
     return fail(k->dtype == MSA_BF16 || k->dtype == MSA_FP16 ? MSA_ERR_UNSUPPORTED : MSA_ERR_INVALID_ARGUMENT,
                 "k_cache: dtype %s must equal q's (%s) or be fp8_e4m3fn", dname(k->dtype), dname(q->dtype));
@@ -100,10 +102,10 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
   if (page_size != 64 && page_size != 128) return fail(MSA_ERR_UNSUPPORTED, "page_size %d: only 64 and 128 are supported", page_size);
   if (k->shape[2] != page_size)
     return fail(MSA_ERR_INVALID_ARGUMENT, "k_cache: page dimension %lld != page_size %d", (long long)k->shape[2], page_size);
-  if ((rc = check_tensor(sel, "selected", 3, MSA_INT32, 4))) return rc;
-  if ((rc = check_tensor(bt, "block_tables", 2, MSA_INT32, 4))) return rc;
-  if ((rc = check_tensor(cu, "cu_seqlens_q", 1, MSA_INT64, 8))) return rc;
-  if ((rc = check_tensor(used, "used_kv_lens", 1, MSA_INT32, 4))) return rc;
+  if ((rc = check_tensor(sel, "selected", 3, MSA_INT32, 4, nd))) return rc;
+  if ((rc = check_tensor(bt, "block_tables", 2, MSA_INT32, 4, nd))) return rc;
+  if ((rc = check_tensor(cu, "cu_seqlens_q", 1, MSA_INT64, 8, nd))) return rc;
+  if ((rc = check_tensor(used, "used_kv_lens", 1, MSA_INT32, 4, nd))) return rc;
   if (causal != 0 && causal != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   const int64_t Tq = q->shape[0], Hq = q->shape[1], Hkv = k->shape[1], NP = k->shape[0];
   const int64_t B = bt->shape[0], MP = bt->shape[1];
@@ -119,12 +121,12 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
   if (used->shape[0] != B) return fail(MSA_ERR_INVALID_ARGUMENT, "used_kv_lens: expected %lld entries", (long long)B);
   if (B > 0 && MP < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "block_tables: max_pages must be >= 1");
   if (out) {
-    if ((rc = check_tensor(out, "out", 3, q->dtype, 16))) return rc;
+    if ((rc = check_tensor(out, "out", 3, q->dtype, 16, nd))) return rc;
     if (out->shape[0] != Tq || out->shape[1] != Hq || out->shape[2] != 128)
       return fail(MSA_ERR_INVALID_ARGUMENT, "out: shape must equal q's");
   }
   if (lse) {
-    if ((rc = check_tensor(lse, "lse", 2, MSA_FP32, 4))) return rc;
+    if ((rc = check_tensor(lse, "lse", 2, MSA_FP32, 4, nd))) return rc;
     if (lse->shape[0] != Hq || lse->shape[1] != Tq) return fail(MSA_ERR_INVALID_ARGUMENT, "lse: shape must be [Hq, Tq]");
   }
   // int32 indexing limits of the kernels
@@ -155,8 +157,26 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
 }
 
 // ---------------------------------------------------------------------------
-// workspace: one growable device buffer per device
+// workspace
+//
+// A call needs three kinds of device memory besides its inputs and outputs:
+//   - a counter set (work-queue heads, totals), zero when the call starts;
+//   - the residual token bitmaps (one bit per (row, token)), zero when the
+//     call starts; only calls that may have residual slots use them;
+//   - planning arrays and, for calls that may have residual slots, the
+//     KV-outer partial results (layout() below).
+// Absent chunks read a page of zeros, a static device array that is never
+// written.
+//
+// The library-owned workspace (msa_kvouter_attention) keeps two counter sets
+// used on alternate calls and a bitmap that every call leaves zeroed, so no
+// fill runs per call; it grows on demand (synchronising the device once).
+// A caller-owned workspace (msa_kvouter_attention_ws) holds one counter set
+// and the bitmap at its start, cleared by a fill kernel at the start of
+// every call that uses them.
 // ---------------------------------------------------------------------------
+__device__ __attribute__((aligned(256))) uint8_t g_zero_page[msa::kZeroPageBytes] = {};
+
 struct Carve {
   size_t off = 0;
   template <typename T>
@@ -169,15 +189,17 @@ struct Carve {
 };
 
 // Lays the planning and partial arrays out in `base` (or only sizes them when
-// base is null). Returns the bytes used. The counters, the zero page and the
-// bitmap live in the separate zero-state buffer.
-size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
+// base is null). Returns the bytes used. `residual`: the arrays of the
+// residual inversion (bitmap copies and prefixes, the residual order);
+// `with_partials`: the KV-outer partials and the tile tables. Calls whose
+// tiles are all finished by the front kernel (front_only) need neither.
+size_t layout(const Dims& d, char* base, msa::Params* p, bool residual, bool with_partials) {
   Carve c;
   const size_t nslots = (size_t)d.Tq * d.Hkv * d.K;
   const size_t TG = (size_t)d.Tq * d.Hkv;
   const size_t words = (size_t)d.NR * d.W;
-  p->wordpre = c.take<uint32_t>(base, words);
-  p->wordbits = c.take<uint32_t>(base, words);
+  p->wordpre = c.take<uint32_t>(base, residual ? words : 0);
+  p->wordbits = c.take<uint32_t>(base, residual ? words : 0);
   p->slot_flag = c.take<uint8_t>(base, nslots);
   p->tok_chain = c.take<int32_t>(base, TG);
   p->tok_nres = c.take<int32_t>(base, TG);
@@ -186,8 +208,8 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   p->row_cnt = c.take<int32_t>(base, d.NR);
   p->row_off = c.take<int32_t>(base, (size_t)d.NR + 1);
   p->unit_off = c.take<int32_t>(base, (size_t)d.NR + 1);
-  p->ent = c.take<int32_t>(base, nslots);
-  p->slot_pos = c.take<int32_t>(base, nslots);
+  p->ent = c.take<int32_t>(base, residual ? nslots : 0);
+  p->slot_pos = c.take<int32_t>(base, residual ? nslots : 0);
   if (with_partials) {
     p->scratch_row = c.take<char>(base, 8192);
     p->res_list = c.take<int32_t>(base, nslots);
@@ -211,101 +233,90 @@ size_t layout(const Dims& d, char* base, msa::Params* p, bool with_partials) {
   return c.off + 256;
 }
 
-struct DeviceWs {
-  void* ptr = nullptr;   // scratch: planning arrays and partial results
-  size_t bytes = 0;
-  void* zs = nullptr;    // zero-state: counter sets, zero page, bitmap
-  size_t zs_bytes = 0;
+constexpr size_t kCntSetBytes = 256;  // one counter set, padded
+static_assert(msa::kCntSlots * sizeof(int32_t) <= kCntSetBytes, "counter set");
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  bool ready = false;           // num_cu and zero_page are known
   int num_cu = 0;
-  int parity = 0;        // counter set of the next call
-  bool dirty = false;    // zero-state must be cleared before use
+  const void* zero_page = nullptr;  // device address of g_zero_page on this device
+  // the library-owned workspace
+  void* ptr = nullptr;  // planning arrays and partial results
+  size_t bytes = 0;
+  void* zs = nullptr;   // zero-state: two counter sets, then the bitmap
+  size_t zs_bytes = 0;
+  int parity = 0;       // counter set of the next call
+  bool dirty = false;   // zero-state must be cleared before use
 };
 
+// Held by every entry point that touches a device's state, from the lease of
+// its workspace through the last launch that uses it (launches are
+// asynchronous, so this is short).
 std::mutex g_ws_mutex;
-std::vector<DeviceWs> g_ws;
+DeviceState g_dev[kMaxDevices];
 
-struct WsLease {
-  void* scratch;
-  char* zs;
-  int num_cu;
-  int parity;
-  bool clear;
-  DeviceWs* ws;
-};
-
-// Scratch of `need` bytes and a zero-state buffer holding `bitmap_words`.
-// Growing either synchronises the device; a new zero-state buffer is zeroed.
-// the compute-unit count of device dev, queried once (g_ws_mutex held)
-int32_t ensure_cu_count(DeviceWs& w, int dev) {
-  if (w.num_cu == 0) {
+// State of the current device (g_ws_mutex held): compute-unit count and the
+// zero page's address are queried once per device.
+int32_t device_state(DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  DeviceState& w = g_dev[dev];
+  if (!w.ready) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return fail(MSA_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
+    void* zp = nullptr;
+    if (hipGetSymbolAddress(&zp, HIP_SYMBOL(g_zero_page)) != hipSuccess || !zp) {
+      (void)hipGetLastError();
+      return fail(MSA_ERR_HIP, "cannot resolve the zero page on device %d", dev);
+    }
     w.num_cu = n;
+    w.zero_page = zp;
+    w.ready = true;
   }
-  return 0;
+  *out = &w;
+  return MSA_OK;
 }
 
-// compute units of the current device
-int32_t current_cu_count(int* n) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
-  std::lock_guard<std::mutex> lk(g_ws_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  const int32_t rc = ensure_cu_count(g_ws[dev], dev);
-  *n = g_ws[dev].num_cu;
-  return rc;
-}
-
-int32_t get_workspace(size_t need, size_t bitmap_words, WsLease* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice failed: no usable HIP device");
-  std::lock_guard<std::mutex> lk(g_ws_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  DeviceWs& w = g_ws[dev];
-  if (int32_t rc = ensure_cu_count(w, dev)) return rc;
-  const size_t zs_need = msa::kZsHeaderBytes + bitmap_words * 4;
-  if (w.bytes < need || w.zs_bytes < zs_need) {
-    if (w.ptr || w.zs) {
-      if (hipDeviceSynchronize() != hipSuccess) return fail(MSA_ERR_HIP, "hipDeviceSynchronize failed while growing the workspace");
-    }
-    if (w.bytes < need) {
-      if (w.ptr) (void)hipFree(w.ptr);
+// The library-owned workspace of the device (g_ws_mutex held): scratch of
+// `need` bytes and a zero-state buffer of two counter sets plus
+// `bitmap_words` words. Growing either synchronises the device; a new
+// zero-state buffer is zeroed.
+int32_t grow_workspace(DeviceState& w, size_t need, size_t bitmap_words) {
+  const size_t zs_need = 2 * kCntSetBytes + bitmap_words * 4;
+  if (w.bytes >= need && w.zs_bytes >= zs_need) return MSA_OK;
+  if (w.ptr || w.zs) {
+    if (hipDeviceSynchronize() != hipSuccess) return fail(MSA_ERR_HIP, "hipDeviceSynchronize failed while growing the workspace");
+  }
+  if (w.bytes < need) {
+    if (w.ptr) (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.bytes = 0;
+    const size_t alloc = std::max(need, (size_t)1 << 20);
+    if (hipMalloc(&w.ptr, alloc) != hipSuccess) {
+      (void)hipGetLastError();
       w.ptr = nullptr;
-      w.bytes = 0;
-      const size_t alloc = std::max(need, (size_t)1 << 20);
-      if (hipMalloc(&w.ptr, alloc) != hipSuccess) {
-        (void)hipGetLastError();
-        w.ptr = nullptr;
-        return fail(MSA_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", alloc);
-      }
-      w.bytes = alloc;
+      return fail(MSA_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", alloc);
     }
-    if (w.zs_bytes < zs_need) {
-      if (w.zs) (void)hipFree(w.zs);
-      w.zs = nullptr;
-      w.zs_bytes = 0;
-      const size_t alloc = std::max(zs_need, (size_t)1 << 20);
-      if (hipMalloc(&w.zs, alloc) != hipSuccess) {
-        (void)hipGetLastError();
-        w.zs = nullptr;
-        return fail(MSA_ERR_OUT_OF_MEMORY, "zero-state allocation of %zu bytes failed", alloc);
-      }
-      if (hipMemset(w.zs, 0, alloc) != hipSuccess) {
-        w.dirty = true;
-      } else {
-        w.dirty = false;
-      }
-      w.zs_bytes = alloc;
-      w.parity = 0;
-    }
+    w.bytes = alloc;
   }
-  out->scratch = w.ptr;
-  out->zs = (char*)w.zs;
-  out->num_cu = w.num_cu;
-  out->parity = w.parity;
-  out->clear = w.dirty;
-  out->ws = &w;
+  if (w.zs_bytes < zs_need) {
+    if (w.zs) (void)hipFree(w.zs);
+    w.zs = nullptr;
+    w.zs_bytes = 0;
+    const size_t alloc = std::max(zs_need, (size_t)1 << 20);
+    if (hipMalloc(&w.zs, alloc) != hipSuccess) {
+      (void)hipGetLastError();
+      w.zs = nullptr;
+      return fail(MSA_ERR_OUT_OF_MEMORY, "zero-state allocation of %zu bytes failed", alloc);
+    }
+    w.dirty = hipMemset(w.zs, 0, alloc) != hipSuccess;
+    w.zs_bytes = alloc;
+    w.parity = 0;
+  }
   return MSA_OK;
 }
 
@@ -333,6 +344,72 @@ void fill_inputs(msa::Params* p, const Dims& d, const msa_tensor* sel, const msa
   p->scale_log2 = (float)(1.0 / std::sqrt(128.0) * 1.4426950408889634);
 }
 
+// The attention launch plan. Tiles of one token each make every tile's chain
+// its token's whole selection, so no slot is residual and the front kernel
+// finishes every tile (at most 16 query rows per token); the index, unit and
+// tile kernels are then not launched. Used for decode (one query token per
+// sequence slot, Tq == B) and for small decode-shaped batches (Tq <= 4B)
+// whose tokens all fit in one round of front workgroups, where launches cost
+// more than the KV a sequence's tokens would otherwise share.
+struct Plan {
+  Dims d;
+  bool narrow;      // decode-shaped: the front kernel streams residual-free tiles of <= 16 rows
+  bool front_only;  // every tile is finished by the front kernel
+};
+
+Plan make_plan(const Dims& dims, int num_cu) {
+  Plan pl;
+  pl.d = dims;
+  pl.narrow = dims.G <= 16 && (int64_t)dims.Tq <= 4 * (int64_t)dims.B;
+  pl.front_only = pl.narrow && (dims.Tq == dims.B || (int64_t)dims.Tq * dims.Hkv <= 2 * (int64_t)num_cu);
+  if (pl.front_only) pl.d.T = 1;
+  return pl;
+}
+
+// bytes of a caller-owned workspace for plan pl: counter set, bitmap (calls
+// with possible residual slots), planning arrays and partials
+size_t ws_bytes_for(const Plan& pl) {
+  msa::Params tmp{};
+  const size_t head = kCntSetBytes + (pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W * 4);
+  return ((head + 255) & ~size_t(255)) + layout(pl.d, nullptr, &tmp, !pl.front_only, !pl.front_only);
+}
+
+// Enqueues the kernels of one attention call. `counters` is zero on entry
+// (or is cleared by the fill when clear_words > 0); counters_next, when not
+// null, is cleared by the call's last kernel for the next call.
+hipError_t enqueue_attention(msa::Params& p, const Plan& pl, int num_cu, uint32_t* clear, int64_t clear_words,
+                             hipStream_t st) {
+  const Dims& d = pl.d;
+  // decode-shaped batches (few queries per sequence, at most 16 query rows
+  // per token) finish their residual-free tiles in the front kernel, one
+  // workgroup per token; otherwise the front kernel runs one workgroup per
+  // tile and lists every tile for the tile kernel
+  p.stream_narrow = pl.narrow ? 1 : 0;
+  p.list_tiles = p.stream_narrow;  // otherwise the tile kernel enumerates every tile itself
+  p.front_only = pl.front_only ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (clear_words > 0) e = msa::launch_fill(clear, clear_words, 0u, st);
+  if (e == hipSuccess) e = msa::launch_front(p, d.q_elem, d.kv_elem, st);
+  // decode-shaped batches rarely have residual slots: there the unit kernel
+  // derives the residual order itself and the materialising pass (one more
+  // launch) is skipped
+  p.ent_ready = p.stream_narrow ? 0 : 1;
+  if (!pl.front_only) {
+    if (e == hipSuccess) e = msa::launch_index(p, p.ent_ready != 0, st);
+    if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, num_cu, st);
+    if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, num_cu, st);
+  }
+  return e;
+}
+
+void fill_attention_io(msa::Params* p, const msa_tensor* q, const msa_tensor* k, const msa_tensor* v,
+                       msa_tensor* out, msa_tensor* lse) {
+  p->q = q->data;
+  p->k = k->data;
+  p->v = v->data;
+  p->out = out->data;
+  p->lse = lse ? (float*)lse->data : nullptr;
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -420,7 +497,7 @@ int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches)
 }
 
 
-const char* msa_last_error(void) { return g_err.c_str(); }
+const char* msa_last_error(void) { return g_err; }
 
 const char* msa_version(void) { return "msa_kvouter 0.1.0 (gfx950)"; }
 
@@ -435,64 +512,90 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
                         causal, out, lse, &d);
   if (rc) return rc;
   if (d.Tq == 0) return ok();
-  // Tiles of one token each make every tile's chain its token's whole
-  // selection, so no slot is residual and the front kernel finishes every
-  // tile (at most 16 query rows per token); the index, unit and tile kernels
-  // are then not launched. Used for decode (one query token per sequence
-  // slot, Tq == B) and for small decode-shaped batches (Tq <= 4B) whose
-  // tokens all fit in one round of front workgroups, where launches cost
-  // more than the KV a sequence's tokens would otherwise share.
-  int ncu = 0;
-  if ((rc = current_cu_count(&ncu))) return rc;
-  const bool narrow = d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B;
-  const bool front_only = narrow && (d.Tq == d.B || (int64_t)d.Tq * d.Hkv <= 2 * (int64_t)ncu);
-  if (front_only) d.T = 1;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);  // held through the last launch
+  DeviceState* w = nullptr;
+  if ((rc = device_state(&w))) return rc;
+  const Plan pl = make_plan(d, w->num_cu);
   msa::Params p{};
-  const size_t need = layout(d, nullptr, &p, true);
-  WsLease ws;
-  if ((rc = get_workspace(need, (size_t)d.NR * d.W, &ws))) return rc;
-  layout(d, (char*)ws.scratch, &p, true);
+  const size_t need = layout(pl.d, nullptr, &p, !pl.front_only, !pl.front_only);
+  if ((rc = grow_workspace(*w, need, pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W))) return rc;
+  layout(pl.d, (char*)w->ptr, &p, !pl.front_only, !pl.front_only);
   p.slot_pos = nullptr;  // the per-token residual lists replace it here
-  fill_inputs(&p, d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
-  // decode-shaped batches (few queries per sequence, at most 16 query rows
-  // per token) finish their residual-free tiles in the front kernel, one
-  // workgroup per token; otherwise the front kernel runs one workgroup per
-  // tile and lists every tile for the tile kernel
-  p.stream_narrow = (d.G <= 16 && (int64_t)d.Tq <= 4 * (int64_t)d.B) ? 1 : 0;
-  p.list_tiles = p.stream_narrow;  // otherwise the tile kernel enumerates every tile itself
-  p.front_only = front_only ? 1 : 0;
-  int32_t* sets = (int32_t*)ws.zs;
-  p.counters = sets + ws.parity * msa::kCntSlots;
-  p.counters_next = sets + (1 - ws.parity) * msa::kCntSlots;
-  p.zero_page = ws.zs + 2 * msa::kCntSlots * sizeof(int32_t);
-  p.bitmap = (uint32_t*)(ws.zs + msa::kZsHeaderBytes);
-  p.q = q->data;
-  p.k = k_cache->data;
-  p.v = v_cache->data;
-  p.out = out->data;
-  p.lse = lse ? (float*)lse->data : nullptr;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
-  if (e == hipSuccess) e = msa::launch_front(p, d.q_elem, d.kv_elem, st);
-  // decode-shaped batches rarely have residual slots: there the unit kernel
-  // derives the residual order itself and the materialising pass (one more
-  // launch) is skipped
-  p.ent_ready = p.stream_narrow ? 0 : 1;
-  if (!front_only) {
-    if (e == hipSuccess) e = msa::launch_index(p, p.ent_ready != 0, st);
-    if (e == hipSuccess) e = msa::launch_units(p, d.q_elem, d.kv_elem, ws.num_cu, st);
-    if (e == hipSuccess) e = msa::launch_tiles(p, d.q_elem, d.kv_elem, ws.num_cu, st);
+  fill_inputs(&p, pl.d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
+  fill_attention_io(&p, q, k_cache, v_cache, out, lse);
+  int32_t* sets = (int32_t*)w->zs;
+  p.counters = sets + w->parity * (kCntSetBytes / 4);
+  p.counters_next = sets + (1 - w->parity) * (kCntSetBytes / 4);
+  p.zero_page = w->zero_page;
+  p.bitmap = (uint32_t*)((char*)w->zs + 2 * kCntSetBytes);
+  const hipError_t e = enqueue_attention(p, pl, w->num_cu, (uint32_t*)w->zs,
+                                         w->dirty ? (int64_t)(w->zs_bytes / 4) : 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    w->dirty = true;  // some kernels may not have run: clear everything next time
+    return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
+  w->dirty = false;
+  w->parity = 1 - w->parity;
+  return ok();
+}
+
+int32_t msa_kvouter_workspace_bytes(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                                    const msa_tensor* selected, const msa_tensor* block_tables,
+                                    const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                                    int32_t page_size, int32_t causal, size_t* bytes) {
+  if (!bytes) return fail(MSA_ERR_INVALID_ARGUMENT, "bytes: null pointer");
+  *bytes = 0;
+  Dims d;
+  const int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                              causal, nullptr, nullptr, &d, /*need_data=*/false);
+  if (rc) return rc;
+  if (d.Tq == 0) return ok();
+  // the largest plan any device can choose for these shapes: a batch of
+  // one token per sequence is front-only everywhere; other decode-shaped
+  // batches are front-only only when they fit a device's front workgroups
+  Plan pl = make_plan(d, 0);
+  *bytes = ws_bytes_for(pl);
+  return ok();
+}
+
+int32_t msa_kvouter_attention_ws(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                                 const msa_tensor* selected, const msa_tensor* block_tables,
+                                 const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                                 int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                        causal, out, lse, &d);
+  if (rc) return rc;
+  if (d.Tq == 0) return ok();
+  if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace: null pointer");
+  if ((uintptr_t)workspace % 256) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace: not 256-byte aligned");
+  DeviceState* w = nullptr;
   {
-    std::lock_guard<std::mutex> lk(g_ws_mutex);
-    if (e != hipSuccess) {
-      ws.ws->dirty = true;  // some kernels may not have run: clear everything next time
-    } else {
-      ws.ws->dirty = false;
-      ws.ws->parity = 1 - ws.parity;
-    }
+    std::lock_guard<std::mutex> lk(g_ws_mutex);  // device facts only; the workspace is the caller's
+    if ((rc = device_state(&w))) return rc;
   }
+  const Plan pl = make_plan(d, w->num_cu);
+  const size_t need = ws_bytes_for(pl);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "workspace: %zu bytes given, this call needs %zu", workspace_bytes, need);
+  char* base = (char*)workspace;
+  const size_t bitmap_words = pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W;
+  const size_t head = (kCntSetBytes + bitmap_words * 4 + 255) & ~size_t(255);
+  msa::Params p{};
+  layout(pl.d, base + head, &p, !pl.front_only, !pl.front_only);
+  p.slot_pos = nullptr;
+  fill_inputs(&p, pl.d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
+  fill_attention_io(&p, q, k_cache, v_cache, out, lse);
+  p.counters = (int32_t*)base;
+  p.counters_next = nullptr;
+  p.zero_page = w->zero_page;
+  p.bitmap = (uint32_t*)(base + kCntSetBytes);
+  // A front-only call uses neither the counters nor the bitmap (every tile is
+  // finished where it is classified); any other call clears both first.
+  const int64_t clear_words = pl.front_only ? 0 : (int64_t)((kCntSetBytes + bitmap_words * 4) / 4);
+  const hipError_t e = enqueue_attention(p, pl, w->num_cu, (uint32_t*)base, clear_words, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -534,10 +637,12 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   d.T = tile_tokens;
   d.Tu = unit_tokens;
   msa::Params p{};
-  const size_t need = layout(d, nullptr, &p, false);
-  WsLease ws;
-  if ((rc = get_workspace(need, (size_t)d.NR * d.W, &ws))) return rc;
-  layout(d, (char*)ws.scratch, &p, false);
+  const size_t need = layout(d, nullptr, &p, true, false);
+  std::lock_guard<std::mutex> lk(g_ws_mutex);  // held through the last launch
+  DeviceState* w = nullptr;
+  if ((rc = device_state(&w))) return rc;
+  if ((rc = grow_workspace(*w, need, (size_t)d.NR * d.W))) return rc;
+  layout(d, (char*)w->ptr, &p, true, false);
   fill_inputs(&p, d, selected, nullptr, cu_seqlens_q, used_kv_lens, causal);
   p.T = tile_tokens;
   p.Tu = unit_tokens;
@@ -545,8 +650,8 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   p.list_tiles = 1;
   p.counters = o->counters;  // caller-visible counters; the bitmap stays internal
   p.counters_next = nullptr;
-  p.zero_page = ws.zs + 2 * msa::kCntSlots * sizeof(int32_t);
-  p.bitmap = (uint32_t*)(ws.zs + msa::kZsHeaderBytes);
+  p.zero_page = w->zero_page;
+  p.bitmap = (uint32_t*)((char*)w->zs + 2 * kCntSetBytes);
   p.slot_flag = o->slot_flag;
   p.tok_chain = o->tok_chain;
   p.tok_nres = o->tok_nres;
@@ -558,17 +663,16 @@ int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens
   p.tile_items = o->tile_items;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (ws.clear) e = msa::launch_fill((uint32_t*)ws.zs, (int64_t)(ws.ws->zs_bytes / 4), 0u, st);
+  if (w->dirty) e = msa::launch_fill((uint32_t*)w->zs, (int64_t)(w->zs_bytes / 4), 0u, st);
   if (e == hipSuccess) e = msa::launch_fill((uint32_t*)o->counters, 8, 0u, st);
   if (e == hipSuccess) e = msa::launch_fill((uint32_t*)o->slot_pos, (int64_t)Tq * Hkv * K, 0xFFFFFFFFu, st);
   if (e == hipSuccess) e = msa::launch_front(p, -1, -1, st);
   if (e == hipSuccess) e = msa::launch_index(p, true, st);
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mutex);
-    if (e != hipSuccess) ws.ws->dirty = true;
-    else if (ws.clear) ws.ws->dirty = false;
+  if (e != hipSuccess) {
+    w->dirty = true;
+    return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  w->dirty = false;
   return ok();
 }
 
@@ -703,13 +807,16 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
   // is the caller's `scores` or the library workspace.
   const bool fused = Tq > 4 * B && nb_cap <= 256;
   float* table = nullptr;
+  std::unique_lock<std::mutex> lk(g_ws_mutex, std::defer_lock);
   if (!fused) {
     if (scores) {
       table = (float*)scores->data;
     } else {
-      WsLease ws;
-      if ((rc = get_workspace((size_t)Tq * Hkv * nb_cap * sizeof(float), 0, &ws))) return rc;
-      table = (float*)ws.scratch;
+      lk.lock();  // held through the launches that use the library's workspace
+      DeviceState* w = nullptr;
+      if ((rc = device_state(&w))) return rc;
+      if ((rc = grow_workspace(*w, (size_t)Tq * Hkv * nb_cap * sizeof(float), 0))) return rc;
+      table = (float*)w->ptr;
     }
   }
   msa::profile_mark(msa::kKSelect, true, (hipStream_t)stream);

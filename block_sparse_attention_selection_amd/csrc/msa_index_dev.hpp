@@ -1,6 +1,6 @@
-// msa_index_dev.hpp -- device functions of the residual inversion, shared by
-// the staged index kernels (msa_index.hip) and the persistent back kernel
-// (msa_forward.hip).
+// msa_index_dev.hpp -- device functions of the residual inversion and of the
+// tile descriptors, shared by the classifiers (msa_forward.hip), the index
+// kernels (msa_index.hip) and the unit and tile kernels (msa_tiles.hip).
 #pragma once
 
 #include "msa_device.hpp"
@@ -121,12 +121,13 @@ __device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, i
 // s, nt tokens, KV head g, chain of n_ch blocks): tdesc[2 item] = (t0, s, nt,
 // n_ch), tdesc[2 item + 1] = (reachable keys Leff, base position: pos =
 // base + token, g, nfull), and the table ctab[item * 4 topk + ...] of
-// (element offset low, high, first key, keys present) per chunk, offset -1
-// for a chunk no row can see. The table lists first the nfull chunks every
-// row of the tile sees whole (all keys below Leff and at or before the first
-// row's position), then the others, each class in chain order, so that the
-// tile kernel runs its unmasked loop up to nfull. One wave calls this (lane
-// 0..63).
+// (element offset low, high, first key, keys present) per chunk. A chunk no
+// row can see, or whose page id lies outside the pool, has offset -1 and no
+// keys present. The table lists first the nfull chunks every row of the
+// tile sees whole (32 keys present, all at or before the first row's
+// position), then the others, each class in chain order, so that the tile
+// kernel runs its unmasked loop up to nfull and masks the rest against
+// their first key + keys present. One wave calls this (lane 0..63).
 __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t0, int s, int nt, int n_ch, int L,
                                                 int Tq_s, int64_t q0, int g, const int* chain, int lane) {
   const int Leff = min(L, p.MP * p.P);
@@ -134,26 +135,39 @@ __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t
   const int pmax = p.causal ? base + t0 + nt - 1 : INT_MAX;
   const int pmin = p.causal ? base + t0 : INT_MAX;
   const size_t K4 = 4 * (size_t)p.K;
-  const int n = 4 * n_ch;
+  const int n = 4 * n_ch;  // at most 4 * 64: four batches of 64 chunks
   auto key_of = [&](int ci) { return 128 * chain[ci >> 2] + 32 * (ci & 3); };
-  auto whole = [&](int ci) {
+  int64_t offs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = 64 * i + lane;
+    const int key0 = ci < n ? key_of(ci) : 0;
+    offs[i] = (ci >= n || key0 > pmax) ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
+  }
+  auto whole = [&](int ci, int64_t off) {
     const int k0 = key_of(ci);
-    return k0 + 31 < Leff && k0 + 31 <= pmin;
+    return off >= 0 && k0 + 31 < Leff && k0 + 31 <= pmin;
   };
   int nfull = 0;
-  for (int b = 0; b < n; b += 64) nfull += __popcll(__ballot(b + lane < n && whole(b + lane)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = 64 * i + lane;
+    nfull += __popcll(__ballot(ci < n && whole(ci, offs[i])));
+  }
   const uint64_t below = (1ull << lane) - 1ull;
   int fb = 0, pb = 0;  // whole / other chunks of earlier batches
-  for (int b = 0; b < n; b += 64) {
-    const int ci = b + lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = 64 * i + lane;
     const bool in = ci < n;
-    const bool f = in && whole(ci);
+    const int64_t off = offs[i];
+    const bool f = in && whole(ci, off);
     const uint64_t bf = __ballot(f), bo = __ballot(in && !f);
     if (in) {
       const int at = f ? fb + __popcll(bf & below) : nfull + pb + __popcll(bo & below);
       const int key0 = key_of(ci);
-      const int64_t off = key0 > pmax ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
-      p.ctab[(size_t)item * K4 + at] = int4{(int)(uint32_t)(uint64_t)off, (int)(off >> 32), key0, min(32, Leff - key0)};
+      const int present = off >= 0 ? min(32, Leff - key0) : 0;
+      p.ctab[(size_t)item * K4 + at] = int4{(int)(uint32_t)(uint64_t)off, (int)(off >> 32), key0, present};
     }
     fb += __popcll(bf);
     pb += __popcll(bo);

@@ -18,13 +18,13 @@ enum Counter {
   kCntSlots = 64,     // counters per set
 };
 
-// zero-state buffer: two counter sets used on alternate calls, a page of
-// zeros that absent chunks are read from, and the residual token bitmaps.
-// Every call leaves it as it found it: the bitmap words are cleared by the
-// kernel that consumes them and the tile kernel clears the counter set of
-// the next call.
+// A page of zeros that absent chunks are read from (a static device array,
+// never written). The counter sets and the residual token bitmaps are zero
+// when a call starts: the library-owned zero-state buffer is left that way
+// by every call (the bitmap words are cleared by the kernel that consumes
+// them, and the call's last kernel clears the counter set of the next call);
+// a caller-owned workspace is cleared by a fill kernel instead.
 constexpr size_t kZeroPageBytes = 16384;
-constexpr size_t kZsHeaderBytes = 2 * kCntSlots * sizeof(int32_t) + kZeroPageBytes;
 
 enum ElemCode { kElemBF16 = 0, kElemF16 = 1, kElemFP8 = 2 };
 

@@ -1,22 +1,25 @@
-// msa_tiles.hip -- 128-row query tiles on v_mfma_f32_32x32x16 (gfx950).
+// msa_tiles.hip -- query rows in groups of 32 per wave on
+// v_mfma_f32_32x32x16 (gfx950).
 //
 // Two kernels of the prefill-shaped path (fw-ai/minimax-kernels README,
 // intro: a selected KV block is loaded once and every query that selected it
 // is processed against it):
-//   k_units  KV-outer units. A unit (window) is up to Tu tokens that picked
-//            block b of KV head g outside their tile's chain; its rows are
-//            the tokens x the G query heads of g. The block is staged once
-//            in LDS per sequence and every piece of at most 128 rows is
-//            multiplied against it, writing one normalised bf16/fp16
-//            partial O and one LSE per (residual slot, head).
-//   k_tiles  one tile per item: the chain (blocks picked by every token of
-//            the tile) streams through a ring of LDS chunk slots while the
-//            tile's rows stay in registers; the unit partials of the tile's
-//            residual slots are then merged by their LSE and the final O and
-//            LSE are written (the combine of the pages' design, fused into
-//            the tile's epilogue).
+//   k_units  KV-outer units, 4 waves (pieces of up to 128 query rows). A unit
+//            (window) is up to Tu tokens that picked block b of KV head g
+//            outside their tile's chain; its rows are the tokens x the G
+//            query heads of g. The block is staged once in LDS per sequence
+//            and every piece is multiplied against it, writing one
+//            normalised bf16/fp16 partial O and one LSE per (residual slot,
+//            head).
+//   k_tiles  8 waves, one tile of up to 256 query rows per item: the chain
+//            (blocks picked by every token of the tile) streams through a
+//            ring of LDS chunk slots while the tile's rows stay in
+//            registers; the unit partials of the tile's residual slots are
+//            then merged by their LSE and the final O and LSE are written
+//            (the combine of the pages' design, fused into the tile's
+//            epilogue).
 //
-// Each of the four waves owns 32 query rows. Scores are computed transposed,
+// Each wave owns 32 query rows. Scores are computed transposed,
 // S^T = K Q^T, so that the D fragment of a lane holds 16 keys of one query
 // row; those probabilities are the B operand of O^T = V^T P^T as they stand.
 // The V^T operand is read from the row-major LDS tile with the transposing
@@ -32,8 +35,9 @@
 // accumulator already holds them. O^T d-tile t (0..3) covers d = 32t + m.
 //
 // LDS tiles of 32 keys x 128 dims (16-bit) are stored row-major with the
-// 16-byte pieces of row r XOR-swizzled by r & 15, which keeps the K-operand
-// reads (one row per lane) and the transposing V reads conflict-light.
+// 16-byte pieces of row r XOR-swizzled (K tiles by r & 15, V tiles by
+// 4 (r & 3)), which keeps the K-operand reads (one row per lane) and the
+// transposing V reads conflict-light.
 #include <limits.h>
 
 #include "msa_device.hpp"
@@ -645,6 +649,7 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
   const int64_t* cu = seq_lds ? s_cu : p.cu;
   const int* used = seq_lds ? s_used : p.used;
   int st_s = -1, st_b = -1, st_g = -1;  // staged block (uniform)
+  unsigned st_absent = 0u;              // bit q: chunk q of the staged block has no keys (page outside the pool)
   DmaLane dl;
   dl.init();
   XcdQueue wq;
@@ -737,20 +742,22 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
         if (p.causal && tok >= 0) rt.pos = base + tok;
         if (s_run != st_s || b != st_b || g != st_g) {
           ring_barrier();  // every wave is done with the previous block
+          int64_t offs[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) offs[q] = chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff);
+          st_absent = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st_absent |= offs[q] < 0 ? 1u << q : 0u;
           if constexpr (kFp8) {
             Raw8 raw[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v,
-                                   chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff), Leff - (kBlk * b + 32 * q),
+              raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, offs[q], Leff - (kBlk * b + 32 * q),
                                    p.zero_page);
 #pragma unroll
             for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
             __syncthreads();
           } else {
-            int64_t offs[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) offs[q] = chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               issue_chunk16(p.k, p.v, offs[q], Leff - (kBlk * b + 32 * q), dl, s_blk + q * kSlotU4,
@@ -769,8 +776,10 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
           for (int q = 0; q < 4; ++q) {
             const int key0 = kBlk * b + 32 * q;
             if (key0 >= Leff || key0 > pmax) break;
-            const bool full = key0 + 31 < Leff && key0 + 31 <= pmin;
-            rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, Leff, s_run, !full,
+            // keys [key0, lim) are present: none when the chunk's page is absent
+            const int lim = ((st_absent >> q) & 1u) ? key0 : min(Leff, key0 + 32);
+            const bool full = lim == key0 + 32 && key0 + 31 <= pmin;
+            rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, lim, s_run, !full,
                            p.scale_log2);
           }
         }
@@ -936,7 +945,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
     const int t0 = d0.x, s = d0.y, nt = d0.z;
     const int nck = nt > 0 ? 4 * d0.w : 0;
     const int nfull = min(d1.w, nck);
-    const int Leff = d1.x, base = d1.y, g = d1.z;
+    const int base = d1.y, g = d1.z;
     const int rows = nt * G;
     const int pmin = p.causal ? base + t0 : INT_MAX;
     const bool lds_res = nt * K <= kPosMax;
@@ -976,8 +985,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
           const int4 e = s_tab[bf][ci];
           if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
-            const bool full = e.z + 31 < Leff && e.z + 31 <= pmin;
-            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, Leff, s, !full, p.scale_log2);
+            // keys [e.z, e.z + e.w) are present (e.w < 32 only at the used length)
+            const bool full = e.w == 32 && e.z + 31 <= pmin;
+            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, e.z + e.w, s, !full, p.scale_log2);
           }
           if (stager && ci + 1 < nck)
             store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
@@ -1031,13 +1041,16 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
             chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? 4 * dn.w : 0, off, nr);
           }
           issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + nx));
-          const int key0 = mask ? s_tab[bf][ci].z : 0;
+          // a masked chunk's keys [key0, lim) are present: none when its page
+          // is absent or no row sees it, fewer than 32 at the used length
+          const int4 ec = mask ? s_tab[bf][ci] : int4{0, 0, 0, 0};
+          const int key0 = ec.z, lim = ec.z + ec.w;
           const char* vprev = (const char*)(slot_ptr(rbase + (ci > 0 ? ci - 1 : 0)) + kChunkU4);
           const char* vcur = (const char*)(slot_ptr(rbase + ci) + kChunkU4);
           const u32x4* knext = slot_ptr(rbase + (ci + 1 < nck ? ci + 1 : ci));
-          const float alpha = mask ? tile_iter<CT, true>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, Leff,
+          const float alpha = mask ? tile_iter<CT, true>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, lim,
                                                          p.scale_log2, out.sc, out.pp, out.vpre)
-                                   : tile_iter<CT, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, Leff,
+                                   : tile_iter<CT, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, lim,
                                                           p.scale_log2, out.sc, out.pp, out.vpre);
           rows_rescale(rt, alpha);
         };

@@ -110,14 +110,81 @@ typedef struct msa_tensor {
  *
  * Scratch memory: the library keeps one growable workspace per device
  * (allocated with hipMalloc on first use or when a larger problem arrives;
- * growing synchronises the device). Concurrent calls on different streams of
- * the same device share that workspace and must not overlap in time.
+ * growing synchronises the device, so the first call at a new size is neither
+ * asynchronous nor capturable into a graph). Calls into one device are
+ * serialised on the host while they enqueue (the library holds a lock from
+ * the workspace lease through the last launch), so several host threads may
+ * call it; but the workspace is one buffer, so calls on different streams of
+ * one device must not overlap in time on the device. Callers that need
+ * either, or that capture the call into a graph, pass their own workspace to
+ * msa_kvouter_attention_ws instead.
+ *
+ * Stages. The pass runs as up to five kernels on `stream`: classification of
+ * every query tile (chains of shared picks, residual picks), the residual
+ * inversion (per-(block, KV head) token lists, the index builder), the
+ * KV-outer units (partial O and LSE per residual pick, split into windows of
+ * bounded rows: the load-balancing split), and the tile kernel, which runs the
+ * chains and merges each row's residual partials by LSE before writing out
+ * and lse. The combine of the pages' design is fused into that last kernel's
+ * epilogue, so no partial of a chain ever leaves registers; that is why there
+ * are no separate split, forward-partials or combine entry points. The index
+ * builder is exposed for bit-exact tests (msa_build_index).
  */
 int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
                               const msa_tensor* v_cache, const msa_tensor* selected,
                               const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
                               const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
                               msa_tensor* out, msa_tensor* lse, void* stream);
+
+/*
+ * msa_kvouter_workspace_bytes -- bytes of the caller-owned workspace that
+ * msa_kvouter_attention_ws needs for these shapes (the same descriptors as
+ * msa_kvouter_attention without out / lse; only shapes and dtypes are read,
+ * data pointers may be NULL). Writes 0 for Tq == 0. The size depends on
+ * shapes only, and it is the largest any device needs for them:
+ *
+ *   - a batch with one query token per sequence (Tq == B) and Hq/Hkv <= 16
+ *     (decode): planning arrays only, Tq*Hkv*(5*topk + 12) +
+ *     12*Hkv*ceil(max_pages*page_size/128) bytes plus 256-byte alignment
+ *     per array (about 72 KB for 64 sequences, Hkv = 8, top-16);
+ *   - any other call: in addition the residual token bitmaps
+ *     (ceil(max_pages*page_size/128) * Hkv * ceil(Tq/32) words), the
+ *     residual order and tile tables, and the KV-outer partial results sized
+ *     for every slot being residual: Tq*Hkv*topk*(Hq/Hkv) rows of 256 bytes
+ *     (O in q's type) plus 4 bytes (LSE). This worst case is reached when no
+ *     two consecutive tokens share a pick; which slots are residual is only
+ *     known on the device. A 16384-token prefill with Hq = 64, Hkv = 8 and
+ *     top-16 needs about 4.45 GB.
+ *
+ * Errors as for msa_kvouter_attention (descriptor errors only).
+ */
+int32_t msa_kvouter_workspace_bytes(const msa_tensor* q, const msa_tensor* k_cache,
+                                    const msa_tensor* v_cache, const msa_tensor* selected,
+                                    const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                                    const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                                    size_t* bytes);
+
+/*
+ * msa_kvouter_attention_ws -- msa_kvouter_attention with a caller-owned
+ * workspace: `workspace` is device memory of `workspace_bytes` bytes (at
+ * least msa_kvouter_workspace_bytes for these shapes, 256-byte aligned) that
+ * the call uses as scratch until the stream reaches the end of its work; its
+ * contents need not be initialised and are unspecified afterwards. The call
+ * allocates nothing, synchronises nothing and issues no memset: it validates
+ * on the host, then enqueues its kernels on `stream` (the first of them
+ * clears the counters and bitmaps it needs, except for decode batches, which
+ * use neither), so it can be captured into a HIP graph. Calls with distinct
+ * workspaces may run concurrently on different streams; calls that share a
+ * workspace must not overlap in time. Arguments, results and errors are
+ * otherwise those of msa_kvouter_attention; a workspace that is too small or
+ * misaligned is MSA_ERR_INVALID_ARGUMENT.
+ */
+int32_t msa_kvouter_attention_ws(const msa_tensor* q, const msa_tensor* k_cache,
+                                 const msa_tensor* v_cache, const msa_tensor* selected,
+                                 const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                                 const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                                 msa_tensor* out, msa_tensor* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * msa_build_index -- the selection inversion and work split, exposed so that

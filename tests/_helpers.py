@@ -97,3 +97,41 @@ def compare(wl: W.Workload, out, lse, pairs, ref_out, ref_lse):
     err_l = np.abs(l[fin] - ref_lse[fin]) if fin.any() else np.zeros(1)
     assert err_l.max() <= ATOL_LSE, f"lse max err {err_l.max():.3e}"
     return float(err_o.max()), float(err_l.max())
+
+
+def product_tiles(wl: W.Workload):
+    """Tile and unit-window sizes the library uses for a prefill-shaped call:
+    tiles of min(128, 256/G) tokens, windows of min(8 max(1, 128/G), 512)."""
+    G = wl.G
+    return min(128, max(1, 256 // G)), min(8 * max(1, 128 // G), 512)
+
+
+def stratified_pairs(wl: W.Workload, per_tile: int = 3, seed: int = 0):
+    """(t, g) pairs that reach every tile item of the tile kernel (the first,
+    the last and random tokens of every tile, for every KV head) and every
+    KV-outer window of the unit kernel (its first and last token), at the
+    tile and window sizes the library uses. Every item of the work queues,
+    whatever XCD range it falls in, is then compared."""
+    from oracle import index_ref
+
+    rng = np.random.default_rng(seed)
+    T, Tu = product_tiles(wl)
+    pairs = set()
+    cu = wl.cu_seqlens_q
+    for s in range(wl.B):
+        for t0 in range(int(cu[s]), int(cu[s + 1]), T):
+            t1 = min(t0 + T, int(cu[s + 1]))
+            toks = {t0, t1 - 1} | set(int(x) for x in rng.integers(t0, t1, size=max(0, per_tile - 2)))
+            for g in range(wl.Hkv):
+                pairs.update(t * wl.Hkv + g for t in toks)
+    nb_max = (wl.block_tables.shape[1] * wl.page_size + 127) // 128
+    ref = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G,
+                          list_all_tiles=True)
+    HK = wl.Hkv * wl.topk
+    for r in range(ref.row_off.size - 1):
+        a, b = int(ref.row_off[r]), int(ref.row_off[r + 1])
+        for w0 in range(a, b, Tu):
+            for e in (w0, min(w0 + Tu, b) - 1):
+                slot = int(ref.ent[e])
+                pairs.add((slot // HK) * wl.Hkv + (slot // wl.topk) % wl.Hkv)
+    return np.array(sorted(pairs), dtype=np.int64)

@@ -206,3 +206,101 @@ def test_select_blocks_argument_checks():
     assert call_sel(args(), causal=2) == INV
     assert call_sel(args(Tq=0)) == 0                                       # nothing to select
     assert call_sel(args(sc=[4, 2, 2]), P=32) == UNS                       # page size
+
+
+# ---------------------------------------------------------------------------
+# caller-owned workspace: the size query (shapes only) and host-side refusals
+# ---------------------------------------------------------------------------
+def ws_bytes(a, null_data=False):
+    lib = msa.load()
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    if null_data:
+        for key in ("q", "k", "v", "sel", "bt", "cu", "used"):
+            a[key].data = 0
+    n = ctypes.c_size_t(123)
+    rc = lib.msa_kvouter_workspace_bytes(r(a["q"]), r(a["k"]), r(a["v"]), r(a["sel"]), r(a["bt"]), r(a["cu"]),
+                                         r(a["used"]), a["P"], a["causal"], ctypes.byref(n))
+    return rc, int(n.value)
+
+
+def _align(n):
+    return (n + 255) // 256 * 256
+
+
+def expected_ws(Tq, Hq, Hkv, K, B, MP, P):
+    """The documented size: counters, then (non-decode calls) the bitmap, then
+    the planning arrays and partials, each array 256-byte aligned."""
+    G, nb = Hq // Hkv, -(-MP * P // 128)
+    NR, W, ns, TG = nb * Hkv, -(-Tq // 32), Tq * Hkv * K, Tq * Hkv
+    decode = Tq == B and G <= 16
+    head = _align(256 + (0 if decode else NR * W * 4))
+    sizes = [0 if decode else NR * W * 4] * 2 + [ns, TG * 4, TG * 4, ns * 4, TG * 4, NR * 4, (NR + 1) * 4,
+                                                 (NR + 1) * 4, 0 if decode else ns * 4, 0 if decode else ns * 4]
+    if not decode:
+        T = min(128, max(1, 256 // G))
+        items = ((Tq + T - 1) // T + B) * Hkv
+        sizes += [8192, ns * 4, ns, ns * 16, 2 * items * 16, items * 4 * K * 16,
+                  (ns * G + 31) // 32 * 32 * 128 * 2, ns * G * 4]
+    off = 0
+    for n in sizes:
+        off = _align(off) + n
+    return head + off + 256
+
+
+@pytest.mark.parametrize("shape", [
+    dict(Tq=64, Hq=64, Hkv=8, K=16, B=64, MP=512, P=64),    # decode: planning arrays only
+    dict(Tq=4, Hq=16, Hkv=2, K=4, B=2, MP=4, P=64),         # small prefill-shaped batch
+    dict(Tq=300, Hq=32, Hkv=1, K=32, B=3, MP=40, P=128),    # MQA prefill
+    dict(Tq=64, Hq=64, Hkv=2, K=8, B=64, MP=16, P=64),      # decode with G = 32: not front-only
+])
+def test_workspace_bytes_matches_the_documented_layout(shape):
+    a = good(Tq=shape["Tq"], Hq=shape["Hq"], Hkv=shape["Hkv"], NP=16, P=shape["P"], K=shape["K"], B=shape["B"],
+             MP=shape["MP"])
+    rc, n = ws_bytes(a, null_data=True)   # shapes only: data pointers may be NULL
+    assert rc == 0
+    assert n == expected_ws(**shape)
+
+
+def test_workspace_bytes_of_a_decode_batch_is_small_and_of_a_prefill_holds_every_partial():
+    dec = ws_bytes(good(Tq=64, Hq=64, Hkv=8, K=16, B=64, MP=512, P=64))[1]
+    assert dec < 100_000
+    Tq, Hq, Hkv, K = 16384, 64, 8, 16
+    pre = ws_bytes(good(Tq=Tq, Hq=Hq, Hkv=Hkv, K=K, B=1, MP=128, P=128))[1]
+    assert pre >= Tq * Hkv * K * (Hq // Hkv) * (256 + 4)          # every slot's partial rows
+    assert pre < 1.05 * Tq * Hkv * K * (Hq // Hkv) * (256 + 4) + 100e6
+
+
+def test_workspace_bytes_refuses_what_the_call_refuses():
+    a = good(Tq=0)
+    assert ws_bytes(a) == (0, 0)
+    a = good()
+    a["q"] = desc([4, 16, 64], msa.MSA_BF16)
+    assert ws_bytes(a)[0] == UNS
+    lib = msa.load()
+    b = good()
+    r = ctypes.byref
+    assert lib.msa_kvouter_workspace_bytes(r(b["q"]), r(b["k"]), r(b["v"]), r(b["sel"]), r(b["bt"]), r(b["cu"]),
+                                           r(b["used"]), 64, 1, None) == INV
+
+
+def call_ws(a, ws, nbytes):
+    lib = msa.load()
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    rc = lib.msa_kvouter_attention_ws(r(a["q"]), r(a["k"]), r(a["v"]), r(a["sel"]), r(a["bt"]), r(a["cu"]),
+                                      r(a["used"]), a["P"], a["causal"], r(a["out"]), r(a["lse"]), ws, nbytes, None)
+    return rc, lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("name,mutate,code", BAD, ids=[b[0] for b in BAD])
+def test_ws_call_refuses_bad_descriptors_like_the_allocating_call(name, mutate, code):
+    a = good()
+    mutate(a)
+    rc, msg = call_ws(a, FAKE, 1 << 30)
+    assert rc == code, (rc, msg)
+
+
+def test_ws_call_refuses_a_missing_or_misaligned_workspace():
+    assert call_ws(good(), None, 1 << 20)[0] == INV
+    rc, msg = call_ws(good(), FAKE + 64, 1 << 20)
+    assert rc == INV and "aligned" in msg
+    assert call_ws(good(Tq=0), None, 0)[0] == 0   # nothing to do, nothing needed

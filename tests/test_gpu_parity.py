@@ -5,13 +5,15 @@ without keys must give O = 0 and LSE = -inf on both sides. Index arrays are
 compared bit for bit with the integer CPU reference. Unselected pages and
 rows beyond each sequence's used length hold NaN poison throughout.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import workloads as W
 
-from _helpers import all_pairs, compare, device_inputs, oracle_pairs, run_gpu, sample_pairs
+from _helpers import all_pairs, compare, device_inputs, oracle_pairs, product_tiles, run_gpu, stratified_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -98,9 +100,13 @@ def test_index_builder_bitexact_named(name):
     _index_case(wl, T, T, list_all=name == "varlen_mqa")
 
 
-def test_index_builder_bitexact_prefill_shared():
-    wl = W.make("prefill_shared")
-    _index_case(wl, 16, 16, list_all=True)
+@pytest.mark.parametrize("name", ["prefill_shared", "varlen_mqa", "dense_causal"])
+def test_index_builder_bitexact_product_tiles(name):
+    # the tile and window sizes the attention call itself uses (32-token
+    # tiles and 128-token windows at G = 8; 8 and 32 at G = 32)
+    wl = W.make(name)
+    T, Tu = product_tiles(wl)
+    _index_case(wl, T, min(Tu, 128), list_all=True)
 
 
 # ---------------------------------------------------------------------------
@@ -163,6 +169,105 @@ def test_parity_edge_cases_tile_path(case):
     _full(wl)
 
 
+# Tiles of 128 tokens (G <= 2) with wide selections: a tile's tokens x
+# top-k exceed the 4096 residual positions the tile kernel keeps in LDS, so
+# its epilogue reads each row's residual counts and positions from global
+# memory. Chains of shared picks plus per-token residual picks.
+LONG_TILES = [
+    # (tq_per_seq, kv_lens, Hq, Hkv, P, topk, kv dtype)
+    ([160, 130], [7000, 6400], 4, 4, 128, 48, None),                 # G = 1, 128-token tiles
+    ([140, 9], [9000, 3000], 4, 2, 64, 64, None),                    # G = 2, top-64
+    ([150], [8200], 8, 4, 64, 40, torch.float8_e4m3fn),              # G = 2, fp8 cache
+]
+
+
+@pytest.mark.parametrize("case", range(len(LONG_TILES)))
+def test_parity_long_tiles_merge_from_global(case):
+    tq, lens, Hq, Hkv, P, K, kvd = LONG_TILES[case]
+    wl = W.make_custom(540 + case, tq, lens, Hq, Hkv, P, topk=K, causal=True, pick="diag",
+                       kv_dtype=kvd, shared_chunk=32, shared_picks=K // 2)
+    T, _ = product_tiles(wl)
+    assert T == 128 and min(T, max(tq)) * K > 4096
+    _full(wl)
+
+
+# Decode with more than 16 query heads per KV head (MQA): one token per
+# sequence, 32 or 64 rows per token.
+MQA_DECODE = [
+    (32, None), (64, None), (32, torch.float8_e4m3fn), (64, torch.float8_e4m3fn),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MQA_DECODE)))
+def test_parity_mqa_decode(case):
+    Hq, kvd = MQA_DECODE[case]
+    rng = np.random.default_rng(560 + case)
+    lens = [int(x) for x in rng.integers(300, 5000, size=24)]
+    wl = W.make_custom(560 + case, [1] * 24, lens, Hq, 1, 64, topk=8, causal=True, pick="diag", kv_dtype=kvd)
+    _full(wl)
+
+
+# Decode-shaped batches too large for one round of front workgroups
+# (Tq <= 4B, G <= 16, Tq != B, Tq * Hkv > 2 * CUs): the front kernel lists
+# tiles with residual slots, and the unit kernel derives the residual order
+# from the bitmaps itself.
+@pytest.mark.parametrize("kvd", [None, torch.float8_e4m3fn])
+def test_parity_decode_shaped_batch_with_residuals(kvd):
+    rng = np.random.default_rng(580)
+    lens = [int(x) for x in rng.integers(2100, 4000, size=160)]
+    wl = W.make_custom(581 if kvd is None else 582, [2] * 160, lens, 64, 8, 64, topk=16, causal=True,
+                       pick="random", kv_dtype=kvd)
+    assert wl.Tq <= 4 * wl.B and wl.Tq * wl.Hkv > 2 * 256
+    _full(wl)
+
+
+# Page ids outside [0, num_pages) are a precondition violation; the pass
+# still treats such a page as holding no keys, on every path. With every
+# page of a block outside the pool the result equals the oracle's with that
+# block's picks removed.
+PAGE_CASES = {
+    "decode": dict(tq=[1] * 8, lens=[900, 2000, 700, 1500, 1300, 640, 2500, 1100], Hq=16, Hkv=2, P=128, K=6,
+                   pick="random", shared=0),
+    "decode_fp8": dict(tq=[1] * 8, lens=[900, 2000, 700, 1500, 1300, 640, 2500, 1100], Hq=16, Hkv=2, P=128, K=6,
+                       pick="random", shared=0, kvd=torch.float8_e4m3fn),
+    "tiles": dict(tq=[40, 30], lens=[3000, 2000], Hq=16, Hkv=2, P=128, K=8, pick="diag", shared=4),
+    "tiles_fp8": dict(tq=[40, 30], lens=[3000, 2000], Hq=16, Hkv=2, P=128, K=8, pick="diag", shared=4,
+                      kvd=torch.float8_e4m3fn),
+    "tiles_page64": dict(tq=[40, 30], lens=[3000, 2000], Hq=16, Hkv=2, P=64, K=8, pick="diag", shared=4),
+}
+
+
+@pytest.mark.parametrize("name", list(PAGE_CASES))
+def test_pages_outside_the_pool_hold_no_keys(name):
+    import dataclasses
+
+    c = PAGE_CASES[name]
+    wl = W.make_custom(590 + list(PAGE_CASES).index(name), c["tq"], c["lens"], c["Hq"], c["Hkv"], c["P"],
+                       topk=c["K"], causal=True, pick=c["pick"], kv_dtype=c.get("kvd"),
+                       shared_chunk=16 if c["shared"] else 0, shared_picks=c["shared"])
+    bt = wl.block_tables.copy()
+    sel_ref = wl.selected.copy()
+    cu = wl.cu_seqlens_q
+    ppb = 128 // wl.page_size
+    for s in range(wl.B):
+        picks = wl.selected[cu[s]:cu[s + 1]]
+        nblk = -(-int(wl.used_kv_lens[s]) // 128)
+        valid = picks[(picks >= 0) & (picks < nblk)]
+        if valid.size == 0:
+            continue
+        b = int(np.bincount(valid).argmax())       # the block most tokens of s picked
+        for lp in range(b * ppb, min((b + 1) * ppb, bt.shape[1])):
+            bt[s, lp] = wl.num_pages + 3 if s % 2 == 0 else -2
+        sel_ref[cu[s]:cu[s + 1]][picks == b] = -1
+    d = device_inputs(wl)
+    d["block_tables"] = torch.from_numpy(bt).cuda()
+    out, lse = run_gpu(wl, d)
+    ref_wl = dataclasses.replace(wl, selected=sel_ref)
+    pairs = all_pairs(wl)
+    ref_o, ref_l = oracle_pairs(ref_wl, pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+
+
 def test_parity_shared_chunks_with_residuals():
     # tiles with long chains plus residual picks (the prefill pattern at small size)
     wl = W.make_custom(611, [64, 48], [4096, 3000], 16, 2, 128, topk=10, causal=True, pick="diag",
@@ -174,40 +279,46 @@ def test_parity_decode_gqa():
     _full(W.make("decode_gqa"))
 
 
-def test_parity_decode_fp8_sampled():
-    wl = W.make("decode_fp8")
-    out, lse = run_gpu(wl)
-    pairs = sample_pairs(wl, 96)
-    ref_o, ref_l = oracle_pairs(wl, pairs)
-    compare(wl, out, lse, pairs, ref_o, ref_l)
+def test_parity_decode_fp8_full():
+    # every (token, KV head) pair of the 256-sequence fp8 decode batch
+    _full(W.make("decode_fp8"))
 
 
-def test_parity_prefill_shared_sampled():
-    wl = W.make("prefill_shared")
-    out, lse = run_gpu(wl)
-    pairs = sample_pairs(wl, 128)
-    ref_o, ref_l = oracle_pairs(wl, pairs)
-    compare(wl, out, lse, pairs, ref_o, ref_l)
-    assert not torch.isnan(out.float()).any()
-
-
-def test_parity_varlen_mqa_sampled():
+def test_parity_varlen_mqa_full():
+    # every (token, KV head) pair of the varlen MQA prefill (fp16)
     wl = W.make("varlen_mqa")
+    _full(wl)
+
+
+def _stratified(name):
+    wl = W.make(name)
     out, lse = run_gpu(wl)
-    pairs = sample_pairs(wl, 128)
+    assert not torch.isnan(out.float()).any()
+    pairs = stratified_pairs(wl)
     ref_o, ref_l = oracle_pairs(wl, pairs)
     compare(wl, out, lse, pairs, ref_o, ref_l)
-    assert not torch.isnan(out.float()).any()
+    return pairs
 
 
-def test_parity_dense_causal_sampled():
+def test_parity_prefill_shared_every_tile_and_window():
+    # every tile item (3 tokens each, all KV heads) and every unit window
+    pairs = _stratified("prefill_shared")
+    assert pairs.size >= 3 * 512 * 8
+
+
+def test_parity_dense_causal_every_tile():
     # every visible block selected: dense causal attention through the sparse path
-    wl = W.make("dense_causal")
-    out, lse = run_gpu(wl)
-    pairs = sample_pairs(wl, 128)
-    ref_o, ref_l = oracle_pairs(wl, pairs)
-    compare(wl, out, lse, pairs, ref_o, ref_l)
-    assert not torch.isnan(out.float()).any()
+    _stratified("dense_causal")
+
+
+FULL = pytest.mark.skipif(not os.environ.get("MSA_PARITY_FULL"),
+                          reason="every pair at full size takes minutes of oracle time; set MSA_PARITY_FULL=1")
+
+
+@FULL
+@pytest.mark.parametrize("name", ["prefill_shared", "dense_causal"])
+def test_parity_full_size_every_pair(name):
+    _full(W.make(name))
 
 
 @pytest.mark.parametrize("causal", [True, False])
