@@ -440,6 +440,19 @@ def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
             secs += time.perf_counter() - t0
         reps += 1
     frac = n / tot
+    # one thread: growing slices of the same pairs until min_seconds / 2
+    done, secs1 = 0, 0.0
+    m = max(1, n // 64)
+    while secs1 < min_seconds / 2:
+        for q, k, v, sel, bt, toks in groups:
+            part = toks[:m]
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, sel, bt, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, pairs=part, threads=1)
+            secs1 += time.perf_counter() - t0
+            done += part.size
+            if secs1 >= min_seconds / 2:
+                break
+        m = min(2 * m, n)
     return dict(
         value=round(acct["unique_kv_bytes"] * frac * reps / secs / 1e9, 4),
         unit="GB/s",
@@ -447,6 +460,8 @@ def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
         kind="oracle",
         sample=f"{n} of {tot} (token, kv-head) pairs of one batch ({100 * frac:.0f}%), repeated {reps}x "
                f"({secs:.1f} s of fp64 oracle time); unique-KV bytes scaled by the sampled fraction",
+        single_thread_value=round(acct["unique_kv_bytes"] * done / tot / secs1 / 1e9, 4),
+        single_thread_sample=f"{done} pairs of the same sample on one thread ({secs1:.1f} s)",
     )
 
 
@@ -542,9 +557,20 @@ def main():
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
-    # same steps again with HIP events recorded on the call's stream around
-    # the dominant kernel (the events add a little time between kernels, so
-    # the step time above is taken without them)
+    # the distribution of single steps: the same steps with one event
+    # between consecutive calls (an event adds a little time, so the mean
+    # step above is taken without them)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    per_step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
+
+    # same steps again, timing the dominant kernels: their dispatches record
+    # HIP events at the kernels' start and end (msa_profile_enable), so the
+    # kernel time excludes everything between launches
     msa.profile_enable(dom)
     for i in range(args.steps):
         step(i)
@@ -574,8 +600,11 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
     roof["traffic"] = measured_traffic(args.workload, dom)
+    roof["traffic_kind"] = ("FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy's counts: bytes between "
+                            "L2 and the data fabric, MALL hits included, so an upper bound on HBM bytes")
     roof["kernel"] = "+".join(dom)
     roof["kernel_avg_us"] = round(k_avg_ms * 1e3, 2)
+    roof["kernel_within_step"] = bool(k_avg_ms <= ms_step)
     roof["per_kernel_avg_us"] = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in per_kernel.items()}
     roof["launches"] = k_n
 
@@ -607,6 +636,9 @@ def main():
             "unique_kv_bytes_per_step": int(ukv),
             "effective_flops_per_step": int(flops),
             "decode_step_us": round(ms_step * 1e3, 2),
+            "step_us_median": round(float(np.median(per_step_us)), 2),
+            "step_us_p10": round(float(np.percentile(per_step_us, 10)), 2),
+            "step_us_p90": round(float(np.percentile(per_step_us, 90)), 2),
             "effective_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
             "parallelism": "single GPU",

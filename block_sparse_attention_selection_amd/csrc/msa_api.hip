@@ -175,7 +175,7 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
 // and the bitmap at its start, cleared by a fill kernel at the start of
 // every call that uses them.
 // ---------------------------------------------------------------------------
-__device__ __attribute__((aligned(256))) uint8_t g_zero_page[msa::kZeroPageBytes] = {};
+static __device__ __align__(256) uint8_t g_zero_page[msa::kZeroPageBytes] = {};
 
 struct Carve {
   size_t off = 0;
@@ -410,6 +410,34 @@ void fill_attention_io(msa::Params* p, const msa_tensor* q, const msa_tensor* k,
   p->out = out->data;
   p->lse = lse ? (float*)lse->data : nullptr;
 }
+
+// One attention call whose scratch is `base` (a caller-owned workspace or
+// the no-allocation array, at least ws_bytes_for(pl) bytes): one counter set
+// and the bitmap first, then the planning arrays and partials. Nothing is
+// allocated and nothing waits; a front-only call uses neither the counters
+// nor the bitmap (every tile is finished where it is classified), any other
+// call clears both with a fill kernel first.
+int32_t run_in_workspace(const Plan& pl, const DeviceState& w, char* base, const msa_tensor* q,
+                         const msa_tensor* k_cache, const msa_tensor* v_cache, const msa_tensor* selected,
+                         const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                         const msa_tensor* used_kv_lens, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                         hipStream_t st) {
+  const size_t bitmap_words = pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W;
+  const size_t head = (kCntSetBytes + bitmap_words * 4 + 255) & ~size_t(255);
+  msa::Params p{};
+  layout(pl.d, base + head, &p, !pl.front_only, !pl.front_only);
+  p.slot_pos = nullptr;
+  fill_inputs(&p, pl.d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
+  fill_attention_io(&p, q, k_cache, v_cache, out, lse);
+  p.counters = (int32_t*)base;
+  p.counters_next = nullptr;
+  p.zero_page = w.zero_page;
+  p.bitmap = (uint32_t*)(base + kCntSetBytes);
+  const int64_t clear_words = pl.front_only ? 0 : (int64_t)((kCntSetBytes + bitmap_words * 4) / 4);
+  const hipError_t e = enqueue_attention(p, pl, w.num_cu, (uint32_t*)base, clear_words, st);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -427,7 +455,6 @@ struct ProfRec {
 std::mutex g_prof_mutex;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
-hipEvent_t g_open[msa::kNumKernelIds] = {};
 
 hipEvent_t pooled_event() {
   if (!g_event_pool.empty()) {
@@ -441,19 +468,28 @@ hipEvent_t pooled_event() {
 }
 }  // namespace
 
-void msa::profile_mark(int kernel, bool begin, hipStream_t st) {
-  if (!(g_profile_mask & (1u << kernel))) return;
+msa::ProfSpan msa::profile_begin(int kid) {
+  ProfSpan sp{kid, nullptr, nullptr};
+  if (!(g_profile_mask & (1u << kid))) return sp;
   std::lock_guard<std::mutex> lk(g_prof_mutex);
-  hipEvent_t e = pooled_event();
-  if (!e) return;
-  (void)hipEventRecord(e, st);
-  if (begin) {
-    g_open[kernel] = e;
-  } else if (g_open[kernel]) {
-    g_prof.push_back({kernel, g_open[kernel], e});
-    g_open[kernel] = nullptr;
+  hipEvent_t a = pooled_event(), b = a ? pooled_event() : nullptr;
+  if (!a || !b) {
+    if (a) g_event_pool.push_back(a);
+    return sp;
+  }
+  sp.a = a;
+  sp.b = b;
+  return sp;
+}
+
+void msa::profile_end(const ProfSpan& sp, bool launched) {
+  if (!sp.a) return;
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  if (launched) {
+    g_prof.push_back({sp.kid, sp.a, sp.b});
   } else {
-    g_event_pool.push_back(e);
+    g_event_pool.push_back(sp.a);
+    g_event_pool.push_back(sp.b);
   }
 }
 
@@ -580,24 +616,8 @@ int32_t msa_kvouter_attention_ws(const msa_tensor* q, const msa_tensor* k_cache,
   const size_t need = ws_bytes_for(pl);
   if (workspace_bytes < need)
     return fail(MSA_ERR_INVALID_ARGUMENT, "workspace: %zu bytes given, this call needs %zu", workspace_bytes, need);
-  char* base = (char*)workspace;
-  const size_t bitmap_words = pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W;
-  const size_t head = (kCntSetBytes + bitmap_words * 4 + 255) & ~size_t(255);
-  msa::Params p{};
-  layout(pl.d, base + head, &p, !pl.front_only, !pl.front_only);
-  p.slot_pos = nullptr;
-  fill_inputs(&p, pl.d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
-  fill_attention_io(&p, q, k_cache, v_cache, out, lse);
-  p.counters = (int32_t*)base;
-  p.counters_next = nullptr;
-  p.zero_page = w->zero_page;
-  p.bitmap = (uint32_t*)(base + kCntSetBytes);
-  // A front-only call uses neither the counters nor the bitmap (every tile is
-  // finished where it is classified); any other call clears both first.
-  const int64_t clear_words = pl.front_only ? 0 : (int64_t)((kCntSetBytes + bitmap_words * 4) / 4);
-  const hipError_t e = enqueue_attention(p, pl, w->num_cu, (uint32_t*)base, clear_words, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return run_in_workspace(pl, *w, (char*)workspace, q, k_cache, v_cache, selected, block_tables, cu_seqlens_q,
+                          used_kv_lens, causal, out, lse, (hipStream_t)stream);
 }
 
 int32_t msa_build_index(const msa_tensor* selected, const msa_tensor* cu_seqlens_q,
@@ -723,12 +743,10 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
   if (N * Hkv * 32 >= (1ll << 31) || NP * Hkv * page_size >= (1ll << 40))
     return fail(MSA_ERR_UNSUPPORTED, "problem too large");
   if (N == 0) return ok();
-  msa::profile_mark(msa::kKStore, true, (hipStream_t)stream);
   hipError_t e = msa::launch_store_kv(k_new->data, has_v ? v_new->data : nullptr, (const int64_t*)loc->data,
                                       k_cache->data, has_v ? v_cache->data : nullptr, (int)N, (int)Hkv, page_size,
                                       NP, elem_of(k_new->dtype),
                                       k_cache->dtype == MSA_FP8_E4M3FN, (hipStream_t)stream);
-  msa::profile_mark(msa::kKStore, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -819,10 +837,8 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
       table = (float*)w->ptr;
     }
   }
-  msa::profile_mark(msa::kKSelect, true, (hipStream_t)stream);
   hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, table,
                                     (hipStream_t)stream);
-  msa::profile_mark(msa::kKSelect, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

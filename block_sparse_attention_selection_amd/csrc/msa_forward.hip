@@ -672,16 +672,15 @@ hipError_t launch_widen_fp8(const void* in, int64_t n, int out_elem, void* out, 
 }
 
 template <typename CT, typename KVT, bool ATTN>
-static hipError_t launch_front_t(const Params& p, hipStream_t st) {
+static hipError_t launch_front_t(const ProfSpan& sp, const Params& p, hipStream_t st) {
   const int Teff = p.T > 0 ? p.T : 1;
   const size_t lds = (size_t)Teff * p.K * sizeof(int);
   const unsigned gx = p.stream_narrow ? (unsigned)p.Tq : (unsigned)((p.Tq + Teff - 1) / Teff + p.B);
-  hipLaunchKernelGGL((k_front<CT, KVT, ATTN>), dim3(gx, p.Hkv), dim3(256), lds, st, p);
-  return hipGetLastError();
+  return launch_k(sp, true, true, k_front<CT, KVT, ATTN>, dim3(gx, p.Hkv), dim3(256), (uint32_t)lds, st, p);
 }
 
 hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st) {
-  profile_mark(kKFront, true, st);
+  const ProfSpan sp = profile_begin(kKFront);
   hipError_t e;
   // outside decode mode the front kernel only classifies: the light
   // instantiation (no attention registers or LDS) keeps many workgroups per CU
@@ -689,17 +688,16 @@ hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st
   if (!p.stream_narrow && Teff * p.K <= kWaveSlots) {
     // every tile is listed or enumerated: one wave per tile
     const int ntiles = (p.Tq + Teff - 1) / Teff + p.B;
-    hipLaunchKernelGGL(k_classify_waves, dim3((ntiles + 3) / 4, p.Hkv), dim3(256), 0, st, p, ntiles);
-    e = hipGetLastError();
+    e = launch_k(sp, true, true, k_classify_waves, dim3((ntiles + 3) / 4, p.Hkv), dim3(256), 0, st, p, ntiles);
   } else if (q_elem < 0 || !p.stream_narrow)
-    e = launch_front_t<bf16_t, bf16_t, false>(p, st);
+    e = launch_front_t<bf16_t, bf16_t, false>(sp, p, st);
   else if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(p, st)
-                            : launch_front_t<bf16_t, bf16_t, true>(p, st);
+    e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(sp, p, st)
+                            : launch_front_t<bf16_t, bf16_t, true>(sp, p, st);
   else
-    e = kv_elem == kElemFP8 ? launch_front_t<f16_t, fp8_e4m3_t, true>(p, st)
-                            : launch_front_t<f16_t, f16_t, true>(p, st);
-  profile_mark(kKFront, false, st);
+    e = kv_elem == kElemFP8 ? launch_front_t<f16_t, fp8_e4m3_t, true>(sp, p, st)
+                            : launch_front_t<f16_t, f16_t, true>(sp, p, st);
+  profile_end(sp, e == hipSuccess);
   return e;
 }
 

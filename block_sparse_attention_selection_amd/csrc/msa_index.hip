@@ -70,17 +70,15 @@ __global__ __launch_bounds__(256) void k_emit(Params p) {
 }
 
 hipError_t launch_index(const Params& p, bool materialise, hipStream_t st) {
-  profile_mark(kKIndex, true, st);
+  const ProfSpan sp = profile_begin(kKIndex);
   const int rows_per_task = max(1, 2048 / max(p.W, 1));
   const int ntasks = (p.NR + rows_per_task - 1) / rows_per_task;
-  hipLaunchKernelGGL(k_index, dim3(ntasks), dim3(256), 0, st, p, rows_per_task, ntasks);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_k(sp, true, !materialise, k_index, dim3(ntasks), dim3(256), 0, st, p, rows_per_task, ntasks);
   if (e == hipSuccess && materialise) {
     const int64_t nslots = (int64_t)p.Tq * p.Hkv * p.K;
-    hipLaunchKernelGGL(k_emit, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, p);
-    e = hipGetLastError();
+    e = launch_k(sp, false, true, k_emit, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, p);
   }
-  profile_mark(kKIndex, false, st);
+  profile_end(sp, e == hipSuccess);
   return e;
 }
 

@@ -1,6 +1,7 @@
 // msa_internal.hpp -- host/device shared parameter block and launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,11 +87,33 @@ struct Params {
   float* lpart;  // [residual slots, G] LSE (log2 units)
 };
 
-// kernel timing hooks (msa_api.hip): no-ops unless msa_profile_enable set the bit
+// Kernel timing (msa_api.hip), off unless msa_profile_enable set the bit of
+// a kernel id. A span covers the kernels of one launcher call: while its id
+// is profiled it holds a pair of pooled HIP events that the dispatches
+// themselves record (hipExtLaunchKernel), the first kernel's start and the
+// last kernel's end, so it measures the kernels' execution and nothing the
+// host or the stream does around them.
 enum KernelId { kKIndex = 0, kKFront = 1, kKUnits = 2, kKTiles = 3, kKStore = 4, kKSelect = 5 };
 constexpr int kNumKernelIds = 6;
 extern volatile uint32_t g_profile_mask;
-void profile_mark(int kernel, bool begin, hipStream_t st);
+struct ProfSpan {
+  int kid;
+  hipEvent_t a, b;  // null when the kernel id is not profiled
+};
+ProfSpan profile_begin(int kid);
+void profile_end(const ProfSpan& sp, bool launched);
+
+// launch of one kernel of a span (first: its dispatch records the span's
+// start event; last: its end event)
+template <typename F, typename... Args>
+inline hipError_t launch_k(const ProfSpan& sp, bool first, bool last, F kernel, dim3 grid, dim3 block,
+                           uint32_t shm, hipStream_t st, Args... args) {
+  if (sp.a)
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, st, first ? sp.a : nullptr, last ? sp.b : nullptr, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 // residual inversion: row counts and row scan; `materialise` also writes the

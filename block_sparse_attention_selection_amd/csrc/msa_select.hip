@@ -381,52 +381,49 @@ __global__ __launch_bounds__(256) void k_select_lists(SelectParams p, const floa
 }
 
 template <typename QT, typename KT, int NRB, int NW>
-static void launch_fused_npl(const SelectParams& p, dim3 grid, size_t lds, hipStream_t st) {
+static hipError_t launch_fused_npl(const ProfSpan& sp, const SelectParams& p, dim3 grid, size_t lds,
+                                   hipStream_t st) {
   const dim3 block(64 * NW);
-  if (p.nb_cap <= 64)
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 1>), grid, block, lds, st, p);
-  else if (p.nb_cap <= 128)
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 2>), grid, block, lds, st, p);
-  else
-    hipLaunchKernelGGL((k_select<QT, KT, NRB, NW, 4>), grid, block, lds, st, p);
+  if (p.nb_cap <= 64) return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 1>, grid, block, lds, st, p);
+  if (p.nb_cap <= 128) return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 2>, grid, block, lds, st, p);
+  return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 4>, grid, block, lds, st, p);
 }
 
-static void launch_lists(const SelectParams& p, const float* sc, hipStream_t st) {
+static hipError_t launch_lists(const ProfSpan& sp, const SelectParams& p, const float* sc, hipStream_t st) {
   const dim3 grid((unsigned)(((int64_t)p.Tq * p.Hkv + 3) / 4)), block(256);
-  if (p.nb_cap <= 64)
-    hipLaunchKernelGGL((k_select_lists<1>), grid, block, 0, st, p, sc);
-  else if (p.nb_cap <= 128)
-    hipLaunchKernelGGL((k_select_lists<2>), grid, block, 0, st, p, sc);
-  else if (p.nb_cap <= 256)
-    hipLaunchKernelGGL((k_select_lists<4>), grid, block, 0, st, p, sc);
-  else if (p.nb_cap <= 512)
-    hipLaunchKernelGGL((k_select_lists<8>), grid, block, 0, st, p, sc);
-  else
-    hipLaunchKernelGGL((k_select_lists<kSelMaxBlocks / 64>), grid, block, 0, st, p, sc);
+  if (p.nb_cap <= 64) return launch_k(sp, false, true, k_select_lists<1>, grid, block, 0, st, p, sc);
+  if (p.nb_cap <= 128) return launch_k(sp, false, true, k_select_lists<2>, grid, block, 0, st, p, sc);
+  if (p.nb_cap <= 256) return launch_k(sp, false, true, k_select_lists<4>, grid, block, 0, st, p, sc);
+  if (p.nb_cap <= 512) return launch_k(sp, false, true, k_select_lists<8>, grid, block, 0, st, p, sc);
+  return launch_k(sp, false, true, k_select_lists<kSelMaxBlocks / 64>, grid, block, 0, st, p, sc);
 }
 
 template <typename QT, typename KT>
-static hipError_t launch_select_t(const SelectParams& p, float* table, hipStream_t st) {
+static hipError_t launch_select_t(const ProfSpan& sp, const SelectParams& p, float* table, hipStream_t st) {
   if (!table) {
     // fused: 64-token tiles of 4 waves, every score in LDS (nb_cap <= 256)
     const int64_t tiles = ((int64_t)p.Tq + 63) / 64 + p.B;  // each sequence adds at most one partial tile
     const size_t lds = (size_t)64 * p.nb_cap * sizeof(float);
-    launch_fused_npl<QT, KT, 4, 4>(p, dim3((unsigned)(tiles * p.Hkv)), lds, st);
-  } else {
-    const int64_t tiles = ((int64_t)p.Tq + 15) / 16 + p.B;
-    const int nsplit = (p.nb_cap + kSelSplitBlocks - 1) / kSelSplitBlocks;
-    hipLaunchKernelGGL((k_select_scores<QT, KT>), dim3((unsigned)(tiles * p.Hkv * nsplit)),
-                       dim3(64 * kSelSplitWaves), 0, st, p, table, nsplit);
-    launch_lists(p, table, st);
+    return launch_fused_npl<QT, KT, 4, 4>(sp, p, dim3((unsigned)(tiles * p.Hkv)), lds, st);
   }
-  return hipGetLastError();
+  const int64_t tiles = ((int64_t)p.Tq + 15) / 16 + p.B;
+  const int nsplit = (p.nb_cap + kSelSplitBlocks - 1) / kSelSplitBlocks;
+  hipError_t e = launch_k(sp, true, false, k_select_scores<QT, KT>, dim3((unsigned)(tiles * p.Hkv * nsplit)),
+                          dim3(64 * kSelSplitWaves), 0, st, p, table, nsplit);
+  if (e == hipSuccess) e = launch_lists(sp, p, table, st);
+  return e;
 }
 
 hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, hipStream_t st) {
   if (p.Tq == 0 || p.Hkv == 0) return hipSuccess;
+  const ProfSpan sp = profile_begin(kKSelect);
+  hipError_t e;
   if (q_elem == kElemBF16)
-    return fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(p, table, st) : launch_select_t<bf16_t, bf16_t>(p, table, st);
-  return fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(p, table, st) : launch_select_t<f16_t, f16_t>(p, table, st);
+    e = fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(sp, p, table, st) : launch_select_t<bf16_t, bf16_t>(sp, p, table, st);
+  else
+    e = fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(sp, p, table, st) : launch_select_t<f16_t, f16_t>(sp, p, table, st);
+  profile_end(sp, e == hipSuccess);
+  return e;
 }
 
 }  // namespace msa

@@ -93,18 +93,25 @@ hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, v
   const int64_t nslots = num_pages * P;
   const uint16_t* k16 = (const uint16_t*)kn;
   const uint16_t* v16 = (const uint16_t*)vn;
+  const ProfSpan sp = profile_begin(kKStore);
+  hipError_t e;
   if (in_elem == kElemBF16) {
     if (fp8_cache)
-      hipLaunchKernelGGL((k_store_kv<bf16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
+      e = launch_k(sp, true, true, k_store_kv<bf16_t, true>, grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P,
+                   nslots, ntensors);
     else
-      hipLaunchKernelGGL((k_store_kv<bf16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
+      e = launch_k(sp, true, true, k_store_kv<bf16_t, false>, grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P,
+                   nslots, ntensors);
   } else {
     if (fp8_cache)
-      hipLaunchKernelGGL((k_store_kv<f16_t, true>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
+      e = launch_k(sp, true, true, k_store_kv<f16_t, true>, grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P,
+                   nslots, ntensors);
     else
-      hipLaunchKernelGGL((k_store_kv<f16_t, false>), grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P, nslots, ntensors);
+      e = launch_k(sp, true, true, k_store_kv<f16_t, false>, grid, block, 0, st, k16, v16, loc, kc, vc, N, Hkv, P,
+                   nslots, ntensors);
   }
-  return hipGetLastError();
+  profile_end(sp, e == hipSuccess);
+  return e;
 }
 
 }  // namespace msa

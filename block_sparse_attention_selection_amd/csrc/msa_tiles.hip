@@ -1204,40 +1204,38 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
 // launchers
 // ---------------------------------------------------------------------------
 template <typename CT, typename KVT>
-static hipError_t launch_units_t(const Params& p, int num_cu, hipStream_t st) {
-  hipLaunchKernelGGL((k_units<CT, KVT>), dim3(num_cu * 2), dim3(256), 0, st, p);
-  return hipGetLastError();
+static hipError_t launch_units_t(const ProfSpan& sp, const Params& p, int num_cu, hipStream_t st) {
+  return launch_k(sp, true, true, k_units<CT, KVT>, dim3(num_cu * 2), dim3(256), 0, st, p);
 }
 
 template <typename CT, typename KVT>
-static hipError_t launch_tiles_t(const Params& p, int num_cu, hipStream_t st) {
-  hipLaunchKernelGGL((k_tiles<CT, KVT>), dim3(num_cu), dim3(kTileThreads), 0, st, p);
-  return hipGetLastError();
+static hipError_t launch_tiles_t(const ProfSpan& sp, const Params& p, int num_cu, hipStream_t st) {
+  return launch_k(sp, true, true, k_tiles<CT, KVT>, dim3(num_cu), dim3(kTileThreads), 0, st, p);
 }
 
 hipError_t launch_units(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
-  profile_mark(kKUnits, true, st);
+  const ProfSpan sp = profile_begin(kKUnits);
   hipError_t e;
   if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_units_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
-                            : launch_units_t<bf16_t, bf16_t>(p, num_cu, st);
+    e = kv_elem == kElemFP8 ? launch_units_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+                            : launch_units_t<bf16_t, bf16_t>(sp, p, num_cu, st);
   else
-    e = kv_elem == kElemFP8 ? launch_units_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
-                            : launch_units_t<f16_t, f16_t>(p, num_cu, st);
-  profile_mark(kKUnits, false, st);
+    e = kv_elem == kElemFP8 ? launch_units_t<f16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+                            : launch_units_t<f16_t, f16_t>(sp, p, num_cu, st);
+  profile_end(sp, e == hipSuccess);
   return e;
 }
 
 hipError_t launch_tiles(const Params& p, int q_elem, int kv_elem, int num_cu, hipStream_t st) {
-  profile_mark(kKTiles, true, st);
+  const ProfSpan sp = profile_begin(kKTiles);
   hipError_t e;
   if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_tiles_t<bf16_t, fp8_e4m3_t>(p, num_cu, st)
-                            : launch_tiles_t<bf16_t, bf16_t>(p, num_cu, st);
+    e = kv_elem == kElemFP8 ? launch_tiles_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+                            : launch_tiles_t<bf16_t, bf16_t>(sp, p, num_cu, st);
   else
-    e = kv_elem == kElemFP8 ? launch_tiles_t<f16_t, fp8_e4m3_t>(p, num_cu, st)
-                            : launch_tiles_t<f16_t, f16_t>(p, num_cu, st);
-  profile_mark(kKTiles, false, st);
+    e = kv_elem == kElemFP8 ? launch_tiles_t<f16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+                            : launch_tiles_t<f16_t, f16_t>(sp, p, num_cu, st);
+  profile_end(sp, e == hipSuccess);
   return e;
 }
 

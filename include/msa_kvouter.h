@@ -334,12 +334,14 @@ int32_t msa_validate_inputs(const msa_tensor* q, const msa_tensor* k_cache,
 
 /*
  * Kernel timing for benchmarks. msa_profile_enable(mask) makes every later
- * msa_kvouter_attention (and msa_store_kv) call record a pair of HIP events on its stream
- * around each launch of the kernels whose bit is set in `mask`
- * (1 << MSA_KERNEL_*); mask 0 turns recording off. Enabling discards
- * earlier records. msa_profile_collect waits for the recorded events of one
- * kernel and returns their summed duration (ms) and the number of launches,
- * then forgets them. Recording costs one event pair per timed launch.
+ * call time the kernels whose bit is set in `mask` (1 << MSA_KERNEL_*);
+ * mask 0 turns timing off. Enabling discards earlier records. For each timed
+ * launch of a kernel family the dispatches themselves record a pair of HIP
+ * events (hipExtLaunchKernel): the start of the family's first kernel and
+ * the end of its last, so a record measures kernel execution only, not the
+ * host or the stream around it. msa_profile_collect waits for the recorded
+ * events of one family and returns their summed duration (ms) and the
+ * number of timed launches, then forgets them.
  */
 enum {
   MSA_KERNEL_INDEX = 0, /* residual inversion: row counts and scan */
