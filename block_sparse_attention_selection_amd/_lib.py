@@ -75,6 +75,8 @@ def load():
         lib.msa_kvouter_attention.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
         lib.msa_kvouter_workspace_bytes.restype = i32
         lib.msa_kvouter_workspace_bytes.argtypes = [T, T, T, T, T, T, T, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.msa_kvouter_attention_noalloc.restype = i32
+        lib.msa_kvouter_attention_noalloc.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
         lib.msa_kvouter_attention_ws.restype = i32
         lib.msa_kvouter_attention_ws.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp, ctypes.c_size_t, vp]
         lib.msa_build_index.restype = i32
@@ -174,6 +176,21 @@ def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens
                                               nbytes, _stream(q.device))
     _check(rc)
     return (out, lse) if return_lse else out
+
+
+def kvouter_attention_noalloc(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,
+                              page_size: int, causal: bool = False, out: torch.Tensor, lse: torch.Tensor | None = None):
+    """msa_kvouter_attention_noalloc: the pass with the library's fixed
+    per-device scratch array; ``out`` (and ``lse`` when wanted) must be
+    given, so nothing is allocated. Returns ``out`` or ``(out, lse)``."""
+    lib = load()
+    _device_check(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, out, lse)
+    ds = [describe(x) for x in (q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens)]
+    with torch.cuda.device(q.device):
+        rc = lib.msa_kvouter_attention_noalloc(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                               _ref(describe(out)), _ref(describe(lse)), _stream(q.device))
+    _check(rc)
+    return out if lse is None else (out, lse)
 
 
 def workspace_bytes(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens_q, used_kv_lens,

@@ -177,6 +177,13 @@ int32_t validate(const msa_tensor* q, const msa_tensor* k, const msa_tensor* v, 
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) uint8_t g_zero_page[msa::kZeroPageBytes] = {};
 
+// Scratch of msa_kvouter_attention_noalloc: one array per device, held until
+// the process ends. Host code never uses the array's name as a device
+// address: each device's address is resolved once with hipGetSymbolAddress
+// (DeviceState::scratch) and only that address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 struct Carve {
   size_t off = 0;
   template <typename T>
@@ -249,6 +256,7 @@ struct DeviceState {
   size_t zs_bytes = 0;
   int parity = 0;       // counter set of the next call
   bool dirty = false;   // zero-state must be cleared before use
+  void* scratch = nullptr;  // device address of this device's `scratch` array (resolved on first use)
 };
 
 // Held by every entry point that touches a device's state, from the lease of
@@ -617,6 +625,42 @@ int32_t msa_kvouter_attention_ws(const msa_tensor* q, const msa_tensor* k_cache,
   if (workspace_bytes < need)
     return fail(MSA_ERR_INVALID_ARGUMENT, "workspace: %zu bytes given, this call needs %zu", workspace_bytes, need);
   return run_in_workspace(pl, *w, (char*)workspace, q, k_cache, v_cache, selected, block_tables, cu_seqlens_q,
+                          used_kv_lens, causal, out, lse, (hipStream_t)stream);
+}
+
+int32_t msa_kvouter_attention_noalloc(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                                      const msa_tensor* selected, const msa_tensor* block_tables,
+                                      const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                                      int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                                      void* stream) {
+  Dims d;
+  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                        causal, out, lse, &d);
+  if (rc) return rc;
+  if (d.Tq == 0) return ok();
+  // held through the launches: calls from several host threads enqueue one
+  // at a time (their kernels still share the array on the device)
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  DeviceState* w = nullptr;
+  if ((rc = device_state(&w))) return rc;
+  if (!w->scratch) {
+    // this device's copy of the array, resolved once with the device current
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(MSA_ERR_HIP, "cannot resolve the no-allocation scratch array on this device");
+    }
+    w->scratch = ptr;
+  }
+  const Plan pl = make_plan(d, w->num_cu);
+  const size_t need = ws_bytes_for(pl);
+  if (need > kNoAllocScratchBytes)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; msa_kvouter_attention_noalloc holds %zu (use "
+                "msa_kvouter_attention or msa_kvouter_attention_ws)",
+                need, kNoAllocScratchBytes);
+  return run_in_workspace(pl, *w, (char*)w->scratch, q, k_cache, v_cache, selected, block_tables, cu_seqlens_q,
                           used_kv_lens, causal, out, lse, (hipStream_t)stream);
 }
 

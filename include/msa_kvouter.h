@@ -187,6 +187,27 @@ int32_t msa_kvouter_attention_ws(const msa_tensor* q, const msa_tensor* k_cache,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * msa_kvouter_attention_noalloc -- msa_kvouter_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, results and
+ * errors; the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine): its scratch is a fixed array of 32 MiB in the library's
+ * device code, one per device, which each device holds until the process
+ * ends. A call that needs more scratch than that (msa_kvouter_workspace_bytes
+ * reports the need; decode batches need kilobytes, a prefill's KV-outer
+ * partials take about Tq*Hkv*topk*(Hq/Hkv)*260 bytes) is refused with
+ * MSA_ERR_UNSUPPORTED and enqueues nothing. Every call on a device uses that
+ * device's one array, and each call clears what must start at zero itself:
+ * calls that overlap in time on one device (different streams, or graphs
+ * replayed concurrently) race on it and must be ordered by the caller.
+ */
+int32_t msa_kvouter_attention_noalloc(const msa_tensor* q, const msa_tensor* k_cache,
+                                      const msa_tensor* v_cache, const msa_tensor* selected,
+                                      const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                                      const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                                      msa_tensor* out, msa_tensor* lse, void* stream);
+
+/*
  * msa_build_index -- the selection inversion and work split, exposed so that
  * their integer outputs can be compared bit for bit with a CPU reference.
  * (The pages name an index builder and a load-balancing scheduler among the
