@@ -45,6 +45,8 @@ DESCRIPTIONS = {
                   "Hq=32, Hkv=1, d=128, page 128, top-32, causal, fp16",
     "decode_fp8": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
                   "K/V fp8 e4m3fn, q bf16, causal",
+    "decode_mqa": "256 seqs x 1 query, Hq=32, Hkv=1 (MQA), d=128, L~U[8192,32768], page 64 shuffled, "
+                  "top-16 blocks of 128 (last block forced), causal, bf16",
     "dense_causal": "1 seq, Tq=L=8192, Hq=64, Hkv=8, d=128, page 128, every visible block selected "
                     "(top-64), causal, bf16: dense causal attention through the sparse path",
     "kv_store_fp8": "paged K/V store (the step before the pass): 32768 new tokens x Hkv=8 x d=128, "
@@ -63,7 +65,7 @@ SELECT_METRIC = {"select_decode": ("index-key HBM GB/s, block selection (scores 
 # the prefill-shaped workloads the attention's MFMA work is split between
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
-DOMINANT = {"tiny": ["front"], "decode_gqa": ["front"], "decode_fp8": ["front"],
+DOMINANT = {"tiny": ["front"], "decode_gqa": ["front"], "decode_fp8": ["front"], "decode_mqa": ["front"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
             "dense_causal": ["tiles"], "kv_store_fp8": ["store"], "select_decode": ["select"],
             "select_prefill": ["select"]}
@@ -164,6 +166,16 @@ PROF_COPY_CMD = ("rocprofv3 --pmc {c} --output-format csv -d $ROOT/gpurun_out/tr
                  "-- python3 $ROOT/bench.py --calibrate-copy")
 KERNEL_KEYS = {"front": "k_front", "units": "k_units", "tiles": "k_tiles", "classify": "k_classify_waves",
                "index": "k_index", "emit": "k_emit", "store": "k_store_kv", "select": "k_select"}
+# SQ counter passes (each within one pass's hardware limits: at most 8 SQ
+# and 2 GRBM counters), one rocprofv3 run each
+COUNTER_SETS = {
+    "issue": ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+              "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR"],
+    "busy": ["GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+             "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT"],
+}
+PROF_SET_CMD = ("rocprofv3 --pmc {counters} --output-format csv -d $ROOT/gpurun_out/counters/{w}_{s} -o run "
+                "-- python3 $ROOT/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline")
 
 
 def write_profile_summaries(src):
@@ -197,6 +209,58 @@ def write_profile_summaries(src):
         (f_kib, _), f_name = max((v, k) for k, v in cf.items() if "copy" in k.lower())
         (w_kib, _), _ = max((v, k) for k, v in cw.items() if "copy" in k.lower())
         factors = ((1 << 30) / f_kib, (1 << 30) / w_kib, f_kib, w_kib, f_name)
+    def counter_sets(w):
+        """{kernel short name: {counter: average per dispatch}} over the counter passes of w"""
+        acc = defaultdict(lambda: defaultdict(list))
+        for sname in COUNTER_SETS:
+            f = one(os.path.join("counters", f"{w}_{sname}", "**", "*counter_collection.csv"))
+            if not f:
+                continue
+            for r in csv.DictReader(open(f)):
+                for short, pat in KERNEL_KEYS.items():
+                    if pat in r["Kernel_Name"]:
+                        acc[short][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+    for w in DESCRIPTIONS:
+        cs = counter_sets(w)
+        if cs:
+            sha = kernel_sources_sha256(w)
+            lines = [f"# {w}: SQ counters per dispatch", "", f"Workload: {DESCRIPTIONS[w]}.", "",
+                     "Commands (from the repository root on an MI355X; `$ROOT` is that root), one per pass:", "",
+                     "```"]
+            lines += [PROF_SET_CMD.format(counters=" ".join(c), w=w, s=n) for n, c in COUNTER_SETS.items()]
+            lines += ["```", "", f"Kernel sources: sha256 {sha}.", "",
+                      "Averages per dispatch, summed over the chip. Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES "
+                      "/ (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs); per-MFMA ratios divide instruction "
+                      "counts by SQ_INSTS_MFMA (wave-level instructions).", ""]
+            names = sorted({c for d in cs.values() for c in d})
+            kern = [k for k in ("tiles", "units", "front", "classify", "index", "emit", "select", "store") if k in cs]
+            lines += ["| Counter | " + " | ".join(f"`{KERNEL_KEYS[k]}`" for k in kern) + " |",
+                      "|---|" + "---|" * len(kern)]
+            for c in names:
+                lines.append(f"| {c} | " + " | ".join(f"{cs[k].get(c, float('nan')):.4g}" for k in kern) + " |")
+
+            def ratio(k, a, b):
+                x, y = cs[k].get(a), cs[k].get(b)
+                return f"{x / y:.3g}" if x is not None and y else "-"
+            lines += ["", "| Derived | " + " | ".join(f"`{KERNEL_KEYS[k]}`" for k in kern) + " |",
+                      "|---|" + "---|" * len(kern)]
+            for label, a, b in [("VALU instructions per MFMA", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+                                ("fp32 transcendentals per MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
+                                ("LDS instructions per MFMA", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+                                ("SALU instructions per MFMA", "SQ_INSTS_SALU", "SQ_INSTS_MFMA"),
+                                ("waiting share of wave time", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")]:
+                lines.append(f"| {label} | " + " | ".join(ratio(k, a, b) for k in kern) + " |")
+            util = []
+            for k in kern:
+                g, m = cs[k].get("GRBM_GUI_ACTIVE"), cs[k].get("SQ_VALU_MFMA_BUSY_CYCLES")
+                util.append(f"{m / (g / 8 * 256 * 4):.3f}" if g and m is not None else "-")
+            lines.append("| MFMA busy (fraction of SIMD cycles) | " + " | ".join(util) + " |")
+            with open(os.path.join(ROOT, "profiles", f"counters_{w}.md"), "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print("wrote", f"profiles/counters_{w}.md")
+
     for w in DESCRIPTIONS:
         sha = kernel_sources_sha256(w)
         stats = one(os.path.join("prof", w, "**", "*kernel_stats.csv"))
@@ -440,6 +504,7 @@ def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
             secs += time.perf_counter() - t0
         reps += 1
     frac = n / tot
+    cores = oracle.max_threads()
     # one thread: growing slices of the same pairs until min_seconds / 2
     done, secs1 = 0, 0.0
     m = max(1, n // 64)
@@ -456,7 +521,7 @@ def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     return dict(
         value=round(acct["unique_kv_bytes"] * frac * reps / secs / 1e9, 4),
         unit="GB/s",
-        cores=oracle.max_threads(),
+        cores=cores,
         kind="oracle",
         sample=f"{n} of {tot} (token, kv-head) pairs of one batch ({100 * frac:.0f}%), repeated {reps}x "
                f"({secs:.1f} s of fp64 oracle time); unique-KV bytes scaled by the sampled fraction",

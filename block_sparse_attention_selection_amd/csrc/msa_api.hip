@@ -368,8 +368,12 @@ struct Plan {
 Plan make_plan(const Dims& dims, int num_cu) {
   Plan pl;
   pl.d = dims;
-  pl.narrow = dims.G <= 16 && (int64_t)dims.Tq <= 4 * (int64_t)dims.B;
-  pl.front_only = pl.narrow && (dims.Tq == dims.B || (int64_t)dims.Tq * dims.Hkv <= 2 * (int64_t)num_cu);
+  const bool decode_shaped = (int64_t)dims.Tq <= 4 * (int64_t)dims.B;
+  const bool one_round = dims.Tq == dims.B || (int64_t)dims.Tq * dims.Hkv <= 2 * (int64_t)num_cu;
+  // one-token tiles of up to 64 query rows (Hq/Hkv <= 64, e.g. MQA decode)
+  // are streamed by the front kernel's row sets
+  pl.front_only = decode_shaped && one_round && dims.G <= 64;
+  pl.narrow = (dims.G <= 16 && decode_shaped) || pl.front_only;
   if (pl.front_only) pl.d.T = 1;
   return pl;
 }

@@ -36,6 +36,10 @@ namespace msa {
 // marks a residual slot in the classifiers' LDS pick lists (block ids are < 2^30)
 constexpr int kResidualMark = 1 << 30;
 
+// query rows of one tile the front kernel streams when every tile is one
+// token (4 row sets of 16; a token with Hq/Hkv <= 64)
+constexpr int kStreamRowsMax = 64;
+
 // element offset of k-step s (0..3, 32 dims each) for lane group q: pairs of
 // k-steps share one 64-dim slab, so an fp8 lane reads 16 contiguous bytes
 __device__ __forceinline__ int kmap(int s, int q) { return 64 * (s >> 1) + 16 * q + 8 * (s & 1); }
@@ -79,15 +83,18 @@ __device__ __forceinline__ void tile_load_q(RowTile<CT>& rt, const Params& p, in
 // rarely; the probabilities stay below 2^kRescale.
 constexpr float kRescale = 8.0f;
 
-// One 32-key chunk: scores, masked online softmax, P*V.
+// One 32-key chunk, split in two stages so that several row tiles can share
+// one chunk's fragments: tile_probs computes the scores and the masked
+// online-softmax step of one row tile and returns its probabilities as the
+// B operand; tile_pv builds each V^T operand once and accumulates it into
+// every row tile.
 //   ka[j][s]  K fragment: key 16j + c, dims of k-step s
 //   va[e]     V fragment: key key_of(q, e), dims 8c .. 8c+7
 //   key0      token index of key 0 of the chunk; keys at or beyond lim are absent
 //   run_seq   sequence the chunk belongs to (rows of other sequences skip it)
 template <typename CT>
-__device__ __forceinline__ void tile_chunk(RowTile<CT>& rt, const u32x4 (&ka)[2][4],
-                                           const u32x4 (&va)[8], int key0, int lim, int run_seq,
-                                           int q, float scale_log2) {
+__device__ __forceinline__ u32x4 tile_probs(RowTile<CT>& rt, const u32x4 (&ka)[2][4], int key0, int lim,
+                                            int run_seq, int q, float scale_log2) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -124,6 +131,11 @@ __device__ __forceinline__ void tile_chunk(RowTile<CT>& rt, const u32x4 (&ka)[2]
   u32x4 pb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) pb[i] = pack2<CT>(p[2 * i], p[2 * i + 1]);
+  return pb;
+}
+
+template <typename CT, int RS>
+__device__ __forceinline__ void tile_pv(RowTile<CT> (&rt)[RS], const u32x4 (&va)[8], const u32x4 (&pb)[RS]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     u32x4 a;
@@ -132,7 +144,32 @@ __device__ __forceinline__ void tile_chunk(RowTile<CT>& rt, const u32x4 (&ka)[2]
       const uint32_t x0 = va[2 * i][t >> 1], x1 = va[2 * i + 1][t >> 1];
       a[i] = (t & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
     }
-    rt.o[t] = Mma<CT>::run(a, pb, rt.o[t]);
+#pragma unroll
+    for (int r = 0; r < RS; ++r) rt[r].o[t] = Mma<CT>::run(a, pb[r], rt[r].o[t]);
+  }
+}
+
+template <typename CT, int RS>
+__device__ __forceinline__ void tile_chunk(RowTile<CT> (&rt)[RS], const u32x4 (&ka)[2][4], const u32x4 (&va)[8],
+                                           int key0, int lim, int run_seq, int q, float scale_log2) {
+  if constexpr (RS == 1) {
+    // one row tile: each V^T operand is built right before its product
+    const u32x4 pb = tile_probs<CT>(rt[0], ka, key0, lim, run_seq, q, scale_log2);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      u32x4 a;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x0 = va[2 * i][t >> 1], x1 = va[2 * i + 1][t >> 1];
+        a[i] = (t & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+      }
+      rt[0].o[t] = Mma<CT>::run(a, pb, rt[0].o[t]);
+    }
+  } else {
+    u32x4 pb[RS];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) pb[r] = tile_probs<CT>(rt[r], ka, key0, lim, run_seq, q, scale_log2);
+    tile_pv<CT, RS>(rt, va, pb);
   }
 }
 
@@ -174,9 +211,10 @@ struct Frag<CT, CT> {  // 16-bit cache: fragments are used as loaded
 #pragma unroll
     for (int e = 0; e < 8; ++e) va[e] = *(const u32x4*)(vb + key_of(q, e) * kD + 8 * c);
   }
-  __device__ __forceinline__ void compute(RowTile<CT>& rt, int key0, int lim, int seq, int q, float sl2) {
+  template <int RS>
+  __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
     zero_absent_v(va, key0, lim, q);
-    tile_chunk(rt, ka, va, key0, lim, seq, q, sl2);
+    tile_chunk<CT, RS>(rt, ka, va, key0, lim, seq, q, sl2);
   }
 };
 
@@ -192,7 +230,8 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
 #pragma unroll
     for (int e = 0; e < 8; ++e) vr[e] = *(const u32x2*)(vb + key_of(q, e) * kD + 8 * c);
   }
-  __device__ __forceinline__ void compute(RowTile<CT>& rt, int key0, int lim, int seq, int q, float sl2) {
+  template <int RS>
+  __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
     u32x4 ka[2][4], va[8];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -204,14 +243,20 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
 #pragma unroll
     for (int e = 0; e < 8; ++e) va[e] = widen8<CT>(vr[e]);
     zero_absent_v(va, key0, lim, q);
-    tile_chunk(rt, ka, va, key0, lim, seq, q, sl2);
+    tile_chunk<CT, RS>(rt, ka, va, key0, lim, seq, q, sl2);
   }
 };
 
-// Streams the chain of a residual-free tile of at most 16 query rows (see
-// k_front) and writes its final O and LSE. An empty chain writes zeros and
-// an LSE of -inf.
-template <typename CT, typename KVT>
+// Streams the chain of a residual-free tile and writes its final O and LSE
+// (see k_front). The tile's rows are cut into row sets of 16 (1, 2 or 4 for
+// tiles of up to 16, 32 or 64 rows); each wave holds RS row sets, which
+// share every K/V fragment the wave loads. The nrs / RS wave groups each
+// take their row sets, and the waves of a group split the chain's chunks
+// (wave w: group w % ngrp, every (4 / ngrp)-th chunk from w / ngrp). Waves
+// holding the same rows are merged through LDS. RS = 2 serves one decode
+// token with 17 .. 64 query rows, so that four waves stream four distinct
+// chunk sequences. An empty chain writes zeros and an LSE of -inf.
+template <typename CT, typename KVT, int RS>
 __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int s, int L, int Tq_s,
                                              int64_t q0, int rows, int n_ch, int ppb,
                                              const int* s_chain, const int* s_chain_k,
@@ -220,9 +265,9 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Hkv = p.Hkv;
   __shared__ int64_t s_koff[256];  // element offset of each chunk; -1: absent
-  __shared__ float s_o[4][16][kD + 4];
-  __shared__ float s_m[4][16];
-  __shared__ float s_l[4][16];
+  __shared__ float s_o[4][16 * RS][kD + 4];
+  __shared__ float s_m[4][16 * RS];
+  __shared__ float s_l[4][16 * RS];
   const int Leff = min(L, p.MP * p.P);  // keys the page table can reach
   const int nchunks = n_ch * 4;
   for (int ci = tid; ci < nchunks; ci += 256) {
@@ -233,19 +278,27 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
                      ? (((int64_t)page * Hkv + g) * p.P + (key0 % p.P)) * kD
                      : (int64_t)-1;
   }
+  const int nrs = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);  // row sets of 16 rows
+  const int ngrp = max(1, nrs / RS);                      // wave groups, RS row sets each
+  const int nph = 4 / ngrp;                               // chunk phases per group
+  const int grp = wave % ngrp, ph = wave / ngrp;
   const int q = lane >> 4, c = lane & 15;
-  RowTile<CT> rt;
-  tile_reset(rt);
-  int tok = -1, h = 0;
-  rt.seq = -1;
-  rt.pos = -1;
-  if (c < rows) {
-    tok = t + c / p.G;
-    h = g * p.G + (c % p.G);
-    rt.seq = s;
-    rt.pos = p.causal ? (int)(L - Tq_s + (tok - q0)) : INT_MAX;
+  RowTile<CT> rt[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int row = 16 * (grp * RS + r) + c;  // the lane's row in the tile
+    tile_reset(rt[r]);
+    int tok = -1, h = 0;
+    rt[r].seq = -1;
+    rt[r].pos = -1;
+    if (row < rows) {
+      tok = t + row / p.G;
+      h = g * p.G + (row % p.G);
+      rt[r].seq = s;
+      rt[r].pos = p.causal ? (int)(L - Tq_s + (tok - q0)) : INT_MAX;
+    }
+    tile_load_q(rt[r], p, tok, h, q);
   }
-  tile_load_q(rt, p, tok, h, q);
   __syncthreads();
 
   const E* kbase = (const E*)p.k;
@@ -260,59 +313,64 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
     return off >= 0 ? vbase + off : zero;
   };
   auto key0_of = [&](int ci) { return s_koff[ci] >= 0 ? kBlk * s_chain[ci >> 2] + 32 * (ci & 3) : Leff; };
-  const int nmine = (nchunks - wave + 3) / 4;
+  const int nmine = (nchunks - ph + nph - 1) / nph;
   if (nmine > 0) {
     Frag<CT, KVT> fa, fb;
-    int ci = wave;
+    int ci = ph;
     fa.load(kaddr(ci), vaddr(ci), q, c);
     for (;;) {
-      fb.load(kaddr(ci + 4), vaddr(ci + 4), q, c);
+      fb.load(kaddr(ci + nph), vaddr(ci + nph), q, c);
       fa.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
-      ci += 4;
+      ci += nph;
       if (ci >= nchunks) break;
-      fa.load(kaddr(ci + 4), vaddr(ci + 4), q, c);
+      fa.load(kaddr(ci + nph), vaddr(ci + nph), q, c);
       fb.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
-      ci += 4;
+      ci += nph;
       if (ci >= nchunks) break;
     }
   }
 
-  // merge the four waves
-  const float l_row = sum_over_groups(rt.l);
-  if (q == 0) {
-    s_m[wave][c] = rt.m;
-    s_l[wave][c] = l_row;
+  // merge the waves holding each row
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const float l_row = sum_over_groups(rt[r].l);
+    if (q == 0) {
+      s_m[wave][16 * r + c] = rt[r].m;
+      s_l[wave][16 * r + c] = l_row;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[wave][16 * r + c][32 * q + 8 * i + tt] = rt[r].o[tt][i];
   }
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_o[wave][c][32 * q + 8 * r + tt] = rt.o[tt][r];
   __syncthreads();
-  const int row = tid >> 4, d0 = (tid & 15) * 8;
-  if (row >= rows) return;
-  float M = -INFINITY;
+  for (int it = tid; it < 16 * nrs * 16; it += 256) {
+    const int orow = it >> 4, d0 = (it & 15) * 8;  // output row in the tile, its 8 dims
+    if (orow >= rows) break;
+    const int rset = orow >> 4, rc = orow & 15;
+    const int og = rset / RS, lr = 16 * (rset % RS) + rc;  // the row's wave group, its row in those waves
+    float M = -INFINITY;
+    for (int w = og; w < 4; w += ngrp) M = fmaxf(M, s_m[w][lr]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float wsum = 0.f, acc[8];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float wsum = 0.f, acc[8];
+    for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+    for (int w = og; w < 4; w += ngrp) {
+      const float f = exp2f(s_m[w][lr] - Mu);
+      wsum += f * s_l[w][lr];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+      for (int d = 0; d < 8; ++d) acc[d] += f * s_o[w][lr][d0 + d];
+    }
+    const int rtok = t + orow / p.G;
+    const int rh = g * p.G + (orow % p.G);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const float lse2 = wsum > 0.f ? Mu + log2f(wsum) : -INFINITY;
+    u32x4 pk;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float f = exp2f(s_m[w][row] - Mu);
-    wsum += f * s_l[w][row];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] += f * s_o[w][row][d0 + d];
+    for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
+    if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
   }
-  const int rtok = t + row / p.G;
-  const int rh = g * p.G + (row % p.G);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const float lse2 = wsum > 0.f ? Mu + log2f(wsum) : -INFINITY;
-  u32x4 pk;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pk[i] = pack2<CT>(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-  *(u32x4*)((uint16_t*)p.out + ((size_t)rtok * p.Hq + rh) * kD + d0) = pk;
-  if (d0 == 0 && p.lse) p.lse[(size_t)rh * p.Tq + rtok] = lse2 * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -327,8 +385,8 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
 // Every other tile is appended to the tile list. Tokens outside every
 // sequence (decode mode) get zero outputs and an LSE of -inf here.
 // ---------------------------------------------------------------------------
-template <typename CT, typename KVT, bool ATTN>
-__global__ __launch_bounds__(256, 2) void k_front(Params p) {
+template <typename CT, typename KVT, bool ATTN, int RS>
+__global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
   extern __shared__ int s_sel[];  // [nt][K] picks, -1 where the slot is invalid
   __shared__ int s_chain[64];     // chain blocks
   __shared__ int s_chain_k[64];   // leader slot of each chain block
@@ -392,9 +450,11 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
   const int i0 = (int)(t - q0);
   const int nt = (int)min((int64_t)Teff, q1 - t);
   const int rows = nt * p.G;
-  // a decode-mode tile of at most 16 rows is streamed here unless it turns
-  // out to have residual slots
-  const bool stream = ATTN && p.stream_narrow && rows <= 16;
+  // a decode-mode tile of at most 16 rows (of at most 64 when every tile is
+  // one token: front-only calls) is streamed here unless it turns out to
+  // have residual slots
+  const int stream_rows = p.front_only ? kStreamRowsMax : 16;
+  const bool stream = ATTN && p.stream_narrow && rows <= stream_rows;
   const int ppb = kBlk / p.P;  // pages per block
 
   // pages of the leader's picks, looked up while the sequence length loads
@@ -506,7 +566,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     if (lane == 0) {
       s_tile_res = res;
       if (res > 0) p.counters[kCntResidual] = 1;  // "some"; the index kernel writes the total
-      const bool here = p.stream_narrow && rows <= 16 && res == 0;
+      const bool here = p.stream_narrow && rows <= stream_rows && res == 0;
       int item = -1;  // the tile kernel's item for this tile
       if (!here && p.list_tiles) {
         item = atomicAdd(&p.counters[kCntTiles], 1);
@@ -521,7 +581,7 @@ __global__ __launch_bounds__(256, 2) void k_front(Params p) {
     write_tile_desc(p, s_item_idx, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain, tid);
   if constexpr (ATTN) {
     if (stream && s_tile_res == 0)
-      stream_chain<CT, KVT>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
+      stream_chain<CT, KVT, RS>(p, t, g, s, L, Tq_s, q0, rows, n_ch, ppb, s_chain, s_chain_k, s_page);
   }
 }
 
@@ -676,7 +736,10 @@ static hipError_t launch_front_t(const ProfSpan& sp, const Params& p, hipStream_
   const int Teff = p.T > 0 ? p.T : 1;
   const size_t lds = (size_t)Teff * p.K * sizeof(int);
   const unsigned gx = p.stream_narrow ? (unsigned)p.Tq : (unsigned)((p.Tq + Teff - 1) / Teff + p.B);
-  return launch_k(sp, true, true, k_front<CT, KVT, ATTN>, dim3(gx, p.Hkv), dim3(256), (uint32_t)lds, st, p);
+  // one-token tiles of more than 16 query rows: two row sets per wave
+  if (ATTN && p.front_only && p.G > 16)
+    return launch_k(sp, true, true, k_front<CT, KVT, ATTN, 2>, dim3(gx, p.Hkv), dim3(256), (uint32_t)lds, st, p);
+  return launch_k(sp, true, true, k_front<CT, KVT, ATTN, 1>, dim3(gx, p.Hkv), dim3(256), (uint32_t)lds, st, p);
 }
 
 hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st) {

@@ -143,7 +143,7 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  * data pointers may be NULL). Writes 0 for Tq == 0. The size depends on
  * shapes only, and it is the largest any device needs for them:
  *
- *   - a batch with one query token per sequence (Tq == B) and Hq/Hkv <= 16
+ *   - a batch with one query token per sequence (Tq == B) and Hq/Hkv <= 64
  *     (decode): planning arrays only, Tq*Hkv*(5*topk + 12) +
  *     12*Hkv*ceil(max_pages*page_size/128) bytes plus 256-byte alignment
  *     per array (about 72 KB for 64 sequences, Hkv = 8, top-16);

@@ -179,11 +179,15 @@ int msa_oracle_attention(const void* q, int q_dtype, int64_t Tq, int Hq,
     if (used_kv_lens[s] > max_len) max_len = used_kv_lens[s];
 
   int status = ORC_OK;
+  /* the thread count applies to this call only (a num_threads clause, not
+     the process-wide setting) */
+  int nthr = 1;
 #ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
+  nthr = num_threads > 0 ? num_threads : omp_get_max_threads();
 #endif
+  (void)nthr;
 
-#pragma omp parallel
+#pragma omp parallel num_threads(nthr)
   {
     /* per-thread scratch: the key set of one (t, g) and its scores */
     unsigned char* mark = (unsigned char*)malloc((size_t)(max_len > 0 ? max_len : 1));

@@ -232,7 +232,7 @@ def expected_ws(Tq, Hq, Hkv, K, B, MP, P):
     the planning arrays and partials, each array 256-byte aligned."""
     G, nb = Hq // Hkv, -(-MP * P // 128)
     NR, W, ns, TG = nb * Hkv, -(-Tq // 32), Tq * Hkv * K, Tq * Hkv
-    decode = Tq == B and G <= 16
+    decode = Tq == B and G <= 64
     head = _align(256 + (0 if decode else NR * W * 4))
     sizes = [0 if decode else NR * W * 4] * 2 + [ns, TG * 4, TG * 4, ns * 4, TG * 4, NR * 4, (NR + 1) * 4,
                                                  (NR + 1) * 4, 0 if decode else ns * 4, 0 if decode else ns * 4]
@@ -251,7 +251,8 @@ def expected_ws(Tq, Hq, Hkv, K, B, MP, P):
     dict(Tq=64, Hq=64, Hkv=8, K=16, B=64, MP=512, P=64),    # decode: planning arrays only
     dict(Tq=4, Hq=16, Hkv=2, K=4, B=2, MP=4, P=64),         # small prefill-shaped batch
     dict(Tq=300, Hq=32, Hkv=1, K=32, B=3, MP=40, P=128),    # MQA prefill
-    dict(Tq=64, Hq=64, Hkv=2, K=8, B=64, MP=16, P=64),      # decode with G = 32: not front-only
+    dict(Tq=64, Hq=64, Hkv=2, K=8, B=64, MP=16, P=64),      # decode with G = 32: front kernel only
+    dict(Tq=64, Hq=128, Hkv=1, K=8, B=64, MP=16, P=64),     # decode with G = 128: the prefill path
 ])
 def test_workspace_bytes_matches_the_documented_layout(shape):
     a = good(Tq=shape["Tq"], Hq=shape["Hq"], Hkv=shape["Hkv"], NP=16, P=shape["P"], K=shape["K"], B=shape["B"],

@@ -195,6 +195,9 @@ def test_parity_long_tiles_merge_from_global(case):
 # sequence, 32 or 64 rows per token.
 MQA_DECODE = [
     (32, None), (64, None), (32, torch.float8_e4m3fn), (64, torch.float8_e4m3fn),
+    (48, None),   # 3 row sets of 16 in the front kernel, the fourth empty
+    (128, None),  # beyond the front kernel's 64 rows: one-token tiles of the tile kernel
+    (24, torch.float8_e4m3fn),
 ]
 
 
@@ -277,6 +280,11 @@ def test_parity_shared_chunks_with_residuals():
 
 def test_parity_decode_gqa():
     _full(W.make("decode_gqa"))
+
+
+def test_parity_decode_mqa_full():
+    # every pair of the 256-sequence MQA decode batch (32 query heads per KV head)
+    _full(W.make("decode_mqa"))
 
 
 def test_parity_decode_fp8_full():

@@ -17,6 +17,8 @@ Five named workloads (sizes and pick rules in ``CONFIGS`` below):
                   top-k 32 (diagonal + 31 uniform), causal, fp16
   decode_fp8      256 seqs x 1 token, L=65536, Hq=64, Hkv=8, page 64, top-k 16
                   uniform picks, K/V e4m3fn (clamp to +-448 then cast), q bf16
+  decode_mqa      256 seqs x 1 token, Hq=32, Hkv=1 (MQA), otherwise as
+                  decode_gqa
 
 Values are float32 N(0,1) draws converted with torch: bf16 / fp16 by
 round-to-nearest-even ``.to()``, e4m3fn by ``.clamp(-448, 448).to(...)``,
@@ -47,6 +49,7 @@ CONFIGS = {
     "varlen_mqa": dict(seed=1004),
     "decode_fp8": dict(seed=1005),
     "dense_causal": dict(seed=1006),
+    "decode_mqa": dict(seed=1010),
 }
 
 
@@ -228,6 +231,23 @@ def make_decode_gqa(seed=1002, poison=True, batch=64):
                     np.arange(batch + 1), used, bt, sel, NP, poison)
 
 
+def make_decode_mqa(seed=1010, poison=True, batch=256, Hq=32):
+    """MQA decode: batch sequences x 1 query token, Hq query heads on one KV
+    head, L ~ U{8192..32768}, page 64, last block + 15 uniform picks,
+    causal, bf16 (decode_gqa's lengths and picks with Hkv = 1)."""
+    rng = np.random.default_rng(seed)
+    P, Hkv, K = 64, 1, 16
+    used = rng.integers(8192, 32768, size=batch, endpoint=True).astype(np.int32)
+    bt, NP = _page_tables(rng, used, P, max_pages=32768 // P)
+    sel = np.empty((batch, Hkv, K), dtype=np.int32)
+    for s in range(batch):
+        nblk = (int(used[s]) + BLOCK - 1) // BLOCK
+        picks = np.concatenate([[nblk - 1], rng.choice(nblk - 1, size=K - 1, replace=False)])
+        sel[s, 0] = rng.permutation(picks)
+    return assemble("decode_mqa", seed, Hq, Hkv, P, K, True, torch.bfloat16, torch.bfloat16,
+                    np.arange(batch + 1), used, bt, sel, NP, poison)
+
+
 def make_prefill_shared(seed=1003, poison=True, seqlen=16384):
     rng = np.random.default_rng(seed)
     P, Hkv, K, C = 128, 8, 16, 64
@@ -306,6 +326,7 @@ MAKERS = {
     "varlen_mqa": make_varlen_mqa,
     "decode_fp8": make_decode_fp8,
     "dense_causal": make_dense_causal,
+    "decode_mqa": make_decode_mqa,
 }
 
 
