@@ -30,6 +30,7 @@ from ._lib import (
     profile_enable,
     store_kv,
     select_blocks,
+    set_workspace_limit,
     validate_inputs,
     version,
     widen_fp8,
@@ -44,6 +45,7 @@ __all__ = [
     "widen_fp8",
     "store_kv",
     "select_blocks",
+    "set_workspace_limit",
     "validate_inputs",
     "version",
     "load",

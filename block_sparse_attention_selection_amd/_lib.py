@@ -93,6 +93,8 @@ def load():
         lib.msa_profile_enable.argtypes = [ctypes.c_uint32]
         lib.msa_profile_collect.restype = i32
         lib.msa_profile_collect.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        lib.msa_set_workspace_limit.restype = i32
+        lib.msa_set_workspace_limit.argtypes = [ctypes.c_size_t]
         lib.msa_last_error.restype = ctypes.c_char_p
         lib.msa_last_error.argtypes = []
         lib.msa_version.restype = ctypes.c_char_p
@@ -286,6 +288,11 @@ def build_index(selected, cu_seqlens_q, used_kv_lens, *, Hq: int, nb_max: int, c
                                  ctypes.byref(o), _stream(dev))
     _check(rc)
     return res
+
+
+def set_workspace_limit(nbytes: int):
+    """Cap the library-owned workspace (0: no cap); msa_set_workspace_limit."""
+    _check(load().msa_set_workspace_limit(int(nbytes)))
 
 
 KERNELS = {"index": 0, "front": 1, "units": 2, "tiles": 3, "store": 4, "select": 5}

@@ -289,12 +289,19 @@ int32_t device_state(DeviceState** out) {
   return MSA_OK;
 }
 
+// cap on the library-owned workspace of every device (0: none), set by
+// msa_set_workspace_limit (read and written with g_ws_mutex held)
+size_t g_ws_limit = 0;
+
 // The library-owned workspace of the device (g_ws_mutex held): scratch of
 // `need` bytes and a zero-state buffer of two counter sets plus
 // `bitmap_words` words. Growing either synchronises the device; a new
 // zero-state buffer is zeroed.
 int32_t grow_workspace(DeviceState& w, size_t need, size_t bitmap_words) {
   const size_t zs_need = 2 * kCntSetBytes + bitmap_words * 4;
+  if (g_ws_limit && need + zs_need > g_ws_limit)
+    return fail(MSA_ERR_OUT_OF_MEMORY, "this call needs %zu bytes of workspace, above the limit of %zu set with "
+                "msa_set_workspace_limit", need + zs_need, g_ws_limit);
   if (w.bytes >= need && w.zs_bytes >= zs_need) return MSA_OK;
   if (w.ptr || w.zs) {
     if (hipDeviceSynchronize() != hipSuccess) return fail(MSA_ERR_HIP, "hipDeviceSynchronize failed while growing the workspace");
@@ -546,6 +553,12 @@ int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches)
 
 
 const char* msa_last_error(void) { return g_err; }
+
+int32_t msa_set_workspace_limit(size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  g_ws_limit = bytes;
+  return ok();
+}
 
 const char* msa_version(void) { return "msa_kvouter 0.1.0 (gfx950)"; }
 

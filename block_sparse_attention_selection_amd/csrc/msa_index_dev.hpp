@@ -119,15 +119,17 @@ __device__ __forceinline__ int64_t chunk_offset(const Params& p, int s, int g, i
 
 // Descriptor and chunk table of tile item `item` (tile leader t0 of sequence
 // s, nt tokens, KV head g, chain of n_ch blocks): tdesc[2 item] = (t0, s, nt,
-// n_ch), tdesc[2 item + 1] = (reachable keys Leff, base position: pos =
-// base + token, g, nfull), and the table ctab[item * 4 topk + ...] of
-// (element offset low, high, first key, keys present) per chunk. A chunk no
-// row can see, or whose page id lies outside the pool, has offset -1 and no
-// keys present. The table lists first the nfull chunks every row of the
-// tile sees whole (32 keys present, all at or before the first row's
-// position), then the others, each class in chain order, so that the tile
-// kernel runs its unmasked loop up to nfull and masks the rest against
-// their first key + keys present. One wave calls this (lane 0..63).
+// chunks in the table), tdesc[2 item + 1] = (reachable keys Leff, base
+// position: pos = base + token, g, nfull), and the table ctab[item * 4 topk
+// + ...] of (element offset low, high, first key, keys present) per chunk.
+// Chunks that start after the tile's last position are left out (no row
+// sees a key of them); a chunk whose page id lies outside the pool, or that
+// starts at or beyond Leff, has offset -1 and no keys present. The table
+// lists first the nfull chunks every row of the tile sees whole (32 keys
+// present, all at or before the first row's position), then the others,
+// each class in chain order, so that the tile kernel runs its unmasked
+// loop up to nfull and masks the rest against their first key + keys
+// present. One wave calls this (lane 0..63).
 __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t0, int s, int nt, int n_ch, int L,
                                                 int Tq_s, int64_t q0, int g, const int* chain, int lane) {
   const int Leff = min(L, p.MP * p.P);
@@ -138,11 +140,13 @@ __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t
   const int n = 4 * n_ch;  // at most 4 * 64: four batches of 64 chunks
   auto key_of = [&](int ci) { return 128 * chain[ci >> 2] + 32 * (ci & 3); };
   int64_t offs[4];
+  bool used[4];  // the chunk has a key at or before the tile's last position
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ci = 64 * i + lane;
     const int key0 = ci < n ? key_of(ci) : 0;
-    offs[i] = (ci >= n || key0 > pmax) ? (int64_t)-1 : chunk_offset(p, s, g, key0, Leff);
+    used[i] = ci < n && key0 <= pmax;
+    offs[i] = used[i] ? chunk_offset(p, s, g, key0, Leff) : (int64_t)-1;
   }
   auto whole = [&](int ci, int64_t off) {
     const int k0 = key_of(ci);
@@ -152,14 +156,14 @@ __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ci = 64 * i + lane;
-    nfull += __popcll(__ballot(ci < n && whole(ci, offs[i])));
+    nfull += __popcll(__ballot(used[i] && whole(ci, offs[i])));
   }
   const uint64_t below = (1ull << lane) - 1ull;
   int fb = 0, pb = 0;  // whole / other chunks of earlier batches
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ci = 64 * i + lane;
-    const bool in = ci < n;
+    const bool in = used[i];
     const int64_t off = offs[i];
     const bool f = in && whole(ci, off);
     const uint64_t bf = __ballot(f), bo = __ballot(in && !f);
@@ -173,7 +177,7 @@ __device__ __forceinline__ void write_tile_desc(const Params& p, int item, int t
     pb += __popcll(bo);
   }
   if (lane == 0) {
-    p.tdesc[2 * (size_t)item] = int4{t0, s, nt, n_ch};
+    p.tdesc[2 * (size_t)item] = int4{t0, s, nt, fb + pb};
     p.tdesc[2 * (size_t)item + 1] = int4{Leff, base, g, nfull};
   }
 }

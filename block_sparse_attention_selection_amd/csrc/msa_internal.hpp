@@ -130,7 +130,7 @@ hipError_t launch_store_kv(const void* kn, const void* vn, const int64_t* loc, v
                            int P, int64_t num_pages, int in_elem, bool fp8_cache, hipStream_t st);
 
 // block selection (msa_select.hip)
-constexpr int kSelMaxBlocks = 1024;  // blocks per sequence the selection can score (131072 tokens)
+constexpr int kSelMaxBlocks = 2048;  // blocks per sequence the selection can score (262144 tokens)
 struct SelectParams {
   const void* q;          // [Tq, Hkv, 128] index queries, 16-bit
   const void* k;          // [num_pages, Hkv, P, 128] index keys, q's type or e4m3fn

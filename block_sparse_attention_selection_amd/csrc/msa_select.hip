@@ -395,6 +395,7 @@ static hipError_t launch_lists(const ProfSpan& sp, const SelectParams& p, const 
   if (p.nb_cap <= 128) return launch_k(sp, false, true, k_select_lists<2>, grid, block, 0, st, p, sc);
   if (p.nb_cap <= 256) return launch_k(sp, false, true, k_select_lists<4>, grid, block, 0, st, p, sc);
   if (p.nb_cap <= 512) return launch_k(sp, false, true, k_select_lists<8>, grid, block, 0, st, p, sc);
+  if (p.nb_cap <= 1024) return launch_k(sp, false, true, k_select_lists<16>, grid, block, 0, st, p, sc);
   return launch_k(sp, false, true, k_select_lists<kSelMaxBlocks / 64>, grid, block, 0, st, p, sc);
 }
 

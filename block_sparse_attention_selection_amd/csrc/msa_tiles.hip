@@ -943,7 +943,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   for (;;) {
     const int4 d0 = s_desc[bf][0], d1 = s_desc[bf][1];
     const int t0 = d0.x, s = d0.y, nt = d0.z;
-    const int nck = nt > 0 ? 4 * d0.w : 0;
+    const int nck = nt > 0 ? d0.w : 0;  // chunks in the item's table
     const int nfull = min(d1.w, nck);
     const int base = d1.y, g = d1.z;
     const int rows = nt * G;
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
             // the next item's table was issued before chunk kAhead of this
             // item (or drained with the top-up), so it has landed by now
             const int4 dn = s_desc[bf ^ 1][0];
-            chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? 4 * dn.w : 0, off, nr);
+            chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? dn.w : 0, off, nr);
           }
           issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + nx));
           // a masked chunk's keys [key0, lim) are present: none when its page

@@ -318,13 +318,13 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
  *                 dtype or fp8_e4m3fn (scale 1), read through block_tables
  *   block_tables, cu_seqlens_q, used_kv_lens, page_size, causal: as for
  *                 msa_kvouter_attention (the same preconditions)
- *   topk          1 .. 1024, the width of `selected`
+ *   topk          1 .. 2048, the width of `selected`
  *   selected      [Tq, Hkv, topk] int32, written
  *   scores        NULL, or [Tq, Hkv, nb] fp32 with nb = ceil(max_pages *
  *                 page_size / 128): written with every block's score (-inf
  *                 for blocks without a visible token)
  *
- * Sequences may reach at most 1024 blocks (nb <= 1024, else
+ * Sequences may reach at most 2048 blocks (nb <= 2048, else
  * MSA_ERR_UNSUPPORTED). All buffers are caller-owned device memory; the call
  * validates descriptors on the host, enqueues one or two kernels on `stream`
  * and returns. Decode-shaped batches (Tq <= 4 * batch) and tables beyond 256
@@ -374,6 +374,17 @@ enum {
 };
 int32_t msa_profile_enable(uint32_t kernel_mask);
 int32_t msa_profile_collect(int32_t kernel, double* total_ms, int64_t* launches);
+
+/*
+ * msa_set_workspace_limit -- cap the library-owned workspace of every device
+ * at `bytes` (0: no cap, the default). A call whose workspace (planning
+ * arrays, partial results, counters and bitmaps; msa_kvouter_workspace_bytes
+ * reports about the same figure) would exceed the cap returns
+ * MSA_ERR_OUT_OF_MEMORY and enqueues nothing; memory already held is kept.
+ * Calls with a caller-owned workspace are not affected. Lets a caller bound
+ * the library's memory, and lets tests force the out-of-memory path.
+ */
+int32_t msa_set_workspace_limit(size_t bytes);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* msa_last_error(void);

@@ -201,7 +201,7 @@ def test_select_blocks_argument_checks():
     assert call_sel(args(), topk=0) == INV                                 # topk outside [1, 1024]
     assert call_sel(args(topk=5)) == INV                                   # selected width != topk
     assert call_sel(args(sc=[4, 2, 3])) == INV                             # scores: nb = 4*64/128 = 2
-    assert call_sel(args(MP=2100)) == UNS                                  # beyond 1024 blocks
+    assert call_sel(args(MP=4200)) == UNS                                  # beyond 2048 blocks
     assert call_sel(args(P=128)) == INV                                    # page dim != page_size
     assert call_sel(args(), causal=2) == INV
     assert call_sel(args(Tq=0)) == 0                                       # nothing to select

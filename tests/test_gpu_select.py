@@ -105,6 +105,9 @@ CASES = [
     ([2, 3], [10000, 9000], 1, 64, 8, True, torch.float8_e4m3fn),          # 65..128 blocks a row
     ([1, 2], [100000, 20000], 1, 128, 16, True, torch.bfloat16),           # up to 782 blocks a row
     ([1, 1, 1, 1, 1], [3000, 200, 129, 128, 5000], 16, 128, 1, False, torch.float8_e4m3fn),  # 16 heads, top-1
+    ([2], [128000], 1, 64, 16, True, torch.float8_e4m3fn),                 # 1000 blocks a row
+    ([1, 1], [133120, 40000], 1, 128, 32, True, torch.bfloat16),           # 1040 blocks: varlen_mqa's longest
+    ([1, 2], [256000, 3000], 1, 128, 16, False, torch.float8_e4m3fn),       # 2000 blocks, non-causal
 ]
 
 

@@ -129,3 +129,33 @@ def test_ws_call_captured_in_a_graph_replays_like_eager_calls(name):
         _same(eager, (out, lse))
         assert torch.isfinite(junk)
     del g
+
+
+def test_workspace_limit_forces_out_of_memory_and_is_lifted():
+    # the failure path of the library-owned workspace, forced from the host:
+    # a cap below what a prefill call needs makes it fail cleanly with
+    # MSA_ERR_OUT_OF_MEMORY (nothing enqueued), a decode call under the cap
+    # still runs, and lifting the cap restores the prefill call
+    import block_sparse_attention_selection_amd as msa
+
+    pre = _cases()["prefill"]()
+    dec = _cases()["decode"]()
+    dp, dd = device_inputs(pre), device_inputs(dec)
+    ref = _call(pre, dp)
+    torch.cuda.synchronize()
+    msa.set_workspace_limit(1 << 20)
+    try:
+        out = torch.full_like(dp["q"], 7.0)
+        with pytest.raises(msa.MsaError, match="limit") as ei:
+            _call(pre, dp, out=out)
+        assert ei.value.code == -3
+        torch.cuda.synchronize()
+        assert torch.all(out == 7.0)  # refused before anything was enqueued
+        got_dec = _call(dec, dd)      # a decode call needs far less than 1 MiB
+        torch.cuda.synchronize()
+        pairs = all_pairs(dec)
+        ref_o, ref_l = oracle_pairs(dec, pairs)
+        compare(dec, got_dec[0], got_dec[1], pairs, ref_o, ref_l)
+    finally:
+        msa.set_workspace_limit(0)
+    _same(ref, _call(pre, dp))

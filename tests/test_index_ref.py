@@ -11,8 +11,12 @@ import workloads as W
 from oracle import index_ref
 
 
-def literal_plan(selected, cu, used, causal, T, Tu, nb_max, Hkv, K):
-    """Dictionary-and-loop restatement of the rules in index_ref's docstring."""
+def literal_plan(selected, cu, used, causal, T, Tu, nb_max, Hkv, K, G=1, list_all=False):
+    """Dictionary-and-loop restatement of the rules in index_ref's docstring.
+
+    Returns the slot flags, the chains, the residual rows, and per (t, g) the
+    chain length of t's tile and the number of residual slots, and the set
+    of listed tiles (t_leader * Hkv + g)."""
     Tq = selected.shape[0]
     owner = {}
     for s in range(len(used)):
@@ -54,14 +58,33 @@ def literal_plan(selected, cu, used, causal, T, Tu, nb_max, Hkv, K):
         if f == 2:
             r = int(selected[t, g, k]) * Hkv + g
             rows.setdefault(r, []).append((t * Hkv + g) * K + k)
-    return flag, chains, rows
+    nres = {(t, g): sum(1 for k in range(K) if flag[(t, g, k)] == 2) for t in range(Tq) for g in range(Hkv)}
+    chain_len = {(t, g): 0 for t in range(Tq) for g in range(Hkv)}
+    listed = set()
+    step = T if T > 0 else 1  # without chains every token is a tile of its own
+    for s in range(len(used)):
+        for t0 in range(int(cu[s]), int(cu[s + 1]), step):
+            toks = list(range(t0, min(t0 + step, int(cu[s + 1]))))
+            for g in range(Hkv):
+                n = len(chains.get((t0, g), [])) if T > 0 else 0
+                for t in toks:
+                    chain_len[(t, g)] = n
+                if list_all or len(toks) * G > 16 or any(nres[(t, g)] > 0 for t in toks):
+                    listed.add(t0 * Hkv + g)
+    return flag, chains, rows, chain_len, nres, listed
 
 
-def check_against_literal(wl, T, Tu, nb_max):
+def check_against_literal(wl, T, Tu, nb_max, list_all=False):
     Tq, Hkv, K = wl.selected.shape
-    plan = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G)
-    flag, chains, rows = literal_plan(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal,
-                                      T, Tu, nb_max, Hkv, K)
+    plan = index_ref.build(wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, wl.G,
+                           list_all_tiles=list_all)
+    flag, chains, rows, chain_len, nres, listed = literal_plan(
+        wl.selected, wl.cu_seqlens_q, wl.used_kv_lens, wl.causal, T, Tu, nb_max, Hkv, K, wl.G, list_all)
+    for (t, g), n in chain_len.items():
+        assert plan.tok_chain[t, g] == n, (t, g)
+    for (t, g), n in nres.items():
+        assert plan.tok_nres[t, g] == n, (t, g)
+    assert plan.tile_items == listed
     for (t, g, k), f in flag.items():
         assert plan.slot_flag[t, g, k] == f, (t, g, k)
     for key, ch in chains.items():
@@ -77,13 +100,24 @@ def check_against_literal(wl, T, Tu, nb_max):
     assert (plan.slot_pos.reshape(-1) >= 0).sum() == plan.ent.size
 
 
+@pytest.mark.parametrize("list_all", [False, True])
 @pytest.mark.parametrize("T", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("causal", [False, True])
-def test_reference_matches_literal_rules(T, causal):
+def test_reference_matches_literal_rules(T, causal, list_all):
     wl = W.make_custom(100 + T, [3, 5, 1, 0, 4], [300, 700, 129, 50, 520], 4, 2, 64, topk=4,
                        causal=causal, pick="random", shared_chunk=2, shared_picks=2)
     nb_max = (wl.block_tables.shape[1] * 64 + 127) // 128
-    check_against_literal(wl, T, 3, nb_max)
+    check_against_literal(wl, T, 3, nb_max, list_all)
+
+
+def test_reference_matches_literal_tile_listing_by_rows():
+    # tiles of 2 tokens x G = 8 rows are listed only when they hold a
+    # residual slot; tiles of 3 tokens x 8 = 24 rows always
+    for T in (2, 3):
+        wl = W.make_custom(150 + T, [6, 4, 1], [900, 400, 300], 16, 2, 64, topk=3, causal=True, pick="diag",
+                           shared_chunk=T, shared_picks=2)
+        nb_max = (wl.block_tables.shape[1] * 64 + 127) // 128
+        check_against_literal(wl, T, 2, nb_max)
 
 
 def test_reference_matches_literal_with_pads_and_oob():
