@@ -274,6 +274,97 @@ __device__ __forceinline__ u32x4 vfrag_at(const char* vtile, int t, int sp) {
   return a;
 }
 
+// A whole staged block against the rows at once (the unit kernel): the first
+// NQ chunks of the block at sblk (chunk q: K at q * kSlotU4, V kChunkU4
+// after it), chunk q's keys [key0[q], lim[q]) present, masked when bit q of
+// mmask is set (as in rows_probs; a unit's rows all belong to the staged
+// block's sequence). The scores of all NQ chunks are formed first (NQ
+// independent accumulation chains), then one softmax over the row's keys of
+// the block -- its maximum is final, so nothing is ever rescaled -- then
+// O^T = V^T P^T over the NQ chunks. The row state must be the reset one;
+// rt.o is written here.
+template <typename CT, int NQ>
+__device__ __forceinline__ void rows_block(Rows32& rt, const u32x4* sblk, const int (&key0)[4], const int (&lim)[4],
+                                           unsigned mmask, float sl2) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+  f32x16 sa[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sa[q][j] = 0.f;
+  // k-step s of every chunk: its K fragments are read one stage ahead
+  u32x4 kf[2][NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) kf[0][q] = sblk[q * kSlotU4 + pieceK(c, h)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s + 1 < 8) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) kf[(s + 1) & 1][q] = sblk[q * kSlotU4 + pieceK(c, 2 * (s + 1) + h)];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sa[q] = Mma32<CT>::run(kf[s & 1][q], rt.qb[s], sa[q]);
+    // the reads first, then the products
+    if (s + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, NQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if ((mmask >> q) & 1u) {
+      // key (key0 + 4h + the element's offset) is visible iff it is <= bound
+      const int rel = min(rt.pos, lim[q] - 1) - key0[q] - 4 * h;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sa[q][j] = (8 * (j >> 2) + (j & 3)) <= rel ? sa[q][j] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cmax = fmaxf(cmax, sa[q][j]);
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cmax), __float_as_uint(cmax), false, false);
+    cmax = __builtin_amdgcn_fmed3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), INFINITY) * sl2;
+  }
+  const float nmu = cmax == -INFINITY ? 0.f : -cmax;
+  u32x4 pb[NQ][2];
+  float ls = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[q][2 * i], sl2, nmu));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[q][2 * i + 1], sl2, nmu));
+      pb[q][i >> 2][i & 3] = pack2<CT>(p0, p1);
+      ls += p0 + p1;
+    }
+  rt.m = cmax;
+  rt.l = ls;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rt.o[t][j] = 0.f;
+  // key step (q, sp): the four V^T fragments of the next step are read
+  // while this step's four products run
+  u32x4 vf[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) vf[0][t] = vfrag_at((const char*)(sblk + kChunkU4), t, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2 * NQ; ++k) {
+    if (k + 1 < 2 * NQ) {
+      const char* vn = (const char*)(sblk + ((k + 1) >> 1) * kSlotU4 + kChunkU4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vf[(k + 1) & 1][t] = vfrag_at(vn, t, (k + 1) & 1);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rt.o[t] = Mma32<CT>::run(vf[k & 1][t], pb[k >> 1][k & 1], rt.o[t]);
+    if (k + 1 < 2 * NQ) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One iteration of the tile kernel's chunk pipeline, scheduled by hand:
 // O^T += V(prev)^T P(prev)^T, sn = S of the next chunk, and the softmax step
 // of sc (this chunk's scores) giving pn. The work is cut into eight stages:
@@ -772,15 +863,28 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
         const int pmin = p.causal ? base + s_tok[a0] : INT_MAX;
         const int pmax = p.causal ? base + s_tok[a1 - 1] : INT_MAX;
         if (32 * wave < rows) {
-#pragma unroll 1
+          // the block's chunks that some row of the piece sees: a prefix
+          // (keys below the used length and at or before the last row's
+          // position); chunk q's keys [key0, lim) are present (none when its
+          // page is absent), and it is masked unless all 32 are present and
+          // visible to every row
+          int key0[4], lim[4], nq = 0;
+          unsigned mmask = 0u;
+#pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int key0 = kBlk * b + 32 * q;
-            if (key0 >= Leff || key0 > pmax) break;
-            // keys [key0, lim) are present: none when the chunk's page is absent
-            const int lim = ((st_absent >> q) & 1u) ? key0 : min(Leff, key0 + 32);
-            const bool full = lim == key0 + 32 && key0 + 31 <= pmin;
-            rows_chunk<CT>(rt, s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4, key0, lim, s_run, !full,
-                           p.scale_log2);
+            key0[q] = kBlk * b + 32 * q;
+            lim[q] = ((st_absent >> q) & 1u) ? key0[q] : min(Leff, key0[q] + 32);
+            if (key0[q] < Leff && key0[q] <= pmax) nq = q + 1;
+            if (!(lim[q] == key0[q] + 32 && key0[q] + 31 <= pmin)) mmask |= 1u << q;
+          }
+          nq = __builtin_amdgcn_readfirstlane(nq);  // uniform: the piece's, not the lane's
+          mmask = __builtin_amdgcn_readfirstlane(mmask);
+          switch (nq) {
+            case 1: rows_block<CT, 1>(rt, s_blk, key0, lim, mmask, p.scale_log2); break;
+            case 2: rows_block<CT, 2>(rt, s_blk, key0, lim, mmask, p.scale_log2); break;
+            case 3: rows_block<CT, 3>(rt, s_blk, key0, lim, mmask, p.scale_log2); break;
+            case 4: rows_block<CT, 4>(rt, s_blk, key0, lim, mmask, p.scale_log2); break;
+            default: break;
           }
         }
       }
