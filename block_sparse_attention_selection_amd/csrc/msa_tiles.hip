@@ -51,6 +51,28 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// c + a.lo * b.lo + a.hi * b.hi for two packed 16-bit values of T, in fp32
+// (v_dot2_f32_bf16 / v_dot2_f32_f16). With b = (w, 0) or (0, w) it scales one
+// element of a packed pair and accumulates it in a single instruction.
+template <typename T>
+struct Dot2;
+
+template <>
+struct Dot2<bf16_t> {
+  typedef __bf16 t2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(t2, a), __builtin_bit_cast(t2, b), c, false);
+  }
+};
+
+template <>
+struct Dot2<f16_t> {
+  typedef _Float16 t2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(t2, a), __builtin_bit_cast(t2, b), c, false);
+  }
+};
+
 template <typename T>
 struct Mma32;
 
@@ -1259,6 +1281,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         M = m_new;
         const float fi = use ? exp2f(lc - M) : 0.f;
         W += fi;
+        // the weight as a 16-bit value beside a zero: one dot2 instruction
+        // scales and accumulates one element of a packed pair (the weight's
+        // rounding to 16 bits moves O by at most 2^-9 of this partial's share;
+        // the row sum W keeps the fp32 weight)
+        const uint32_t wlo = pack2<CT>(fi, 0.f), whi = wlo << 16;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1269,10 +1296,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {  // group a = 2u + e: words s0[e], s1[e]
               const int a = 2 * u + e;
-              rt.o[t][4 * a] += fi * from_bits16<CT>(s0[e] & 0xFFFFu);
-              rt.o[t][4 * a + 1] += fi * from_bits16<CT>(s0[e] >> 16);
-              rt.o[t][4 * a + 2] += fi * from_bits16<CT>(s1[e] & 0xFFFFu);
-              rt.o[t][4 * a + 3] += fi * from_bits16<CT>(s1[e] >> 16);
+              rt.o[t][4 * a] = Dot2<CT>::run(s0[e], wlo, rt.o[t][4 * a]);
+              rt.o[t][4 * a + 1] = Dot2<CT>::run(s0[e], whi, rt.o[t][4 * a + 1]);
+              rt.o[t][4 * a + 2] = Dot2<CT>::run(s1[e], wlo, rt.o[t][4 * a + 2]);
+              rt.o[t][4 * a + 3] = Dot2<CT>::run(s1[e], whi, rt.o[t][4 * a + 3]);
             }
           }
       };
