@@ -278,8 +278,8 @@ __device__ __forceinline__ void rows_chunk(Rows32& rt, const u32x4* sK, const u3
 // 16sp + 8r + 4h + i (i = (l >> 2) & 3), logical piece 4t + 2((l >> 4) & 1)
 // + ((l & 3) >> 1), half l & 1. With the V swizzle the physical piece is
 // 4(t ^ i) + the low two bits.
-__device__ __forceinline__ u32x4 vfrag_at(const char* vtile, int t, int sp) {
-  const int lane = threadIdx.x & 63, h = lane >> 5;
+__device__ __forceinline__ u32x4 vfrag_at(const char* vtile, int t, int sp, int lane = threadIdx.x & 63) {
+  const int h = lane >> 5;
   const int i4 = (lane >> 2) & 3;
   const int rsub = 4 * h + i4;
   const int psub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -308,7 +308,12 @@ __device__ __forceinline__ u32x4 vfrag_at(const char* vtile, int t, int sp) {
 template <typename CT, int NQ>
 __device__ __forceinline__ void rows_block(Rows32& rt, const u32x4* sblk, const int (&key0)[4], const int (&lim)[4],
                                            unsigned mmask, float sl2) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+  // the lane index, opaque to the compiler: the LDS addresses derived from it
+  // are formed here, once per call, instead of being held in registers across
+  // the whole kernel
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int h = lane >> 5, c = lane & 31;
   f32x16 sa[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
@@ -370,14 +375,14 @@ __device__ __forceinline__ void rows_block(Rows32& rt, const u32x4* sblk, const 
   // while this step's four products run
   u32x4 vf[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) vf[0][t] = vfrag_at((const char*)(sblk + kChunkU4), t, 0);
+  for (int t = 0; t < 4; ++t) vf[0][t] = vfrag_at((const char*)(sblk + kChunkU4), t, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < 2 * NQ; ++k) {
     if (k + 1 < 2 * NQ) {
       const char* vn = (const char*)(sblk + ((k + 1) >> 1) * kSlotU4 + kChunkU4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) vf[(k + 1) & 1][t] = vfrag_at(vn, t, (k + 1) & 1);
+      for (int t = 0; t < 4; ++t) vf[(k + 1) & 1][t] = vfrag_at(vn, t, (k + 1) & 1, lane);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) rt.o[t] = Mma32<CT>::run(vf[k & 1][t], pb[k >> 1][k & 1], rt.o[t]);
@@ -700,6 +705,19 @@ __device__ __forceinline__ void unit_tokens(const Params& p, int r, int rank0, i
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
 
+// Returning atomic add whose result is waited for explicitly (wait_vmcnt,
+// then settle()): the compiler does not see it as a load in flight.
+__device__ __forceinline__ int atomic_add_nowait(int32_t* ptr, int val) {
+  int r;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(r) : "v"(ptr), "v"(val) : "memory");
+  return r;
+}
+__device__ __forceinline__ int settle(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+
 struct XcdQueue {
   int lo, hi, rank, nwg;
   int32_t* head;
@@ -724,10 +742,22 @@ struct XcdQueue {
 // KV head g). The window is cut into pieces -- runs of tokens of one
 // sequence, at most 128 / G tokens each, i.e. at most 128 query rows -- and
 // the pieces are multiplied one after another against the block, which stays
-// staged in LDS until the sequence or the row changes. The next piece's Q is
-// loaded while the current one is multiplied.
+// staged in LDS until the sequence or the row changes.
+//
+// Vector memory operations complete in issue order, and a wait for a load
+// also waits for every store issued before it. So every load a piece needs is
+// issued before the stores of the piece before it: the next piece's Q while
+// the current one is multiplied; at the end of a piece, the next piece's block
+// (when it changes) and, at the end of a window, the next window's first Q,
+// both ahead of the current piece's partial stores. The next window's token
+// list is built in a second LDS buffer at the end of the current window; its
+// descriptor and tokens are loaded during the current window, and the work
+// queue slot of the window after it is taken at the current window's start.
 // ---------------------------------------------------------------------------
 constexpr int kSeqLds = 256;  // cu_seqlens / used_kv_lens cached in LDS up to this many sequences
+// vector memory instructions per lane of the partial stores of a piece
+// (store_part: eight 16-byte stores, then the LSE)
+constexpr int kUnitStoreOps = 9;
 
 __device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok, int head, int h) {
   if (tok < 0) {
@@ -740,15 +770,56 @@ __device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok
   for (int s = 0; s < 8; ++s) qb[s] = *(const u32x4*)(base + 16 * s);
 }
 
+// Scalar (uniform-address) loads of read-only data, waited for in the same
+// statement. They are counted by lgkmcnt, so waiting for them never waits
+// for the vector memory operations in flight.
+__device__ __forceinline__ int64_t sload64(const int64_t* ptr) {
+  int64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+__device__ __forceinline__ int sload32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// The unit kernel's Q rows: every lane loads a row, those without a token
+// token 0's (their results go to the scratch row), so that each call is the
+// same eight loads in every wave and no register is cleared while a load into
+// it may be in flight.
+__device__ __forceinline__ void load_q8_rows(u32x4 (&qb)[8], const Params& p, int tok, int head, int h) {
+  const uint16_t* base = (const uint16_t*)p.q + ((size_t)max(tok, 0) * p.Hq + head) * kD + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qb[s] = *(const u32x4*)(base + 16 * s);
+}
+
+// chunk into LDS (K tile at byte address sK, V tile at sV) by the unit
+// kernel's 256 threads, two 16-byte pieces of K and two of V per lane
+__device__ __forceinline__ void issue_chunk16_256(const void* kb, const void* vb, int64_t off_any, int nrows_any,
+                                                  const DmaLane& dl, uint32_t sK, uint32_t sV) {
+  const int wave = threadIdx.x >> 6;
+  const int64_t off = uniform64(off_any);
+  const int nrows = __builtin_amdgcn_readfirstlane(nrows_any);
+  const bool present = off >= 0 && nrows > 0;
+  const int64_t ob = present ? off * 2 : 0;
+  const int nrec = present ? min(nrows, 32) * 256 : 0;
+  const i32x4v rk = make_rsrc((const char*)kb + ob, nrec), rv = make_rsrc((const char*)vb + ob, nrec);
+  dma16(rk, sK + 2048 * wave, dl.k0);
+  dma16(rk, sK + 2048 * wave + 1024, dl.k1);
+  dma16(rv, sV + 2048 * wave, dl.v0);
+  dma16(rv, sV + 2048 * wave + 1024, dl.v1);
+}
+
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(256, 2) void k_units(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
   __shared__ u32x4 s_blk[kRing * kSlotU4];  // the staged block: chunk q at q * kSlotU4 (K), + kChunkU4 (V)
-  __shared__ int s_tok[kUnitWindow];
-  __shared__ int s_seq[kUnitWindow];
+  __shared__ int s_tok[2][kUnitWindow];     // token lists of two consecutive windows
+  __shared__ int s_seq[2][kUnitWindow];
   __shared__ int64_t s_cu[kSeqLds + 1];
   __shared__ int s_used[kSeqLds];
-  __shared__ int s_item;
+  __shared__ int s_item[2];
   const int nU = p.counters[kCntUnits];
   if (nU == 0) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
@@ -759,8 +830,33 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
     for (int i = tid; i <= p.B; i += 256) s_cu[i] = p.cu[i];
     for (int i = tid; i < p.B; i += 256) s_used[i] = p.used[i];
   }
-  const int64_t* cu = seq_lds ? s_cu : p.cu;
-  const int* used = seq_lds ? s_used : p.used;
+  // sequence bounds from LDS, or from global memory for large batches (never
+  // through a generic pointer: a flat load is counted with the vector memory
+  // operations, and waiting for it would wait for every load and store in
+  // flight)
+  auto cu_at = [&](int i) -> int64_t {
+    if (seq_lds) {
+      int64_t v = s_cu[i];
+      asm volatile("" : "+v"(v));  // keeps the two loads apart (else merged into one flat load)
+      return v;
+    }
+    return p.cu[i];
+  };
+  // the same at a uniform index (the piece's sequence), by scalar loads
+  auto cu_u = [&](int i) { return sload64(p.cu + __builtin_amdgcn_readfirstlane(i)); };
+  auto used_u = [&](int i) { return sload32(p.used + __builtin_amdgcn_readfirstlane(i)); };
+  auto seq_of_tok = [&](int64_t t) {  // as seq_of
+    if (p.B <= 0 || t < cu_at(0)) return -1;
+    int lo = 0, hi = p.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_at(mid) <= t)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return t < cu_at(lo + 1) ? lo : -1;
+  };
   int st_s = -1, st_b = -1, st_g = -1;  // staged block (uniform)
   unsigned st_absent = 0u;              // bit q: chunk q of the staged block has no keys (page outside the pool)
   DmaLane dl;
@@ -768,37 +864,33 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
   XcdQueue wq;
   wq.init(nU, p.counters + kCntXcdU);
   const int64_t slots_per_tok = (int64_t)Hkv * K;
-  // the window's descriptor and tokens (two per thread) are loaded one window ahead
-  // (with ent materialised; otherwise the tokens come from the row's bitmap
-  // words when the window starts, and the window writes its own residual
-  // list entries)
+  // a window's tokens (two per thread) come from the materialised residual
+  // order; otherwise from the row's bitmap words, and the window then writes
+  // its own residual list entries
   const bool have_ent = p.ent_ready != 0;
+  // (the residual order entries themselves; prepare() turns them into tokens,
+  // so that nothing waits for these loads before then)
   auto load_tokens = [&](int4 wd, int (&tk)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int e = tid + 256 * i;
-      tk[i] = (have_ent && e < min(wd.w, p.Tu)) ? (int)(p.ent[wd.z + e] / slots_per_tok) : -1;
+      tk[i] = (have_ent && e < min(wd.w, p.Tu)) ? p.ent[wd.z + e] : -1;
     }
   };
-  if (tid == 0) s_item = wq.next(true);
-  __syncthreads();
-  int u = s_item;
-  __syncthreads();  // s_item is rewritten inside the loop
-  int4 wd = u >= 0 ? p.win_desc[u] : int4{0, 0, 0, 0};
-  int tk[2];
-  load_tokens(wd, tk);
-  while (u >= 0) {
+  // token list and sequences of window wd into buffer bf (every thread calls
+  // it; the caller synchronises before they are read)
+  auto prepare = [&](int bf, int4 wd, const int (&tk)[2]) {
     const int r = wd.x, e0 = wd.z, n = min(wd.w, p.Tu);
-    const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
     if (!have_ent) {
-      for (int i = tid; i < n; i += 256) s_tok[i] = -1;
+      const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
+      for (int i = tid; i < n; i += 256) s_tok[bf][i] = -1;
       __syncthreads();
-      if (wave == 0) unit_tokens(p, r, wd.y, n, s_tok);
+      if (wave == 0) unit_tokens(p, r, wd.y, n, s_tok[bf]);
       __syncthreads();
       for (int idx = tid; idx < n * K; idx += 256) {
         const int tau = idx / K, k = idx - tau * K;
-        if (s_tok[tau] < 0) continue;
-        const size_t slot = ((size_t)s_tok[tau] * Hkv + g) * K + k;
+        if (s_tok[bf][tau] < 0) continue;
+        const size_t slot = ((size_t)s_tok[bf][tau] * Hkv + g) * K + k;
         if (p.selected[slot] == b && p.slot_flag[slot] == 2) p.res_list[slot - k + p.res_rank[slot]] = e0 + tau;
       }
     }
@@ -806,84 +898,131 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
     for (int i = 0; i < 2; ++i) {
       const int e = tid + 256 * i;
       if (e < n) {
-        const int tok = have_ent ? tk[i] : s_tok[e];
-        s_tok[e] = tok;
-        s_seq[e] = tok >= 0 ? seq_of(cu, p.B, tok) : -1;
+        const int tok = have_ent ? (tk[i] < 0 ? -1 : (int)(tk[i] / slots_per_tok)) : s_tok[bf][e];
+        s_tok[bf][e] = tok;
+        s_seq[bf][e] = tok >= 0 ? seq_of_tok(tok) : -1;
       }
     }
-    if (tid == 0) s_item = wq.next(false);
-    __syncthreads();
-    // the next window, in flight while this one is multiplied
-    const int un = s_item;
-    const int4 wdn = un >= 0 ? p.win_desc[un] : int4{0, 0, 0, 0};
-    int tkn[2];
-    load_tokens(wdn, tkn);
+  };
+  // pieces [a0, a1): a run of one sequence, at most Tp tokens
+  auto piece_end = [&](int bf, int n, int a0) {
+    const int sq = s_seq[bf][a0];
+    const int lim = min(n, a0 + Tp);
+    int e = a0 + 1;
+    while (e < lim && s_seq[bf][e] == sq) ++e;
+    return e;
+  };
+  const int rho = 32 * wave + c;
+  const int hr = rho % G;
+  auto row_token = [&](int bf, int a0, int a1) {  // the lane's token in piece [a0, a1), or -1
+    const int tau = rho / G;
+    return (a0 + tau < a1 && s_seq[bf][a0 + tau] >= 0) ? s_tok[bf][a0 + tau] : -1;
+  };
+  // the block (sequence s_run, block b, KV head g) into s_blk: 16-bit caches
+  // by direct-to-LDS loads, waited for by the caller; e4m3fn caches through
+  // registers, widened and written to LDS here
+  auto stage = [&](int s_run_any, int b_any, int g_any) {
+    // uniform: the page table reads below are scalar loads
+    const int s_run = __builtin_amdgcn_readfirstlane(s_run_any);
+    const int b = __builtin_amdgcn_readfirstlane(b_any), g = __builtin_amdgcn_readfirstlane(g_any);
+    const int Leff = min(used_u(s_run), p.MP * p.P);
+    // the page table entries of the four chunks in one load (lane q & 3
+    // reads chunk q's), instead of four dependent round trips
+    int pg = -1;
+    {
+      const int key0 = kBlk * b + 32 * (lane & 3);
+      if (key0 < Leff) pg = p.block_tables[(size_t)s_run * p.MP + key0 / p.P];
+    }
+    int64_t offs[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int key0 = kBlk * b + 32 * q;
+      const int page = __builtin_amdgcn_readlane(pg, q);
+      offs[q] = (key0 >= Leff || page < 0 || page >= p.NP)
+                    ? (int64_t)-1
+                    : (((int64_t)page * p.Hkv + g) * p.P + (key0 % p.P)) * 128;
+    }
+    st_absent = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st_absent |= offs[q] < 0 ? 1u << q : 0u;
+    if constexpr (kFp8) {
+      Raw8 raw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, offs[q], Leff - (kBlk * b + 32 * q),
+                             p.zero_page);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        issue_chunk16_256(p.k, p.v, offs[q], Leff - (kBlk * b + 32 * q), dl, lds_addr(s_blk + q * kSlotU4),
+                          lds_addr(s_blk + q * kSlotU4 + kChunkU4));
+    }
+    st_s = s_run;
+    st_b = b;
+    st_g = g;
+  };
 
-    // pieces [a0, a1): a run of one sequence, at most Tp tokens
-    auto piece_end = [&](int a0) {
-      const int sq = s_seq[a0];
-      const int lim = min(n, a0 + Tp);
-      int e = a0 + 1;
-      while (e < lim && s_seq[e] == sq) ++e;
-      return e;
-    };
-    const int rho = 32 * wave + c;
-    const int head = g * G + (rho % G);
-    const int hr = rho % G;
-    auto row_token = [&](int a0, int a1) {  // the lane's token in piece [a0, a1), or -1
-      const int tau = rho / G;
-      return (a0 + tau < a1 && s_seq[a0 + tau] >= 0) ? s_tok[a0 + tau] : -1;
-    };
-    int a0 = 0, a1 = piece_end(0);
-    Rows32 rt;
-    load_q8(rt.qb, p, row_token(a0, a1), head, h);
+  // the first window, its token list, its first piece's Q and block
+  if (tid == 0) s_item[0] = wq.next(true);
+  __syncthreads();
+  int u = __builtin_amdgcn_readfirstlane(s_item[0]);
+  __syncthreads();
+  if (u < 0) return;
+  int4 wd = p.win_desc[u];
+  int bf = 0;
+  {
+    int tk[2];
+    load_tokens(wd, tk);
+    if (tid == 0) s_item[0] = wq.next(false);
+    prepare(0, wd, tk);
+  }
+  __syncthreads();
+  int un = __builtin_amdgcn_readfirstlane(s_item[0]);  // the next window's item
+  int n = min(wd.w, p.Tu);
+  int a0 = 0, a1 = piece_end(0, n, 0);
+  Rows32 rt;
+  {
+    const int b = wd.x / Hkv, g = wd.x - (wd.x / Hkv) * Hkv;
+    load_q8_rows(rt.qb, p, row_token(0, a0, a1), g * G + hr, h);
+    if (s_seq[0][0] >= 0) stage(s_seq[0][0], b, g);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  for (;;) {
+    const int r = wd.x, e0 = wd.z;
+    const int b = r / Hkv, g = r - (r / Hkv) * Hkv;
+    const int head = g * G + hr;
+    // the next window's descriptor (its item was taken during this window's
+    // predecessor) and, from workgroup-thread 0, the item of the window after
+    // it, neither waited for here
+    const int4 wdn = un >= 0 ? p.win_desc[__builtin_amdgcn_readfirstlane(un)] : int4{0, 0, 0, 0};
+    int nn = 0;
+    if (tid == 0 && un >= 0) nn = atomic_add_nowait(wq.head, 1);  // XcdQueue::next(false)
+    int tkn[2] = {-1, -1};
+    bool tokens_issued = false;
+    u32x4 qn[8];  // the next piece's Q (at the window's end: the next window's first piece)
     for (;;) {
-      const int s_run = s_seq[a0];
-      const int a2 = a1 < n ? piece_end(a1) : a1;
-      u32x4 qn[8];
-      load_q8(qn, p, a1 < n ? row_token(a1, a2) : -1, head, h);  // the next piece's Q, in flight
+      const int s_run = __builtin_amdgcn_readfirstlane(s_seq[bf][a0]);
+      const bool last = a1 >= n;
+      const int a2 = last ? a1 : piece_end(bf, n, a1);
+      if (!last) load_q8_rows(qn, p, row_token(bf, a1, a2), head, h);  // the next piece's Q, in flight
       rows_reset(rt);
       const int rows = (a1 - a0) * G;
       const bool valid = rho < rows;
-      const int tok = valid ? s_tok[a0 + rho / G] : -1;
+      const int tok = valid ? s_tok[bf][a0 + rho / G] : -1;
       rt.seq = s_run;
       rt.pos = INT_MAX;
       if (s_run >= 0) {
-        const int L = used[s_run];
+        const int L = used_u(s_run);
         const int Leff = min(L, p.MP * p.P);
-        const int base = (int)(L - (cu[s_run + 1] - cu[s_run]) - cu[s_run]);  // pos = base + token
+        const int64_t c0 = cu_u(s_run), c1 = cu_u(s_run + 1);
+        const int base = (int)(L - (c1 - c0) - c0);  // pos = base + token
         if (p.causal && tok >= 0) rt.pos = base + tok;
-        if (s_run != st_s || b != st_b || g != st_g) {
-          ring_barrier();  // every wave is done with the previous block
-          int64_t offs[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) offs[q] = chunk_offset(p, s_run, g, kBlk * b + 32 * q, Leff);
-          st_absent = 0u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st_absent |= offs[q] < 0 ? 1u << q : 0u;
-          if constexpr (kFp8) {
-            Raw8 raw[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              raw[q] = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, offs[q], Leff - (kBlk * b + 32 * q),
-                                   p.zero_page);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) store_chunk8<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
-            __syncthreads();
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              issue_chunk16(p.k, p.v, offs[q], Leff - (kBlk * b + 32 * q), dl, s_blk + q * kSlotU4,
-                            s_blk + q * kSlotU4 + kChunkU4);
-            wait_vmcnt<0>();
-            ring_barrier();
-          }
-          st_s = s_run;
-          st_b = b;
-          st_g = g;
-        }
-        const int pmin = p.causal ? base + s_tok[a0] : INT_MAX;
-        const int pmax = p.causal ? base + s_tok[a1 - 1] : INT_MAX;
+        const int pmin = p.causal ? base + s_tok[bf][a0] : INT_MAX;
+        const int pmax = p.causal ? base + s_tok[bf][a1 - 1] : INT_MAX;
         if (32 * wave < rows) {
           // the block's chunks that some row of the piece sees: a prefix
           // (keys below the used length and at or before the last row's
@@ -910,32 +1049,92 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
           }
         }
       }
-      // partial result of the piece's rows: normalised O and log2 LSE. Every
-      // lane stores (rows outside the piece into a scratch row), so that no
-      // branch separates these stores from the next piece's use of its Q and
-      // the compiler's wait for that Q need not include them.
+      // the next window's tokens, once its descriptor has landed
+      if (!tokens_issued) {
+        load_tokens(wdn, tkn);
+        tokens_issued = true;
+      }
+      // the block of the piece after this one
+      int nseq, nb = b, ng = g;
+      if (!last) {
+        nseq = s_seq[bf][a1];
+      } else {
+        // end of the window: the next window's token list into the other
+        // buffer (its last readers finished before this window began) and
+        // the item of the window after it
+        if (un >= 0) prepare(bf ^ 1, wdn, tkn);
+        if (tid == 0) {
+          wait_vmcnt<0>();  // the queue slot taken at the window's start
+          const int v = settle(nn);
+          s_item[bf] = un >= 0 && wq.lo + wq.nwg + v < wq.hi ? wq.lo + wq.nwg + v : -1;
+        }
+        __syncthreads();  // the token list and the item are visible; every wave is done with s_blk
+        nseq = un >= 0 ? s_seq[bf ^ 1][0] : -1;
+        nb = wdn.x / Hkv;
+        ng = wdn.x - nb * Hkv;
+      }
+      // partial result of the piece's rows: normalised O, packed to 16 bits
+      // here (the accumulators are free before the block is staged), and
+      // log2 LSE
       const float l_row = rows_total(rt);
+      u32x4 pk[8];
+      float lse_row;
+      {
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) pk[2 * t + u] = paired16<CT>(rt, t, u, inv);
+        const float mu = rt.m == -INFINITY ? 0.f : rt.m;
+        lse_row = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
+      }
+      const int nseq_u = __builtin_amdgcn_readfirstlane(nseq);
+      const bool restage = nseq_u >= 0 && (nseq_u != st_s || nb != st_b || ng != st_g);
+      if (restage) {
+        if (!last) ring_barrier();  // every wave is done with the staged block
+        stage(nseq_u, nb, ng);
+      }
+      if (last && un >= 0) {
+        // the next window's first piece's Q, ahead of the stores below
+        const int na1 = piece_end(bf ^ 1, min(wdn.w, p.Tu), 0);
+        load_q8_rows(qn, p, row_token(bf ^ 1, 0, na1), ng * G + hr, h);
+      }
+      // Every lane stores (rows outside the piece into a scratch row), so that
+      // the stores are the same kUnitStoreOps instructions in every wave.
       {
         const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
-        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
         char* pbase = (valid ? (char*)p.opart + part_offset(pidx) : (char*)p.scratch_row + 16 * c) + 512 * h;
         float* lrow = (valid && h == 0) ? p.lpart + pidx : (float*)p.scratch_row + 64 + lane;
-        store_part<CT>(pbase, rt, inv);
-        const float mu = rt.m == -INFINITY ? 0.f : rt.m;
-        *lrow = l_row > 0.f ? mu + log2f(l_row) : -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) *(u32x4*)(pbase + (4 * t + 2 * u) * 512) = pk[2 * t + u];
+        *lrow = lse_row;
       }
-      if (a1 >= n) break;
+      if (restage) {
+        // the block's loads were issued before the stores: wait for them but
+        // not for the stores
+        if constexpr (!kFp8) wait_vmcnt<kUnitStoreOps>();
+        ring_barrier();
+      }
+      if (last) break;
       a0 = a1;
       a1 = a2;
 #pragma unroll
       for (int s = 0; s < 8; ++s) rt.qb[s] = qn[s];
     }
-    __syncthreads();  // the window's readers of s_tok / s_seq / s_item are done
+    if (un < 0) break;
     u = un;
     wd = wdn;
-    tk[0] = tkn[0];
-    tk[1] = tkn[1];
+    un = __builtin_amdgcn_readfirstlane(s_item[bf]);
+    bf ^= 1;
+    n = min(wd.w, p.Tu);
+    a0 = 0;
+    a1 = piece_end(bf, n, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) rt.qb[s] = qn[s];
   }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -967,18 +1166,6 @@ constexpr int kTokMax = 256;        // tokens of one tile
 __device__ __forceinline__ void dma4(i32x4v rsrc, uint32_t lds, int voff) {
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
-}
-
-// Returning atomic add whose result is waited for explicitly (wait_vmcnt,
-// then settle()): the compiler does not see it as a load in flight.
-__device__ __forceinline__ int atomic_add_nowait(int32_t* ptr, int val) {
-  int r;
-  asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(r) : "v"(ptr), "v"(val) : "memory");
-  return r;
-}
-__device__ __forceinline__ int settle(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
 }
 
 template <typename CT, typename KVT>
