@@ -145,6 +145,27 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return x;
 }
 
+// Scalar loads of read-only data at a wave-uniform address (taken from the
+// first lane), waited for in the same statement. They are counted by
+// lgkmcnt, so waiting for them never waits for the vector memory operations
+// in flight.
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t a = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int64_t sload64(const int64_t* ptr) {
+  int64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(ptr)) : "memory");
+  return v;
+}
+__device__ __forceinline__ int sload32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(ptr)) : "memory");
+  return v;
+}
+
 // Owner sequence of token t: the largest s with cu[s] <= t, provided
 // t < cu[s+1]; -1 when t lies in no sequence. Stays inside cu[0..B].
 __device__ __forceinline__ int seq_of(const int64_t* __restrict__ cu, int B, int64_t t) {

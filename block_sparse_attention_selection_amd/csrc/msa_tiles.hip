@@ -770,20 +770,6 @@ __device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok
   for (int s = 0; s < 8; ++s) qb[s] = *(const u32x4*)(base + 16 * s);
 }
 
-// Scalar (uniform-address) loads of read-only data, waited for in the same
-// statement. They are counted by lgkmcnt, so waiting for them never waits
-// for the vector memory operations in flight.
-__device__ __forceinline__ int64_t sload64(const int64_t* ptr) {
-  int64_t v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
-}
-__device__ __forceinline__ int sload32(const int32_t* ptr) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
-}
-
 // The unit kernel's Q rows: every lane loads a row, those without a token
 // token 0's (their results go to the scratch row), so that each call is the
 // same eight loads in every wave and no register is cleared while a load into
