@@ -39,6 +39,7 @@ constexpr int kResidualMark = 1 << 30;
 // query rows of one tile the front kernel streams when every tile is one
 // token (4 row sets of 16; a token with Hq/Hkv <= 64)
 constexpr int kStreamRowsMax = 64;
+constexpr int kFrontBitWords = 2048;  // block masks of a classification-only workgroup (8 KB)
 
 // element offset of k-step s (0..3, 32 dims each) for lane group q: pairs of
 // k-steps share one 64-dim slab, so an fp8 lane reads 16 contiguous bytes
@@ -476,12 +477,28 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
   const int Tq_s = (int)(qe - q0);
   const int nblk = L > 0 ? min((L + kBlk - 1) / kBlk, p.nb_max) : 0;
 
+  // Classification-only launches test set membership through bit masks of
+  // the blocks when they fit (one bit test instead of a scan of the top-k):
+  // token tau's picks at bits[tau * wb], the chain's at bits[nt * wb]
+  uint32_t* bits = nullptr;
+  const int wb = (nblk + 31) >> 5;
+  bool use_bits = false;
+  if constexpr (!ATTN) {
+    __shared__ uint32_t s_fbits[kFrontBitWords];
+    bits = s_fbits;
+    use_bits = p.T > 0 && (nt + 1) * wb <= kFrontBitWords;
+    if (use_bits) {
+      for (int i = tid; i < (nt + 1) * wb; i += 256) bits[i] = 0u;
+      __syncthreads();
+    }
+  }
   for (int idx = tid; idx < nt * K; idx += 256) {
     const int tau = idx / K, k = idx - tau * K;
     const int b = (idx < K) ? b_raw : p.selected[((size_t)(t + tau) * Hkv + g) * K + k];
     const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
     const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
     s_sel[idx] = valid ? b : -1;
+    if (use_bits && valid) atomicOr(&bits[tau * wb + (b >> 5)], 1u << (b & 31));
   }
   for (int tau = tid; tau < nt; tau += 256) s_nres[tau] = 0;
   if (tid < 64) s_miss[tid] = 0;
@@ -497,7 +514,11 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
       const int bl = s_sel[k];
       if (bl < 0) continue;
       bool found = false;
-      for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
+      if (use_bits) {
+        found = (bits[tau * wb + (bl >> 5)] >> (bl & 31)) & 1u;
+      } else {
+        for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
+      }
       if (!found) s_miss[k] = 1;
     }
   }
@@ -516,6 +537,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
       s_chain[rank] = bl;
       s_chain_k[rank] = lane;
       p.chain_blk[tg * K + rank] = bl;
+      if (use_bits) atomicOr(&bits[nt * wb + (bl >> 5)], 1u << (bl & 31));
     }
     if (lane == 0) s_nch = __popcll(mask);
   }
@@ -529,7 +551,11 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
     uint8_t flag = 0;
     if (b >= 0) {
       bool cov = false;
-      for (int c = 0; c < n_ch; ++c) cov |= (s_chain[c] == b);
+      if (use_bits) {
+        cov = (bits[nt * wb + (b >> 5)] >> (b & 31)) & 1u;
+      } else {
+        for (int c = 0; c < n_ch; ++c) cov |= (s_chain[c] == b);
+      }
       flag = cov ? 1 : 2;
       if (!cov) {
         const int tt = t + tau;
@@ -592,6 +618,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
 // outside decode mode, where the front kernel only classifies.
 // ---------------------------------------------------------------------------
 constexpr int kWaveSlots = 512;  // tile tokens x topk handled by one wave
+constexpr int kWaveBitWords = 1024;  // per wave: the tokens' block sets and the chain's, as bit masks
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -601,6 +628,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   __shared__ int s_sel[4][kWaveSlots];  // valid picks, -1 where the slot is invalid
+  __shared__ uint32_t s_bits[4][kWaveBitWords];  // token tau's picks at [tau * wb], the chain's at [nt * wb]
   __shared__ int s_chain[4][64];
   __shared__ int s_nres[4][128];
   __shared__ unsigned long long s_miss[4];
@@ -626,12 +654,23 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   const int i0 = (int)(t - q0);
   const int nblk = L > 0 ? min((L + kBlk - 1) / kBlk, p.nb_max) : 0;
   int* sel = s_sel[wave];
+  // Set membership (is a leader pick among a token's picks, is a pick in the
+  // chain) through bit masks of the blocks when they fit, one bit test each,
+  // instead of scans over the top-k
+  const int wb = (nblk + 31) >> 5;  // words per block mask
+  const bool use_bits = p.T > 0 && (nt + 1) * wb <= kWaveBitWords;
+  uint32_t* bits = s_bits[wave];
+  if (use_bits) {
+    for (int i = lane; i < (nt + 1) * wb; i += 64) bits[i] = 0u;
+    wave_lds_sync();
+  }
   for (int idx = lane; idx < nt * K; idx += 64) {
     const int tau = idx / K;
     const int b = p.selected[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)];
     const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
     const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
     sel[idx] = valid ? b : -1;
+    if (use_bits && valid) atomicOr(&bits[tau * wb + (b >> 5)], 1u << (b & 31));
   }
   for (int tau = lane; tau < nt; tau += 64) s_nres[wave][tau] = 0;
   if (lane == 0) s_miss[wave] = 0ull;
@@ -644,7 +683,11 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
       const int bl = sel[k];
       if (bl < 0) continue;
       bool found = false;
-      for (int k2 = 0; k2 < K; ++k2) found |= (sel[tau * K + k2] == bl);
+      if (use_bits) {
+        found = (bits[tau * wb + (bl >> 5)] >> (bl & 31)) & 1u;
+      } else {
+        for (int k2 = 0; k2 < K; ++k2) found |= (sel[tau * K + k2] == bl);
+      }
       if (!found) miss |= 1ull << k;
     }
     if (miss) atomicOr(&s_miss[wave], miss);
@@ -663,6 +706,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     const int rank = __popcll(mask & ((1ull << lane) - 1ull));
     s_chain[wave][rank] = bl;
     p.chain_blk[tg * K + rank] = bl;
+    if (use_bits) atomicOr(&bits[nt * wb + (bl >> 5)], 1u << (bl & 31));
   }
   wave_lds_sync();
   if (p.tdesc) write_tile_desc(p, item, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain[wave], lane);
@@ -674,7 +718,11 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     uint8_t flag = 0;
     if (b >= 0) {
       bool cov = false;
-      for (int c = 0; c < n_ch; ++c) cov |= (s_chain[wave][c] == b);
+      if (use_bits) {
+        cov = (bits[nt * wb + (b >> 5)] >> (b & 31)) & 1u;
+      } else {
+        for (int c = 0; c < n_ch; ++c) cov |= (s_chain[wave][c] == b);
+      }
       flag = cov ? 1 : 2;
       if (!cov) {
         const int tt = t + tau;
