@@ -40,8 +40,9 @@ hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t st) {
   return hipGetLastError();
 }
 
-// rows: each workgroup counts a group of rows (copying and clearing their
-// bitmap words) and publishes the row counts with atomic stores; the last
+// rows: each workgroup counts a group of rows (its four waves one row each at
+// a time, copying and clearing the rows' bitmap words) and publishes the row
+// counts with atomic stores; the last
 // workgroup to finish, found with an atomic counter, scans them. Only
 // atomics carry data between workgroups of this kernel.
 __global__ __launch_bounds__(256) void k_index(Params p, int rows_per_task, int ntasks) {
@@ -49,9 +50,10 @@ __global__ __launch_bounds__(256) void k_index(Params p, int rows_per_task, int 
   __shared__ int s_last;
   if (p.counters[kCntResidual] == 0) return;  // nothing to place (every decode batch)
   const int r0 = blockIdx.x * rows_per_task, r1 = min(r0 + rows_per_task, p.NR);
-  for (int r = r0; r < r1; ++r) {
-    const int total = rowcount_row<256>(p, r, smem);
-    if (threadIdx.x == 0) __hip_atomic_store(&p.row_cnt[r], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // one row per wave at a time
+  for (int r = r0 + (int)(threadIdx.x >> 6); r < r1; r += 4) {
+    const int total = rowcount_row_wave(p, r);
+    if ((threadIdx.x & 63) == 0) __hip_atomic_store(&p.row_cnt[r], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (threadIdx.x == 0) {

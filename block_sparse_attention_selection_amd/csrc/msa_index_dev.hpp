@@ -41,21 +41,29 @@ __device__ __forceinline__ int block_excl_scan(int x, int* total, int* smem) {
   return res;
 }
 
-// Row r (block b, KV head g): popcount prefix of its token bitmap; the words
-// are copied to wordbits and cleared. Returns the row's count to every
-// thread. smem: NT/64 + 1 ints.
-template <int NT>
-__device__ __forceinline__ int rowcount_row(const Params& p, int r, int* smem) {
+// Row r (block b, KV head g): popcount prefix of its token bitmap, by one
+// wave (the words are split over the 64 lanes and scanned with cross-lane
+// shuffles, so a workgroup's rows are processed side by side, one per wave);
+// the words are copied to wordbits and cleared. Returns the row's count to
+// every lane.
+__device__ __forceinline__ int rowcount_row_wave(const Params& p, int r) {
+  const int lane = threadIdx.x & 63;
   uint32_t* bm = p.bitmap + (size_t)r * p.W;
   uint32_t* pre = p.wordpre + (size_t)r * p.W;
   uint32_t* bits = p.wordbits + (size_t)r * p.W;
-  const int per = (p.W + NT - 1) / NT;
-  const int w0 = min((int)threadIdx.x * per, p.W);
+  const int per = (p.W + 63) / 64;
+  const int w0 = min(lane * per, p.W);
   const int w1 = min(w0 + per, p.W);
   int sum = 0;
   for (int w = w0; w < w1; ++w) sum += __popc(bm[w]);
-  int total;
-  int run = block_excl_scan<NT>(sum, &total, smem);
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  int run = incl - sum;
+  const int total = __shfl(incl, 63, 64);
   for (int w = w0; w < w1; ++w) {
     const uint32_t x = bm[w];
     pre[w] = (uint32_t)run;
