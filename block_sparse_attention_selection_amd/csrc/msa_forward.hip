@@ -196,7 +196,14 @@ struct KvElem<fp8_e4m3_t> {
 // register fragments of one 32-key chunk, loaded straight from HBM. The loads
 // are unconditional (absent chunks read the zero page), so the compiler can
 // keep the next chunk's loads in flight while the current one is multiplied.
+// They carry the non-temporal hint: each chunk is read once per call here,
+// and on the MI355X streaming reads with the hint reach ~6.7 TB/s against
+// ~6.1 TB/s without it (microbenchmark, 4 GB read with 16-byte loads).
 // ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T ld_stream(const void* ptr) {
+  return __builtin_nontemporal_load((const T*)ptr);
+}
 template <typename CT, typename KVT>
 struct Frag;
 
@@ -208,9 +215,9 @@ struct Frag<CT, CT> {  // 16-bit cache: fragments are used as loaded
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ka[j][s] = *(const u32x4*)(kb + (16 * j + c) * kD + kmap(s, q));
+      for (int s = 0; s < 4; ++s) ka[j][s] = ld_stream<u32x4>(kb + (16 * j + c) * kD + kmap(s, q));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) va[e] = *(const u32x4*)(vb + key_of(q, e) * kD + 8 * c);
+    for (int e = 0; e < 8; ++e) va[e] = ld_stream<u32x4>(vb + key_of(q, e) * kD + 8 * c);
   }
   template <int RS>
   __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
@@ -227,9 +234,9 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) kr[j][pp] = *(const u32x4*)(kb + (16 * j + c) * kD + 64 * pp + 16 * q);
+      for (int pp = 0; pp < 2; ++pp) kr[j][pp] = ld_stream<u32x4>(kb + (16 * j + c) * kD + 64 * pp + 16 * q);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vr[e] = *(const u32x2*)(vb + key_of(q, e) * kD + 8 * c);
+    for (int e = 0; e < 8; ++e) vr[e] = ld_stream<u32x2>(vb + key_of(q, e) * kD + 8 * c);
   }
   template <int RS>
   __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
