@@ -1086,7 +1086,11 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
         load_q8_rows(qn, p, row_token(bf ^ 1, 0, na1), ng * G + hr, h);
       }
       // Every lane stores (rows outside the piece into a scratch row), so that
-      // the stores are the same kUnitStoreOps instructions in every wave.
+      // the stores are the same kUnitStoreOps instructions in every wave. The
+      // partials are read once, by the tile kernel, long after they leave
+      // L2: they are written and read with the non-temporal hint (same-box
+      // A/B: tile kernel 430 -> 357 us on the MQA batch, 950 -> 926 us on the
+      // shared-selection prefill).
       {
         const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
         char* pbase = (valid ? (char*)p.opart + part_offset(pidx) : (char*)p.scratch_row + 16 * c) + 512 * h;
@@ -1094,8 +1098,8 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) *(u32x4*)(pbase + (4 * t + 2 * u) * 512) = pk[2 * t + u];
-        *lrow = lse_row;
+          for (int u = 0; u < 2; ++u) __builtin_nontemporal_store(pk[2 * t + u], (u32x4*)(pbase + (4 * t + 2 * u) * 512));
+        __builtin_nontemporal_store(lse_row, lrow);
       }
       if (restage) {
         // the block's loads were issued before the stores: wait for them but
@@ -1432,13 +1436,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
       auto fetch = [&](int pos, Part& pt) {
         const bool ok = pos >= 0 && pos < ntot;
         const size_t pidx = ok ? (size_t)pos * G + hr : 0;
-        const float lv = p.lpart[pidx];
+        const float lv = __builtin_nontemporal_load(p.lpart + pidx);
         pt.l = ok ? lv : -INFINITY;
         const char* src = obase + part_offset(pidx);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) pt.d[2 * t + u] = *(const u32x4*)(src + (4 * t + 2 * u) * 512);
+          for (int u = 0; u < 2; ++u) pt.d[2 * t + u] = __builtin_nontemporal_load((const u32x4*)(src + (4 * t + 2 * u) * 512));
       };
       auto merge = [&](const Part& pt) {
         const float lc = pt.l;
