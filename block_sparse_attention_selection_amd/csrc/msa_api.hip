@@ -879,26 +879,23 @@ int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache
   p.topk = topk;
   p.causal = causal;
   p.force_local = force_local;
-  // Prefill-shaped batches: 64-token tiles share each key row among four
-  // 16-token row blocks and keep their scores in LDS (64 * nb_cap floats, so
-  // page tables of at most 256 blocks). Decode-shaped batches (a few queries
-  // per long sequence) and longer tables: the split path, whose score table
-  // is the caller's `scores` or the library workspace.
-  const bool fused = Tq > 4 * B && nb_cap <= 256;
+  // Prefill-shaped batches: 256-token tiles share each block's keys through
+  // LDS. Decode-shaped batches (a few queries per long sequence): 16-token
+  // tiles whose blocks are split over slices. Both write the score table --
+  // the caller's `scores` or the library workspace -- and list it.
+  const bool tiled = Tq > 4 * B;
   float* table = nullptr;
   std::unique_lock<std::mutex> lk(g_ws_mutex, std::defer_lock);
-  if (!fused) {
-    if (scores) {
-      table = (float*)scores->data;
-    } else {
-      lk.lock();  // held through the launches that use the library's workspace
-      DeviceState* w = nullptr;
-      if ((rc = device_state(&w))) return rc;
-      if ((rc = grow_workspace(*w, (size_t)Tq * Hkv * nb_cap * sizeof(float), 0))) return rc;
-      table = (float*)w->ptr;
-    }
+  if (scores) {
+    table = (float*)scores->data;
+  } else {
+    lk.lock();  // held through the launches that use the library's workspace
+    DeviceState* w = nullptr;
+    if ((rc = device_state(&w))) return rc;
+    if ((rc = grow_workspace(*w, (size_t)Tq * Hkv * nb_cap * sizeof(float), 0))) return rc;
+    table = (float*)w->ptr;
   }
-  hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, table,
+  hipError_t e = msa::launch_select(p, elem_of(q_idx->dtype), k_idx_cache->dtype == MSA_FP8_E4M3FN, table, tiled,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(MSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

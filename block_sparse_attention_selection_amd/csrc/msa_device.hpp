@@ -268,4 +268,43 @@ __device__ __forceinline__ int wave_tile_of(const int64_t* __restrict__ cu, int 
   return s_out;
 }
 
+// ---------------------------------------------------------------------------
+// direct-to-LDS buffer loads (shared by the tile, unit and selection kernels)
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte direct-to-LDS buffer load per lane: lane i's bytes land at LDS
+// byte address lds + 16 i. Issued from inline assembly so that the compiler
+// does not treat every later LDS read as a possible reader of the load (it
+// would wait for all loads in flight before the first one): the ring's
+// protocol orders these loads with wait_vmcnt and barriers instead.
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t lds, int voff) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// raw buffer descriptor of nrec bytes at base (stride 0)
+__device__ __forceinline__ i32x4v make_rsrc(const void* base, int nrec) {
+  const uint64_t b = (uint64_t)base;
+  i32x4v r;
+  r.x = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
+  r.z = (int)__builtin_amdgcn_readfirstlane((uint32_t)nrec);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
 }  // namespace msa

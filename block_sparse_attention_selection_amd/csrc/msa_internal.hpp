@@ -143,8 +143,9 @@ struct SelectParams {
 };
 constexpr int kSelSplitBlocks = 16;  // blocks per workgroup of the split (decode-shaped) path
 constexpr int kSelSplitWaves = 4;
-// table == null: the fused path (64-token tiles, scores in LDS, nb_cap <= 256);
-// else the split path, whose score table [Tq, Hkv, nb_cap] fp32 is `table`
-hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, hipStream_t st);
+// scores into the table [Tq, Hkv, nb_cap] fp32 (`table`), by 256-token tiles
+// (tiled: prefill-shaped batches) or by 16-token tiles split over block
+// slices (decode-shaped batches), then the lists from the table
+hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, bool tiled, hipStream_t st);
 
 }  // namespace msa

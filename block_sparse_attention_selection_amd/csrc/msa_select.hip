@@ -15,15 +15,16 @@
 // scores by ascending block id, padded with -1. Blocks without a visible
 // token, and NaN scores, are never selected.
 //
-// Work, prefill-shaped batches: one workgroup of 4 waves per (64-token tile
-// of one sequence, KV head). The waves split the tile's blocks; each computes
-// S^T = K . Q^T with 16x16x32 MFMA for 16 keys at a time, K read from the
-// paged cache straight into operand registers (a lane reads 32 contiguous
-// dims of one key row), and max-pools it into a [tokens][blocks] fp32 table
-// in LDS. Then each wave takes rows of the table and lists their top-k.
-// Decode-shaped batches (a few tokens per long sequence) split each
-// sequence's blocks over several workgroups that write a global score table,
-// and a second launch lists every row from it.
+// Work: S^T = K . Q^T with 16x16x32 MFMA for 16 keys at a time, max-pooled
+// per (query row, block) into an fp32 score table [Tq, Hkv, nb]; a second
+// launch lists every row from the table (one wave per row).
+// Prefill-shaped batches: one workgroup of 4 waves per (256-token tile of
+// one sequence, KV head, slice of 8 blocks); each block's keys are brought
+// into LDS once and shared by the four waves (64 query rows each).
+// Decode-shaped batches (a few tokens per long sequence): 16-token tiles,
+// each sequence's blocks split over several workgroups whose waves read the
+// keys straight from the paged cache into operand registers (a lane reads 32
+// contiguous dims of one key row).
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -46,6 +47,11 @@ struct KeyRow<QT, QT> {  // 16-bit keys: 64 bytes
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = u32x4{0u, 0u, 0u, 0u};
   }
+  // from a block staged in LDS (row r's 16-byte piece c at r * 16 + (c ^ sw))
+  __device__ __forceinline__ void load_lds(const u32x4* blk, int row, int sw, int h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = blk[row * 16 + ((4 * h + i) ^ sw)];
+  }
   __device__ __forceinline__ u32x4 frag(int st) const { return w[st]; }
 };
 
@@ -58,6 +64,11 @@ struct KeyRow<QT, fp8_e4m3_t> {  // e4m3fn keys: 32 bytes, widened exactly when 
     w[1] = p[1];
   }
   __device__ __forceinline__ void zero() { w[0] = w[1] = u32x4{0u, 0u, 0u, 0u}; }
+  // from a block staged in LDS (row r's 16-byte piece c at r * 8 + (c ^ sw))
+  __device__ __forceinline__ void load_lds(const u32x4* blk, int row, int sw, int h) {
+    w[0] = blk[row * 8 + ((2 * h) ^ sw)];
+    w[1] = blk[row * 8 + ((2 * h + 1) ^ sw)];
+  }
   __device__ __forceinline__ u32x4 frag(int st) const {
     const u32x4 x = w[st >> 1];
     return (st & 1) ? widen8<QT>(u32x2{x[2], x[3]}) : widen8<QT>(u32x2{x[0], x[1]});
@@ -318,26 +329,140 @@ __device__ __forceinline__ void topk_row(const SelectParams& p, int64_t t, int g
   for (int i = k + lane; i < p.topk; i += 64) out[i] = -1;
 }
 
-// Fused path (prefill-shaped batches): one workgroup of NW waves per (64-token
-// tile, KV head) scores every block into LDS, then lists each row. Workgroup
-// i runs on XCD i % 8: KV head i % Hkv keeps each head's keys in the L2 of
-// the same XCDs; tiles go last to first, so the tiles that see the most blocks
-// (late in a causal sequence) start first.
-template <typename QT, typename KT, int NRB, int NW, int NPL>
-__global__ __launch_bounds__(64 * NW) void k_select(SelectParams p) {
-  constexpr int T = 16 * NRB;
-  extern __shared__ float s_sc[];  // [T][nb_cap]
-  const int wave = threadIdx.x >> 6;
+// Tiled path (prefill-shaped batches), first pass: one workgroup of 4 waves
+// per (256-token tile of one sequence, KV head, slice of kSelTileBlocks
+// blocks). The slice's blocks pass through two LDS slots by direct-to-LDS
+// loads (the next block lands while the current one is multiplied), and each
+// wave multiplies every block against its own 64 query rows (four 16-row
+// blocks, S^T = K Q^T with 16x16x32 MFMA as in score_blocks), so a key row
+// is read from L2 once per 256 queries. A row's block scores stay in
+// registers until the slice is done and then go to the table sc [Tq, Hkv,
+// nb_cap]; k_select_lists lists the rows.
+constexpr int kSelTileTokens = 256;
+constexpr int kSelTileBlocks = 8;
+
+template <typename QT, typename KT>
+__global__ __launch_bounds__(256, 2) void k_select_tiles(SelectParams p, float* sc, int nsplit) {
+  constexpr int kPc = KeyBytes<KT>::kRow / 16;  // 16-byte pieces per key row: 16 (16-bit) or 8 (e4m3fn)
+  constexpr int kBlkU4 = 128 * kPc;             // pieces per block
+  __shared__ u32x4 s_key[2][kBlkU4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 4, col = lane & 15;
   const int g = (int)(blockIdx.x % (unsigned)p.Hkv);
-  const int tile = (int)(gridDim.x / (unsigned)p.Hkv) - 1 - (int)(blockIdx.x / (unsigned)p.Hkv);
+  const int rest = (int)(blockIdx.x / (unsigned)p.Hkv);
+  const int split = rest % nsplit;
+  const int tile = (int)(gridDim.x / (unsigned)(p.Hkv * nsplit)) - 1 - rest / nsplit;
   SelTile x;
-  if (!sel_tile(p, tile, g, T, &x)) return;
-  if (x.nscan > 0) score_blocks<QT, KT, NRB, NW>(p, x, 0, x.nscan, s_sc, p.nb_cap);
-  __syncthreads();
-  for (int r = wave; r < x.ntok; r += NW) {
-    const int64_t pos = x.pos(r);
-    const int nr = (x.L <= 0 || pos < 0) ? 0 : (int)min((int64_t)x.nb, pos / 128 + 1);
-    topk_row<NPL>(p, x.t0 + r, g, pos, nr, s_sc + r * p.nb_cap, false);
+  if (!sel_tile(p, tile, g, kSelTileTokens, &x)) return;
+  const int b0 = split * kSelTileBlocks;
+  const int nb = min(kSelTileBlocks, x.nscan - b0);  // blocks of this slice
+  if (nb <= 0) return;
+  const int L = x.L;
+  // the wave's query rows 64 wave + 16 rb + col as MFMA B operands (dims
+  // 32 h + 8 st + [0, 8)), and their positions
+  u32x4 qf[4][4];
+  int posr[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int r = 64 * wave + 16 * rb + col;
+    if (r < x.ntok) {
+      const u32x4* q = (const u32x4*)((const uint16_t*)p.q + ((x.t0 + r) * p.Hkv + g) * (int64_t)kD + 32 * h);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) qf[rb][st] = q[st];
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) qf[rb][st] = u32x4{0u, 0u, 0u, 0u};
+    }
+    posr[rb] = (int)max(x.pos(r), (int64_t)-1);
+  }
+  const int pos_lo = (int)max(x.pos(64 * wave), (int64_t)-1);  // the wave's first row sees the fewest keys
+  const int32_t* bt = p.bt + (int64_t)x.s * p.MP;
+  // Block b into slot sl. LDS piece i of the slot holds key row i / kPc, its
+  // 16-byte piece (i % kPc) ^ swz(row): sixteen lanes reading one piece of
+  // sixteen consecutive rows then hit distinct banks. A half without a page
+  // (beyond L) or with a page id outside the cache reads page 0 (num_pages
+  // >= 1 here); the mask removes keys at or beyond L.
+  auto swz = [&](int row) { return kPc == 16 ? (row & 15) : ((row >> 1) & 7); };
+  auto issue_block = [&](int b, int sl) {
+    const int j0 = 128 * b;
+    int pa = j0 < L ? sload32(bt + j0 / p.P) : -1;
+    int pb = p.P == 64 ? (j0 + 64 < L ? sload32(bt + (j0 + 64) / p.P) : -1) : pa;
+    pa = (pa >= 0 && pa < p.num_pages) ? pa : 0;
+    pb = (pb >= 0 && pb < p.num_pages) ? pb : 0;
+    const int rowb = KeyBytes<KT>::kRow, nrec = p.P * rowb;  // one page of one KV head
+    const i32x4v ra = make_rsrc((const uint8_t*)p.k + ((int64_t)pa * p.Hkv + g) * p.P * rowb, nrec);
+    const i32x4v rh = make_rsrc((const uint8_t*)p.k + ((int64_t)pb * p.Hkv + g) * p.P * rowb, nrec);
+    const uint32_t base = lds_addr(s_key[sl]);
+#pragma unroll
+    for (int j = 0; j < kBlkU4 / 256; ++j) {
+      const int i = 256 * j + tid, row = i / kPc, pc = i % kPc;
+      // this load's rows (256 / kPc of them) lie in one 64-row half
+      const bool upper = p.P == 64 && j * (256 / kPc) >= 64;
+      const int rip = p.P == 64 ? (row & 63) : row;  // row within its page (j0 is a multiple of 128)
+      dma16(upper ? rh : ra, base + 4096 * j + 1024 * wave, rip * rowb + 16 * (pc ^ swz(row)));
+    }
+  };
+  float mreg[kSelTileBlocks][4];
+  issue_block(b0, 0);
+#pragma unroll
+  for (int i = 0; i < kSelTileBlocks; ++i) {
+    if (i >= nb) break;
+    const int b = b0 + i;
+    wait_vmcnt<0>();  // block b has landed (this wave's part) ...
+    __syncthreads();  // ... every wave's part; and every wave is done with block b - 1
+    if (i + 1 < nb) issue_block(b + 1, (i + 1) & 1);
+    const u32x4* blk = s_key[i & 1];
+    // a block every key of which every row of the wave sees needs no mask
+    const bool full = 128 * b + 127 < L && 128 * b + 127 <= pos_lo;
+    float m[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) m[rb] = -INFINITY;
+    KeyRow<QT, KT> kr[2];
+    kr[0].load_lds(blk, col, swz(col), h);
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      if (kg + 1 < 8) {
+        const int rn = 16 * (kg + 1) + col;
+        kr[(kg + 1) & 1].load_lds(blk, rn, swz(rn), h);
+      }
+      f32x4 acc[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[rb] = Mma<QT>::run(kr[kg & 1].frag(st), qf[rb][st], acc[rb]);
+      const int jbase = 128 * b + 16 * kg + 4 * h;  // keys of this lane's accumulator rows
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        float v;
+        if (full) {
+          v = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3]));
+        } else {
+          v = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = jbase + e;
+            v = fmaxf(v, (j < L && j <= posr[rb]) ? acc[rb][e] : -INFINITY);
+          }
+        }
+        m[rb] = fmaxf(m[rb], v);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) mreg[i][rb] = max_over_groups(m[rb]);
+  }
+  // the slice's scores of the wave's rows (lanes of group 0 hold them)
+  if (h == 0) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 64 * wave + 16 * rb + col;
+      if (r >= x.ntok) continue;
+      float* dst = sc + ((x.t0 + r) * p.Hkv + g) * (int64_t)p.nb_cap + b0;
+#pragma unroll
+      for (int i = 0; i < kSelTileBlocks; ++i)
+        if (i < nb) dst[i] = mreg[i][rb];
+    }
   }
 }
 
@@ -380,15 +505,6 @@ __global__ __launch_bounds__(256) void k_select_lists(SelectParams p, const floa
   topk_row<NPL>(p, t, g, pos, nr, sc + rid * p.nb_cap, sc == p.scores);
 }
 
-template <typename QT, typename KT, int NRB, int NW>
-static hipError_t launch_fused_npl(const ProfSpan& sp, const SelectParams& p, dim3 grid, size_t lds,
-                                   hipStream_t st) {
-  const dim3 block(64 * NW);
-  if (p.nb_cap <= 64) return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 1>, grid, block, lds, st, p);
-  if (p.nb_cap <= 128) return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 2>, grid, block, lds, st, p);
-  return launch_k(sp, true, true, k_select<QT, KT, NRB, NW, 4>, grid, block, lds, st, p);
-}
-
 static hipError_t launch_lists(const ProfSpan& sp, const SelectParams& p, const float* sc, hipStream_t st) {
   const dim3 grid((unsigned)(((int64_t)p.Tq * p.Hkv + 3) / 4)), block(256);
   if (p.nb_cap <= 64) return launch_k(sp, false, true, k_select_lists<1>, grid, block, 0, st, p, sc);
@@ -400,12 +516,16 @@ static hipError_t launch_lists(const ProfSpan& sp, const SelectParams& p, const 
 }
 
 template <typename QT, typename KT>
-static hipError_t launch_select_t(const ProfSpan& sp, const SelectParams& p, float* table, hipStream_t st) {
-  if (!table) {
-    // fused: 64-token tiles of 4 waves, every score in LDS (nb_cap <= 256)
-    const int64_t tiles = ((int64_t)p.Tq + 63) / 64 + p.B;  // each sequence adds at most one partial tile
-    const size_t lds = (size_t)64 * p.nb_cap * sizeof(float);
-    return launch_fused_npl<QT, KT, 4, 4>(sp, p, dim3((unsigned)(tiles * p.Hkv)), lds, st);
+static hipError_t launch_select_t(const ProfSpan& sp, const SelectParams& p, float* table, bool tiled,
+                                  hipStream_t st) {
+  if (tiled) {
+    // 256-token tiles sharing each block through LDS, then the lists
+    const int64_t tiles = ((int64_t)p.Tq + kSelTileTokens - 1) / kSelTileTokens + p.B;
+    const int nsplit = (p.nb_cap + kSelTileBlocks - 1) / kSelTileBlocks;
+    hipError_t e = launch_k(sp, true, false, k_select_tiles<QT, KT>, dim3((unsigned)(tiles * p.Hkv * nsplit)),
+                            dim3(256), 0, st, p, table, nsplit);
+    if (e == hipSuccess) e = launch_lists(sp, p, table, st);
+    return e;
   }
   const int64_t tiles = ((int64_t)p.Tq + 15) / 16 + p.B;
   const int nsplit = (p.nb_cap + kSelSplitBlocks - 1) / kSelSplitBlocks;
@@ -415,14 +535,16 @@ static hipError_t launch_select_t(const ProfSpan& sp, const SelectParams& p, flo
   return e;
 }
 
-hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, hipStream_t st) {
+hipError_t launch_select(const SelectParams& p, int q_elem, bool fp8_keys, float* table, bool tiled, hipStream_t st) {
   if (p.Tq == 0 || p.Hkv == 0) return hipSuccess;
   const ProfSpan sp = profile_begin(kKSelect);
   hipError_t e;
   if (q_elem == kElemBF16)
-    e = fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(sp, p, table, st) : launch_select_t<bf16_t, bf16_t>(sp, p, table, st);
+    e = fp8_keys ? launch_select_t<bf16_t, fp8_e4m3_t>(sp, p, table, tiled, st)
+                 : launch_select_t<bf16_t, bf16_t>(sp, p, table, tiled, st);
   else
-    e = fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(sp, p, table, st) : launch_select_t<f16_t, f16_t>(sp, p, table, st);
+    e = fp8_keys ? launch_select_t<f16_t, fp8_e4m3_t>(sp, p, table, tiled, st)
+                 : launch_select_t<f16_t, f16_t>(sp, p, table, tiled, st);
   profile_end(sp, e == hipSuccess);
   return e;
 }

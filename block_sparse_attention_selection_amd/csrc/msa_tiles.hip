@@ -49,7 +49,6 @@ namespace msa {
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // c + a.lo * b.lo + a.hi * b.hi for two packed 16-bit values of T, in fp32
 // (v_dot2_f32_bf16 / v_dot2_f32_f16). With b = (w, 0) or (0, w) it scales one
@@ -98,13 +97,6 @@ constexpr int kRing = 4;            // ring slots (bf16/fp16 caches)
 constexpr int kUnitWindow = kUnitWindowTokens;
 constexpr float kRescale32 = 8.0f;  // lazy rescale threshold (powers of two)
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
-// [15:14], expcnt[6:4], lgkmcnt[11:8])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Workgroup barrier that orders LDS accesses (compiler level) without the
 // vmcnt(0) a release fence would add: the ring's direct-to-LDS loads are
@@ -537,7 +529,6 @@ __device__ __forceinline__ void store_part(char* base, const Rows32& rt, float s
 // (off < 0) fall outside the descriptor's range, and out-of-range buffer
 // loads return zeros -- a masked probability is exactly zero, but 0 * NaN is
 // not.
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 struct DmaLane {
   int k0, k1, v0, v1;  // byte offsets within a chunk of the lane's two K and two V loads
@@ -571,30 +562,8 @@ struct DmaLane512 {
   }
 };
 
-// One 16-byte direct-to-LDS buffer load per lane: lane i's bytes land at LDS
-// byte address lds + 16 i. Issued from inline assembly so that the compiler
-// does not treat every later LDS read as a possible reader of the load (it
-// would wait for all loads in flight before the first one): the ring's
-// protocol orders these loads with wait_vmcnt and barriers instead.
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t lds, int voff) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
-}
 
-// raw buffer descriptor of nrec bytes at base (stride 0)
-__device__ __forceinline__ i32x4v make_rsrc(const void* base, int nrec) {
-  const uint64_t b = (uint64_t)base;
-  i32x4v r;
-  r.x = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  r.y = (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
-  r.z = (int)__builtin_amdgcn_readfirstlane((uint32_t)nrec);
-  r.w = kRsrcWord3;
-  return r;
-}
 
-// LDS byte address of a shared-memory pointer
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
 
 // chunk into the ring slot at LDS byte address slot (K tile, then V tile)
 __device__ __forceinline__ void issue_chunk16_512(const void* kb, const void* vb, int64_t off_any, int nrows_any,

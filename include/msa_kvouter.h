@@ -326,13 +326,12 @@ int32_t msa_store_kv(const msa_tensor* k_new, const msa_tensor* v_new, const msa
  *
  * Sequences may reach at most 2048 blocks (nb <= 2048, else
  * MSA_ERR_UNSUPPORTED). All buffers are caller-owned device memory; the call
- * validates descriptors on the host, enqueues one or two kernels on `stream`
- * and returns. Decode-shaped batches (Tq <= 4 * batch) and tables beyond 256
- * blocks keep an fp32 score table of Tq * Hkv * nb entries in `scores` when
- * given, else in the library's per-device workspace (shared with
- * msa_kvouter_attention: calls on different streams of one device must not
- * overlap in time). Errors as for msa_kvouter_attention; Tq == 0 enqueues
- * nothing.
+ * validates descriptors on the host, enqueues two kernels on `stream` (the
+ * scores, then the lists) and returns. The fp32 score table of Tq * Hkv * nb
+ * entries is `scores` when given, else the library's per-device workspace
+ * (shared with msa_kvouter_attention: calls on different streams of one
+ * device must not overlap in time). Errors as for msa_kvouter_attention; Tq
+ * == 0 enqueues nothing.
  */
 int32_t msa_select_blocks(const msa_tensor* q_idx, const msa_tensor* k_idx_cache,
                           const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,

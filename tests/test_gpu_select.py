@@ -119,7 +119,7 @@ def test_select_matches_oracle(case):
     _check(si, sel, sc, _oracle_scores(si), topk, True)
 
 
-@pytest.mark.parametrize("tq, lens", [([5, 90], [900, 3000]), ([2, 1], [4000, 700])])  # fused, split
+@pytest.mark.parametrize("tq, lens", [([5, 90], [900, 3000]), ([2, 1], [4000, 700])])  # tiled, split
 def test_select_without_forced_local_and_fp16(tq, lens):
     si = W.make_selection(320, tq, lens, 2, 64, 6, True, torch.float16, torch.float16)
     sel, sc = _run(si, force_local=False)
