@@ -258,36 +258,35 @@ __device__ __forceinline__ void topk_row(const SelectParams& p, int64_t t, int g
     }
   }
   if constexpr (NPL == 1) {
-    // At most 64 blocks, one per lane. The values map to order-preserving
-    // integers u; the need-th largest u (need = the free places, or fewer
-    // valid blocks) is found bit by bit with wave ballots; the blocks above
-    // it and the lowest-numbered ones equal to it are the list, and each
-    // chosen block's place is the count of chosen blocks ahead of it.
+    // At most 64 blocks, one per lane: the wave's (value, block) pairs are
+    // sorted by a bitonic network (value descending, equal values by
+    // ascending block; values map to order-preserving integers, blocks that
+    // cannot be chosen to 0, below every valid one), all on the vector ALU
+    // with cross-lane shuffles. Lane i then holds the i-th best block.
     const float x0 = v[0] == 0.f ? 0.f : v[0];  // -0 and +0 are one value
     const uint32_t bits = __float_as_uint(x0);
-    const uint32_t u = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
     const bool valid = x0 > -INFINITY;
+    uint32_t key = valid ? ((bits & 0x80000000u) ? ~bits : (bits | 0x80000000u)) : 0u;
+    int blk = lane;
     const int need = min(__popcll(__ballot(valid)), p.topk - k);
-    if (need > 0) {
-      uint32_t T = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        if (__popcll(__ballot(valid && u >= cand)) >= need) T = cand;
+#pragma unroll
+    for (int w = 2; w <= 64; w <<= 1) {
+#pragma unroll
+      for (int j = w >> 1; j > 0; j >>= 1) {
+        const uint32_t pk = (uint32_t)__shfl_xor((int)key, j, 64);
+        const int pb = __shfl_xor(blk, j, 64);
+        const bool p_better = pk > key || (pk == key && pb < blk);
+        // the lower lane of a pair keeps the better of the two where the
+        // w-run is ordered best-first, the worse one elsewhere
+        const bool keep_better = ((lane & j) == 0) == ((lane & w) == 0);
+        if (keep_better == p_better) {
+          key = pk;
+          blk = pb;
+        }
       }
-      const uint64_t gt = __ballot(valid && u > T);
-      const uint64_t eq = __ballot(valid && u == T);
-      const int take = need - __popcll(gt);
-      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes under this one
-      const bool chosen = ((gt >> lane) & 1ull) || (((eq >> lane) & 1ull) && __popcll(eq & below) < take);
-      int place = 0;
-      for (uint64_t m = __ballot(chosen); m; m &= m - 1) {
-        const int o = __ffsll((unsigned long long)m) - 1;
-        const uint32_t uo = (uint32_t)__builtin_amdgcn_readlane((int)u, o);
-        place += (uo > u || (uo == u && o < lane)) ? 1 : 0;
-      }
-      if (chosen) out[k + place] = lane;
-      k += need;
     }
+    if (lane < need) out[k + lane] = blk;
+    k += max(need, 0);
   } else {
     // each lane keeps its own best (value, block); a round reduces them over
     // the wave and only the winning lane rescans its registers
