@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -544,11 +545,21 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference kernel for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and print its size")
+    ap.add_argument("--micro", nargs="*", metavar="WHAT", default=None,
+                    help="only run the rate measurements of lib/msa_rates (hbm, launch, lds, mix, chain; "
+                         "default all): device rates the kernels' designs rest on")
     args = ap.parse_args()
 
     if args.profile_summaries:
         write_profile_summaries(args.profile_summaries)
         return
+    if args.micro is not None:
+        # a child process of its own: this one never touches the GPU
+        from block_sparse_attention_selection_amd.build import RATES
+        if not os.path.exists(RATES):
+            print(f"{RATES} is not built (python -m block_sparse_attention_selection_amd.build)", file=sys.stderr)
+            sys.exit(1)
+        sys.exit(subprocess.call([RATES, *args.micro]))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

@@ -1,4 +1,5 @@
-"""Build libmsa_kvouter.so (HIP, gfx950) in-tree with hipcc.
+"""Build libmsa_kvouter.so (HIP, gfx950) in-tree with hipcc, and the rate
+measurement program lib/msa_rates (run by `python bench.py --micro`).
 
     python -m block_sparse_attention_selection_amd.build
 """
@@ -16,6 +17,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmsa_kvouter.so")
 OBJDIR = os.path.join(ROOT, "_build", "msa")
 SOURCES = ["msa_api.hip", "msa_index.hip", "msa_forward.hip", "msa_tiles.hip", "msa_store.hip", "msa_select.hip"]
+RATES_SRC = "msa_rates.hip"  # a standalone program, not part of the library
+RATES = os.path.join(LIBDIR, "msa_rates")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -41,17 +44,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _build_rates() -> None:
+    tmp = RATES + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], os.path.join(CSRC, RATES_SRC), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {RATES_SRC}:\n{r.stderr}")
+    os.replace(tmp, RATES)
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        rates = ex.submit(_build_rates)
         objs = list(ex.map(_compile, SOURCES))
+        rates.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", RATES)
     return LIB
 
 

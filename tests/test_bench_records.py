@@ -1,5 +1,6 @@
 """Host logic of bench.py: which source changes void a workload's recorded
-HBM-traffic counters (CPU only)."""
+HBM-traffic counters, and the command line of its rate measurements (CPU
+only)."""
 import os
 import shutil
 import sys
@@ -58,3 +59,23 @@ def test_shared_headers_and_the_host_file_void_everything(tree):
         _touch(tree / name)
         after = _hashes()
         assert all(before[w] != after[w] for w in before), name
+
+
+def test_the_rate_program_voids_nothing(tree):
+    # msa_rates.hip is a measurement program, not a kernel of any workload
+    before = _hashes()
+    _touch(tree / "msa_rates.hip")
+    assert _hashes() == before
+
+
+def test_micro_rejects_an_unknown_measurement_before_touching_the_gpu():
+    import subprocess
+
+    from block_sparse_attention_selection_amd.build import RATES
+
+    if not os.path.exists(RATES):
+        pytest.skip("lib/msa_rates is not built")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--micro", "nonesuch"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "unknown measurement nonesuch" in r.stderr
