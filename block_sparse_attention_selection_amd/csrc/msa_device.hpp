@@ -233,10 +233,11 @@ __device__ __forceinline__ int wave_tile_of(const int64_t* __restrict__ cu, int 
   const int lane = threadIdx.x & 63;
   const int per = (B + 63) / 64;
   const int s0 = min(lane * per, B), s1 = min(s0 + per, B);
+  // token counts are below Tq (an int): 32-bit divisions
   int cnt = 0;
   for (int s = s0; s < s1; ++s) {
     const int64_t n = min(cu[s + 1], (int64_t)Tq) - max(cu[s], (int64_t)0);
-    if (n > 0) cnt += (int)((n + T - 1) / T);
+    if (n > 0) cnt += ((int)n + T - 1) / T;
   }
   int incl = cnt;
 #pragma unroll
@@ -254,7 +255,7 @@ __device__ __forceinline__ int wave_tile_of(const int64_t* __restrict__ cu, int 
     for (int s = s0; s < s1; ++s) {
       const int64_t a = max(cu[s], (int64_t)0);
       const int64_t n = min(cu[s + 1], (int64_t)Tq) - a;
-      const int nt = n > 0 ? (int)((n + T - 1) / T) : 0;
+      const int nt = n > 0 ? ((int)n + T - 1) / T : 0;
       if (jj < nt) {
         s_out = s;
         t_out = (int)(a + (int64_t)jj * T);

@@ -626,12 +626,34 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
 // ---------------------------------------------------------------------------
 constexpr int kWaveSlots = 512;  // tile tokens x topk handled by one wave
 constexpr int kWaveBitWords = 1024;  // per wave: the tokens' block sets and the chain's, as bit masks
+constexpr int kOwnWordBlocks = 512;  // whole-word bitmap stores up to this many blocks a sequence (else atomics)
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// A lane's slot of a tile walked in rounds of 64: idx = tau * K + k, moved
+// on by 64 slots per round without a division (K <= 64, so one carry step
+// suffices).
+struct SlotWalk {
+  int idx, tau, k;
+  int dq, dr;  // 64 = dq * K + dr
+  __device__ __forceinline__ SlotWalk(int lane, int K) : idx(lane), tau(lane / K), k(lane - (lane / K) * K) {
+    dq = 64 / K;
+    dr = 64 - dq * K;
+  }
+  __device__ __forceinline__ void next(int K) {
+    idx += 64;
+    tau += dq;
+    k += dr;
+    if (k >= K) {
+      k -= K;
+      ++tau;
+    }
+  }
+};
 
 __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   __shared__ int s_sel[4][kWaveSlots];  // valid picks, -1 where the slot is invalid
@@ -671,13 +693,29 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     for (int i = lane; i < (nt + 1) * wb; i += 64) bits[i] = 0u;
     wave_lds_sync();
   }
-  for (int idx = lane; idx < nt * K; idx += 64) {
-    const int tau = idx / K;
-    const int b = p.selected[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)];
-    const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
-    const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
-    sel[idx] = valid ? b : -1;
-    if (use_bits && valid) atomicOr(&bits[tau * wb + (b >> 5)], 1u << (b & 31));
+  {
+    // every round's pick is requested before the first is used (one round
+    // trip instead of one per round)
+    constexpr int kRounds = kWaveSlots / 64;
+    int braw[kRounds];
+    SlotWalk w(lane, K);
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      braw[r] = w.idx < nt * K ? p.selected[tg * K + (size_t)w.tau * Hkv * K + w.k] : -1;
+      w.next(K);
+    }
+    w = SlotWalk(lane, K);
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      if (w.idx < nt * K) {
+        const int tau = w.tau, b = braw[r];
+        const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
+        const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
+        sel[w.idx] = valid ? b : -1;
+        if (use_bits && valid) atomicOr(&bits[tau * wb + (b >> 5)], 1u << (b & 31));
+      }
+      w.next(K);
+    }
   }
   for (int tau = lane; tau < nt; tau += 64) s_nres[wave][tau] = 0;
   if (lane == 0) s_miss[wave] = 0ull;
@@ -685,8 +723,9 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   // the chain: the leader's valid picks present in every token of the tile
   if (p.T > 0) {
     unsigned long long miss = 0ull;
-    for (int idx = lane + K; idx < nt * K; idx += 64) {
-      const int tau = idx / K, k = idx - tau * K;
+    for (SlotWalk w(lane, K); w.idx < nt * K; w.next(K)) {
+      if (w.tau == 0) continue;  // the leader itself
+      const int tau = w.tau, k = w.k;
       const int bl = sel[k];
       if (bl < 0) continue;
       bool found = false;
@@ -717,11 +756,23 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   }
   wave_lds_sync();
   if (p.tdesc) write_tile_desc(p, item, t, s, nt, n_ch, L, Tq_s, q0, g, s_chain[wave], lane);
-  // flags, residual bits, residual counts
-  int res = 0;
-  for (int idx = lane; idx < nt * K; idx += 64) {
-    const int tau = idx / K;
-    const int b = sel[idx];
+  // flags, residual bits, residual counts, and each residual slot's rank
+  // among its token's residual slots: the residual lanes of a round before
+  // it that hold the same token, plus those of earlier rounds (a token
+  // started in an earlier round continues at lane 0; `carry` counts its
+  // residual slots so far)
+  // A tile whose tokens are exactly one bitmap word (32 tokens from a
+  // multiple of 32, or fewer that are the batch's last) is that word's only
+  // writer: it builds each residual block's word from the block masks and
+  // stores it whole (below) instead of setting bits with device-scope
+  // atomics.
+  const bool own_words =
+      use_bits && (t & 31) == 0 && (nt == 32 || (nt < 32 && t + nt >= p.Tq)) && nblk <= kOwnWordBlocks;
+  int res = 0, carry = 0;
+  for (SlotWalk w(lane, K); w.idx - lane < nt * K; w.next(K)) {
+    const bool act = w.idx < nt * K;
+    const int tau = w.tau;
+    const int b = act ? sel[w.idx] : -1;
     uint8_t flag = 0;
     if (b >= 0) {
       bool cov = false;
@@ -733,22 +784,32 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
       flag = cov ? 1 : 2;
       if (!cov) {
         const int tt = t + tau;
-        atomicOr(&p.bitmap[((size_t)b * Hkv + g) * p.W + (tt >> 5)], 1u << (tt & 31));
+        if (!own_words) atomicOr(&p.bitmap[((size_t)b * Hkv + g) * p.W + (tt >> 5)], 1u << (tt & 31));
         atomicAdd(&s_nres[wave][tau], 1);
         ++res;
       }
     }
-    p.slot_flag[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)] = flag;
-    if (flag == 2) sel[idx] = b | kResidualMark;
+    if (act) p.slot_flag[tg * K + (size_t)tau * Hkv * K + w.k] = flag;
+    const uint64_t resm = __ballot(flag == 2);
+    if (p.res_rank) {
+      const int st = lane - w.k;  // the lane of the token's first slot in this round
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      const uint64_t from = st > 0 ? (~0ull << st) : ~0ull;
+      const int rank = (st < 0 ? carry : 0) + __popcll(resm & below & from);
+      if (flag == 2) p.res_rank[tg * K + (size_t)tau * Hkv * K + w.k] = (uint8_t)rank;
+      const int st63 = 63 - __builtin_amdgcn_readlane(w.k, 63);  // the last lane's token
+      carry = (st63 < 0 ? carry : 0) + __popcll(resm & (st63 > 0 ? (~0ull << st63) : ~0ull));
+    }
   }
-  wave_lds_sync();
-  if (p.res_rank) {  // rank of each residual slot among its token's residual slots
-    for (int idx = lane; idx < nt * K; idx += 64) {
-      if (sel[idx] < 0 || !(sel[idx] & kResidualMark)) continue;
-      const int tau = idx / K;
-      int rank = 0;
-      for (int i = tau * K; i < idx; ++i) rank += (sel[i] >= 0 && (sel[i] & kResidualMark)) ? 1 : 0;
-      p.res_rank[tg * K + (size_t)tau * Hkv * K + (idx - tau * K)] = (uint8_t)rank;
+  wave_lds_sync();  // the residual counts
+  if (own_words) {
+    // block b's word: bit tau for each token that picked b outside the chain
+    // (the masks hold valid picks only; reads of one round share two words)
+    for (int b = lane; b < nblk; b += 64) {
+      const int wi = b >> 5, sh = b & 31;
+      uint32_t word = 0u;
+      for (int tau = 0; tau < nt; ++tau) word |= ((bits[tau * wb + wi] >> sh) & 1u) << tau;
+      if (word != 0u && !((bits[nt * wb + wi] >> sh) & 1u)) p.bitmap[((size_t)b * Hkv + g) * p.W + (t >> 5)] = word;
     }
   }
   for (int tau = lane; tau < nt; tau += 64) {

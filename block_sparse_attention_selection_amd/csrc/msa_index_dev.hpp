@@ -207,8 +207,16 @@ __device__ __forceinline__ int residual_pos(const Params& p, int t, int g, int b
 // malformed cu_seqlens) are ignored: their bit is not set.
 __device__ __forceinline__ void emit_slot(const Params& p, int64_t slot) {
   if (p.slot_flag[slot] != 2) return;
-  const int t = (int)(slot / ((int64_t)p.Hkv * p.K));
-  const int g = (int)((slot / p.K) % p.Hkv);
+  // slot = (t * Hkv + g) * K + k; in 32 bits while the slot numbers fit
+  int t, g;
+  if (slot <= 0xFFFFFFFFll) {
+    const uint32_t tg = (uint32_t)slot / (uint32_t)p.K;
+    t = (int)(tg / (uint32_t)p.Hkv);
+    g = (int)(tg - (uint32_t)t * (uint32_t)p.Hkv);
+  } else {
+    t = (int)(slot / ((int64_t)p.Hkv * p.K));
+    g = (int)((slot / p.K) % p.Hkv);
+  }
   const int b = p.selected[slot];
   if (b < 0 || b >= p.nb_max) return;
   const size_t w = ((size_t)b * p.Hkv + g) * p.W + (t >> 5);
@@ -217,7 +225,7 @@ __device__ __forceinline__ void emit_slot(const Params& p, int64_t slot) {
   p.ent[pos] = (int)slot;
   if (p.slot_pos) p.slot_pos[slot] = pos;
   if (p.res_list) {
-    const int64_t k = slot % p.K;
+    const int64_t k = slot - ((int64_t)t * p.Hkv + g) * p.K;
     p.res_list[slot - k + p.res_rank[slot]] = pos;
   }
 }
