@@ -393,6 +393,28 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
 // Every other tile is appended to the tile list. Tokens outside every
 // sequence (decode mode) get zero outputs and an LSE of -inf here.
 // ---------------------------------------------------------------------------
+// A thread's slot of a tile walked in rounds of S slots: idx = tau * K + k,
+// moved on by S slots per round without a division (S mod K < K, so one
+// carry step suffices).
+template <int S>
+struct SlotWalk {
+  int idx, tau, k;
+  int dq, dr;  // S = dq * K + dr
+  __device__ __forceinline__ SlotWalk(int first, int K) : idx(first), tau(first / K), k(first - (first / K) * K) {
+    dq = S / K;
+    dr = S - dq * K;
+  }
+  __device__ __forceinline__ void next(int K) {
+    idx += S;
+    tau += dq;
+    k += dr;
+    if (k >= K) {
+      k -= K;
+      ++tau;
+    }
+  }
+};
+
 template <typename CT, typename KVT, bool ATTN, int RS>
 __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
   extern __shared__ int s_sel[];  // [nt][K] picks, -1 where the slot is invalid
@@ -499,13 +521,25 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
       __syncthreads();
     }
   }
-  for (int idx = tid; idx < nt * K; idx += 256) {
-    const int tau = idx / K, k = idx - tau * K;
+  // The slot loops below walk the tile's slots without divisions in
+  // classification-only launches (many slots a tile); launches that also
+  // stream (a few slots a tile) keep the plain index arithmetic, which needs
+  // fewer registers.
+  auto load_pick = [&](int idx, int tau, int k) {
     const int b = (idx < K) ? b_raw : p.selected[((size_t)(t + tau) * Hkv + g) * K + k];
     const int64_t pos = (int64_t)L - Tq_s + i0 + tau;
     const bool valid = b >= 0 && b < nblk && (!p.causal || (int64_t)kBlk * b <= pos);
     s_sel[idx] = valid ? b : -1;
     if (use_bits && valid) atomicOr(&bits[tau * wb + (b >> 5)], 1u << (b & 31));
+  };
+  if constexpr (ATTN) {
+    for (int idx = tid; idx < nt * K; idx += 256) {
+      const int tau = idx / K;
+      load_pick(idx, tau, idx - tau * K);
+    }
+  } else {
+#pragma unroll 4
+    for (SlotWalk<256> w(tid, K); w.idx < nt * K; w.next(K)) load_pick(w.idx, w.tau, w.k);
   }
   for (int tau = tid; tau < nt; tau += 256) s_nres[tau] = 0;
   if (tid < 64) s_miss[tid] = 0;
@@ -516,10 +550,9 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
   // One thread per (token, leader pick) looks for the pick in the token's
   // list; a miss marks the pick.
   if (p.T > 0) {
-    for (int idx = tid + K; idx < nt * K; idx += 256) {  // tokens 1 .. nt-1
-      const int tau = idx / K, k = idx - tau * K;
+    auto test_pick = [&](int tau, int k) {
       const int bl = s_sel[k];
-      if (bl < 0) continue;
+      if (bl < 0) return;
       bool found = false;
       if (use_bits) {
         found = (bits[tau * wb + (bl >> 5)] >> (bl & 31)) & 1u;
@@ -527,6 +560,14 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
         for (int k2 = 0; k2 < K; ++k2) found |= (s_sel[tau * K + k2] == bl);
       }
       if (!found) s_miss[k] = 1;
+    };
+    if constexpr (ATTN) {
+      for (int idx = tid + K; idx < nt * K; idx += 256) {  // tokens 1 .. nt-1
+        const int tau = idx / K;
+        test_pick(tau, idx - tau * K);
+      }
+    } else {
+      for (SlotWalk<256> w(tid + K, K); w.idx < nt * K; w.next(K)) test_pick(w.tau, w.k);
     }
   }
   __syncthreads();
@@ -552,8 +593,7 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
   const int n_ch = s_nch;
 
   // flags, residual bits, residual counts
-  for (int idx = tid; idx < nt * K; idx += 256) {
-    const int tau = idx / K;
+  auto flag_slot = [&](int idx, int tau, int k) {
     const int b = s_sel[idx];
     uint8_t flag = 0;
     if (b >= 0) {
@@ -570,8 +610,16 @@ __global__ __launch_bounds__(256, RS == 1 ? 2 : 1) void k_front(Params p) {
         atomicAdd(&s_nres[tau], 1);
       }
     }
-    p.slot_flag[((size_t)(t + tau) * Hkv + g) * K + (idx - tau * K)] = flag;
+    p.slot_flag[((size_t)(t + tau) * Hkv + g) * K + k] = flag;
     if (flag == 2) s_sel[idx] = b | kResidualMark;
+  };
+  if constexpr (ATTN) {
+    for (int idx = tid; idx < nt * K; idx += 256) {
+      const int tau = idx / K;
+      flag_slot(idx, tau, idx - tau * K);
+    }
+  } else {
+    for (SlotWalk<256> w(tid, K); w.idx < nt * K; w.next(K)) flag_slot(w.idx, w.tau, w.k);
   }
   __syncthreads();
   if (p.res_rank) {  // rank of each residual slot among its token's residual slots
@@ -634,26 +682,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A lane's slot of a tile walked in rounds of 64: idx = tau * K + k, moved
-// on by 64 slots per round without a division (K <= 64, so one carry step
-// suffices).
-struct SlotWalk {
-  int idx, tau, k;
-  int dq, dr;  // 64 = dq * K + dr
-  __device__ __forceinline__ SlotWalk(int lane, int K) : idx(lane), tau(lane / K), k(lane - (lane / K) * K) {
-    dq = 64 / K;
-    dr = 64 - dq * K;
-  }
-  __device__ __forceinline__ void next(int K) {
-    idx += 64;
-    tau += dq;
-    k += dr;
-    if (k >= K) {
-      k -= K;
-      ++tau;
-    }
-  }
-};
 
 __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   __shared__ int s_sel[4][kWaveSlots];  // valid picks, -1 where the slot is invalid
@@ -698,13 +726,13 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
     // trip instead of one per round)
     constexpr int kRounds = kWaveSlots / 64;
     int braw[kRounds];
-    SlotWalk w(lane, K);
+    SlotWalk<64> w(lane, K);
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       braw[r] = w.idx < nt * K ? p.selected[tg * K + (size_t)w.tau * Hkv * K + w.k] : -1;
       w.next(K);
     }
-    w = SlotWalk(lane, K);
+    w = SlotWalk<64>(lane, K);
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       if (w.idx < nt * K) {
@@ -723,7 +751,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   // the chain: the leader's valid picks present in every token of the tile
   if (p.T > 0) {
     unsigned long long miss = 0ull;
-    for (SlotWalk w(lane, K); w.idx < nt * K; w.next(K)) {
+    for (SlotWalk<64> w(lane, K); w.idx < nt * K; w.next(K)) {
       if (w.tau == 0) continue;  // the leader itself
       const int tau = w.tau, k = w.k;
       const int bl = sel[k];
@@ -769,7 +797,7 @@ __global__ __launch_bounds__(256) void k_classify_waves(Params p, int ntiles) {
   const bool own_words =
       use_bits && (t & 31) == 0 && (nt == 32 || (nt < 32 && t + nt >= p.Tq)) && nblk <= kOwnWordBlocks;
   int res = 0, carry = 0;
-  for (SlotWalk w(lane, K); w.idx - lane < nt * K; w.next(K)) {
+  for (SlotWalk<64> w(lane, K); w.idx - lane < nt * K; w.next(K)) {
     const bool act = w.idx < nt * K;
     const int tau = w.tau;
     const int b = act ? sel[w.idx] : -1;
