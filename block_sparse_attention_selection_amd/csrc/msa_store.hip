@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kStoreThreads) void k_store_kv(const uint16_t* kn, 
     const int i = row / Hkv, g = row - i * Hkv;
     const int64_t slot = loc[i];
     if (slot < 0 || slot >= nslots) continue;
-    const int64_t page = slot / P, off = slot - page * P;
+    // page sizes are powers of two (64 or 128): a shift, not a 64-bit division
+    const int64_t page = slot >> __builtin_ctz((unsigned)P), off = slot & (P - 1);
     const u32x4* src = (const u32x4*)((is_v ? vn : kn) + (int64_t)row * kD + 16 * piece);
     in[j][0] = src[0];
     in[j][1] = src[1];
