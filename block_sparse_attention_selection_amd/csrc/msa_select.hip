@@ -224,6 +224,129 @@ __device__ __forceinline__ void score_blocks(const SelectParams& p, const SelTil
   }
 }
 
+// One 16-byte direct-to-LDS buffer load per lane with the non-temporal hint
+// (lane i's bytes land at LDS byte address lds + 16 i): key rows that are
+// read once, each load instruction covering whole 128-byte lines.
+__device__ __forceinline__ void dma16_nt(i32x4v rsrc, uint32_t lds, int voff) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"{m0}"(a), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// score_blocks with the key groups staged through LDS: each wave streams its
+// blocks' groups of 16 key rows into a ring of four LDS slots of its own
+// (two groups in flight ahead of the one in use) by direct-to-LDS loads that
+// cover whole lines (one instruction: 64 / kPc complete rows, their pieces
+// swizzled as in k_select_tiles), then reads them in the MFMA layout. Rows
+// are read once a call: the loads carry the non-temporal hint, which the
+// register-loading score_blocks cannot use (there two loads share each
+// line). Page lookups are scalar loads, so no compiler-tracked load waits
+// behind the ring's loads.
+template <typename QT, typename KT, int NRB, int NW>
+__device__ __forceinline__ void score_blocks_staged(const SelectParams& p, const SelTile& x, int b0, int b1,
+                                                    float* dst, int64_t row_stride, u32x4* ring) {
+  constexpr int kPc = KeyBytes<KT>::kRow / 16;  // 16-byte pieces per key row
+  constexpr int kGrpU4 = 16 * kPc;              // pieces per group of 16 rows
+  constexpr int kLd = kGrpU4 / 64;              // load instructions per group
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = x.g, L = x.L;
+  const int h = lane >> 4, col = lane & 15;
+  u32x4 qf[NRB][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = rb * 16 + col;
+    if (r < x.ntok) {
+      const u32x4* q = (const u32x4*)((const uint16_t*)p.q + ((x.t0 + r) * p.Hkv + g) * (int64_t)kD + 32 * h);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) qf[rb][st] = q[st];
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) qf[rb][st] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  int posr[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) posr[rb] = (int)max(x.pos(rb * 16 + col), (int64_t)-1);
+  const int pos_lo = (int)max(x.pos(0), (int64_t)-1);
+  const int32_t* bt = p.bt + (int64_t)x.s * p.MP;
+  auto swz = [&](int row) { return kPc == 16 ? (row & 15) : ((row >> 1) & 7); };
+  // group kg of block b into ring slot sl: LDS piece i of the slot holds row
+  // i / kPc of the group, its piece (i % kPc) ^ swz(row). A half without a
+  // page (beyond L) or with a page id outside the cache reads page 0
+  // (num_pages >= 1 here); the mask removes keys at or beyond L.
+  auto issue = [&](int b, int kg, int sl) {
+    const int j0 = 128 * b + (kg >= 4 ? 64 : 0);
+    int pg = j0 < L ? sload32(bt + j0 / p.P) : -1;
+    pg = (pg >= 0 && pg < p.num_pages) ? pg : 0;
+    const int rowb = KeyBytes<KT>::kRow;
+    const i32x4v rs = make_rsrc((const uint8_t*)p.k + ((int64_t)pg * p.Hkv + g) * p.P * rowb, p.P * rowb);
+    const uint32_t base = lds_addr(ring + kGrpU4 * sl);
+    const int row0 = (16 * kg) & (p.P - 1);  // the group's first row within its page
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) {
+      const int i = 64 * j + lane, r = i / kPc, pc = i % kPc;
+      dma16_nt(rs, base + 1024 * j, (row0 + r) * rowb + 16 * (pc ^ swz(r)));
+    }
+  };
+  const int first = b0 + wave;
+  const int nblk_w = b1 > first ? (b1 - first + NW - 1) / NW : 0;
+  if (nblk_w == 0) return;
+  issue(first, 0, 0);
+  issue(first, 1, 1);
+  for (int bi = 0, b = first; bi < nblk_w; ++bi, b += NW) {
+    const bool has_next = bi + 1 < nblk_w;
+    const bool full = 128 * b + 127 < L && 128 * b + 127 <= pos_lo;
+    float m[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) m[rb] = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      const int gi = 8 * bi + kg;  // this group's number in the wave's stream
+      // the group two ahead (this block's, or the next block's first two)
+      if (kg < 6) {
+        issue(b, kg + 2, (gi + 2) & 3);
+        wait_vmcnt<2 * kLd>();  // group gi has landed (gi + 1 and gi + 2 may be in flight)
+      } else if (has_next) {
+        issue(b + NW, kg - 6, (gi + 2) & 3);
+        wait_vmcnt<2 * kLd>();
+      } else if (kg == 6) {
+        wait_vmcnt<kLd>();  // the last two groups: gi + 1 may be in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      asm volatile("" ::: "memory");  // the slot's reads below follow the wait
+      KeyRow<QT, KT> kr;
+      kr.load_lds(ring + kGrpU4 * (gi & 3), col, swz(col), h);
+      const int jbase = 128 * b + 16 * kg + 4 * h;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = Mma<QT>::run(kr.frag(st), qf[rb][st], acc);
+        float v;
+        if (full) {
+          v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        } else {
+          v = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = jbase + i;
+            v = fmaxf(v, (j < L && j <= posr[rb]) ? acc[i] : -INFINITY);
+          }
+        }
+        m[rb] = fmaxf(m[rb], v);
+      }
+      // every lane's reads of this slot are done before a later issue
+      // overwrites it (two groups on)
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mb = max_over_groups(m[rb]);
+      if (h == 0 && rb * 16 + col < x.ntok) dst[(rb * 16 + col) * row_stride + b] = mb;
+    }
+  }
+}
+
 // The list of one (token t, KV head g) row whose token sits at position pos
 // and sees blocks [0, nr), from its scores row[0, nr) (LDS or global). One
 // wave. Also writes the row to p.scores when requested (unless the row is
@@ -479,8 +602,16 @@ __global__ __launch_bounds__(64 * kSelSplitWaves) void k_select_scores(SelectPar
   if (!sel_tile(p, tile, g, 16, &x)) return;
   const int b0 = split * kSelSplitBlocks, b1 = min(b0 + kSelSplitBlocks, x.nscan);
   if (b0 >= b1) return;
-  score_blocks<QT, KT, 1, kSelSplitWaves>(p, x, b0, b1, sc + (x.t0 * p.Hkv + g) * (int64_t)p.nb_cap,
-                                          (int64_t)p.Hkv * p.nb_cap);
+  float* dst = sc + (x.t0 * p.Hkv + g) * (int64_t)p.nb_cap;
+  if constexpr (sizeof(KT) == 1) {
+    // e4m3fn keys through LDS (8 KB a wave); 16-bit keys would need twice
+    // that and halve the waves a CU holds, so they load straight to registers
+    __shared__ u32x4 s_ring[kSelSplitWaves][4 * 16 * (KeyBytes<KT>::kRow / 16)];
+    score_blocks_staged<QT, KT, 1, kSelSplitWaves>(p, x, b0, b1, dst, (int64_t)p.Hkv * p.nb_cap,
+                                                   s_ring[threadIdx.x >> 6]);
+  } else {
+    score_blocks<QT, KT, 1, kSelSplitWaves>(p, x, b0, b1, dst, (int64_t)p.Hkv * p.nb_cap);
+  }
 }
 
 // Split path, second pass: one wave per (token, KV head) row lists it from
