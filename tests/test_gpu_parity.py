@@ -93,6 +93,20 @@ def test_index_builder_bitexact_custom(T, Tu, causal, list_all):
     _index_case(wl, T, Tu, list_all)
 
 
+@pytest.mark.parametrize("list_all", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+def test_index_builder_bitexact_whole_words(causal, list_all):
+    # 32-token tiles that start at multiples of 32 are the only writers of
+    # their bitmap words (tokens 0-31, 32-63) and store them whole; the last
+    # tile (tokens 64-68) owns its word because no token follows it; a
+    # second batch whose first sequence ends at 30 tokens leaves every word
+    # shared (set bit by bit)
+    for seed, tq, lens in ((41, [32, 37], [3000, 6000]), (42, [30, 7, 33], [2000, 900, 4100])):
+        wl = W.make_custom(seed, tq, lens, 16, 2, 64, topk=6, causal=causal, pick="random",
+                           shared_chunk=8, shared_picks=3)
+        _index_case(wl, 32, 16, list_all)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_gqa", "varlen_mqa"])
 def test_index_builder_bitexact_named(name):
     wl = W.make(name)
