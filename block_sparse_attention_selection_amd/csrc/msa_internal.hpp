@@ -80,7 +80,7 @@ struct Params {
   int4* win_desc;      // attention: per unit-kernel window (row, first rank, first entry, entries)
   int4* tdesc;         // attention: per tile item, 2 x int4 (see write_tile_desc)
   int4* ctab;          // attention: per tile item, 4 topk chunk entries
-  void* scratch_row;  // 8 KB that stores of rows outside a tile or piece may land in
+  void* scratch_row;  // 8 KB that stores of rows outside a tile may land in
   // partial results of the KV-outer units
   void* opart;   // normalised O per (residual slot, head) row, in q's 16-bit type, in blocks of
                  // 32 rows: row r's 16-byte chunk k at byte (r >> 5) * 8192 + k * 512 + (r & 31) * 16

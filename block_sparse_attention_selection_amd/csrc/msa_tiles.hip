@@ -727,6 +727,10 @@ constexpr int kSeqLds = 256;  // cu_seqlens / used_kv_lens cached in LDS up to t
 // vector memory instructions per lane of the partial stores of a piece
 // (store_part: eight 16-byte stores, then the LSE)
 constexpr int kUnitStoreOps = 9;
+// buffer offset of a store to drop: past the end of any descriptor it meets
+constexpr int kDropOff = 1 << 30;
+// cache policy operand of the buffer builtins: the non-temporal hint
+constexpr int kBufNT = 2;
 
 __device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok, int head, int h) {
   if (tok < 0) {
@@ -739,8 +743,8 @@ __device__ __forceinline__ void load_q8(u32x4 (&qb)[8], const Params& p, int tok
   for (int s = 0; s < 8; ++s) qb[s] = *(const u32x4*)(base + 16 * s);
 }
 
-// The unit kernel's Q rows: every lane loads a row, those without a token
-// token 0's (their results go to the scratch row), so that each call is the
+// The unit kernel's Q rows: every lane loads a row, a lane without a token
+// that of token 0 (its results are never stored), so that each call is the
 // same eight loads in every wave and no register is cleared while a load into
 // it may be in flight.
 __device__ __forceinline__ void load_q8_rows(u32x4 (&qb)[8], const Params& p, int tok, int head, int h) {
@@ -1054,21 +1058,31 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
         const int na1 = piece_end(bf ^ 1, min(wdn.w, p.Tu), 0);
         load_q8_rows(qn, p, row_token(bf ^ 1, 0, na1), ng * G + hr, h);
       }
-      // Every lane stores (rows outside the piece into a scratch row), so that
-      // the stores are the same kUnitStoreOps instructions in every wave. The
-      // partials are read once, by the tile kernel, long after they leave
+      // Every wave issues the same kUnitStoreOps stores: buffer stores through
+      // a descriptor over the two 32-row groups of the partial layout that
+      // the wave's 32 rows can touch, where a row outside the piece takes an
+      // offset past the descriptor's end, so the hardware drops its store
+      // (no memory write, and still one instruction in the wave's count).
+      // The partials are read once, by the tile kernel, long after they leave
       // L2: they are written and read with the non-temporal hint (same-box
       // A/B: tile kernel 430 -> 357 us on the MQA batch, 950 -> 926 us on the
       // shared-selection prefill).
       {
-        const size_t pidx = (size_t)(e0 + a0 + rho / G) * G + hr;
-        char* pbase = (valid ? (char*)p.opart + part_offset(pidx) : (char*)p.scratch_row + 16 * c) + 512 * h;
-        float* lrow = (valid && h == 0) ? p.lpart + pidx : (float*)p.scratch_row + 64 + lane;
+        const int64_t wrow = uniform64((int64_t)(e0 + a0) * G + 32 * wave);  // the wave's first row
+        const int64_t grp = wrow >> 5;
+        const int64_t pidx = wrow + c;  // row (e0 + a0 + rho / G) * G + hr
+        const int ooff = valid ? (int)((pidx >> 5) - grp) * 8192 + (int)(pidx & 31) * 16 + 512 * h : kDropOff;
+        const int loff = valid && h == 0 ? (int)(pidx - 32 * grp) * 4 : kDropOff;
+        const __amdgpu_buffer_rsrc_t ro =
+            __builtin_amdgcn_make_buffer_rsrc((char*)p.opart + grp * 8192, (short)0, 2 * 8192, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rl =
+            __builtin_amdgcn_make_buffer_rsrc(p.lpart + 32 * grp, (short)0, 64 * 4, kRsrcWord3);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) __builtin_nontemporal_store(pk[2 * t + u], (u32x4*)(pbase + (4 * t + 2 * u) * 512));
-        __builtin_nontemporal_store(lse_row, lrow);
+          for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(pk[2 * t + u], ro, ooff + (4 * t + 2 * u) * 512, 0, kBufNT);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_row), rl, loff, 0, kBufNT);
       }
       if (restage) {
         // the block's loads were issued before the stores: wait for them but
