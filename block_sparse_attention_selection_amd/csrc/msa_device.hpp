@@ -166,6 +166,19 @@ __device__ __forceinline__ int sload32(const int32_t* ptr) {
   return v;
 }
 
+// 16 bytes at a wave-uniform address, through the constant address space:
+// the compiler issues a scalar load and places its wait. Only for memory
+// that no kernel running at the same time writes. The pointer is rebuilt
+// from its (wave-uniform) integer value, else the compiler turns the load
+// back into a global one, which it makes scalar only where no store of the
+// kernel may precede it.
+__device__ __forceinline__ int4 const_load(const int4* ptr) {
+  typedef int v4 __attribute__((ext_vector_type(4)));
+  const uint64_t a = (uint64_t)uniform_ptr(ptr);
+  const v4 v = *(const __attribute__((address_space(4))) v4*)a;
+  return int4{v.x, v.y, v.z, v.w};
+}
+
 // Owner sequence of token t: the largest s with cu[s] <= t, provided
 // t < cu[s+1]; -1 when t lies in no sequence. Stays inside cu[0..B].
 __device__ __forceinline__ int seq_of(const int64_t* __restrict__ cu, int B, int64_t t) {
@@ -273,6 +286,7 @@ __device__ __forceinline__ int wave_tile_of(const int64_t* __restrict__ cu, int 
 // direct-to-LDS buffer loads (shared by the tile, unit and selection kernels)
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and

@@ -224,10 +224,13 @@ enum { kNoLds = 1, kNoMfma = 2, kNoValu = 4, kNoBranch = 8, kOwn = 16 };
 // the softmax.
 template <int VAR>
 __device__ __forceinline__ float iter_parts(Rows32& rt, const f32x16& sc, const u32x4 (&pp)[2], const char* vprev,
-                                            const u32x4 (&vpre)[2], const char* vcur, const u32x4* knext, float sl2,
-                                            f32x16& sn, u32x4 (&pn)[2], u32x4 (&vnext)[2]) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-  auto kfrag = [&](int st) { return (VAR & kNoLds) ? rt.qb[(st + 3) & 7] : knext[pieceK(c, 2 * st + h)]; };
+                                            const u32x4 (&vpre)[2], const char* vcur, const u32x4* knext,
+                                            uint32_t koff0, float sl2, f32x16& sn, u32x4 (&pn)[2],
+                                            u32x4 (&vnext)[2]) {
+  const uint32_t ka0 = lds_addr(knext) + koff0;
+  auto kfrag = [&](int st) {
+    return (VAR & kNoLds) ? rt.qb[(st + 3) & 7] : *(const lds_u32x4*)(uintptr_t)(ka0 ^ (32u * st));
+  };
   auto vfrag = [&](int t, int sp) { return (VAR & kNoLds) ? rt.qb[(t + 2 * sp) & 7] : vfrag_at(vprev, t, sp); };
   const f32x16 sa = sc;
   u32x4 va[8], ka[8];
@@ -250,16 +253,14 @@ __device__ __forceinline__ float iter_parts(Rows32& rt, const f32x16& sc, const 
     }
     if (!(VAR & kNoValu)) {
       if (i == 0) {
-        cmax = sa[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sa[j]);
+        cmax = hw_max3(hw_max3(hw_max3(sa[0], sa[1], sa[2]), sa[3], sa[4]), sa[5], sa[6]);
       } else if (i == 1) {
-#pragma unroll
-        for (int j = 8; j < 16; ++j) cmax = fmaxf(cmax, sa[j]);
+        cmax = hw_max3(hw_max3(hw_max3(cmax, sa[7], sa[8]), sa[9], sa[10]), sa[11], sa[12]);
+        cmax = hw_max(hw_max3(cmax, sa[13], sa[14]), sa[15]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cmax), __float_as_uint(cmax), false, false);
-        cmax = __builtin_amdgcn_fmed3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), INFINITY) * sl2;
+        cmax = hw_max(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
         const float m_new = cmax > rt.m + kRescale32 ? cmax : rt.m;
-        alpha = m_new == rt.m ? 1.f : exp2f(rt.m - m_new);
+        alpha = m_new == rt.m ? 1.f : __builtin_amdgcn_exp2f(rt.m - m_new);
         rt.m = m_new;
         nmu = (m_new == -INFINITY) ? 0.f : -m_new;
       } else {
@@ -270,7 +271,7 @@ __device__ __forceinline__ float iter_parts(Rows32& rt, const f32x16& sc, const 
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q], sl2, nmu));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q + 1], sl2, nmu));
           pn[q >> 2][q & 3] = pack2<bf16_t>(p0, p1);
-          ls += p0 + p1;
+          ls = q == 0 ? p0 + p1 : ls + (p0 + p1);
         }
       }
     } else if (i == 7) {
@@ -297,7 +298,7 @@ __device__ __forceinline__ float iter_parts(Rows32& rt, const f32x16& sc, const 
 // ring of bf16 K/V chunks, one barrier per chunk
 template <int VAR>
 __global__ __launch_bounds__(512, 1) void k_chain(float* out, int steps, uint32_t seed) {
-  __shared__ u32x4 ring[8 * kSlotU4];
+  __shared__ __attribute__((aligned(256))) u32x4 ring[8 * kSlotU4];
   const int tid = threadIdx.x, lane = tid & 63;
   for (int i = tid; i < 8 * kSlotU4; i += 512) {
     uint32_t w[4];
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(512, 1) void k_chain(float* out, int steps, uint32_
   A.pp[0] = A.pp[1] = u32x4{0u, 0u, 0u, 0u};
   A.vpre[0] = A.vpre[1] = ring[lane];
   const float sl2 = 0.1275f;  // 128^-0.5 * log2(e)
+  const uint32_t koff0 = k_lane_offset0();
   auto slot = [&](int ci) { return ring + (ci & 7) * kSlotU4; };
   auto step = [&](int ci, const Pipe& in, Pipe& o) {
     loop_barrier();
@@ -332,9 +334,10 @@ __global__ __launch_bounds__(512, 1) void k_chain(float* out, int steps, uint32_
     const u32x4* knext = slot(ci + 1);
     float alpha;
     if (VAR & kOwn)
-      alpha = tile_iter<bf16_t, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, 0, 32, sl2, o.sc, o.pp, o.vpre);
+      alpha = tile_iter<bf16_t, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, koff0, 0, 32, sl2, o.sc, o.pp,
+                                       o.vpre);
     else
-      alpha = iter_parts<VAR>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, sl2, o.sc, o.pp, o.vpre);
+      alpha = iter_parts<VAR>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, koff0, sl2, o.sc, o.pp, o.vpre);
     if (VAR & kNoBranch)
       rt.l += alpha;  // no rescale branch
     else

@@ -384,6 +384,33 @@ __device__ __forceinline__ void rows_block(Rows32& rt, const u32x4* sblk, const 
   }
 }
 
+// The max instructions as they stand. fmaxf would first quiet a possible
+// signalling NaN in each operand that does not come from arithmetic the
+// compiler can see (matrix-core results, lane swaps), one instruction per
+// operand; scores hold no NaN (masked ones are -inf), so the chunk step
+// takes the hardware's max directly.
+__device__ __forceinline__ float hw_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float hw_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Byte offset, within a K tile, of the fragment a lane reads for product
+// st of a chunk: 16 pieceK(c, 2 st + h) = 256 c + 16 ((2 st + h) ^ (c & 15)).
+// The swizzle leaves st in bits 5-7 of the offset, where it enters by XOR:
+// the offset is that of product 0 XOR 32 st. Bits 5-7 of a tile base that
+// is a multiple of 256 bytes are zero, so the XOR can be applied to base +
+// offset: one register per lane, one add per chunk and one XOR per read.
+__device__ __forceinline__ uint32_t k_lane_offset0() {
+  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+  return 16u * (uint32_t)pieceK(c, h);
+}
+
 // One iteration of the tile kernel's chunk pipeline, scheduled by hand:
 // O^T += V(prev)^T P(prev)^T, sn = S of the next chunk, and the softmax step
 // of sc (this chunk's scores) giving pn. The work is cut into eight stages:
@@ -398,10 +425,13 @@ __device__ __forceinline__ void rows_block(Rows32& rt, const u32x4* sblk, const 
 // accumulator rescale factor (see rows_probs).
 template <typename CT, bool kMask>
 __device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u32x4 (&pp)[2], const char* vprev,
-                                           const u32x4 (&vpre)[2], const char* vcur, const u32x4* knext, int key0,
-                                           int lim, float sl2, f32x16& sn, u32x4 (&pn)[2], u32x4 (&vnext)[2]) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-  auto kfrag = [&](int st) { return knext[pieceK(c, 2 * st + h)]; };
+                                           const u32x4 (&vpre)[2], const char* vcur, const u32x4* knext,
+                                           uint32_t koff0, int key0, int lim, float sl2, f32x16& sn,
+                                           u32x4 (&pn)[2], u32x4 (&vnext)[2]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  // knext is a slot of a ring that starts on a 256-byte boundary
+  const uint32_t ka0 = lds_addr(knext) + koff0;
+  auto kfrag = [&](int st) { return *(const lds_u32x4*)(uintptr_t)(ka0 ^ (32u * st)); };
 
   f32x16 sa = sc;
   u32x4 va[8], ka[8];
@@ -429,16 +459,17 @@ __device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u
 #pragma unroll
         for (int j = 0; j < 16; ++j) sa[j] = (8 * (j >> 2) + (j & 3)) <= rel ? sa[j] : -INFINITY;
       }
-      cmax = sa[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sa[j]);
+      cmax = hw_max3(hw_max3(hw_max3(sa[0], sa[1], sa[2]), sa[3], sa[4]), sa[5], sa[6]);
     } else if (i == 1) {
-#pragma unroll
-      for (int j = 8; j < 16; ++j) cmax = fmaxf(cmax, sa[j]);
+      cmax = hw_max3(hw_max3(hw_max3(cmax, sa[7], sa[8]), sa[9], sa[10]), sa[11], sa[12]);
+      cmax = hw_max(hw_max3(cmax, sa[13], sa[14]), sa[15]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cmax), __float_as_uint(cmax), false, false);
-      cmax = __builtin_amdgcn_fmed3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), INFINITY) * sl2;
+      cmax = hw_max(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
       const float m_new = cmax > rt.m + kRescale32 ? cmax : rt.m;
-      alpha = m_new == rt.m ? 1.f : exp2f(rt.m - m_new);
+      // a new maximum exceeds the old by more than 2^kRescale32, so the
+      // factor is below 2^-8: the hardware exponential (results below the
+      // normal range flush to zero) is exact enough for it
+      alpha = m_new == rt.m ? 1.f : __builtin_amdgcn_exp2f(rt.m - m_new);
       rt.m = m_new;
       nmu = (m_new == -INFINITY) ? 0.f : -m_new;
     } else {
@@ -450,7 +481,7 @@ __device__ __forceinline__ float tile_iter(Rows32& rt, const f32x16& sc, const u
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q], sl2, nmu));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * q + 1], sl2, nmu));
         pn[q >> 2][q & 3] = pack2<CT>(p0, p1);
-        ls += p0 + p1;
+        ls = q == 0 ? p0 + p1 : ls + (p0 + p1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1144,13 +1175,14 @@ __device__ __forceinline__ void dma4(i32x4v rsrc, uint32_t lds, int voff) {
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   constexpr bool kFp8 = sizeof(KVT) == 1;
-  __shared__ u32x4 s_ring[kRingT * kSlotU4];
+  __shared__ __attribute__((aligned(256))) u32x4 s_ring[kRingT * kSlotU4];
   __shared__ int4 s_tab[2][kTabMax];  // chunk tables of the current and the next item
   __shared__ int4 s_desc[2][2];       // their descriptors
   __shared__ int s_pos[kPosMax];      // the current item's residual positions, [token][rank]
   __shared__ int s_nres[kTokMax];     // and residual counts
   __shared__ int s_item;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const uint32_t koff0 = k_lane_offset0();
   if (blockIdx.x == 0 && p.counters_next)
     for (int i = tid; i < kCntSlots; i += kTileThreads) p.counters_next[i] = 0;
   const int G = p.G, Hkv = p.Hkv, K = p.K, K4 = 4 * p.K;
@@ -1196,6 +1228,20 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
   auto chunk_of = [&](int bf, int ci, int n, int64_t& off, int& nrows) {
     if (ci < n) {
       const int4 e = s_tab[bf][ci];
+      off = (int64_t)(((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x);
+      nrows = e.w;
+    } else {
+      off = -1;
+      nrows = 0;
+    }
+  };
+  // the same entry of item `item`'s table, by a scalar load from global
+  // memory: the tables are written by an earlier kernel and only read by
+  // this one, so the constant address space applies, and the chunk step
+  // spends no vector instruction or LDS read on it
+  auto chunk_const = [&](int item, int ci, int n, int64_t& off, int& nrows) {
+    if (ci < n) {
+      const int4 e = const_load(p.ctab + (size_t)item * K4 + ci);
       off = (int64_t)(((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x);
       nrows = e.w;
     } else {
@@ -1317,14 +1363,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           const int nx = ci + kAhead;
           int64_t off = -1;
           int nr = 0;
-          if (nx < nck) chunk_of(bf, nx, nck, off, nr);  // this item's table: visible since the item began
-          wait_vmcnt<2 * (kAhead - 2)>();                 // chunk ci+1 has landed
-          loop_barrier();                                 // ... for every wave; and slot (ci - 2) % kRingT is free
+          if (nx < nck) chunk_const(cur, nx, nck, off, nr);
+          wait_vmcnt<2 * (kAhead - 2)>();  // chunk ci+1 has landed
+          loop_barrier();                  // ... for every wave; and slot (ci - 2) % kRingT is free
           if (nx >= nck && nxt >= 0 && (ci >= kAhead - 1 || first_real > 0)) {
-            // the next item's table was issued before chunk kAhead of this
-            // item (or drained with the top-up), so it has landed by now
-            const int4 dn = s_desc[bf ^ 1][0];
-            chunk_of(bf ^ 1, nx - nck, dn.z > 0 ? dn.w : 0, off, nr);
+            // a chunk of the next item (its first chunks are issued by this
+            // loop once it is past chunk kAhead - 1, or after a top-up)
+            const int4 dn = const_load(p.tdesc + 2 * (size_t)nxt);
+            chunk_const(nxt, nx - nck, dn.z > 0 ? dn.w : 0, off, nr);
           }
           issue_chunk16_512(p.k, p.v, off, nr, dl, slot_addr(rbase + nx));
           // a masked chunk's keys [key0, lim) are present: none when its page
@@ -1334,10 +1380,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           const char* vprev = (const char*)(slot_ptr(rbase + (ci > 0 ? ci - 1 : 0)) + kChunkU4);
           const char* vcur = (const char*)(slot_ptr(rbase + ci) + kChunkU4);
           const u32x4* knext = slot_ptr(rbase + (ci + 1 < nck ? ci + 1 : ci));
-          const float alpha = mask ? tile_iter<CT, true>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, lim,
-                                                         p.scale_log2, out.sc, out.pp, out.vpre)
-                                   : tile_iter<CT, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, key0, lim,
-                                                          p.scale_log2, out.sc, out.pp, out.vpre);
+          const float alpha = mask ? tile_iter<CT, true>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, koff0, key0,
+                                                         lim, p.scale_log2, out.sc, out.pp, out.vpre)
+                                   : tile_iter<CT, false>(rt, in.sc, in.pp, vprev, in.vpre, vcur, knext, koff0, key0,
+                                                          lim, p.scale_log2, out.sc, out.pp, out.vpre);
           rows_rescale(rt, alpha);
         };
         int ci = 0;
