@@ -23,6 +23,7 @@ from ._lib import (
     MsaError,
     build_index,
     kvouter_attention,
+    kvouter_attention_mxfp4,
     kvouter_attention_noalloc,
     lib_path,
     load,
@@ -39,6 +40,7 @@ from ._lib import (
 
 __all__ = [
     "kvouter_attention",
+    "kvouter_attention_mxfp4",
     "kvouter_attention_noalloc",
     "workspace_bytes",
     "build_index",

@@ -74,6 +74,8 @@ def load():
         lib.msa_kvouter_attention.restype = i32
         lib.msa_kvouter_attention.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
         lib.msa_kvouter_workspace_bytes.restype = i32
+        lib.msa_kvouter_attention_mxfp4.restype = i32
+        lib.msa_kvouter_attention_mxfp4.argtypes = [T, T, T, T, T, T, T, T, T, i32, i32, T, T, vp]
         lib.msa_kvouter_workspace_bytes.argtypes = [T, T, T, T, T, T, T, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
         lib.msa_kvouter_attention_noalloc.restype = i32
         lib.msa_kvouter_attention_noalloc.argtypes = [T, T, T, T, T, T, T, i32, i32, T, T, vp]
@@ -176,6 +178,30 @@ def kvouter_attention(q, k_cache, v_cache, selected, block_tables, *, cu_seqlens
             rc = lib.msa_kvouter_attention_ws(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
                                               _ref(do), _ref(dl), workspace.data_ptr() if nbytes else None,
                                               nbytes, _stream(q.device))
+    _check(rc)
+    return (out, lse) if return_lse else out
+
+
+def kvouter_attention_mxfp4(q, k_codes, k_scales, v_codes, v_scales, selected, block_tables, *, cu_seqlens_q,
+                            used_kv_lens, page_size: int, causal: bool = False, return_lse: bool = False,
+                            out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """msa_kvouter_attention_mxfp4: the pass over MXFP4 caches (uint8 codes
+    ``[NP, Hkv, P, 64]`` and e8m0 scales ``[NP, Hkv, P, 4]``, for K and for
+    V), decode-shaped batches of bf16 queries. Returns ``out`` or
+    ``(out, lse)`` as :func:`kvouter_attention`."""
+    lib = load()
+    _device_check(q, k_codes, k_scales, v_codes, v_scales, selected, block_tables, cu_seqlens_q, used_kv_lens,
+                  out, lse)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    ds = [describe(x) for x in (q, k_codes, k_scales, v_codes, v_scales, selected, block_tables, cu_seqlens_q,
+                                used_kv_lens)]
+    do, dl = describe(out), describe(lse if return_lse or lse is not None else None)
+    with torch.cuda.device(q.device):
+        rc = lib.msa_kvouter_attention_mxfp4(*[_ref(d) for d in ds], int(page_size), int(bool(causal)),
+                                             _ref(do), _ref(dl), _stream(q.device))
     _check(rc)
     return (out, lse) if return_lse else out
 

@@ -562,28 +562,29 @@ int32_t msa_set_workspace_limit(size_t bytes) {
 
 const char* msa_version(void) { return "msa_kvouter 0.1.0 (gfx950)"; }
 
-int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
-                              const msa_tensor* selected, const msa_tensor* block_tables,
-                              const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
-                              int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
-                              void* stream) {
-  Dims d;
-  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
-  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
-                        causal, out, lse, &d);
-  if (rc) return rc;
-  if (d.Tq == 0) return ok();
+// One attention call on the library's workspace, the arguments validated
+// (d). k / v are the caches' descriptors (for MXFP4 caches the codes), with
+// the MXFP4 scales in k_scale / v_scale (else null).
+static int32_t attention_library_ws(const Dims& d, const msa_tensor* q, const msa_tensor* k, const msa_tensor* v,
+                             const uint8_t* k_scale, const uint8_t* v_scale, const msa_tensor* selected,
+                             const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                             const msa_tensor* used_kv_lens, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                             void* stream) {
+  int32_t rc;
   std::lock_guard<std::mutex> lk(g_ws_mutex);  // held through the last launch
   DeviceState* w = nullptr;
   if ((rc = device_state(&w))) return rc;
   const Plan pl = make_plan(d, w->num_cu);
+  if (k_scale && !pl.front_only) return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: decode-shaped batches only");
   msa::Params p{};
   const size_t need = layout(pl.d, nullptr, &p, !pl.front_only, !pl.front_only);
   if ((rc = grow_workspace(*w, need, pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W))) return rc;
   layout(pl.d, (char*)w->ptr, &p, !pl.front_only, !pl.front_only);
   p.slot_pos = nullptr;  // the per-token residual lists replace it here
   fill_inputs(&p, pl.d, selected, block_tables, cu_seqlens_q, used_kv_lens, causal);
-  fill_attention_io(&p, q, k_cache, v_cache, out, lse);
+  fill_attention_io(&p, q, k, v, out, lse);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   int32_t* sets = (int32_t*)w->zs;
   p.counters = sets + w->parity * (kCntSetBytes / 4);
   p.counters_next = sets + (1 - w->parity) * (kCntSetBytes / 4);
@@ -598,6 +599,62 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, co
   w->dirty = false;
   w->parity = 1 - w->parity;
   return ok();
+}
+
+int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,
+                              const msa_tensor* selected, const msa_tensor* block_tables,
+                              const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                              int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                              void* stream) {
+  Dims d;
+  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  int32_t rc = validate(q, k_cache, v_cache, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size,
+                        causal, out, lse, &d);
+  if (rc) return rc;
+  if (d.Tq == 0) return ok();
+  return attention_library_ws(d, q, k_cache, v_cache, nullptr, nullptr, selected, block_tables, cu_seqlens_q,
+                              used_kv_lens, causal, out, lse, stream);
+}
+
+int32_t msa_kvouter_attention_mxfp4(const msa_tensor* q, const msa_tensor* k_codes, const msa_tensor* k_scales,
+                                    const msa_tensor* v_codes, const msa_tensor* v_scales,
+                                    const msa_tensor* selected, const msa_tensor* block_tables,
+                                    const msa_tensor* cu_seqlens_q, const msa_tensor* used_kv_lens,
+                                    int32_t page_size, int32_t causal, msa_tensor* out, msa_tensor* lse,
+                                    void* stream) {
+  if (!out) return fail(MSA_ERR_INVALID_ARGUMENT, "out: null descriptor");
+  int32_t rc;
+  // the code and scale arrays: [num_pages, Hkv, page_size, 64] and [..., 4] bytes
+  if ((rc = check_tensor(k_codes, "k_codes", 4, MSA_UINT8, 16))) return rc;
+  if ((rc = check_tensor(v_codes, "v_codes", 4, MSA_UINT8, 16))) return rc;
+  if ((rc = check_tensor(k_scales, "k_scales", 4, MSA_UINT8, 4))) return rc;
+  if ((rc = check_tensor(v_scales, "v_scales", 4, MSA_UINT8, 4))) return rc;
+  if (k_codes->shape[3] != 64)
+    return fail(MSA_ERR_UNSUPPORTED, "k_codes: %lld bytes a row, only 64 (head dim 128) is supported",
+                (long long)k_codes->shape[3]);
+  for (int i = 0; i < 4; ++i)
+    if (v_codes->shape[i] != k_codes->shape[i]) return fail(MSA_ERR_INVALID_ARGUMENT, "v_codes: shape differs from k_codes");
+  for (int i = 0; i < 3; ++i)
+    if (k_scales->shape[i] != k_codes->shape[i] || v_scales->shape[i] != k_codes->shape[i])
+      return fail(MSA_ERR_INVALID_ARGUMENT, "k_scales / v_scales: pages, heads and rows must match the codes'");
+  if (k_scales->shape[3] != 4 || v_scales->shape[3] != 4)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_scales / v_scales: 4 scales a row expected");
+  // everything else: the common validation, given the caches' page geometry
+  // as one-byte values, 128 a row, at the codes' addresses
+  msa_tensor kg = *k_codes, vg = *v_codes;
+  kg.dtype = vg.dtype = MSA_FP8_E4M3FN;
+  kg.shape[3] = vg.shape[3] = 128;
+  Dims d;
+  if ((rc = validate(q, &kg, &vg, selected, block_tables, cu_seqlens_q, used_kv_lens, page_size, causal, out, lse,
+                     &d)))
+    return rc;
+  if (q->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: q must be bf16");
+  if (d.Tq == 0) return ok();
+  if (d.Tq != d.B || d.G > 64)
+    return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: one query token per sequence slot (Tq == B) and Hq/Hkv <= 64 only");
+  d.kv_elem = msa::kElemFP4;
+  return attention_library_ws(d, q, k_codes, v_codes, (const uint8_t*)k_scales->data, (const uint8_t*)v_scales->data,
+                              selected, block_tables, cu_seqlens_q, used_kv_lens, causal, out, lse, stream);
 }
 
 int32_t msa_kvouter_workspace_bytes(const msa_tensor* q, const msa_tensor* k_cache, const msa_tensor* v_cache,

@@ -33,6 +33,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 struct fp8_e4m3_t {  // storage tag for e4m3fn caches
   uint8_t bits;
 };
+struct mxfp4_t {  // storage tag for MXFP4 caches: e2m1 codes, two a byte, and e8m0 scales
+  uint8_t bits;
+};
 
 // ---------------------------------------------------------------------------
 // MFMA on raw 128-bit fragments, by 16-bit element type
@@ -127,6 +130,24 @@ __device__ __forceinline__ u32x4 widen8(u32x2 v) {
   r[1] = widen2_hi<T>(v[0]);
   r[2] = widen2_lo<T>(v[1]);
   r[3] = widen2_hi<T>(v[1]);
+  return r;
+}
+
+// An e8m0 scale byte b as the float 2^(b - 127) (b = 0: 2^-127, a denormal;
+// b = 255, the format's NaN, is not supported and reads as infinity)
+__device__ __forceinline__ float e8m0_scale(uint32_t b) {
+  return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
+// 8 e2m1 codes (one dword, the code of value 2i in the low nibble of byte i)
+// times scale -> 8 bf16 values (four dwords), exactly while the products are
+// within bf16's range (the conversion instruction scales before rounding)
+__device__ __forceinline__ u32x4 widen_fp4(uint32_t w, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
   return r;
 }
 

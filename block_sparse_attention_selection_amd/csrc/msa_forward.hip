@@ -27,6 +27,8 @@
 // Hopper", section "Summary", widens its fp8 decode operands the same way.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "msa_device.hpp"
 #include "msa_index_dev.hpp"
 #include "msa_internal.hpp"
@@ -191,6 +193,10 @@ template <>
 struct KvElem<fp8_e4m3_t> {
   typedef uint8_t type;
 };
+template <>
+struct KvElem<mxfp4_t> {
+  typedef uint8_t type;
+};
 
 // ---------------------------------------------------------------------------
 // register fragments of one 32-key chunk, loaded straight from HBM. The loads
@@ -211,7 +217,8 @@ template <typename CT>
 struct Frag<CT, CT> {  // 16-bit cache: fragments are used as loaded
   u32x4 ka[2][4];
   u32x4 va[8];
-  __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, int q, int c) {
+  __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, const uint8_t*, const uint8_t*, int q,
+                                       int c) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -230,7 +237,8 @@ template <typename CT>
 struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is used
   u32x4 kr[2][2];
   u32x2 vr[8];
-  __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, int q, int c) {
+  __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const uint8_t*, const uint8_t*, int q,
+                                       int c) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -250,6 +258,53 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
       }
 #pragma unroll
     for (int e = 0; e < 8; ++e) va[e] = widen8<CT>(vr[e]);
+    zero_absent_v(va, key0, lim, q);
+    tile_chunk<CT, RS>(rt, ka, va, key0, lim, seq, q, sl2);
+  }
+};
+
+// MXFP4 cache (OCP microscaling: 32 consecutive values of a row share an
+// e8m0 scale; e2m1 codes two a byte, 64 bytes a row, and 4 scale bytes a
+// row): raw codes and the rows' scale words until the chunk is used, then
+// widened to bf16 with the scale applied. The fragments are those of the
+// 16-bit cache: K row 16 j + c, dims 64 pp + 16 q .. +16 (code bytes 32 pp +
+// 8 q .. +8, scale 2 pp + q / 2); V row key_of(q, e), dims 8 c .. 8 c + 8
+// (code bytes 4 c .. +4, scale c / 4).
+template <typename CT>
+struct Frag<CT, mxfp4_t> {
+  u32x2 kc[2][2];
+  uint32_t ks[2];
+  uint32_t vc[8];
+  uint32_t vs[8];
+  __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const uint8_t* ksb, const uint8_t* vsb,
+                                       int q, int c) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) kc[j][pp] = ld_stream<u32x2>(kb + (16 * j + c) * 64 + 32 * pp + 8 * q);
+      ks[j] = ld_stream<uint32_t>(ksb + (16 * j + c) * 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vc[e] = ld_stream<uint32_t>(vb + key_of(q, e) * 64 + 4 * c);
+      vs[e] = ld_stream<uint32_t>(vsb + key_of(q, e) * 4);
+    }
+  }
+  template <int RS>
+  __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
+    static_assert(sizeof(CT) == 2, "MXFP4 caches widen to bf16");
+    const int c = threadIdx.x & 15;
+    u32x4 ka[2][4], va[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const float sc = e8m0_scale((ks[j] >> (8 * (2 * pp + (q >> 1)))) & 0xFFu);
+        ka[j][2 * pp] = widen_fp4(kc[j][pp][0], sc);
+        ka[j][2 * pp + 1] = widen_fp4(kc[j][pp][1], sc);
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) va[e] = widen_fp4(vc[e], e8m0_scale((vs[e] >> (8 * (c >> 2))) & 0xFFu));
     zero_absent_v(va, key0, lim, q);
     tile_chunk<CT, RS>(rt, ka, va, key0, lim, seq, q, sl2);
   }
@@ -312,26 +367,34 @@ __device__ __forceinline__ void stream_chain(const Params& p, int t, int g, int 
   const E* kbase = (const E*)p.k;
   const E* vbase = (const E*)p.v;
   const E* zero = (const E*)p.zero_page;
+  // element offsets to byte offsets: MXFP4 codes are half a byte a value,
+  // their scales one byte per 32 values
+  constexpr int kCodeShift = std::is_same<KVT, mxfp4_t>::value ? 1 : 0;
   auto kaddr = [&](int ci) -> const E* {
     const int64_t off = ci < nchunks ? s_koff[ci] : (int64_t)-1;
-    return off >= 0 ? kbase + off : zero;
+    return off >= 0 ? kbase + (off >> kCodeShift) : zero;
   };
   auto vaddr = [&](int ci) -> const E* {
     const int64_t off = ci < nchunks ? s_koff[ci] : (int64_t)-1;
-    return off >= 0 ? vbase + off : zero;
+    return off >= 0 ? vbase + (off >> kCodeShift) : zero;
+  };
+  auto saddr = [&](const uint8_t* base, int ci) -> const uint8_t* {
+    if constexpr (!kCodeShift) return nullptr;  // no scales
+    const int64_t off = ci < nchunks ? s_koff[ci] : (int64_t)-1;
+    return off >= 0 ? base + (off >> 5) : (const uint8_t*)p.zero_page;
   };
   auto key0_of = [&](int ci) { return s_koff[ci] >= 0 ? kBlk * s_chain[ci >> 2] + 32 * (ci & 3) : Leff; };
   const int nmine = (nchunks - ph + nph - 1) / nph;
   if (nmine > 0) {
     Frag<CT, KVT> fa, fb;
     int ci = ph;
-    fa.load(kaddr(ci), vaddr(ci), q, c);
+    fa.load(kaddr(ci), vaddr(ci), saddr(p.k_scale, ci), saddr(p.v_scale, ci), q, c);
     for (;;) {
-      fb.load(kaddr(ci + nph), vaddr(ci + nph), q, c);
+      fb.load(kaddr(ci + nph), vaddr(ci + nph), saddr(p.k_scale, ci + nph), saddr(p.v_scale, ci + nph), q, c);
       fa.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
       ci += nph;
       if (ci >= nchunks) break;
-      fa.load(kaddr(ci + nph), vaddr(ci + nph), q, c);
+      fa.load(kaddr(ci + nph), vaddr(ci + nph), saddr(p.k_scale, ci + nph), saddr(p.v_scale, ci + nph), q, c);
       fb.compute(rt, key0_of(ci), Leff, s, q, p.scale_log2);
       ci += nph;
       if (ci >= nchunks) break;
@@ -899,8 +962,9 @@ hipError_t launch_front(const Params& p, int q_elem, int kv_elem, hipStream_t st
   } else if (q_elem < 0 || !p.stream_narrow)
     e = launch_front_t<bf16_t, bf16_t, false>(sp, p, st);
   else if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_front_t<bf16_t, fp8_e4m3_t, true>(sp, p, st)
-                            : launch_front_t<bf16_t, bf16_t, true>(sp, p, st);
+    e = kv_elem == kElemFP8   ? launch_front_t<bf16_t, fp8_e4m3_t, true>(sp, p, st)
+        : kv_elem == kElemFP4 ? launch_front_t<bf16_t, mxfp4_t, true>(sp, p, st)
+                              : launch_front_t<bf16_t, bf16_t, true>(sp, p, st);
   else
     e = kv_elem == kElemFP8 ? launch_front_t<f16_t, fp8_e4m3_t, true>(sp, p, st)
                             : launch_front_t<f16_t, f16_t, true>(sp, p, st);

@@ -27,7 +27,7 @@ enum Counter {
 // a caller-owned workspace is cleared by a fill kernel instead.
 constexpr size_t kZeroPageBytes = 16384;
 
-enum ElemCode { kElemBF16 = 0, kElemF16 = 1, kElemFP8 = 2 };
+enum ElemCode { kElemBF16 = 0, kElemF16 = 1, kElemFP8 = 2, kElemFP4 = 3 };
 
 // tokens of one KV-outer work item (the unit kernel's LDS token list)
 constexpr int kUnitWindowTokens = 512;
@@ -85,6 +85,9 @@ struct Params {
   void* opart;   // normalised O per (residual slot, head) row, in q's 16-bit type, in blocks of
                  // 32 rows: row r's 16-byte chunk k at byte (r >> 5) * 8192 + k * 512 + (r & 31) * 16
   float* lpart;  // [residual slots, G] LSE (log2 units)
+  // MXFP4 caches: e8m0 scales [num_pages, Hkv, P, 4] (else null)
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
 };
 
 // Kernel timing (msa_api.hip), off unless msa_profile_enable set the bit of

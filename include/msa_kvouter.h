@@ -137,6 +137,38 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
                               msa_tensor* out, msa_tensor* lse, void* stream);
 
 /*
+ * msa_kvouter_attention_mxfp4 -- the forward pass over MXFP4 K/V caches.
+ *
+ * The MSA summary page ("Highlighted Details") lists FP4 and NVFP4 among the
+ * kernels' formats without defining a scale format. Read here as the OCP
+ * microscaling format MXFP4: every 32 consecutive values of a K or V row
+ * (dims 32 j .. 32 j + 31) share one e8m0 scale byte s, the value 2^(s - 127)
+ * (s = 255, the format's NaN, is not supported); each value is an e2m1 code
+ * (sign, two exponent bits with bias 1, one mantissa bit: magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6), two codes a byte, value 2 i in the low nibble of byte
+ * i. A cached value is code x scale, exactly.
+ *
+ *   k_codes      [num_pages, Hkv, page_size, 64]  uint8, 16-byte aligned
+ *   k_scales     [num_pages, Hkv, page_size, 4]   uint8 (e8m0), 4-byte aligned
+ *   v_codes, v_scales  the same shapes
+ *   q            [Tq, Hq, 128] bf16
+ *   other arguments as msa_kvouter_attention
+ *
+ * Supported: one query token per sequence slot (Tq == B, the decode step)
+ * and Hq/Hkv <= 64, where the decode kernel finishes every (token, KV head)
+ * alone and widens the codes to bf16 (scale applied) right before the
+ * products; other shapes and fp16 queries return MSA_ERR_UNSUPPORTED. Errors,
+ * preconditions, scratch and threading as msa_kvouter_attention (the
+ * library's workspace; there is no caller-workspace variant).
+ */
+int32_t msa_kvouter_attention_mxfp4(const msa_tensor* q, const msa_tensor* k_codes,
+                                    const msa_tensor* k_scales, const msa_tensor* v_codes,
+                                    const msa_tensor* v_scales, const msa_tensor* selected,
+                                    const msa_tensor* block_tables, const msa_tensor* cu_seqlens_q,
+                                    const msa_tensor* used_kv_lens, int32_t page_size, int32_t causal,
+                                    msa_tensor* out, msa_tensor* lse, void* stream);
+
+/*
  * msa_kvouter_workspace_bytes -- bytes of the caller-owned workspace that
  * msa_kvouter_attention_ws needs for these shapes (the same descriptors as
  * msa_kvouter_attention without out / lse; only shapes and dtypes are read,

@@ -16,6 +16,9 @@ Contents
   * ``index_ref``      -- integer CPU reference of the selection inversion and
                           the work split that the GPU index builder must match
                           bit for bit.
+  * ``mxfp4``          -- exact decoder of MXFP4 caches (e2m1 codes, e8m0
+                          scales per 32 values), the reading of the pages'
+                          FP4; parity unpinned against the pages.
   * ``store_ref``      -- reference of the paged K/V store with its fp8 e4m3fn
                           cast (the step before the pass).
   * ``select_ref``     -- reference of block selection (index-key block scores,

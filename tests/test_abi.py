@@ -117,6 +117,70 @@ def test_invalid_descriptors_are_refused_on_the_host(name, mutate, code):
     assert msg
 
 
+# ---------------------------------------------------------------------------
+# msa_kvouter_attention_mxfp4: host refusals
+# ---------------------------------------------------------------------------
+def good_fp4(Tq=2, Hq=16, Hkv=2, NP=8, P=64, K=4, B=2, MP=4):
+    a = good(Tq=Tq, Hq=Hq, Hkv=Hkv, NP=NP, P=P, K=K, B=B, MP=MP)
+    del a["k"], a["v"]
+    a.update(kc=desc([NP, Hkv, P, 64], msa.MSA_UINT8), ks=desc([NP, Hkv, P, 4], msa.MSA_UINT8),
+             vc=desc([NP, Hkv, P, 64], msa.MSA_UINT8), vs=desc([NP, Hkv, P, 4], msa.MSA_UINT8))
+    return a
+
+
+def call_fp4(a):
+    lib = msa.load()
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    rc = lib.msa_kvouter_attention_mxfp4(r(a["q"]), r(a["kc"]), r(a["ks"]), r(a["vc"]), r(a["vs"]), r(a["sel"]),
+                                         r(a["bt"]), r(a["cu"]), r(a["used"]), a["P"], a["causal"], r(a["out"]),
+                                         r(a["lse"]), None)
+    return rc, lib.msa_last_error().decode()
+
+
+BAD_FP4 = [
+    ("codes dtype", lambda a: a.update(kc=desc([8, 2, 64, 64], msa.MSA_FP8_E4M3FN)), INV),
+    ("codes row bytes", lambda a: a.update(kc=desc([8, 2, 64, 32], msa.MSA_UINT8),
+                                           vc=desc([8, 2, 64, 32], msa.MSA_UINT8)), UNS),
+    ("v codes shape", lambda a: a.update(vc=desc([9, 2, 64, 64], msa.MSA_UINT8)), INV),
+    ("scales per row", lambda a: a.update(ks=desc([8, 2, 64, 8], msa.MSA_UINT8)), INV),
+    ("scales pages", lambda a: a.update(vs=desc([7, 2, 64, 4], msa.MSA_UINT8)), INV),
+    ("misaligned codes", lambda a: a.update(kc=desc([8, 2, 64, 64], msa.MSA_UINT8, data=FAKE + 8)), INV),
+    ("misaligned scales", lambda a: a.update(ks=desc([8, 2, 64, 4], msa.MSA_UINT8, data=FAKE + 2)), INV),
+    ("fp16 q", lambda a: a.update(q=desc([2, 16, 128], msa.MSA_FP16), out=desc([2, 16, 128], msa.MSA_FP16)), UNS),
+    ("prefill shape", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_BF16), sel=desc([4, 2, 4], msa.MSA_INT32),
+                                         out=desc([4, 16, 128], msa.MSA_BF16), lse=desc([16, 4], msa.MSA_FP32)),
+     UNS),
+    ("G 128", lambda a: a.update(q=desc([2, 128, 128], msa.MSA_BF16), kc=desc([8, 1, 64, 64], msa.MSA_UINT8),
+                                 ks=desc([8, 1, 64, 4], msa.MSA_UINT8), vc=desc([8, 1, 64, 64], msa.MSA_UINT8),
+                                 vs=desc([8, 1, 64, 4], msa.MSA_UINT8), sel=desc([2, 1, 4], msa.MSA_INT32),
+                                 out=desc([2, 128, 128], msa.MSA_BF16), lse=desc([128, 2], msa.MSA_FP32)), UNS),
+    ("page size 32", lambda a: a.update(P=32), UNS),
+    ("selected shape", lambda a: a.update(sel=desc([2, 3, 4], msa.MSA_INT32)), INV),
+    ("null scales", lambda a: a.update(vs=None), INV),
+    ("null out", lambda a: a.update(out=None), INV),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", BAD_FP4, ids=[b[0] for b in BAD_FP4])
+def test_mxfp4_descriptors_are_refused_on_the_host(name, mutate, code):
+    a = good_fp4()
+    mutate(a)
+    rc, msg = call_fp4(a)
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_mxfp4_empty_batch_enqueues_nothing():
+    rc, msg = call_fp4(good_fp4(Tq=0, B=0))
+    assert rc == 0, msg
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_mxfp4_no_device_is_an_error_not_a_crash():
+    rc, msg = call_fp4(good_fp4())
+    assert rc == -4 and msg
+
+
 def test_empty_batch_enqueues_nothing():
     a = good(Tq=0)
     rc, msg = call(a)

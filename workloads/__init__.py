@@ -19,11 +19,17 @@ Five named workloads (sizes and pick rules in ``CONFIGS`` below):
                   uniform picks, K/V e4m3fn (clamp to +-448 then cast), q bf16
   decode_mqa      256 seqs x 1 token, Hq=32, Hkv=1 (MQA), otherwise as
                   decode_gqa
+  decode_fp4      decode_fp8's batch with MXFP4 K/V caches (below)
 
 Values are float32 N(0,1) draws converted with torch: bf16 / fp16 by
 round-to-nearest-even ``.to()``, e4m3fn by ``.clamp(-448, 448).to(...)``,
 the cast rule stated in the sglang pull request "Speed up MiniMax-M3 sparse
 attention on Hopper", section "Verification".
+
+MXFP4 caches (``kv_dtype`` torch.uint8) hold, per K or V row, 64 bytes of
+e2m1 codes drawn uniformly (every byte value) and 4 e8m0 scale bytes drawn
+uniformly from MXFP4_SCALES, each from its own seeded stream; the poison of
+such a row is the scale byte 0xFF. Their values are the oracle's to decode.
 
 Only the (physical page, KV head) slices that some pick can touch receive
 drawn values; the rest of the pool is filled on the device (NaN poison for
@@ -40,7 +46,12 @@ import torch
 BLOCK = 128
 HEAD_DIM = 128
 
-_POISON_BITS = {torch.bfloat16: 0x7FC0, torch.float16: 0x7E00, torch.float8_e4m3fn: 0x7F}
+_POISON_BITS = {torch.bfloat16: 0x7FC0, torch.float16: 0x7E00, torch.float8_e4m3fn: 0x7F,
+                torch.float32: 0x7FC00000}
+
+# e8m0 scale bytes of drawn MXFP4 rows (scales 2^-3 .. 2^0), and the poison
+MXFP4_SCALES = (124, 125, 126, 127)
+MXFP4_POISON = 0xFF
 
 CONFIGS = {
     "tiny": dict(seed=1001),
@@ -50,6 +61,7 @@ CONFIGS = {
     "decode_fp8": dict(seed=1005),
     "dense_causal": dict(seed=1006),
     "decode_mqa": dict(seed=1010),
+    "decode_fp4": dict(seed=1011),
 }
 
 
@@ -76,6 +88,12 @@ class Workload:
     v_vals: torch.Tensor
     poison: bool = True
     meta: dict = field(default_factory=dict)
+    k_scales: torch.Tensor | None = None  # MXFP4 caches: [n, page_size, 4] e8m0 bytes
+    v_scales: torch.Tensor | None = None
+
+    @property
+    def mxfp4(self):
+        return self.kv_dtype == torch.uint8
 
     @property
     def B(self):
@@ -105,6 +123,9 @@ def filled(shape, dtype: torch.dtype, poison: bool, device="cpu") -> torch.Tenso
     if dtype == torch.float8_e4m3fn:
         raw = torch.full(shape, _POISON_BITS[dtype] if poison else 0, dtype=torch.uint8, device=device)
         return raw.view(torch.float8_e4m3fn)
+    if dtype == torch.float32:
+        raw = torch.full(shape, _POISON_BITS[dtype] if poison else 0, dtype=torch.int32, device=device)
+        return raw.view(dtype)
     raw = torch.full(shape, _POISON_BITS[dtype] if poison else 0, dtype=torch.int16, device=device)
     return raw.view(dtype)
 
@@ -144,6 +165,20 @@ def _draw_slices(seed, wl_pages, wl_heads, page_size, kv_dtype, poison_rows=None
                 bits[i, first_bad:] = _POISON_BITS[kv_dtype]
         kv.append(out)
     return kv[0], kv[1]
+
+
+def _draw_mxfp4(seed, n, page_size, poison_rows=None):
+    """MXFP4 codes [n, P, 64] and scales [n, P, 4] of K, then of V."""
+    out = []
+    for stream in (4, 5):
+        r = np.random.default_rng([seed, stream])
+        codes = torch.from_numpy(r.integers(0, 256, size=(n, page_size, HEAD_DIM // 2), dtype=np.uint8))
+        scales = torch.from_numpy(r.choice(np.asarray(MXFP4_SCALES, dtype=np.uint8), size=(n, page_size, 4)))
+        if poison_rows is not None:
+            for i, first_bad in poison_rows:
+                scales[i, first_bad:] = MXFP4_POISON
+        out.append((codes, scales))
+    return out
 
 
 def needed_slices(block_tables, used, selected, cu, page_size, Hkv, all_pages=False, num_pages=0):
@@ -196,12 +231,16 @@ def assemble(name, seed, Hq, Hkv, page_size, topk, causal, q_dtype, kv_dtype, cu
     q = to_dtype(qr.standard_normal((Tq, Hq, HEAD_DIM), dtype=np.float32), q_dtype)
     pages, heads = needed_slices(bt, used, selected, cu, page_size, Hkv, all_pages, num_pages)
     prow = _poison_rows(pages, bt, used, page_size) if poison else None
-    kv, vv = _draw_slices(seed, pages, heads, page_size, kv_dtype, prow)
+    ks = vs = None
+    if kv_dtype == torch.uint8:  # MXFP4
+        (kv, ks), (vv, vs) = _draw_mxfp4(seed, len(pages), page_size, prow)
+    else:
+        kv, vv = _draw_slices(seed, pages, heads, page_size, kv_dtype, prow)
     return Workload(name=name, seed=seed, Hq=Hq, Hkv=Hkv, page_size=page_size, topk=topk,
                     causal=causal, q_dtype=q_dtype, kv_dtype=kv_dtype, cu_seqlens_q=cu,
                     used_kv_lens=used, block_tables=bt, selected=selected, num_pages=num_pages,
                     q=q, slice_page=pages, slice_head=heads, k_vals=kv, v_vals=vv,
-                    poison=poison, meta=dict(meta or {}))
+                    poison=poison, meta=dict(meta or {}), k_scales=ks, v_scales=vs)
 
 
 # ----------------------------------------------------------------------------
@@ -302,6 +341,22 @@ def make_decode_fp8(seed=1005, poison=True, batch=256):
                     np.arange(batch + 1), used, bt, sel, NP, poison)
 
 
+def make_decode_fp4(seed=1011, poison=True, batch=256):
+    """decode_fp8's batch (256 seqs x 1 token, L=65536, Hq=64, Hkv=8, page
+    64, top-k 16 uniform picks, causal, q bf16) with MXFP4 K/V caches."""
+    rng = np.random.default_rng(seed)
+    P, Hkv, K, L = 64, 8, 16, 65536
+    used = np.full(batch, L, dtype=np.int32)
+    bt, NP = _page_tables(rng, used, P)
+    nblk = L // BLOCK
+    sel = np.empty((batch, Hkv, K), dtype=np.int32)
+    for s in range(batch):
+        for g in range(Hkv):
+            sel[s, g] = rng.permutation(rng.choice(nblk, size=K, replace=False))
+    return assemble("decode_fp4", seed, 64, Hkv, P, K, True, torch.bfloat16, torch.uint8,
+                    np.arange(batch + 1), used, bt, sel, NP, poison)
+
+
 def make_dense_causal(seed=1006, poison=True, seqlen=8192):
     """Dense causal attention as the case where every visible block is
     selected: 1 sequence, Tq = L = seqlen, Hq 64, Hkv 8, page 128, top-64
@@ -326,6 +381,7 @@ MAKERS = {
     "varlen_mqa": make_varlen_mqa,
     "decode_fp8": make_decode_fp8,
     "dense_causal": make_dense_causal,
+    "decode_fp4": make_decode_fp4,
     "decode_mqa": make_decode_mqa,
 }
 
@@ -399,8 +455,40 @@ def make_custom(seed, tq_per_seq, kv_lens, Hq, Hkv, page_size, topk, causal=Fals
 # ----------------------------------------------------------------------------
 # materialisation
 # ----------------------------------------------------------------------------
+def to_mxfp4(wl: Workload) -> Workload:
+    """The same workload with MXFP4 caches: every drawn slice's K and V rows
+    get fresh MXFP4 draws (seeded by the workload's seed)."""
+    import dataclasses
+
+    prow = _poison_rows(wl.slice_page, wl.block_tables, wl.used_kv_lens, wl.page_size) if wl.poison else None
+    (kc, ks), (vc, vs) = _draw_mxfp4(wl.seed, len(wl.slice_page), wl.page_size, prow)
+    return dataclasses.replace(wl, kv_dtype=torch.uint8, k_vals=kc, v_vals=vc, k_scales=ks, v_scales=vs)
+
+
+def mxfp4_pool(wl: Workload, device="cpu", poison=None):
+    """Full MXFP4 pools on ``device``: codes [num_pages, Hkv, P, 64] and
+    scales [num_pages, Hkv, P, 4] of K, then of V. Slices nobody draws hold
+    code and scale bytes 0xFF (poison) or zeros."""
+    assert wl.mxfp4
+    poison = wl.poison if poison is None else poison
+    fill = MXFP4_POISON if poison else 0
+    out = []
+    for vals, sc in ((wl.k_vals, wl.k_scales), (wl.v_vals, wl.v_scales)):
+        codes = torch.full((wl.num_pages, wl.Hkv, wl.page_size, HEAD_DIM // 2), fill, dtype=torch.uint8,
+                           device=device)
+        scales = torch.full((wl.num_pages, wl.Hkv, wl.page_size, 4), fill, dtype=torch.uint8, device=device)
+        if len(wl.slice_page):
+            pg = torch.from_numpy(wl.slice_page).to(device)
+            hd = torch.from_numpy(wl.slice_head).to(device)
+            codes[pg, hd] = vals.to(device)
+            scales[pg, hd] = sc.to(device)
+        out += [codes, scales]
+    return tuple(out)
+
+
 def kv_pool(wl: Workload, device="cpu", poison=None):
     """Full [num_pages, Hkv, P, 128] K and V pools on ``device``."""
+    assert not wl.mxfp4, "MXFP4 workloads: mxfp4_pool"
     poison = wl.poison if poison is None else poison
     shape = (wl.num_pages, wl.Hkv, wl.page_size, HEAD_DIM)
     k = filled(shape, wl.kv_dtype, poison, device)
@@ -413,8 +501,11 @@ def kv_pool(wl: Workload, device="cpu", poison=None):
     return k, v
 
 
+_BIT_VIEWS = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+
+
 def _bits(x: torch.Tensor) -> torch.Tensor:
-    return x.view(torch.uint8) if x.element_size() == 1 else x.view(torch.int16)
+    return x.view(_BIT_VIEWS[x.element_size()])
 
 
 def compact_cache(wl: Workload, heads=None):
