@@ -48,6 +48,8 @@ DESCRIPTIONS = {
                   "K/V fp8 e4m3fn, q bf16, causal",
     "decode_mqa": "256 seqs x 1 query, Hq=32, Hkv=1 (MQA), d=128, L~U[8192,32768], page 64 shuffled, "
                   "top-16 blocks of 128 (last block forced), causal, bf16",
+    "decode_fp4": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
+                  "K/V MXFP4 (e2m1 codes, e8m0 scale per 32 values), q bf16, causal",
     "dense_causal": "1 seq, Tq=L=8192, Hq=64, Hkv=8, d=128, page 128, every visible block selected "
                     "(top-64), causal, bf16: dense causal attention through the sparse path",
     "kv_store_fp8": "paged K/V store (the step before the pass): 32768 new tokens x Hkv=8 x d=128, "
@@ -67,6 +69,7 @@ SELECT_METRIC = {"select_decode": ("index-key HBM GB/s, block selection (scores 
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
 DOMINANT = {"tiny": ["front"], "decode_gqa": ["front"], "decode_fp8": ["front"], "decode_mqa": ["front"],
+            "decode_fp4": ["front"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
             "dense_causal": ["tiles"], "kv_store_fp8": ["store"], "select_decode": ["select"],
             "select_prefill": ["select"]}
@@ -103,9 +106,10 @@ def accounting(wl):
     uk = np.unique(key[valid])
     ub = uk % nbmax
     us = uk // nbmax // Hkv
-    kv_elem = wl.k_vals.element_size()
+    # bytes of one K (or V) row: 128 values, or MXFP4's 64 code and 4 scale bytes
+    row_bytes = 64 + 4 if wl.mxfp4 else 128 * wl.k_vals.element_size()
     block_tokens = np.minimum(128 * ub + 128, used[us]) - 128 * ub
-    unique_kv = float(block_tokens.sum()) * 128 * 2 * kv_elem
+    unique_kv = float(block_tokens.sum()) * 2 * row_bytes
     q_elem = wl.q.element_size()
     qo = float(Tq * wl.Hq) * (128 * q_elem * 2 + 4)
     return dict(unique_kv_bytes=unique_kv, effective_flops=flops, qo_bytes=qo)
@@ -476,6 +480,25 @@ def bench_select(args, torch, msa):
     print(json.dumps(res), flush=True)
 
 
+def _decoded(wl, g):
+    """The MXFP4 workload's slices of KV head g as exact fp32 values, decoded
+    by the oracle (its caches are then those the oracle's attention reads)."""
+    import dataclasses
+
+    import torch
+    from oracle import mxfp4
+
+    keep = wl.slice_head == g
+    idx = torch.from_numpy(np.nonzero(keep)[0])
+
+    def dec(codes, scales):
+        return torch.from_numpy(mxfp4.dequantize(codes[idx].numpy(), scales[idx].numpy())).float()
+
+    return dataclasses.replace(wl, kv_dtype=torch.float32, slice_page=wl.slice_page[keep],
+                               slice_head=wl.slice_head[keep], k_vals=dec(wl.k_vals, wl.k_scales),
+                               v_vals=dec(wl.v_vals, wl.v_scales), k_scales=None, v_scales=None)
+
+
 def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     """Time the fp64 oracle over a bounded sample of (token, KV head) pairs.
 
@@ -493,7 +516,7 @@ def cpu_baseline(wl, acct, budget_pairs=None, min_seconds=5.0):
     groups = []
     for g in np.unique(pairs % wl.Hkv):
         toks = pairs[pairs % wl.Hkv == g] // wl.Hkv
-        k, v, bt = W.compact_cache(wl, heads=[int(g)])
+        k, v, bt = W.compact_cache(_decoded(wl, int(g)) if wl.mxfp4 else wl, heads=[int(g)])
         q = wl.q[:, g * G:(g + 1) * G, :].contiguous()
         sel = np.ascontiguousarray(wl.selected[:, g:g + 1, :])
         groups.append((q, k, v, sel, bt, toks))
@@ -597,8 +620,11 @@ def main():
     for i in range(2):
         t0 = time.time()
         wl = W.make(args.workload, seed=seed0 + 1000 * i, poison=False)
-        k, v = W.kv_pool(wl, device=dev)
-        d = dict(q=wl.q.to(dev), k=k, v=v, sel=torch.from_numpy(wl.selected).to(dev),
+        if wl.mxfp4:
+            k, ks, v, vs = W.mxfp4_pool(wl, device=dev)
+        else:
+            (k, v), ks, vs = W.kv_pool(wl, device=dev), None, None
+        d = dict(q=wl.q.to(dev), k=k, v=v, ks=ks, vs=vs, sel=torch.from_numpy(wl.selected).to(dev),
                  bt=torch.from_numpy(wl.block_tables).to(dev),
                  cu=torch.from_numpy(wl.cu_seqlens_q).to(dev), used=torch.from_numpy(wl.used_kv_lens).to(dev))
         d["out"] = torch.empty_like(d["q"])
@@ -610,9 +636,14 @@ def main():
 
     def step(i):
         wl, d, _ = batches[i % 2]
-        msa.kvouter_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], cu_seqlens_q=d["cu"],
-                              used_kv_lens=d["used"], page_size=wl.page_size, causal=wl.causal,
-                              return_lse=True, out=d["out"], lse=d["lse"])
+        if wl.mxfp4:
+            msa.kvouter_attention_mxfp4(d["q"], d["k"], d["ks"], d["v"], d["vs"], d["sel"], d["bt"],
+                                        cu_seqlens_q=d["cu"], used_kv_lens=d["used"], page_size=wl.page_size,
+                                        causal=wl.causal, return_lse=True, out=d["out"], lse=d["lse"])
+        else:
+            msa.kvouter_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], cu_seqlens_q=d["cu"],
+                                  used_kv_lens=d["used"], page_size=wl.page_size, causal=wl.causal,
+                                  return_lse=True, out=d["out"], lse=d["lse"])
 
     for i in range(args.warmup):
         step(i)
@@ -703,7 +734,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bfloat16": "bf16", "float16": "fp16"}[str(wl0.q_dtype).split(".")[-1]]
-                 + ("+fp8kv" if wl0.kv_dtype != wl0.q_dtype else ""),
+                 + ("+mxfp4kv" if wl0.mxfp4 else "+fp8kv" if wl0.kv_dtype != wl0.q_dtype else ""),
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",

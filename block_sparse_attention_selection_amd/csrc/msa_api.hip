@@ -627,8 +627,8 @@ int32_t msa_kvouter_attention_mxfp4(const msa_tensor* q, const msa_tensor* k_cod
   // the code and scale arrays: [num_pages, Hkv, page_size, 64] and [..., 4] bytes
   if ((rc = check_tensor(k_codes, "k_codes", 4, MSA_UINT8, 16))) return rc;
   if ((rc = check_tensor(v_codes, "v_codes", 4, MSA_UINT8, 16))) return rc;
-  if ((rc = check_tensor(k_scales, "k_scales", 4, MSA_UINT8, 4))) return rc;
-  if ((rc = check_tensor(v_scales, "v_scales", 4, MSA_UINT8, 4))) return rc;
+  if ((rc = check_tensor(k_scales, "k_scales", 4, MSA_UINT8, 16))) return rc;
+  if ((rc = check_tensor(v_scales, "v_scales", 4, MSA_UINT8, 16))) return rc;
   if (k_codes->shape[3] != 64)
     return fail(MSA_ERR_UNSUPPORTED, "k_codes: %lld bytes a row, only 64 (head dim 128) is supported",
                 (long long)k_codes->shape[3]);

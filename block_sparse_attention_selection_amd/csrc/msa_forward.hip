@@ -269,13 +269,15 @@ struct Frag<CT, fp8_e4m3_t> {  // e4m3fn cache: raw bytes until the chunk is use
 // widened to bf16 with the scale applied. The fragments are those of the
 // 16-bit cache: K row 16 j + c, dims 64 pp + 16 q .. +16 (code bytes 32 pp +
 // 8 q .. +8, scale 2 pp + q / 2); V row key_of(q, e), dims 8 c .. 8 c + 8
-// (code bytes 4 c .. +4, scale c / 4).
+// (code bytes 4 c .. +4, scale c / 4). The V rows of lane group q are rows
+// 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3, so their scale words come in
+// two 16-byte loads.
 template <typename CT>
 struct Frag<CT, mxfp4_t> {
   u32x2 kc[2][2];
   uint32_t ks[2];
   uint32_t vc[8];
-  uint32_t vs[8];
+  u32x4 vs[2];
   __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const uint8_t* ksb, const uint8_t* vsb,
                                        int q, int c) {
 #pragma unroll
@@ -285,10 +287,9 @@ struct Frag<CT, mxfp4_t> {
       ks[j] = ld_stream<uint32_t>(ksb + (16 * j + c) * 4);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      vc[e] = ld_stream<uint32_t>(vb + key_of(q, e) * 64 + 4 * c);
-      vs[e] = ld_stream<uint32_t>(vsb + key_of(q, e) * 4);
-    }
+    for (int e = 0; e < 8; ++e) vc[e] = ld_stream<uint32_t>(vb + key_of(q, e) * 64 + 4 * c);
+    vs[0] = ld_stream<u32x4>(vsb + key_of(q, 0) * 4);
+    vs[1] = ld_stream<u32x4>(vsb + key_of(q, 4) * 4);
   }
   template <int RS>
   __device__ __forceinline__ void compute(RowTile<CT> (&rt)[RS], int key0, int lim, int seq, int q, float sl2) {
@@ -304,7 +305,7 @@ struct Frag<CT, mxfp4_t> {
         ka[j][2 * pp + 1] = widen_fp4(kc[j][pp][1], sc);
       }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) va[e] = widen_fp4(vc[e], e8m0_scale((vs[e] >> (8 * (c >> 2))) & 0xFFu));
+    for (int e = 0; e < 8; ++e) va[e] = widen_fp4(vc[e], e8m0_scale((vs[e >> 2][e & 3] >> (8 * (c >> 2))) & 0xFFu));
     zero_absent_v(va, key0, lim, q);
     tile_chunk<CT, RS>(rt, ka, va, key0, lim, seq, q, sl2);
   }

@@ -149,7 +149,7 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  * i. A cached value is code x scale, exactly.
  *
  *   k_codes      [num_pages, Hkv, page_size, 64]  uint8, 16-byte aligned
- *   k_scales     [num_pages, Hkv, page_size, 4]   uint8 (e8m0), 4-byte aligned
+ *   k_scales     [num_pages, Hkv, page_size, 4]   uint8 (e8m0), 16-byte aligned
  *   v_codes, v_scales  the same shapes
  *   q            [Tq, Hq, 128] bf16
  *   other arguments as msa_kvouter_attention

@@ -145,7 +145,7 @@ BAD_FP4 = [
     ("scales per row", lambda a: a.update(ks=desc([8, 2, 64, 8], msa.MSA_UINT8)), INV),
     ("scales pages", lambda a: a.update(vs=desc([7, 2, 64, 4], msa.MSA_UINT8)), INV),
     ("misaligned codes", lambda a: a.update(kc=desc([8, 2, 64, 64], msa.MSA_UINT8, data=FAKE + 8)), INV),
-    ("misaligned scales", lambda a: a.update(ks=desc([8, 2, 64, 4], msa.MSA_UINT8, data=FAKE + 2)), INV),
+    ("misaligned scales", lambda a: a.update(ks=desc([8, 2, 64, 4], msa.MSA_UINT8, data=FAKE + 4)), INV),
     ("fp16 q", lambda a: a.update(q=desc([2, 16, 128], msa.MSA_FP16), out=desc([2, 16, 128], msa.MSA_FP16)), UNS),
     ("prefill shape", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_BF16), sel=desc([4, 2, 4], msa.MSA_INT32),
                                          out=desc([4, 16, 128], msa.MSA_BF16), lse=desc([16, 4], msa.MSA_FP32)),
