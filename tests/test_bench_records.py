@@ -79,3 +79,27 @@ def test_micro_rejects_an_unknown_measurement_before_touching_the_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "unknown measurement nonesuch" in r.stderr
+
+
+def test_unique_kv_bytes_count_mxfp4_rows_at_68_bytes():
+    # the bench's algorithmic bytes against a direct count: every distinct
+    # (sequence, KV head, block) a valid pick reads, its keys below the used
+    # length, times 2 (K and V) x the bytes of a row
+    import numpy as np
+
+    import workloads as W
+
+    wl = W.make_custom(5, [1] * 6, [900, 2000, 700, 1500, 64, 129], 16, 2, 64, 6, causal=True)
+    seen = set()
+    for t in range(wl.Tq):
+        s = int(np.searchsorted(wl.cu_seqlens_q, t, side="right") - 1)
+        L = int(wl.used_kv_lens[s])
+        pos = L - 1  # one token per sequence: the last position
+        for g in range(wl.Hkv):
+            for b in wl.selected[t, g]:
+                b = int(b)
+                if 0 <= b < (L + 127) // 128 and 128 * b <= pos:
+                    seen.add((s, g, b, min(128, L - 128 * b)))
+    keys = sum(n for (_, _, _, n) in seen)
+    assert bench.accounting(wl)["unique_kv_bytes"] == keys * 2 * 128 * 2          # bf16 rows
+    assert bench.accounting(W.to_mxfp4(wl))["unique_kv_bytes"] == keys * 2 * 68   # 64 code + 4 scale bytes
