@@ -50,6 +50,8 @@ DESCRIPTIONS = {
                   "top-16 blocks of 128 (last block forced), causal, bf16",
     "decode_fp4": "256 seqs x 1 query, L=65536, Hq=64, Hkv=8, d=128, page 64, top-16 uniform, "
                   "K/V MXFP4 (e2m1 codes, e8m0 scale per 32 values), q bf16, causal",
+    "prefill_fp4": "1 seq, Tq=L=16384, Hq=64, Hkv=8, d=128, page 128, top-16; chunks of 64 queries "
+                   "share 12 picks, diagonal forced, causal, q bf16, K/V MXFP4",
     "dense_causal": "1 seq, Tq=L=8192, Hq=64, Hkv=8, d=128, page 128, every visible block selected "
                     "(top-64), causal, bf16: dense causal attention through the sparse path",
     "kv_store_fp8": "paged K/V store (the step before the pass): 32768 new tokens x Hkv=8 x d=128, "
@@ -69,7 +71,7 @@ SELECT_METRIC = {"select_decode": ("index-key HBM GB/s, block selection (scores 
 # the KV-outer unit kernel and the tile kernel (chains plus the LSE merge),
 # so the two are timed together.
 DOMINANT = {"tiny": ["front"], "decode_gqa": ["front"], "decode_fp8": ["front"], "decode_mqa": ["front"],
-            "decode_fp4": ["front"],
+            "decode_fp4": ["front"], "prefill_fp4": ["units", "tiles"],
             "prefill_shared": ["units", "tiles"], "varlen_mqa": ["units", "tiles"],
             "dense_causal": ["tiles"], "kv_store_fp8": ["store"], "select_decode": ["select"],
             "select_prefill": ["select"]}

@@ -575,7 +575,6 @@ static int32_t attention_library_ws(const Dims& d, const msa_tensor* q, const ms
   DeviceState* w = nullptr;
   if ((rc = device_state(&w))) return rc;
   const Plan pl = make_plan(d, w->num_cu);
-  if (k_scale && !pl.front_only) return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: decode-shaped batches only");
   msa::Params p{};
   const size_t need = layout(pl.d, nullptr, &p, !pl.front_only, !pl.front_only);
   if ((rc = grow_workspace(*w, need, pl.front_only ? 0 : (size_t)pl.d.NR * pl.d.W))) return rc;
@@ -650,8 +649,6 @@ int32_t msa_kvouter_attention_mxfp4(const msa_tensor* q, const msa_tensor* k_cod
     return rc;
   if (q->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: q must be bf16");
   if (d.Tq == 0) return ok();
-  if (d.Tq != d.B || d.G > 64)
-    return fail(MSA_ERR_UNSUPPORTED, "MXFP4 caches: one query token per sequence slot (Tq == B) and Hq/Hkv <= 64 only");
   d.kv_elem = msa::kElemFP4;
   return attention_library_ws(d, q, k_codes, v_codes, (const uint8_t*)k_scales->data, (const uint8_t*)v_scales->data,
                               selected, block_tables, cu_seqlens_q, used_kv_lens, causal, out, lse, stream);

@@ -40,6 +40,8 @@
 // transposing V reads conflict-light.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "msa_device.hpp"
 #include "msa_index_dev.hpp"
 #include "msa_internal.hpp"
@@ -652,6 +654,41 @@ __device__ __forceinline__ void store_chunk8(const Raw8& r, u32x4* sK, u32x4* sV
   sV[pieceV(row, 2 * lc + 1)] = widen8<CT>(u32x2{r.v[2], r.v[3]});
 }
 
+// MXFP4 caches: each thread loads the 8 code bytes of the same 16 dims of
+// one key row and the row's scale word, then widens them (the scale of dims
+// 16 lc .. 16 lc + 15 is byte lc / 2) into the same two swizzled pieces.
+// off is the chunk's element offset: its codes start at off / 2 bytes, its
+// scales at off / 32.
+struct Raw4 {
+  u32x2 k, v;
+  uint32_t ks, vs;
+};
+
+__device__ __forceinline__ Raw4 load_chunk4(const Params& p, int64_t off, int nrows) {
+  const int row = threadIdx.x >> 3, lc = threadIdx.x & 7;
+  const bool ok = off >= 0 && row < nrows;
+  const int64_t ec = (off >> 1) + (int64_t)row * 64 + 8 * lc, es = (off >> 5) + (int64_t)row * 4;
+  const char* zero = (const char*)p.zero_page + 8 * (threadIdx.x & 63);
+  Raw4 r;
+  r.k = ok ? *(const u32x2*)((const uint8_t*)p.k + ec) : *(const u32x2*)zero;
+  r.v = ok ? *(const u32x2*)((const uint8_t*)p.v + ec) : *(const u32x2*)zero;
+  r.ks = ok ? *(const uint32_t*)(p.k_scale + es) : 0u;  // absent rows: zero codes
+  r.vs = ok ? *(const uint32_t*)(p.v_scale + es) : 0u;
+  return r;
+}
+
+template <typename CT>
+__device__ __forceinline__ void store_chunk4(const Raw4& r, u32x4* sK, u32x4* sV) {
+  static_assert(std::is_same<CT, bf16_t>::value, "MXFP4 caches widen to bf16");
+  const int row = threadIdx.x >> 3, lc = threadIdx.x & 7;
+  const uint32_t sh = 8 * (lc >> 1);
+  const float sk = e8m0_scale((r.ks >> sh) & 0xFFu), sv = e8m0_scale((r.vs >> sh) & 0xFFu);
+  sK[pieceK(row, 2 * lc)] = widen_fp4(r.k[0], sk);
+  sK[pieceK(row, 2 * lc + 1)] = widen_fp4(r.k[1], sk);
+  sV[pieceV(row, 2 * lc)] = widen_fp4(r.v[0], sv);
+  sV[pieceV(row, 2 * lc + 1)] = widen_fp4(r.v[1], sv);
+}
+
 // ---------------------------------------------------------------------------
 // Tokens with ranks [rank0, rank0 + n) among the set bits of row r (one
 // wave): the word holding rank0 is found by two rounds of sampled loads of
@@ -803,7 +840,8 @@ __device__ __forceinline__ void issue_chunk16_256(const void* kb, const void* vb
 
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(256, 2) void k_units(Params p) {
-  constexpr bool kFp8 = sizeof(KVT) == 1;
+  constexpr bool kFp8 = sizeof(KVT) == 1;  // e4m3fn or MXFP4: staged through registers
+  constexpr bool kFp4 = std::is_same<KVT, mxfp4_t>::value;
   __shared__ u32x4 s_blk[kRing * kSlotU4];  // the staged block: chunk q at q * kSlotU4 (K), + kChunkU4 (V)
   __shared__ int s_tok[2][kUnitWindow];     // token lists of two consecutive windows
   __shared__ int s_seq[2][kUnitWindow];
@@ -935,7 +973,13 @@ __global__ __launch_bounds__(256, 2) void k_units(Params p) {
     st_absent = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) st_absent |= offs[q] < 0 ? 1u << q : 0u;
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      Raw4 raw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) raw[q] = load_chunk4(p, offs[q], Leff - (kBlk * b + 32 * q));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_chunk4<CT>(raw[q], s_blk + q * kSlotU4, s_blk + q * kSlotU4 + kChunkU4);
+    } else if constexpr (kFp8) {
       Raw8 raw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -1174,7 +1218,21 @@ __device__ __forceinline__ void dma4(i32x4v rsrc, uint32_t lds, int voff) {
 
 template <typename CT, typename KVT>
 __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
-  constexpr bool kFp8 = sizeof(KVT) == 1;
+  constexpr bool kFp8 = sizeof(KVT) == 1;  // e4m3fn or MXFP4: staged through registers
+  constexpr bool kFp4 = std::is_same<KVT, mxfp4_t>::value;
+  using RawT = typename std::conditional<kFp4, Raw4, Raw8>::type;
+  auto ld_raw = [&](int64_t off, int nr) -> RawT {
+    if constexpr (kFp4)
+      return load_chunk4(p, off, nr);
+    else
+      return load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
+  };
+  auto st_raw = [&](const RawT& r, u32x4* sK, u32x4* sV) {
+    if constexpr (kFp4)
+      store_chunk4<CT>(r, sK, sV);
+    else
+      store_chunk8<CT>(r, sK, sV);
+  };
   __shared__ __attribute__((aligned(256))) u32x4 s_ring[kRingT * kSlotU4];
   __shared__ int4 s_tab[2][kTabMax];  // chunk tables of the current and the next item
   __shared__ int4 s_desc[2][2];       // their descriptors
@@ -1305,15 +1363,15 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
         int nr;
         const bool stager = tid < 256;  // 32 rows x 8 pieces of K and of V
         chunk_of(bf, 0, nck, off, nr);
-        Raw8 raw{};
+        RawT raw{};
         if (stager) {
-          raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
-          store_chunk8<CT>(raw, s_ring, s_ring + kChunkU4);
+          raw = ld_raw(off, nr);
+          st_raw(raw, s_ring, s_ring + kChunkU4);
         }
         __syncthreads();
         for (int ci = 0; ci < nck; ++ci) {
           chunk_of(bf, ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
-          if (stager) raw = load_chunk8((const uint8_t*)p.k, (const uint8_t*)p.v, off, nr, p.zero_page);
+          if (stager) raw = ld_raw(off, nr);
           const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
           const int4 e = s_tab[bf][ci];
           if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
@@ -1322,7 +1380,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
             rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, e.z + e.w, s, !full, p.scale_log2);
           }
           if (stager && ci + 1 < nck)
-            store_chunk8<CT>(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+            st_raw(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
           __syncthreads();
         }
       } else {
@@ -1554,8 +1612,9 @@ hipError_t launch_units(const Params& p, int q_elem, int kv_elem, int num_cu, hi
   const ProfSpan sp = profile_begin(kKUnits);
   hipError_t e;
   if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_units_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
-                            : launch_units_t<bf16_t, bf16_t>(sp, p, num_cu, st);
+    e = kv_elem == kElemFP8   ? launch_units_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+        : kv_elem == kElemFP4 ? launch_units_t<bf16_t, mxfp4_t>(sp, p, num_cu, st)
+                              : launch_units_t<bf16_t, bf16_t>(sp, p, num_cu, st);
   else
     e = kv_elem == kElemFP8 ? launch_units_t<f16_t, fp8_e4m3_t>(sp, p, num_cu, st)
                             : launch_units_t<f16_t, f16_t>(sp, p, num_cu, st);
@@ -1567,8 +1626,9 @@ hipError_t launch_tiles(const Params& p, int q_elem, int kv_elem, int num_cu, hi
   const ProfSpan sp = profile_begin(kKTiles);
   hipError_t e;
   if (q_elem == kElemBF16)
-    e = kv_elem == kElemFP8 ? launch_tiles_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
-                            : launch_tiles_t<bf16_t, bf16_t>(sp, p, num_cu, st);
+    e = kv_elem == kElemFP8   ? launch_tiles_t<bf16_t, fp8_e4m3_t>(sp, p, num_cu, st)
+        : kv_elem == kElemFP4 ? launch_tiles_t<bf16_t, mxfp4_t>(sp, p, num_cu, st)
+                              : launch_tiles_t<bf16_t, bf16_t>(sp, p, num_cu, st);
   else
     e = kv_elem == kElemFP8 ? launch_tiles_t<f16_t, fp8_e4m3_t>(sp, p, num_cu, st)
                             : launch_tiles_t<f16_t, f16_t>(sp, p, num_cu, st);

@@ -154,12 +154,12 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  *   q            [Tq, Hq, 128] bf16
  *   other arguments as msa_kvouter_attention
  *
- * Supported: one query token per sequence slot (Tq == B, the decode step)
- * and Hq/Hkv <= 64, where the decode kernel finishes every (token, KV head)
- * alone and widens the codes to bf16 (scale applied) right before the
- * products; other shapes and fp16 queries return MSA_ERR_UNSUPPORTED. Errors,
- * preconditions, scratch and threading as msa_kvouter_attention (the
- * library's workspace; there is no caller-workspace variant).
+ * Every shape msa_kvouter_attention accepts, with bf16 queries (fp16
+ * queries return MSA_ERR_UNSUPPORTED). The codes are widened to bf16, scale
+ * applied, right before the products: in registers by the decode kernel, on
+ * their way into LDS by the KV-outer and tile kernels. Errors, preconditions,
+ * scratch and threading as msa_kvouter_attention (the library's workspace;
+ * there is no caller-workspace variant).
  */
 int32_t msa_kvouter_attention_mxfp4(const msa_tensor* q, const msa_tensor* k_codes,
                                     const msa_tensor* k_scales, const msa_tensor* v_codes,

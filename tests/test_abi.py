@@ -147,13 +147,6 @@ BAD_FP4 = [
     ("misaligned codes", lambda a: a.update(kc=desc([8, 2, 64, 64], msa.MSA_UINT8, data=FAKE + 8)), INV),
     ("misaligned scales", lambda a: a.update(ks=desc([8, 2, 64, 4], msa.MSA_UINT8, data=FAKE + 4)), INV),
     ("fp16 q", lambda a: a.update(q=desc([2, 16, 128], msa.MSA_FP16), out=desc([2, 16, 128], msa.MSA_FP16)), UNS),
-    ("prefill shape", lambda a: a.update(q=desc([4, 16, 128], msa.MSA_BF16), sel=desc([4, 2, 4], msa.MSA_INT32),
-                                         out=desc([4, 16, 128], msa.MSA_BF16), lse=desc([16, 4], msa.MSA_FP32)),
-     UNS),
-    ("G 128", lambda a: a.update(q=desc([2, 128, 128], msa.MSA_BF16), kc=desc([8, 1, 64, 64], msa.MSA_UINT8),
-                                 ks=desc([8, 1, 64, 4], msa.MSA_UINT8), vc=desc([8, 1, 64, 64], msa.MSA_UINT8),
-                                 vs=desc([8, 1, 64, 4], msa.MSA_UINT8), sel=desc([2, 1, 4], msa.MSA_INT32),
-                                 out=desc([2, 128, 128], msa.MSA_BF16), lse=desc([128, 2], msa.MSA_FP32)), UNS),
     ("page size 32", lambda a: a.update(P=32), UNS),
     ("selected shape", lambda a: a.update(sel=desc([2, 3, 4], msa.MSA_INT32)), INV),
     ("null scales", lambda a: a.update(vs=None), INV),

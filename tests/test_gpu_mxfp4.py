@@ -102,10 +102,34 @@ def test_mxfp4_zero_pool_outside_the_drawn_slices():
     compare(wl, out, lse, pairs, ref_o, ref_l)
 
 
-def test_mxfp4_refuses_a_prefill_batch():
+PREFILL = {
+    # name: make_custom arguments
+    "shared_chunks_with_residuals": dict(tq=[40, 30], lens=[3000, 2000], Hq=16, Hkv=2, P=128, K=8, pick="diag",
+                                         shared_chunk=8, shared_picks=4),
+    "varlen_mqa_like": dict(tq=[37, 5, 60], lens=[2500, 700, 4000], Hq=32, Hkv=1, P=128, K=8, pick="diag"),
+    "page64_non_causal": dict(tq=[20, 12], lens=[1500, 900], Hq=16, Hkv=2, P=64, K=6, pick="random", causal=False),
+    "one_token_tiles_g128": dict(tq=[1, 1, 1], lens=[2000, 700, 3100], Hq=128, Hkv=1, P=64, K=6, pick="random"),
+    "decode_shaped_with_residuals": dict(tq=[2] * 160, lens=[300 + 37 * i for i in range(160)], Hq=16, Hkv=2, P=64,
+                                         K=6, pick="random"),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_parity_mxfp4_unit_and_tile_paths(name):
+    a = dict(PREFILL[name])
+    wl = W.to_mxfp4(W.make_custom(3030 + len(name), a.pop("tq"), a.pop("lens"), a.pop("Hq"), a.pop("Hkv"), a.pop("P"),
+                                  a.pop("K"), causal=a.pop("causal", True), **a))
+    out, lse = _run(wl)
+    pairs = all_pairs(wl)
+    ref_o, ref_l = oracle_pairs(_reference(wl), pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+
+
+def test_mxfp4_refuses_fp16_queries():
     import block_sparse_attention_selection_amd as msa
 
-    wl = W.to_mxfp4(W.make_custom(78, [3, 2], [700, 900], 16, 2, 64, 4, causal=True))
+    wl = W.to_mxfp4(W.make_custom(78, [1, 1], [700, 900], 16, 2, 64, 4, causal=True))
+    wl.q = wl.q.to(torch.float16)
     with pytest.raises(msa.MsaError) as e:
         _run(wl)
     assert e.value.code == -2

@@ -20,6 +20,7 @@ Five named workloads (sizes and pick rules in ``CONFIGS`` below):
   decode_mqa      256 seqs x 1 token, Hq=32, Hkv=1 (MQA), otherwise as
                   decode_gqa
   decode_fp4      decode_fp8's batch with MXFP4 K/V caches (below)
+  prefill_fp4     prefill_shared's recipe with MXFP4 K/V caches
 
 Values are float32 N(0,1) draws converted with torch: bf16 / fp16 by
 round-to-nearest-even ``.to()``, e4m3fn by ``.clamp(-448, 448).to(...)``,
@@ -62,6 +63,7 @@ CONFIGS = {
     "dense_causal": dict(seed=1006),
     "decode_mqa": dict(seed=1010),
     "decode_fp4": dict(seed=1011),
+    "prefill_fp4": dict(seed=1012),
 }
 
 
@@ -357,6 +359,13 @@ def make_decode_fp4(seed=1011, poison=True, batch=256):
                     np.arange(batch + 1), used, bt, sel, NP, poison)
 
 
+def make_prefill_fp4(seed=1012, poison=True):
+    """prefill_shared's recipe (seed 1012) with MXFP4 K/V caches."""
+    wl = to_mxfp4(make_prefill_shared(seed=seed, poison=poison))
+    wl.name = "prefill_fp4"
+    return wl
+
+
 def make_dense_causal(seed=1006, poison=True, seqlen=8192):
     """Dense causal attention as the case where every visible block is
     selected: 1 sequence, Tq = L = seqlen, Hq 64, Hkv 8, page 128, top-64
@@ -382,6 +391,7 @@ MAKERS = {
     "decode_fp8": make_decode_fp8,
     "dense_causal": make_dense_causal,
     "decode_fp4": make_decode_fp4,
+    "prefill_fp4": make_prefill_fp4,
     "decode_mqa": make_decode_mqa,
 }
 
