@@ -43,13 +43,14 @@ def _reference(wl, heads=None):
                                v_vals=dec(wl.v_vals, wl.v_scales), k_scales=None, v_scales=None)
 
 
-def _run(wl, poison=None):
+def _run(wl, poison=None, block_tables=None):
     import block_sparse_attention_selection_amd as msa
 
     kc, ks, vc, vs = W.mxfp4_pool(wl, "cuda", poison)
     dev = lambda a: torch.from_numpy(a).cuda()
+    bt = wl.block_tables if block_tables is None else block_tables
     out, lse = msa.kvouter_attention_mxfp4(
-        wl.q.cuda(), kc, ks, vc, vs, dev(wl.selected), dev(wl.block_tables), cu_seqlens_q=dev(wl.cu_seqlens_q),
+        wl.q.cuda(), kc, ks, vc, vs, dev(wl.selected), dev(bt), cu_seqlens_q=dev(wl.cu_seqlens_q),
         used_kv_lens=dev(wl.used_kv_lens), page_size=wl.page_size, causal=wl.causal, return_lse=True)
     torch.cuda.synchronize()
     return out, lse
@@ -122,6 +123,41 @@ def test_parity_mxfp4_unit_and_tile_paths(name):
     out, lse = _run(wl)
     pairs = all_pairs(wl)
     ref_o, ref_l = oracle_pairs(_reference(wl), pairs)
+    compare(wl, out, lse, pairs, ref_o, ref_l)
+
+
+# Page ids outside the pool (past its end, or negative) hold no keys: the
+# same result as the oracle with the picks of those blocks removed.
+PAGE_CASES = {
+    "decode": dict(tq=[1] * 8, lens=[900, 2000, 700, 1500, 1300, 640, 2500, 1100], Hq=16, Hkv=2, P=128, K=6,
+                   pick="random"),
+    "tiles": dict(tq=[40, 30], lens=[3000, 2000], Hq=16, Hkv=2, P=64, K=8, pick="diag", shared_chunk=16,
+                  shared_picks=4),
+}
+
+
+@pytest.mark.parametrize("name", list(PAGE_CASES))
+def test_mxfp4_pages_outside_the_pool_hold_no_keys(name):
+    a = dict(PAGE_CASES[name])
+    wl = W.to_mxfp4(W.make_custom(690 + len(name), a.pop("tq"), a.pop("lens"), a.pop("Hq"), a.pop("Hkv"),
+                                  a.pop("P"), a.pop("K"), causal=True, **a))
+    bt = wl.block_tables.copy()
+    sel_ref = wl.selected.copy()
+    cu = wl.cu_seqlens_q
+    ppb = 128 // wl.page_size
+    for s in range(wl.B):
+        picks = wl.selected[cu[s]:cu[s + 1]]
+        nblk = -(-int(wl.used_kv_lens[s]) // 128)
+        valid = picks[(picks >= 0) & (picks < nblk)]
+        if valid.size == 0:
+            continue
+        b = int(np.bincount(valid).argmax())  # the block most tokens of s picked
+        for lp in range(b * ppb, min((b + 1) * ppb, bt.shape[1])):
+            bt[s, lp] = wl.num_pages + 3 if s % 2 == 0 else -2
+        sel_ref[cu[s]:cu[s + 1]][picks == b] = -1
+    out, lse = _run(wl, block_tables=bt)
+    pairs = all_pairs(wl)
+    ref_o, ref_l = oracle_pairs(_reference(dataclasses.replace(wl, selected=sel_ref)), pairs)
     compare(wl, out, lse, pairs, ref_o, ref_l)
 
 
