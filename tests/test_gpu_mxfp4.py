@@ -169,3 +169,19 @@ def test_mxfp4_refuses_fp16_queries():
     with pytest.raises(msa.MsaError) as e:
         _run(wl)
     assert e.value.code == -2
+
+
+@pytest.mark.parametrize("name", ["gqa_page64_causal", "shared_chunks_with_residuals"])
+def test_mxfp4_deterministic_bits(name):
+    if name in CASES:
+        tq, lens, Hq, Hkv, P, K, causal, pick, pad = CASES[name]
+        wl = W.to_mxfp4(W.make_custom(2024 + len(name), tq, lens, Hq, Hkv, P, K, causal=causal, pick=pick,
+                                      pad_every=pad))
+    else:
+        a = dict(PREFILL[name])
+        wl = W.to_mxfp4(W.make_custom(3030 + len(name), a.pop("tq"), a.pop("lens"), a.pop("Hq"), a.pop("Hkv"),
+                                      a.pop("P"), a.pop("K"), causal=a.pop("causal", True), **a))
+    o1, l1 = _run(wl)
+    o2, l2 = _run(wl)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
