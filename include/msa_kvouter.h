@@ -143,7 +143,8 @@ int32_t msa_kvouter_attention(const msa_tensor* q, const msa_tensor* k_cache,
  * kernels' formats without defining a scale format. Read here as the OCP
  * microscaling format MXFP4: every 32 consecutive values of a K or V row
  * (dims 32 j .. 32 j + 31) share one e8m0 scale byte s, the value 2^(s - 127)
- * (s = 255, the format's NaN, is not supported); each value is an e2m1 code
+ * (s = 255, the format's NaN, is not supported, nor are s > 252, whose
+ * largest values overflow the bf16 the kernels widen to); each value is an e2m1 code
  * (sign, two exponent bits with bias 1, one mantissa bit: magnitudes 0, 0.5,
  * 1, 1.5, 2, 3, 4, 6), two codes a byte, value 2 i in the low nibble of byte
  * i. A cached value is code x scale, exactly.
