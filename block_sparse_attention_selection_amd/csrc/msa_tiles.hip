@@ -1368,20 +1368,48 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_tiles(Params p) {
           raw = ld_raw(off, nr);
           st_raw(raw, s_ring, s_ring + kChunkU4);
         }
-        __syncthreads();
-        for (int ci = 0; ci < nck; ++ci) {
-          chunk_of(bf, ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
-          if (stager) raw = ld_raw(off, nr);
-          const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
-          const int4 e = s_tab[bf][ci];
-          if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
-            // keys [e.z, e.z + e.w) are present (e.w < 32 only at the used length)
-            const bool full = e.w == 32 && e.z + 31 <= pmin;
-            rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, e.z + e.w, s, !full, p.scale_log2);
-          }
-          if (stager && ci + 1 < nck)
-            st_raw(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+        if constexpr (kFp4) {
+          // MXFP4 chunks are 6 registers of raw bytes a thread: two are kept
+          // in flight (chunk ci+1 in one set, ci+2 loading into the other,
+          // the sets swapping roles every chunk; a set is loaded again only
+          // after its chunk went to LDS)
+          RawT rb{};
+          chunk_of(bf, 1 < nck ? 1 : 0, nck, off, nr);
+          if (stager) rb = ld_raw(off, nr);
           __syncthreads();
+          auto step = [&](int ci, const RawT& next, RawT& after) {
+            chunk_of(bf, ci + 2 < nck ? ci + 2 : ci, nck, off, nr);
+            if (stager) after = ld_raw(off, nr);
+            const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
+            const int4 e = s_tab[bf][ci];
+            if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
+              const bool full = e.w == 32 && e.z + 31 <= pmin;
+              rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, e.z + e.w, s, !full, p.scale_log2);
+            }
+            if (stager && ci + 1 < nck)
+              st_raw(next, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+            __syncthreads();
+          };
+          for (int ci = 0; ci < nck; ci += 2) {
+            step(ci, rb, raw);
+            if (ci + 1 < nck) step(ci + 1, raw, rb);
+          }
+        } else {
+          __syncthreads();
+          for (int ci = 0; ci < nck; ++ci) {
+            chunk_of(bf, ci + 1 < nck ? ci + 1 : ci, nck, off, nr);
+            if (stager) raw = ld_raw(off, nr);
+            const u32x4* sK = s_ring + (ci & 1) * kSlotU4;
+            const int4 e = s_tab[bf][ci];
+            if (32 * wave < rows && !(e.x == -1 && e.y == -1)) {
+              // keys [e.z, e.z + e.w) are present (e.w < 32 only at the used length)
+              const bool full = e.w == 32 && e.z + 31 <= pmin;
+              rows_chunk<CT>(rt, sK, sK + kChunkU4, e.z, e.z + e.w, s, !full, p.scale_log2);
+            }
+            if (stager && ci + 1 < nck)
+              st_raw(raw, s_ring + ((ci + 1) & 1) * kSlotU4, s_ring + ((ci + 1) & 1) * kSlotU4 + kChunkU4);
+            __syncthreads();
+          }
         }
       } else {
         // chunks not brought in by the previous item's loop
